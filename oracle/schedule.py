@@ -1,0 +1,248 @@
+"""Integer-time pipeline schedule simulator.  TEST INFRASTRUCTURE ONLY.
+
+Model ([Guide] "Mathematical Modeling: Bubble Fractions, Memory Bounds,
+and Speedups" and "The Mechanics of Pipeline Bubbles"):
+
+* p stages, m microbatches, integer op costs (cF, cB, cW); the model has no
+  communication term, so a dependency is satisfied the instant it ends.
+* Dependencies: F(i,j) after F(i-1,j);  B(i,j) after F(i,j) and B(i+1,j);
+  W(i,j) after B(i,j).
+* GPipe and 1F1B keep the backward atomic ([Guide] "Core Innovation 1",
+  the "Backward Decomposition" box): one op "BW" of cost cB + cW, and the
+  upstream stage's backward waits for the whole of it.
+* GPipe ("1. The GPipe Bubble"): each stage runs F0..F(m-1), then the
+  backwards in ascending microbatch order.
+* 1F1B ("2. The 1F1B Schedule" and the "Conventional 1F1B" figure): stage i
+  runs w = min(p-1-i, m) warm-up forwards, then pairs (F(w+k), BW(k)), then
+  the remaining backwards.  Every op starts at max(stage free, deps done).
+* ZB(M) greedy ("Core Innovation 2" and the scheduler listing): event
+  driven.  At each completion time all completions are applied first; then
+  every idle stage picks, in order:
+    1. the lowest-microbatch ready B;
+    2. else the lowest-microbatch ready F if its active count < M
+       (the count then rises by one);
+    3. else the lowest-microbatch ready W (the count then falls by one --
+       the W releases that microbatch's stashed activations);
+    4. else it stays idle until the next completion.
+  The listing's fourth rule (start a forward regardless of the limit) is
+  dropped: it contradicts the hard ceiling on in-flight activations stated
+  under "Memory Management & Activation Rollback".  [Ghost]'s prose ranks F
+  above B, but both code listings (the [Guide] scheduler and [Ghost]'s
+  "The Code Behind the Curtain") try B first; the code is followed.
+
+Results are exact (``fractions.Fraction``).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from fractions import Fraction
+from typing import Dict, List, Tuple
+
+GPIPE, ONE_F_ONE_B, ZB = "gpipe", "1f1b", "zb"
+
+
+@dataclass
+class Op:
+    type: str      # "F", "B", "W" ("B" of an atomic backward is followed by its "W")
+    mb: int
+    start: int
+    end: int
+
+
+@dataclass
+class StageStats:
+    busy: int
+    first_start: int
+    last_end: int
+    peak_active: int
+
+    @property
+    def window(self) -> int:
+        return self.last_end - self.first_start
+
+    @property
+    def in_window_idle(self) -> Fraction:
+        return Fraction(self.window - self.busy, self.window)
+
+
+@dataclass
+class Result:
+    kind: str
+    p: int
+    m: int
+    M: int
+    costs: Tuple[int, int, int]
+    ops: List[List[Op]]                 # per stage, in execution order
+    stats: List[StageStats]
+    makespan: int
+    arrive_f: List[List[int]] = field(default_factory=list)   # [stage][mb]
+    arrive_b: List[List[int]] = field(default_factory=list)
+
+    def idle_over_makespan(self, i: int) -> Fraction:
+        return Fraction(self.makespan - self.stats[i].busy, self.makespan)
+
+    def idle_over_busy(self, i: int) -> Fraction:
+        return Fraction(self.makespan - self.stats[i].busy, self.stats[i].busy)
+
+    def order(self, i: int) -> List[Tuple[str, int]]:
+        return [(o.type, o.mb) for o in self.ops[i]]
+
+
+def _fixed_orders(kind: str, p: int, m: int) -> List[List[Tuple[str, int]]]:
+    orders = []
+    for i in range(p):
+        if kind == GPIPE:
+            seq = [("F", j) for j in range(m)] + [("BW", j) for j in range(m)]
+        else:
+            w = min(p - 1 - i, m)
+            seq = [("F", j) for j in range(w)]
+            for k in range(m - w):
+                seq += [("F", w + k), ("BW", k)]
+            seq += [("BW", j) for j in range(m - w, m)]
+        orders.append(seq)
+    return orders
+
+
+def _simulate_fixed(kind, p, m, costs):
+    cF, cB, cW = costs
+    orders = _fixed_orders(kind, p, m)
+    end: Dict[Tuple[str, int, int], int] = {}
+    free = [0] * p
+    pos = [0] * p
+    placed: List[List[Tuple[str, int, int, int]]] = [[] for _ in range(p)]
+    remaining = sum(len(o) for o in orders)
+    while remaining:
+        progressed = False
+        for i in range(p):
+            while pos[i] < len(orders[i]):
+                t, j = orders[i][pos[i]]
+                if t == "F":
+                    deps = [("F", i - 1, j)] if i > 0 else []
+                    cost = cF
+                else:
+                    deps = [("F", i, j)] + ([("BW", i + 1, j)] if i < p - 1 else [])
+                    cost = cB + cW
+                if any(d not in end for d in deps):
+                    break
+                s = max([free[i]] + [end[d] for d in deps])
+                end[(t, i, j)] = s + cost
+                free[i] = s + cost
+                placed[i].append((t, j, s, s + cost))
+                pos[i] += 1
+                remaining -= 1
+                progressed = True
+        if not progressed:
+            raise RuntimeError("fixed order deadlocked")
+    ops, stats = [], []
+    for i in range(p):
+        lst, active, peak = [], 0, 0
+        for t, j, s, e in placed[i]:
+            if t == "F":
+                active += 1
+                peak = max(peak, active)
+                lst.append(Op("F", j, s, e))
+            else:
+                active -= 1
+                lst.append(Op("B", j, s, s + cB))
+                lst.append(Op("W", j, s + cB, e))
+        busy = m * (cF + cB + cW)
+        ops.append(lst)
+        stats.append(StageStats(busy, lst[0].start, lst[-1].end, peak))
+    arrive_f = [[end[("F", i - 1, j)] if i > 0 else 0 for j in range(m)] for i in range(p)]
+    arrive_b = [[end[("BW", i + 1, j)] if i < p - 1 else 0 for j in range(m)] for i in range(p)]
+    return ops, stats, arrive_f, arrive_b
+
+
+def _simulate_zb(p, m, M, costs):
+    cF, cB, cW = costs
+    cost = {"F": cF, "B": cB, "W": cW}
+    done: Dict[Tuple[str, int, int], int] = {}
+    started = {("F", i, j): False for i in range(p) for j in range(m)}
+    started.update({("B", i, j): False for i in range(p) for j in range(m)})
+    started.update({("W", i, j): False for i in range(p) for j in range(m)})
+    running: List[Tuple[int, str, int, int]] = []   # (end, type, stage, mb)
+    busy_stage = [False] * p
+    active = [0] * p
+    peak = [0] * p
+    ops: List[List[Op]] = [[] for _ in range(p)]
+    t = 0
+    total = 3 * p * m
+    n_done = 0
+    while n_done < total:
+        # 1) apply every completion at time t
+        still = []
+        for (e, ty, i, j) in running:
+            if e == t:
+                done[(ty, i, j)] = e
+                busy_stage[i] = False
+                n_done += 1
+            else:
+                still.append((e, ty, i, j))
+        running = still
+        # 2) every idle stage picks an op
+        for i in range(p):
+            if busy_stage[i]:
+                continue
+            pick = None
+            for j in range(m):          # rule 1: lowest ready B
+                if (not started[("B", i, j)] and ("F", i, j) in done
+                        and (i == p - 1 or ("B", i + 1, j) in done)):
+                    pick = ("B", j)
+                    break
+            if pick is None and active[i] < M:   # rule 2: lowest ready F
+                for j in range(m):
+                    if not started[("F", i, j)] and (i == 0 or ("F", i - 1, j) in done):
+                        pick = ("F", j)
+                        break
+            if pick is None:               # rule 3: lowest ready W
+                for j in range(m):
+                    if not started[("W", i, j)] and ("B", i, j) in done:
+                        pick = ("W", j)
+                        break
+            if pick is None:
+                continue
+            ty, j = pick
+            started[(ty, i, j)] = True
+            if ty == "F":
+                active[i] += 1
+                peak[i] = max(peak[i], active[i])
+            elif ty == "W":
+                active[i] -= 1
+            e = t + cost[ty]
+            running.append((e, ty, i, j))
+            busy_stage[i] = True
+            ops[i].append(Op(ty, j, t, e))
+        if n_done == total:
+            break
+        if not running:
+            raise RuntimeError("zero-bubble greedy deadlocked (memory limit too small?)")
+        t = min(e for (e, _, _, _) in running)
+    stats = []
+    for i in range(p):
+        busy = sum(o.end - o.start for o in ops[i])
+        stats.append(StageStats(busy, ops[i][0].start, ops[i][-1].end, peak[i]))
+    arrive_f = [[done[("F", i - 1, j)] if i > 0 else 0 for j in range(m)] for i in range(p)]
+    arrive_b = [[done[("B", i + 1, j)] if i < p - 1 else 0 for j in range(m)] for i in range(p)]
+    return ops, stats, arrive_f, arrive_b
+
+
+def simulate(kind: str, p: int, m: int, M: int = 0, costs=(1, 1, 1)) -> Result:
+    """Simulate one iteration of a p-stage pipeline over m microbatches.
+
+    kind: "gpipe", "1f1b" or "zb" (M = memory limit in microbatches, p..2p
+    on the pages; any M >= 1 is accepted).  Costs are integers with
+    cF >= 1 and cB >= 1; cW >= 0 for the atomic schedules and >= 1 for zb.
+    """
+    cF, cB, cW = (int(c) for c in costs)
+    if p < 1 or m < 1 or cF < 1 or cB < 1 or cW < 0:
+        raise ValueError("bad arguments")
+    if kind in (GPIPE, ONE_F_ONE_B):
+        ops, stats, af, ab = _simulate_fixed(kind, p, m, (cF, cB, cW))
+    elif kind == ZB:
+        if M < 1 or cW < 1:
+            raise ValueError("zb needs M >= 1 and cW >= 1")
+        ops, stats, af, ab = _simulate_zb(p, m, M, (cF, cB, cW))
+    else:
+        raise ValueError(kind)
+    makespan = max(s.last_end for s in stats)
+    return Result(kind, p, m, M, (cF, cB, cW), ops, stats, makespan, af, ab)

@@ -1,0 +1,166 @@
+"""Pins for the schedule simulator (CPU only): the pages' closed forms and
+printed table values, plus an independent rule checker that re-derives the
+greedy rules and the dependencies from the simulator's op list alone."""
+import os
+from fractions import Fraction
+
+import pytest
+
+from oracle.schedule import simulate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+COSTS = [(1, 1, 1), (1, 2, 0), (2, 3, 1), (3, 5, 2)]
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+@pytest.mark.parametrize("kind", ["gpipe", "1f1b"])
+def test_atomic_schedules_closed_forms(kind):
+    """[Guide]: GPipe and 1F1B bubble = (p-1)/(m+p-1) of the makespan, i.e.
+    (p-1)/m of the busy time, for every stage."""
+    for costs in COSTS:
+        for p in range(2, 13):
+            for m in range(1, 49):
+                r = simulate(kind, p, m, costs=costs)
+                for i in range(p):
+                    assert r.idle_over_makespan(i) == Fraction(p - 1, m + p - 1)
+                    assert r.idle_over_busy(i) == Fraction(p - 1, m)
+
+
+def test_printed_1f1b_table():
+    for p, m, pct in _rows("guide_1f1b_bubble_table.txt"):
+        r = simulate("1f1b", int(p), int(m))
+        assert round(float(r.idle_over_makespan(0)) * 100, 1) == float(pct)
+
+
+def test_printed_closed_form_values():
+    for kind, p, m, num, den, what in _rows("guide_closed_forms.txt"):
+        r = simulate(kind, int(p), int(m))
+        got = r.idle_over_makespan(0) if what == "idle_over_makespan" else r.idle_over_busy(0)
+        assert got == Fraction(int(num), int(den))
+
+
+def test_1f1b_peak_memory_bounded_by_p():
+    """[Guide] "2. The 1F1B Schedule": peak activation memory <= p."""
+    for p in range(2, 10):
+        for m in range(1, 30):
+            r = simulate("1f1b", p, m)
+            for i in range(p):
+                assert r.stats[i].peak_active == min(p - i, m)
+
+
+def test_zb_2p_bubble_closed_form_and_zero_in_window():
+    """[Guide] "2. Zero-Bubble ZB-1F1B Bubble Duration" and "ZB-2p": for
+    m >= 2p the bubble is (p-1)/(3m) of the busy time and ZB-2p leaves no
+    idle time between a stage's first and last op."""
+    for p in range(2, 13):
+        for m in range(2 * p, 49):
+            r = simulate("zb", p, m, M=2 * p)
+            for i in range(p):
+                assert r.idle_over_busy(i) == Fraction(p - 1, 3 * m)
+                assert r.stats[i].in_window_idle == 0
+
+
+def test_zb_makespan_equals_lower_bound_at_2p():
+    r = simulate("zb", 8, 16, M=16)
+    assert r.makespan == 7 * 1 + 16 * 3 == 55
+
+
+def _check_valid_and_greedy(r):
+    """Independent checker: dependencies, no overlap, memory limit, and for
+    zb the greedy priority rule at every decision instant."""
+    p, m, M = r.p, r.m, r.M
+    cF, cB, cW = r.costs
+    end = {}
+    start = {}
+    for i in range(p):
+        for o in r.ops[i]:
+            end[(o.type, i, o.mb)] = o.end
+            start[(o.type, i, o.mb)] = o.start
+    for i in range(p):
+        ops = r.ops[i]
+        assert sorted((o.type, o.mb) for o in ops) == sorted(
+            [(t, j) for t in "FBW" for j in range(m)])
+        for a, b in zip(ops, ops[1:]):
+            assert a.end <= b.start
+        for o in ops:
+            if o.type == "F" and i > 0:
+                assert start[("F", i, o.mb)] >= end[("F", i - 1, o.mb)]
+            if o.type == "B":
+                assert o.start >= end[("F", i, o.mb)]
+                if i < p - 1:
+                    assert o.start >= end[("B", i + 1, o.mb)] if r.kind == "zb" else True
+            if o.type == "W":
+                assert o.start >= end[("B", i, o.mb)]
+    if r.kind != "zb":
+        return
+    for i in range(p):
+        active = 0
+        ops = r.ops[i]
+        decision_times = sorted({0} | {e for (t, s, j), e in end.items()})
+        k = 0
+        free_at = 0
+        for t in decision_times:
+            if t < free_at:
+                continue
+            # state of this stage at time t, from the op list only
+            fdone = lambda s, j: end.get(("F", s, j), 1 << 60) <= t
+            bdone = lambda s, j: end.get(("B", s, j), 1 << 60) <= t
+            started = {(o.type, o.mb) for o in ops if o.start < t}
+            act = sum(1 for o in ops if o.start < t and o.type == "F") - \
+                sum(1 for o in ops if o.start < t and o.type == "W")
+            readyB = [j for j in range(m) if ("B", j) not in started and fdone(i, j)
+                      and (i == p - 1 or bdone(i + 1, j))]
+            readyF = [j for j in range(m) if ("F", j) not in started and (i == 0 or fdone(i - 1, j))]
+            readyW = [j for j in range(m) if ("W", j) not in started and bdone(i, j)]
+            if readyB:
+                want = ("B", min(readyB))
+            elif readyF and act < M:
+                want = ("F", min(readyF))
+            elif readyW:
+                want = ("W", min(readyW))
+            else:
+                want = None
+            at_t = [o for o in ops if o.start == t]
+            if want is None:
+                assert not at_t
+            else:
+                assert len(at_t) == 1 and (at_t[0].type, at_t[0].mb) == want, (i, t, want, at_t)
+                free_at = at_t[0].end
+        assert max(0, act) <= M
+        assert r.stats[i].peak_active <= M
+
+
+@pytest.mark.parametrize("costs", [(1, 1, 1), (2, 3, 1), (3, 2, 2), (1, 1, 3)])
+def test_zb_greedy_rule_checker(costs):
+    for p in (2, 3, 4, 6):
+        for m in (1, 3, 2 * p, 2 * p + 3):
+            for M in range(p, 2 * p + 1):
+                _check_valid_and_greedy(simulate("zb", p, m, M=M, costs=costs))
+
+
+def test_atomic_schedules_valid():
+    for kind in ("gpipe", "1f1b"):
+        for p in (2, 5):
+            for m in (1, 4, 9):
+                _check_valid_and_greedy(simulate(kind, p, m, costs=(2, 3, 1)))
+
+
+def test_1f1b_stage_order_matches_figure():
+    """[Guide] "Conventional 1F1B Pipeline Schedule" figure (p = 4)."""
+    r = simulate("1f1b", 4, 8)
+    fig = {0: "F0 F1 F2 F3 B0 F4 B1 F5 B2", 1: "F0 F1 F2 B0 F3 B1 F4 B2",
+           2: "F0 F1 B0 F2 B1 F3 B2", 3: "F0 B0 F1 B1 F2 B2"}
+    for i, want in fig.items():
+        got = " ".join(f"{t}{j}" for t, j in r.order(i) if t != "W")
+        assert got.startswith(want)
+
+
+def test_zb_memory_limit_respected_and_deadlock_free():
+    for p in range(2, 9):
+        for M in range(p, 2 * p + 1):
+            r = simulate("zb", p, 3 * p, M=M)
+            assert all(s.peak_active <= M for s in r.stats)
