@@ -1,0 +1,245 @@
+/*
+ * zb.h -- C ABI of the split-backward pipeline stage library (libzb.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One pipeline stage of a transformer, with the backward pass split in two
+ * (the split is the subject of "Zero-Bubble Pipeline Parallelism Guide for
+ * LLMs", section "Core Innovation 1: Mathematical Decomposition of the
+ * Backward Pass", and of the arXiv abstract page "Zero Bubble Pipeline
+ * Parallelism"):
+ *
+ *   F : Y  = X . W^T                  (forward; stashes what B and W need)
+ *   B : dX = dY . W  (+ activation backward)   critical path, sent upstream
+ *   W : dW += dY^T . X  (fp32, in place)       local, deferrable
+ *
+ * The stage API mirrors the Guide's "Step-by-Step Implementation" listing
+ * (forward_microbatch / backward_input_bx / backward_weight_bw); the schedule
+ * generator follows the Guide's scheduler listing and "Core Innovation 2".
+ *
+ * Conventions for every call below
+ * --------------------------------
+ * - Pointers named "device" point to HIP device memory the CALLER owns and
+ *   keeps alive for as long as the library may touch it (weights, dW,
+ *   workspace: until zb_stage_destroy; x/y/dx/dy: until the stream work of
+ *   the call has finished).  The library allocates no device memory.
+ * - Weights are stored [out, in], row-major (PyTorch's linear layout); the
+ *   Guide's Y = X.W uses W_eq = W^T.  Activations are [tokens, features],
+ *   row-major, contiguous.  bf16 is IEEE bfloat16 bit patterns.
+ * - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *   Compute calls only enqueue work and return; errors that are known when
+ *   the call is made are returned at once and nothing is enqueued.
+ *   Device-side failures surface as ZB_EHIP from a later call.
+ * - zb_last_error() returns a thread-local message for the last failure.
+ * - A zb_stage is not thread safe: issue its calls from one host thread.
+ */
+#ifndef ZB_H_
+#define ZB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct zb_stage zb_stage;
+
+enum {
+    ZB_OK = 0,
+    ZB_EINVAL = -1,        /* bad argument or unsupported shape              */
+    ZB_ESTATE = -2,        /* op out of order for this microbatch            */
+    ZB_ERING_FULL = -3,    /* F would exceed the stash ring (memory limit)   */
+    ZB_EHIP = -4,          /* a HIP runtime call failed                      */
+    ZB_ENOMEM = -5         /* workspace smaller than zb_stage_workspace_bytes */
+};
+
+enum { ZB_F32 = 0, ZB_BF16 = 1 };
+
+/* Stage kinds.
+ *  ZB_LINEAR   one layer Y = X W^T; in = hidden, out = ffn.  Weight list: {W[ffn,hidden]}.
+ *  ZB_MLP_GELU fc1 -> GeLU(tanh) -> fc2, no bias.  Weights {W1[ffn,hidden], W2[hidden,ffn]}.
+ *  ZB_LLAMA    n_layers pre-norm decoder layers: RMSNorm, causal GQA
+ *              attention (no RoPE), residual, RMSNorm, SwiGLU MLP, residual.
+ *              Weights per layer l, in this order:
+ *                Wqkv[(n_heads+2*n_kv_heads)*head_dim, hidden] (rows: q | k | v),
+ *                Wo[hidden, n_heads*head_dim], Wgu[2*ffn, hidden] (rows: gate | up),
+ *                Wd[hidden, ffn], g1[hidden], g2[hidden] (RMSNorm gains). */
+enum { ZB_LINEAR = 0, ZB_MLP_GELU = 1, ZB_LLAMA = 2 };
+
+typedef struct {
+    int32_t kind;        /* ZB_LINEAR / ZB_MLP_GELU / ZB_LLAMA                    */
+    int32_t dtype;       /* ZB_F32 (ZB_LINEAR only) or ZB_BF16                     */
+    int32_t n_layers;    /* ZB_LLAMA: decoder layers; otherwise 1                  */
+    int32_t tokens;      /* T = batch * sequence length of one microbatch          */
+    int32_t hidden;      /* model width h                                         */
+    int32_t ffn;         /* MLP width (ZB_LINEAR: output width)                   */
+    int32_t n_heads;     /* ZB_LLAMA: query heads                                  */
+    int32_t n_kv_heads;  /* ZB_LLAMA: key/value heads; n_heads % n_kv_heads == 0    */
+    int32_t head_dim;    /* ZB_LLAMA: must be 128                                  */
+    float rms_eps;       /* ZB_LLAMA: RMSNorm epsilon (inside the square root)     */
+    int32_t ring_slots;  /* R: microbatches whose activations may be stashed at once */
+} zb_stage_desc;
+
+/* Number of weight tensors of a stage (and of dW buffers): 1, 2 or 6*n_layers. */
+int32_t zb_stage_num_weights(const zb_stage_desc* desc);
+
+/* Bytes of device workspace zb_stage_create needs: the stash ring
+ * (ring_slots slots) plus per-pass scratch.  Returns 0 for an invalid desc
+ * (zb_last_error says why). */
+size_t zb_stage_workspace_bytes(const zb_stage_desc* desc);
+
+/* Create a stage.  weights[i] / dw[i] are device pointers in the weight order
+ * of the kind (see above); weights are ZB_BF16 (or ZB_F32 for an fp32 linear
+ * stage), dw buffers are always fp32 of the same shape.  workspace is device
+ * memory of at least zb_stage_workspace_bytes(desc) bytes, 256-byte aligned.
+ * The library keeps the pointers (not copies).  dW is NOT cleared: call
+ * zb_stage_zero_grad before the first W of an iteration.
+ * Errors: ZB_EINVAL (desc/shape), ZB_ENOMEM (ws_bytes too small), ZB_EHIP. */
+int32_t zb_stage_create(const zb_stage_desc* desc, void* const* weights, float* const* dw,
+                        void* workspace, size_t ws_bytes, zb_stage** out);
+
+/* Release host state (events).  Waits for no device work: synchronize the
+ * streams first.  NULL is accepted. */
+void zb_stage_destroy(zb_stage* st);
+
+/* F for microbatch mb (Guide listing: forward_microbatch).  x: device [T, hidden]
+ * (caller's, read during the call's stream work), y: device [T, out]
+ * (out = hidden, or ffn for ZB_LINEAR).  Stashes into ring slot mb % R
+ * everything B and W need (a copy of x included).
+ * Errors: ZB_EINVAL (mb < 0, NULL pointers); ZB_ESTATE (F(mb) already issued
+ * or mb not the next in ascending order); ZB_ERING_FULL (slot mb % R still
+ * holds a microbatch whose W has not been issued -- the memory ceiling of
+ * the Guide's "Memory Management & Activation Rollback").  If the slot's
+ * previous W was issued on another stream, F waits for it on the device. */
+int32_t zb_fwd(zb_stage* st, int32_t mb, const void* x, void* y, void* stream);
+
+/* B for microbatch mb (Guide listing: backward_input_bx).  dy: device
+ * [T, out] output gradient, dx: device [T, hidden] input gradient.  Fuses the
+ * activation backward (GeLU / SwiGLU) and, for ZB_LLAMA, RMSNorm and
+ * attention backward.  Stashes the output gradients W needs.
+ * Errors: ZB_ESTATE unless F(mb) was issued and B(mb) was not. */
+int32_t zb_bwd_input(zb_stage* st, int32_t mb, const void* dy, void* dx, void* stream);
+
+/* W for microbatch mb (Guide listing: backward_weight_bw):
+ * dW[i] += (this microbatch's weight gradient), fp32, deterministic (no
+ * atomics; calls add in issue order).  Frees ring slot mb % R once the
+ * device work has completed.  W must be issued in ascending mb order.
+ * Errors: ZB_ESTATE unless B(mb) was issued and W(mb) was not, or mb is not
+ * the next W in ascending order. */
+int32_t zb_bwd_weight_accum(zb_stage* st, int32_t mb, void* stream);
+
+/* Set every dW buffer to 0 (a fill kernel on stream) and reset the
+ * microbatch counters for a new iteration.  Errors: ZB_ESTATE if a
+ * microbatch is still in flight (F issued, W not). */
+int32_t zb_stage_zero_grad(zb_stage* st, void* stream);
+
+/* Device pointer of a stashed tensor, for inspection by tests: ring slot of
+ * microbatch mb, decoder layer (0 for the other kinds), tensor index
+ * (kind-specific, see the library's stash table).  Writes rows/cols/dtype.
+ * Valid between F(mb) (or B(mb) for gradients) and W(mb). */
+int32_t zb_stage_stash_tensor(zb_stage* st, int32_t mb, int32_t layer, int32_t which,
+                              void** ptr, int32_t* rows, int32_t* cols, int32_t* dtype);
+
+/* ------------------------------------------------------------ schedules -- */
+
+/* Op of a per-stage schedule (the Guide scheduler listing's task types). */
+enum { ZB_OP_F = 0, ZB_OP_B = 1, ZB_OP_W = 2 };
+typedef struct { int32_t type; int32_t mb; } zb_op;
+
+/* Schedule kinds: GPipe and 1F1B with the backward kept whole (each B is
+ * followed at once by its W), and the memory-limited zero-bubble greedy. */
+enum { ZB_SCHED_GPIPE = 0, ZB_SCHED_1F1B = 1, ZB_SCHED_ZB = 2 };
+
+typedef struct {
+    int64_t makespan;      /* pipeline makespan (all stages), cost units   */
+    int64_t busy;          /* this stage's busy time                       */
+    int64_t first_start;   /* this stage's first op start                  */
+    int64_t last_end;      /* this stage's last op end                     */
+    int32_t peak_active;   /* most microbatches stashed at once            */
+    int32_t n_ops;         /* 3 * m                                        */
+} zb_sched_stats;
+
+/* Generate stage `stage`'s op order for a p-stage, m-microbatch iteration by
+ * integer-time simulation of the whole pipeline (no communication cost).
+ *   GPIPE: all F, then all backwards ("1. The GPipe Bubble").
+ *   1F1B : min(p-1-stage, m) warm-up F, then F/B pairs, then the remaining
+ *          backwards ("2. The 1F1B Schedule").
+ *   ZB   : at every completion time each idle stage takes the lowest ready
+ *          B; else the lowest ready F if fewer than mem_limit microbatches
+ *          are stashed; else the lowest ready W (which releases one); else
+ *          waits ("Core Innovation 2" and the scheduler listing, without its
+ *          unconditional-forward fallback, which would break the ceiling).
+ * Costs cF, cB >= 1; cW >= 0 (>= 1 for ZB).  Host only, no GPU needed.
+ * Outputs (each may be NULL): ops[3m], start[3m], end[3m] of this stage;
+ * arrive_f[m] = end of F(stage-1, j) (0 on stage 0), arrive_b[m] = end of the
+ * downstream backward of j (B for ZB, the whole backward otherwise; 0 on the
+ * last stage); stats.  cap = capacity of ops/start/end.
+ * Returns the number of ops (3m) or ZB_EINVAL (bad arguments, cap < 3m,
+ * mem_limit too small to make progress). */
+int32_t zb_schedule_generate(int32_t kind, int32_t p, int32_t m, int32_t mem_limit,
+                             int32_t cF, int32_t cB, int32_t cW, int32_t stage,
+                             zb_op* ops, int64_t* start, int64_t* end, int32_t cap,
+                             int64_t* arrive_f, int64_t* arrive_b, zb_sched_stats* stats);
+
+/* ------------------------------------------------------------- executor -- */
+
+enum {
+    ZB_EXEC_ORDERED = 0,  /* ops start strictly in list order (W on lo_stream,
+                             chained to its neighbours by events)            */
+    ZB_EXEC_FILLER = 1    /* W runs on lo_stream as soon as its B is done,
+                             alongside F/B on hi_stream                       */
+};
+
+typedef struct {
+    double t_first_start_ms;  /* relative to the executor's time origin      */
+    double t_last_end_ms;
+    double window_ms;         /* t_last_end - t_first_start                   */
+    double busy_ms;           /* union of op intervals                         */
+    double in_window_idle;    /* (window - busy) / window                      */
+    double wait_late_ms;      /* sum over waits of (wait end - deadline) > 0   */
+} zb_run_stats;
+
+/* Run one iteration of a stage schedule on the GPU (the "list of ops, then
+ * run" shape of the Ghost page's conceptual scheduler).  ops[n] as produced
+ * by zb_schedule_generate.  Before F(j) the high stream waits until
+ * t0 + arrive_f[j] * unit_ms, before B(j) until t0 + arrive_b[j] * unit_ms,
+ * where t0 is taken on the device when the run starts; the waits are timed
+ * with the GPU's constant-rate wall clock and always end.  x[j], dy[j] are
+ * the per-microbatch inputs, y[j], dx[j] the outputs (device, caller-owned).
+ * Both streams must be default-priority HIP streams (NULL = create and
+ * destroy private ones).  op_ms (may be NULL) receives 2*n doubles: start and
+ * end of each op in ms since t0.  Blocks until the run has finished.
+ * Errors: as the compute calls, plus ZB_EINVAL for a malformed op list. */
+int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t n,
+                              const double* arrive_f, const double* arrive_b, double unit_ms,
+                              const void* const* x, void* const* y,
+                              const void* const* dy, void* const* dx,
+                              void* hi_stream, void* lo_stream, int32_t mode,
+                              zb_run_stats* stats, double* op_ms);
+
+/* ------------------------------------------------------------- kernels --- */
+
+/* One GEMM through the stage's kernels, for kernel-level tests and timing.
+ *   C[M,N] (op)= opA(A)[M,K] . opB(B)[K,N]
+ *   a_kmajor: 1 -> A[m*lda + k], 0 -> A[k*lda + m];
+ *   b_kmajor: 1 -> B[n*ldb + k], 0 -> B[k*ldb + n];
+ *   dtype ZB_BF16: A, B bf16; out_f32 = 0 -> C bf16 (C = acc),
+ *                  out_f32 = 1 -> C fp32 and C += acc (the W-pass epilogue).
+ *   dtype ZB_F32: A, B, C fp32; out_f32 must be 1; accumulate = C += acc, else C = acc.
+ * M, N, K >= 1; bf16 needs K, and M (if a_kmajor == 0), N (if b_kmajor == 0),
+ * and every leading dimension to be multiples of 8.  Errors: ZB_EINVAL. */
+int32_t zb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K,
+                const void* A, int64_t lda, int32_t a_kmajor,
+                const void* B, int64_t ldb, int32_t b_kmajor,
+                void* C, int64_t ldc, int32_t out_f32, int32_t accumulate, void* stream);
+
+/* Thread-local description of the last error (never NULL). */
+const char* zb_last_error(void);
+
+/* Library version string. */
+const char* zb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZB_H_ */

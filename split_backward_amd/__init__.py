@@ -1,0 +1,289 @@
+"""Python binding of libzb (the split-backward pipeline stage for MI355X).
+
+Argument marshalling only: every step of F, B and W runs in the HIP kernels
+of libzb.so.  PyTorch supplies device memory (tensors) and streams; tensors
+are passed to the C ABI as raw device pointers.  If libzb.so is missing the
+import of this module still works, but every call raises -- there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzb.so")
+
+# ---- constants mirrored from include/zb.h ---------------------------------
+OK, EINVAL, ESTATE, ERING_FULL, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+LINEAR, MLP_GELU, LLAMA = 0, 1, 2
+OP_F, OP_B, OP_W = 0, 1, 2
+SCHED_GPIPE, SCHED_1F1B, SCHED_ZB = 0, 1, 2
+EXEC_ORDERED, EXEC_FILLER = 0, 1
+
+KIND = {"linear": LINEAR, "mlp": MLP_GELU, "llama": LLAMA}
+SCHED = {"gpipe": SCHED_GPIPE, "1f1b": SCHED_1F1B, "zb": SCHED_ZB}
+OPNAME = {OP_F: "F", OP_B: "B", OP_W: "W"}
+
+# stash tensor indices ("which")
+LIN_X, LIN_DY = 0, 1
+MLP_X, MLP_A, MLP_H, MLP_DY, MLP_DA = 0, 1, 2, 3, 4
+(L_X, L_R1, L_N1, L_QKV, L_A, L_LSE, L_H1, L_R2, L_N2, L_GU, L_S,
+ L_DOUT, L_DGU, L_DN2, L_DH1, L_DQKV, L_DN1) = range(17)
+
+
+class ZbError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libzb error {code}: {msg}")
+        self.code = code
+
+
+class StageDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("dtype", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("ring_slots", ctypes.c_int32)]
+
+
+class Op(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int32), ("mb", ctypes.c_int32)]
+
+
+class SchedStats(ctypes.Structure):
+    _fields_ = [("makespan", ctypes.c_int64), ("busy", ctypes.c_int64), ("first_start", ctypes.c_int64),
+                ("last_end", ctypes.c_int64), ("peak_active", ctypes.c_int32), ("n_ops", ctypes.c_int32)]
+
+
+class RunStats(ctypes.Structure):
+    _fields_ = [("t_first_start_ms", ctypes.c_double), ("t_last_end_ms", ctypes.c_double),
+                ("window_ms", ctypes.c_double), ("busy_ms", ctypes.c_double),
+                ("in_window_idle", ctypes.c_double), ("wait_late_ms", ctypes.c_double)]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_PROTOS = {
+    "zb_stage_num_weights": (_i32, [ctypes.POINTER(StageDesc)]),
+    "zb_stage_workspace_bytes": (_sz, [ctypes.POINTER(StageDesc)]),
+    "zb_stage_create": (_i32, [ctypes.POINTER(StageDesc), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _sz,
+                               ctypes.POINTER(_vp)]),
+    "zb_stage_destroy": (None, [_vp]),
+    "zb_fwd": (_i32, [_vp, _i32, _vp, _vp, _vp]),
+    "zb_bwd_input": (_i32, [_vp, _i32, _vp, _vp, _vp]),
+    "zb_bwd_weight_accum": (_i32, [_vp, _i32, _vp]),
+    "zb_stage_zero_grad": (_i32, [_vp, _vp]),
+    "zb_stage_stash_tensor": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
+                                     ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "zb_schedule_generate": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Op),
+                                    ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, ctypes.POINTER(_i64),
+                                    ctypes.POINTER(_i64), ctypes.POINTER(SchedStats)]),
+    "zb_stage_run_schedule": (_i32, [_vp, ctypes.POINTER(Op), _i32, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.c_double, ctypes.POINTER(_vp),
+                                     ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _vp, _i32,
+                                     ctypes.POINTER(RunStats), ctypes.POINTER(ctypes.c_double)]),
+    "zb_gemm": (_i32, [_i32, _i32, _i32, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _vp]),
+    "zb_last_error": (ctypes.c_char_p, []),
+    "zb_version": (ctypes.c_char_p, []),
+}
+EXPORTS = tuple(_PROTOS)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libzb.so once.  Raises if it has not been built: there is no
+    fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m split_backward_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def last_error() -> str:
+    return lib().zb_last_error().decode()
+
+
+def check(rc: int) -> int:
+    if rc < 0:
+        raise ZbError(rc, last_error())
+    return rc
+
+
+# ---- schedules (host only) -------------------------------------------------
+
+def schedule_generate(kind: str, p: int, m: int, mem_limit: int = 0, costs=(1, 1, 1), stage: int = 0) -> dict:
+    """Per-stage op order from the library's generator (no GPU needed)."""
+    n = 3 * m
+    ops = (Op * n)()
+    st = (ctypes.c_int64 * n)()
+    en = (ctypes.c_int64 * n)()
+    af = (ctypes.c_int64 * m)()
+    ab = (ctypes.c_int64 * m)()
+    stats = SchedStats()
+    cnt = lib().zb_schedule_generate(SCHED[kind], p, m, mem_limit, costs[0], costs[1], costs[2], stage, ops, st,
+                                     en, n, af, ab, ctypes.byref(stats))
+    check(cnt)
+    return {
+        "ops": [(OPNAME[ops[i].type], ops[i].mb) for i in range(cnt)],
+        "start": list(st[:cnt]), "end": list(en[:cnt]),
+        "arrive_f": list(af), "arrive_b": list(ab),
+        "makespan": stats.makespan, "busy": stats.busy, "first_start": stats.first_start,
+        "last_end": stats.last_end, "peak_active": stats.peak_active,
+    }
+
+
+# ---- device side (needs torch + a GPU) -------------------------------------
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def weight_shapes(kind: str, hidden: int, ffn: int, n_layers: int = 1, n_heads: int = 1, n_kv_heads: int = 1,
+                  head_dim: int = 128) -> List[tuple]:
+    if kind == "linear":
+        return [(ffn, hidden)]
+    if kind == "mlp":
+        return [(ffn, hidden), (hidden, ffn)]
+    qd, kvd = n_heads * head_dim, n_kv_heads * head_dim
+    out = []
+    for _ in range(n_layers):
+        out += [(qd + 2 * kvd, hidden), (hidden, qd), (2 * ffn, hidden), (hidden, ffn), (hidden,), (hidden,)]
+    return out
+
+
+class Stage:
+    """One pipeline stage on the current GPU.
+
+    weights: device tensors in the kind's weight order (bf16, or fp32 for an
+    fp32 linear stage).  The fp32 dW buffers and the workspace (stash ring +
+    scratch) are allocated here with torch and handed to the library.
+    """
+
+    def __init__(self, kind: str, tokens: int, hidden: int, ffn: int, weights: Sequence, *, dtype: str = "bf16",
+                 n_layers: int = 1, n_heads: int = 1, n_kv_heads: int = 1, head_dim: int = 128,
+                 rms_eps: float = 1e-5, ring_slots: int = 2, device=None):
+        import torch
+        self.torch = torch
+        self.desc = StageDesc(KIND[kind], BF16 if dtype == "bf16" else F32, n_layers, tokens, hidden, ffn,
+                              n_heads, n_kv_heads, head_dim, rms_eps, ring_slots)
+        self.kind = kind
+        self.dtype = dtype
+        L = lib()
+        nw = check(L.zb_stage_num_weights(ctypes.byref(self.desc)))
+        if len(weights) != nw:
+            raise ValueError(f"expected {nw} weights, got {len(weights)}")
+        device = device or weights[0].device
+        self.device = device
+        want = torch.bfloat16 if dtype == "bf16" else torch.float32
+        for w in weights:
+            if w.dtype != want or not w.is_contiguous() or w.device != device:
+                raise ValueError("weights must be contiguous device tensors of the stage dtype")
+        self.weights = list(weights)
+        self.dw = [torch.zeros(w.shape, dtype=torch.float32, device=device) for w in weights]
+        nbytes = L.zb_stage_workspace_bytes(ctypes.byref(self.desc))
+        if nbytes == 0:
+            raise ZbError(EINVAL, last_error())
+        self.ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.ws.data_ptr()) % 256
+        self.ws_off = off
+        wp = (ctypes.c_void_p * nw)(*[_ptr(w) for w in self.weights])
+        dp = (ctypes.c_void_p * nw)(*[_ptr(d) for d in self.dw])
+        h = ctypes.c_void_p()
+        check(L.zb_stage_create(ctypes.byref(self.desc), wp, dp, ctypes.c_void_p(self.ws.data_ptr() + off), nbytes,
+                                ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            try:
+                self.torch.cuda.synchronize(self.device)
+            except Exception:
+                pass
+            lib().zb_stage_destroy(h)
+            self.handle = None
+
+    @property
+    def act_dtype(self):
+        return self.torch.bfloat16 if self.dtype == "bf16" else self.torch.float32
+
+    @property
+    def out_width(self) -> int:
+        return self.desc.ffn if self.kind == "linear" else self.desc.hidden
+
+    def fwd(self, mb: int, x, y=None, stream=None):
+        if y is None:
+            y = self.torch.empty((self.desc.tokens, self.out_width), dtype=self.act_dtype, device=self.device)
+        check(lib().zb_fwd(self.handle, mb, _ptr(x), _ptr(y), _stream_ptr(stream)))
+        return y
+
+    def bwd_input(self, mb: int, dy, dx=None, stream=None):
+        if dx is None:
+            dx = self.torch.empty((self.desc.tokens, self.desc.hidden), dtype=self.act_dtype, device=self.device)
+        check(lib().zb_bwd_input(self.handle, mb, _ptr(dy), _ptr(dx), _stream_ptr(stream)))
+        return dx
+
+    def bwd_weight(self, mb: int, stream=None):
+        check(lib().zb_bwd_weight_accum(self.handle, mb, _stream_ptr(stream)))
+
+    def zero_grad(self, stream=None):
+        check(lib().zb_stage_zero_grad(self.handle, _stream_ptr(stream)))
+
+    def stash(self, mb: int, layer: int, which: int):
+        """Torch view of a stashed tensor (valid until W(mb) completes)."""
+        p, r, c, dt = ctypes.c_void_p(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        check(lib().zb_stage_stash_tensor(self.handle, mb, layer, which, ctypes.byref(p), ctypes.byref(r),
+                                          ctypes.byref(c), ctypes.byref(dt)))
+        torch = self.torch
+        off = p.value - self.ws.data_ptr()
+        tdt = torch.float32 if dt.value == F32 else torch.bfloat16
+        nbytes = r.value * c.value * (4 if dt.value == F32 else 2)
+        return self.ws[off:off + nbytes].view(tdt).view(r.value, c.value)
+
+    def run_schedule(self, ops, arrive_f, arrive_b, unit_ms: float, xs, ys, dys, dxs, mode: int = EXEC_ORDERED,
+                     hi_stream=None, lo_stream=None):
+        n = len(ops)
+        opa = (Op * n)(*[Op({"F": OP_F, "B": OP_B, "W": OP_W}[t], j) for t, j in ops])
+        m = len(xs)
+        af = (ctypes.c_double * m)(*[float(a) for a in arrive_f])
+        ab = (ctypes.c_double * m)(*[float(a) for a in arrive_b])
+        P = lambda ts: (ctypes.c_void_p * m)(*[_ptr(t) for t in ts])
+        stats = RunStats()
+        op_ms = (ctypes.c_double * (2 * n))()
+        hs = hi_stream.cuda_stream if hi_stream is not None else None
+        ls = lo_stream.cuda_stream if lo_stream is not None else None
+        check(lib().zb_stage_run_schedule(self.handle, opa, n, af, ab, unit_ms, P(xs), P(ys), P(dys), P(dxs), hs, ls,
+                                          mode, ctypes.byref(stats), op_ms))
+        return {"window_ms": stats.window_ms, "busy_ms": stats.busy_ms, "in_window_idle": stats.in_window_idle,
+                "t_first_start_ms": stats.t_first_start_ms, "t_last_end_ms": stats.t_last_end_ms,
+                "wait_late_ms": stats.wait_late_ms,
+                "op_ms": [(op_ms[2 * i], op_ms[2 * i + 1]) for i in range(n)]}
+
+
+def gemm(A, B, C, *, a_kmajor: bool, b_kmajor: bool, M: int, N: int, K: int, accumulate: bool = False,
+         lda: int = None, ldb: int = None, ldc: int = None, stream=None):
+    """C (op)= opA(A) . opB(B) through the library's GEMM kernels."""
+    import torch
+    dt = F32 if A.dtype == torch.float32 else BF16
+    out_f32 = 1 if C.dtype == torch.float32 else 0
+    lda = lda if lda is not None else A.shape[-1]
+    ldb = ldb if ldb is not None else B.shape[-1]
+    ldc = ldc if ldc is not None else C.shape[-1]
+    check(lib().zb_gemm(dt, M, N, K, _ptr(A), lda, int(a_kmajor), _ptr(B), ldb, int(b_kmajor), _ptr(C), ldc,
+                        out_f32, int(accumulate), _stream_ptr(stream)))
+    return C

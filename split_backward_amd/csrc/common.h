@@ -1,0 +1,91 @@
+// Shared declarations of libzb: error reporting, launch helpers and the
+// kernel launchers each translation unit provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/zb.h"
+
+namespace zb {
+
+// ---------------------------------------------------------------- errors --
+void set_error(const std::string& msg);
+int32_t fail(int32_t code, const std::string& msg);
+
+#define ZB_HIP(expr)                                                             \
+    do {                                                                         \
+        hipError_t e_ = (expr);                                                  \
+        if (e_ != hipSuccess)                                                    \
+            return ::zb::fail(ZB_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+// Device types used by every kernel file.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// ------------------------------------------------------------ GEMM API ----
+// Epilogues of the bf16 MFMA GEMM.  acc is the fp32 tile of A.B.
+enum Epi : int {
+    EPI_STORE = 0,        // C(bf16) = acc
+    EPI_RESID = 1,        // C(bf16) = acc + R(bf16)                    (residual add)
+    EPI_ACCUM_F32 = 2,    // C(f32) += acc                              (W pass)
+    EPI_GELU_FWD = 3,     // C(bf16) = acc (pre-activation), C2(bf16) = gelu_tanh(acc)
+    EPI_GELU_BWD = 4,     // C(bf16) = acc * gelu_tanh'(R)              (R = stashed pre-activation)
+    EPI_SWIGLU_FWD = 5,   // paired tiles: C = [g | u] (bf16), C2 = silu(g) * u (bf16)
+    EPI_SWIGLU_BWD = 6,   // acc = ds; R = [g | u]; C = [dg | du] (bf16)
+};
+
+struct GemmDesc {
+    int M, N, K;
+    const void* A; int64_t lda; int a_kmajor;   // opA[m][k] = a_kmajor ? A[m*lda+k] : A[k*lda+m]
+    const void* B; int64_t ldb; int b_kmajor;   // opB[k][n] = b_kmajor ? B[n*ldb+k] : B[k*ldb+n]
+    void* C; int64_t ldc;
+    int epi;
+    const void* R; int64_t ldr;                // residual / stash operand of the epilogue
+    void* C2; int64_t ldc2;                    // second output of the epilogue
+    int half_n;                                // EPI_SWIGLU_*: width of g (= ffn)
+};
+
+int32_t gemm_bf16(const GemmDesc& d, hipStream_t s);
+int32_t gemm_f32(const GemmDesc& d, int accumulate, hipStream_t s);
+
+// ------------------------------------------------- elementwise / norms ----
+int32_t fill_f32(float* p, size_t n, float v, hipStream_t s);
+int32_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
+// n = RMS(x) * g, r = 1/sqrt(mean(x^2)+eps) per row; x, n bf16 [T, H]; r f32 [T].
+int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps,
+                    hipStream_t s);
+// dx = dres + r * (dn*g - xhat * mean(dn*g*xhat)), xhat = x*r.
+int32_t rmsnorm_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn,
+                    const bf16_t* dres, bf16_t* dx, int T, int H, hipStream_t s);
+// dgamma[h] += sum_t dn[t,h] * x[t,h] * r[t]   (partials in scratch, fixed order)
+int32_t rmsnorm_dgamma(const bf16_t* x, const float* r, const bf16_t* dn, float* dgamma,
+                       float* scratch, int T, int H, hipStream_t s);
+size_t rmsnorm_dgamma_scratch_floats(int T, int H);
+
+// -------------------------------------------------------------- attention --
+// Causal GQA attention, head_dim 128.  q/k/v are column blocks of the packed
+// qkv [T, (nq + 2 nkv) * 128] buffer; o [T, nq*128]; lse f32 [nq, T].
+int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s);
+// dqkv [T, (nq + 2 nkv)*128]; delta scratch f32 [nq, T].
+int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout,
+                 bf16_t* dqkv, float* delta, int T, int nq, int nkv, hipStream_t s);
+
+// --------------------------------------------------------------- timing ---
+int32_t stamp_now(uint64_t* dst, hipStream_t s);
+int32_t wait_until(const uint64_t* t0, uint64_t delta_ticks, uint64_t* wait_end, hipStream_t s);
+uint64_t wall_clock_hz();
+
+}  // namespace zb

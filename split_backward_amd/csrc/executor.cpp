@@ -1,0 +1,164 @@
+// One-GPU stage executor: replays a generated per-stage schedule with the
+// arrivals of upstream activations and downstream gradients emulated by GPU
+// waits on the device's constant-rate wall clock.
+//
+// F and B (the critical path of the Guide's "Core Innovation 1") run on the
+// high stream behind their arrival waits; W runs on the low (filler) stream
+// ("Core Innovation 2": W fills what would otherwise be idle time).  Both
+// streams keep the default priority; the ordering the schedule asks for is
+// enforced with events instead:
+//   ORDERED: every op waits for the end of the op before it in the list, so
+//            the GPU executes exactly the generated order.
+//   FILLER:  W waits only for its own B (and F of a reused ring slot waits
+//            for the W that frees it), so W soaks up whatever gaps remain.
+// Each op is bracketed by two clock-stamp kernels; idle time is the part of
+// the stage's window [first op start, last op end] that no op interval covers.
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "common.h"
+#include "stage.h"
+
+using namespace zb;
+
+namespace {
+
+struct StreamGuard {
+    hipStream_t s = nullptr;
+    bool own = false;
+    ~StreamGuard() {
+        if (own && s) (void)hipStreamDestroy(s);
+    }
+};
+
+struct EventPool {
+    std::vector<hipEvent_t> ev;
+    ~EventPool() {
+        for (auto e : ev) (void)hipEventDestroy(e);
+    }
+};
+
+}  // namespace
+
+extern "C" int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t n, const double* arrive_f,
+                                         const double* arrive_b, double unit_ms, const void* const* x, void* const* y,
+                                         const void* const* dy, void* const* dx, void* hi_stream, void* lo_stream,
+                                         int32_t mode, zb_run_stats* stats, double* op_ms) {
+    if (!st || !ops || n < 1 || n > MAX_RUN_OPS || !arrive_f || !arrive_b || !(unit_ms >= 0.0) || !x || !y || !dy ||
+        !dx)
+        return fail(ZB_EINVAL, "zb_stage_run_schedule: bad argument");
+    if (mode != ZB_EXEC_ORDERED && mode != ZB_EXEC_FILLER) return fail(ZB_EINVAL, "zb_stage_run_schedule: bad mode");
+    int nmb = 0;
+    for (int k = 0; k < n; ++k) {
+        if (ops[k].type < ZB_OP_F || ops[k].type > ZB_OP_W || ops[k].mb < 0)
+            return fail(ZB_EINVAL, "zb_stage_run_schedule: malformed op " + std::to_string(k));
+        nmb = std::max(nmb, ops[k].mb + 1);
+    }
+    for (int j = 0; j < nmb; ++j)
+        if (!(arrive_f[j] >= 0.0) || !(arrive_b[j] >= 0.0) || arrive_f[j] > 1e6 || arrive_b[j] > 1e6)
+            return fail(ZB_EINVAL, "zb_stage_run_schedule: arrival times must be in [0, 1e6] units");
+
+    StreamGuard hi, lo;
+    hi.s = static_cast<hipStream_t>(hi_stream);
+    lo.s = static_cast<hipStream_t>(lo_stream);
+    if (!hi.s) {
+        ZB_HIP(hipStreamCreateWithFlags(&hi.s, hipStreamNonBlocking));
+        hi.own = true;
+    }
+    if (!lo.s) {
+        ZB_HIP(hipStreamCreateWithFlags(&lo.s, hipStreamNonBlocking));
+        lo.own = true;
+    }
+    EventPool pool;
+    pool.ev.resize(n + 1, nullptr);
+    for (auto& e : pool.ev) ZB_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+
+    const double hz = (double)wall_clock_hz();
+    const double ticks_per_ms = hz / 1000.0;
+    uint64_t* t0 = st->stamps;
+    uint64_t* stamp = st->stamps + 1;           // 2 per op
+    uint64_t* wait_end = st->stamps + 1 + 2 * n;  // 1 per op
+
+    int32_t rc = stamp_now(t0, hi.s);
+    if (rc) return rc;
+    ZB_HIP(hipEventRecord(pool.ev[n], hi.s));
+    ZB_HIP(hipStreamWaitEvent(lo.s, pool.ev[n], 0));
+
+    int prev = -1;
+    hipStream_t prev_stream = nullptr;
+    for (int k = 0; k < n && rc == ZB_OK; ++k) {
+        const zb_op op = ops[k];
+        const bool is_w = op.type == ZB_OP_W;
+        hipStream_t s = is_w ? lo.s : hi.s;
+        if (mode == ZB_EXEC_ORDERED && prev >= 0 && prev_stream != s) {
+            hipError_t e = hipStreamWaitEvent(s, pool.ev[prev], 0);
+            if (e != hipSuccess) { rc = fail(ZB_EHIP, "hipStreamWaitEvent failed"); break; }
+        }
+        if (!is_w) {
+            const double a = op.type == ZB_OP_F ? arrive_f[op.mb] : arrive_b[op.mb];
+            const uint64_t delta = (uint64_t)std::llround(a * unit_ms * ticks_per_ms);
+            rc = wait_until(t0, delta, wait_end + k, s);
+            if (rc) break;
+        }
+        rc = stamp_now(stamp + 2 * k, s);
+        if (rc) break;
+        if (op.type == ZB_OP_F) rc = zb_fwd(st, op.mb, x[op.mb], y[op.mb], s);
+        else if (op.type == ZB_OP_B) rc = zb_bwd_input(st, op.mb, dy[op.mb], dx[op.mb], s);
+        else rc = zb_bwd_weight_accum(st, op.mb, s);
+        if (rc) break;
+        rc = stamp_now(stamp + 2 * k + 1, s);
+        if (rc) break;
+        hipError_t e = hipEventRecord(pool.ev[k], s);
+        if (e != hipSuccess) { rc = fail(ZB_EHIP, "hipEventRecord failed"); break; }
+        prev = k;
+        prev_stream = s;
+    }
+    // Drain both streams whether or not the issue loop completed.
+    hipError_t e1 = hipStreamSynchronize(hi.s);
+    hipError_t e2 = hipStreamSynchronize(lo.s);
+    if (rc) return rc;
+    if (e1 != hipSuccess || e2 != hipSuccess) return fail(ZB_EHIP, "stream synchronize failed after the run");
+
+    std::vector<uint64_t> host(1 + 3 * (size_t)n);
+    ZB_HIP(hipMemcpy(host.data(), st->stamps, host.size() * sizeof(uint64_t), hipMemcpyDeviceToHost));
+    const uint64_t base = host[0];
+    auto ms = [&](uint64_t t) { return ((double)(int64_t)(t - base)) / ticks_per_ms; };
+    std::vector<std::pair<double, double>> iv(n);
+    double late = 0.0;
+    for (int k = 0; k < n; ++k) {
+        iv[k] = {ms(host[1 + 2 * k]), ms(host[2 + 2 * k])};
+        if (op_ms) {
+            op_ms[2 * k] = iv[k].first;
+            op_ms[2 * k + 1] = iv[k].second;
+        }
+        if (ops[k].type != ZB_OP_W) {
+            const double a = (ops[k].type == ZB_OP_F ? arrive_f[ops[k].mb] : arrive_b[ops[k].mb]) * unit_ms;
+            late += std::max(0.0, ms(host[1 + 2 * n + k]) - a);
+        }
+    }
+    if (stats) {
+        std::vector<std::pair<double, double>> srt = iv;
+        std::sort(srt.begin(), srt.end());
+        double busy = 0.0, cs = srt[0].first, ce = srt[0].second;
+        for (size_t i = 1; i < srt.size(); ++i) {
+            if (srt[i].first > ce) {
+                busy += ce - cs;
+                cs = srt[i].first;
+                ce = srt[i].second;
+            } else {
+                ce = std::max(ce, srt[i].second);
+            }
+        }
+        busy += ce - cs;
+        double first = srt[0].first, last = 0.0;
+        for (auto& p : iv) last = std::max(last, p.second);
+        stats->t_first_start_ms = first;
+        stats->t_last_end_ms = last;
+        stats->window_ms = last - first;
+        stats->busy_ms = busy;
+        stats->in_window_idle = stats->window_ms > 0 ? (stats->window_ms - busy) / stats->window_ms : 0.0;
+        stats->wait_late_ms = late;
+    }
+    return ZB_OK;
+}

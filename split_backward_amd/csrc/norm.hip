@@ -1,0 +1,251 @@
+// Memory-bound kernels of the Llama stage: RMSNorm forward / input backward,
+// the RMSNorm gain gradient (a weight gradient, so it belongs to W), fills,
+// and the executor's clock kernels.
+//
+// RMSNorm: y = x r g with r = (mean(x^2) + eps)^(-1/2);
+//          dx = r (dy g - xhat mean(dy g xhat)), xhat = x r;  dg = sum_t dy xhat.
+#include "common.h"
+
+namespace zb {
+namespace {
+
+constexpr int RT = 256;  // threads per row block
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < RT / 64; ++i) t += red[i];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = uint32_t(f2bf(f[2 * i])) | (uint32_t(f2bf(f[2 * i + 1])) << 16);
+    return v;
+}
+
+// One workgroup per row; H is a multiple of 8 and at most 8 * RT * 4.
+template <int CH>
+__global__ __launch_bounds__(RT) void rms_fwd_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ g,
+                                                     bf16_t* __restrict__ n, float* __restrict__ r, int H, float eps) {
+    __shared__ float red[RT / 64];
+    const int64_t row = blockIdx.x;
+    const bf16_t* xr = x + row * H;
+    float v[CH][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int col = (threadIdx.x + c * RT) * 8;
+        if (col < H) {
+            unpack8(*reinterpret_cast<const u32x4*>(xr + col), v[c]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += v[c][i] * v[c][i];
+        }
+    }
+    const float tot = block_sum(ss, red);
+    const float rr = 1.f / sqrtf(tot / float(H) + eps);
+    if (threadIdx.x == 0) r[row] = rr;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int col = (threadIdx.x + c * RT) * 8;
+        if (col < H) {
+            float gg[8], o[8];
+            unpack8(*reinterpret_cast<const u32x4*>(g + col), gg);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = v[c][i] * rr * gg[i];
+            *reinterpret_cast<u32x4*>(n + row * H + col) = pack8(o);
+        }
+    }
+}
+
+template <int CH>
+__global__ __launch_bounds__(RT) void rms_bwd_kernel(const bf16_t* __restrict__ x, const float* __restrict__ r,
+                                                     const bf16_t* __restrict__ g, const bf16_t* __restrict__ dn,
+                                                     const bf16_t* __restrict__ dres, bf16_t* __restrict__ dx, int H) {
+    __shared__ float red[RT / 64];
+    const int64_t row = blockIdx.x;
+    const float rr = r[row];
+    float xh[CH][8], dg[CH][8];
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int col = (threadIdx.x + c * RT) * 8;
+        if (col < H) {
+            float gg[8];
+            unpack8(*reinterpret_cast<const u32x4*>(x + row * H + col), xh[c]);
+            unpack8(*reinterpret_cast<const u32x4*>(dn + row * H + col), dg[c]);
+            unpack8(*reinterpret_cast<const u32x4*>(g + col), gg);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xh[c][i] *= rr;
+                dg[c][i] *= gg[i];
+                dot += dg[c][i] * xh[c][i];
+            }
+        }
+    }
+    const float mean = block_sum(dot, red) / float(H);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int col = (threadIdx.x + c * RT) * 8;
+        if (col < H) {
+            float res[8], o[8];
+            unpack8(*reinterpret_cast<const u32x4*>(dres + row * H + col), res);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = res[i] + rr * (dg[c][i] - xh[c][i] * mean);
+            *reinterpret_cast<u32x4*>(dx + row * H + col) = pack8(o);
+        }
+    }
+}
+
+// dgamma partials: block (column pair block, row chunk of DG_ROWS rows).
+constexpr int DG_ROWS = 64;
+__global__ __launch_bounds__(256) void dgamma_partial_kernel(const bf16_t* __restrict__ x, const float* __restrict__ r,
+                                                             const bf16_t* __restrict__ dn, float* __restrict__ part,
+                                                             int T, int H) {
+    const int col = (blockIdx.x * 256 + threadIdx.x) * 2;
+    const int t0 = blockIdx.y * DG_ROWS;
+    if (col >= H) return;
+    float s0 = 0.f, s1 = 0.f;
+    const int t1 = min(T, t0 + DG_ROWS);
+    for (int t = t0; t < t1; ++t) {
+        const uint32_t xv = *reinterpret_cast<const uint32_t*>(x + (int64_t)t * H + col);
+        const uint32_t dv = *reinterpret_cast<const uint32_t*>(dn + (int64_t)t * H + col);
+        const float rt = r[t];
+        s0 += __uint_as_float(dv << 16) * (__uint_as_float(xv << 16) * rt);
+        s1 += __uint_as_float(dv & 0xffff0000u) * (__uint_as_float(xv & 0xffff0000u) * rt);
+    }
+    part[(int64_t)blockIdx.y * H + col] = s0;
+    part[(int64_t)blockIdx.y * H + col + 1] = s1;
+}
+
+__global__ __launch_bounds__(256) void dgamma_reduce_kernel(const float* __restrict__ part, float* __restrict__ dgamma,
+                                                            int nchunks, int H) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= H) return;
+    float s = 0.f;
+    for (int c = 0; c < nchunks; ++c) s += part[(int64_t)c * H + col];
+    dgamma[col] += s;
+}
+
+__global__ void fill_f32_kernel(float* p, size_t n, float v) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+__global__ void stamp_kernel(uint64_t* dst) {
+    if (threadIdx.x == 0) *dst = wall_clock64();
+}
+
+// Spin until the device wall clock reaches *t0 + delta.  The deadline is at
+// most `delta` ticks after the kernel starts (t0 lies in the past), and a
+// hard cap ends the wait regardless, so every launch finishes.
+__global__ void wait_kernel(const uint64_t* t0, uint64_t delta, uint64_t cap, uint64_t* wait_end) {
+    if (threadIdx.x != 0) return;
+    const uint64_t start = wall_clock64();
+    const uint64_t deadline = __atomic_load_n(t0, __ATOMIC_RELAXED) + delta;
+    const uint64_t limit = start + cap;
+    uint64_t now = start;
+    while (now < deadline && now < limit) {
+        __builtin_amdgcn_s_sleep(1);
+        now = wall_clock64();
+    }
+    if (wait_end) *wait_end = now;
+}
+
+template <int CH>
+int32_t launch_rms_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps, hipStream_t s) {
+    hipLaunchKernelGGL(rms_fwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, g, n, r, H, eps);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+template <int CH>
+int32_t launch_rms_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn, const bf16_t* dres,
+                       bf16_t* dx, int T, int H, hipStream_t s) {
+    hipLaunchKernelGGL(rms_bwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, r, g, dn, dres, dx, H);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+}  // namespace
+
+int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps, hipStream_t s) {
+    if (H % 8 || H > 8 * RT * 4 || T <= 0) return fail(ZB_EINVAL, "rmsnorm: hidden must be a multiple of 8 and <= 8192");
+    const int ch = (H / 8 + RT - 1) / RT;
+    if (ch <= 1) return launch_rms_fwd<1>(x, g, n, r, T, H, eps, s);
+    if (ch <= 2) return launch_rms_fwd<2>(x, g, n, r, T, H, eps, s);
+    return launch_rms_fwd<4>(x, g, n, r, T, H, eps, s);
+}
+
+int32_t rmsnorm_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn, const bf16_t* dres,
+                    bf16_t* dx, int T, int H, hipStream_t s) {
+    if (H % 8 || H > 8 * RT * 4 || T <= 0) return fail(ZB_EINVAL, "rmsnorm: hidden must be a multiple of 8 and <= 8192");
+    const int ch = (H / 8 + RT - 1) / RT;
+    if (ch <= 1) return launch_rms_bwd<1>(x, r, g, dn, dres, dx, T, H, s);
+    if (ch <= 2) return launch_rms_bwd<2>(x, r, g, dn, dres, dx, T, H, s);
+    return launch_rms_bwd<4>(x, r, g, dn, dres, dx, T, H, s);
+}
+
+size_t rmsnorm_dgamma_scratch_floats(int T, int H) { return (size_t)((T + DG_ROWS - 1) / DG_ROWS) * H; }
+
+int32_t rmsnorm_dgamma(const bf16_t* x, const float* r, const bf16_t* dn, float* dgamma, float* scratch, int T,
+                       int H, hipStream_t s) {
+    if (H % 2 || T <= 0) return fail(ZB_EINVAL, "dgamma: bad shape");
+    const int nch = (T + DG_ROWS - 1) / DG_ROWS;
+    hipLaunchKernelGGL(dgamma_partial_kernel, dim3((H / 2 + 255) / 256, nch), dim3(256), 0, s, x, r, dn, scratch, T, H);
+    ZB_HIP(hipGetLastError());
+    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3((H + 255) / 256), dim3(256), 0, s, scratch, dgamma, nch, H);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+int32_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
+    if (n == 0) return ZB_OK;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+int32_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s) {
+    if (n == 0 || dst == src) return ZB_OK;
+    ZB_HIP(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s));
+    return ZB_OK;
+}
+
+int32_t stamp_now(uint64_t* dst, hipStream_t s) {
+    hipLaunchKernelGGL(stamp_kernel, dim3(1), dim3(64), 0, s, dst);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+uint64_t wall_clock_hz() {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 100000000ull;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        return 100000000ull;
+    return (uint64_t)khz * 1000ull;
+}
+
+int32_t wait_until(const uint64_t* t0, uint64_t delta_ticks, uint64_t* wait_end, hipStream_t s) {
+    const uint64_t cap = wall_clock_hz() * 30ull;  // never spin longer than 30 s
+    hipLaunchKernelGGL(wait_kernel, dim3(1), dim3(64), 0, s, t0, delta_ticks, cap, wait_end);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+}  // namespace zb

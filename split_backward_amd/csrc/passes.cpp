@@ -1,0 +1,193 @@
+// F, B and W passes of each stage kind, as sequences of kernel launches on
+// one stream.  Shapes use T tokens, H = hidden, F = ffn; weights are [out, in].
+//
+// Per linear layer (the "Core Innovation 1" decomposition of "Zero-Bubble
+// Pipeline Parallelism Guide for LLMs", in the listing's [out, in] layout):
+//   F: Y = X W^T     B: dX = dY W     W: dW += dY^T X  (fp32, in place)
+#include "common.h"
+#include "stage.h"
+
+namespace zb {
+namespace {
+
+GemmDesc nt(int M, int N, int K, const void* X, int64_t ldx, const void* W, int64_t ldw, void* C, int64_t ldc,
+            int epi = EPI_STORE) {
+    GemmDesc g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = X; g.lda = ldx; g.a_kmajor = 1;
+    g.B = W; g.ldb = ldw; g.b_kmajor = 1;
+    g.C = C; g.ldc = ldc; g.epi = epi;
+    return g;
+}
+// C[M,N] = A[M,K] . W[K,N] with W stored [K=out, N=in]
+GemmDesc nn(int M, int N, int K, const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
+            int epi = EPI_STORE) {
+    GemmDesc g = nt(M, N, K, A, lda, W, ldw, C, ldc, epi);
+    g.b_kmajor = 0;
+    return g;
+}
+// dW[M=out, N=in] += dY[T, out]^T . X[T, in]
+GemmDesc tn(int M, int N, int T, const void* dY, int64_t ldy, const void* X, int64_t ldx, float* dW) {
+    GemmDesc g{};
+    g.M = M; g.N = N; g.K = T;
+    g.A = dY; g.lda = ldy; g.a_kmajor = 0;
+    g.B = X; g.ldb = ldx; g.b_kmajor = 0;
+    g.C = dW; g.ldc = N; g.epi = EPI_ACCUM_F32;
+    return g;
+}
+
+#define ZB_TRY(expr)                     \
+    do {                                 \
+        int32_t rc_ = (expr);            \
+        if (rc_ != ZB_OK) return rc_;    \
+    } while (0)
+
+int32_t linear_gemm(const zb_stage& st, const GemmDesc& g, hipStream_t s) {
+    if (st.desc.dtype == ZB_F32) return gemm_f32(g, g.epi == EPI_ACCUM_F32, s);
+    return gemm_bf16(g, s);
+}
+
+const bf16_t* cbf(const void* p) { return static_cast<const bf16_t*>(p); }
+bf16_t* bf(void* p) { return static_cast<bf16_t*>(p); }
+
+}  // namespace
+
+int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s) {
+    const zb_stage_desc& d = st.desc;
+    const int T = d.tokens, H = d.hidden, F = d.ffn;
+    if (d.kind == ZB_LINEAR) {
+        void* xs = st.slot_tensor(mb, 0, LIN_X);
+        ZB_TRY(copy_bytes(xs, x, (size_t)T * H * (d.dtype == ZB_F32 ? 4 : 2), s));
+        return linear_gemm(st, nt(T, F, H, xs, H, st.w[0], H, y, F), s);
+    }
+    if (d.kind == ZB_MLP_GELU) {
+        void* xs = st.slot_tensor(mb, 0, MLP_X);
+        void* a = st.slot_tensor(mb, 0, MLP_A);
+        void* h = st.slot_tensor(mb, 0, MLP_H);
+        ZB_TRY(copy_bytes(xs, x, (size_t)T * H * 2, s));
+        GemmDesc g1 = nt(T, F, H, xs, H, st.w[0], H, a, F, EPI_GELU_FWD);
+        g1.C2 = h;
+        g1.ldc2 = F;
+        ZB_TRY(gemm_bf16(g1, s));
+        return gemm_bf16(nt(T, H, F, h, F, st.w[1], F, y, H), s);
+    }
+    const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
+    for (int l = 0; l < d.n_layers; ++l) {
+        void* const* w = &st.w[6 * l];
+        bf16_t* xl = bf(st.slot_tensor(mb, l, L_X));
+        if (l == 0) ZB_TRY(copy_bytes(xl, x, (size_t)T * H * 2, s));
+        float* r1 = static_cast<float*>(st.slot_tensor(mb, l, L_R1));
+        bf16_t* n1 = bf(st.slot_tensor(mb, l, L_N1));
+        bf16_t* qkv = bf(st.slot_tensor(mb, l, L_QKV));
+        bf16_t* a = bf(st.slot_tensor(mb, l, L_A));
+        float* lse = static_cast<float*>(st.slot_tensor(mb, l, L_LSE));
+        bf16_t* h1 = bf(st.slot_tensor(mb, l, L_H1));
+        float* r2 = static_cast<float*>(st.slot_tensor(mb, l, L_R2));
+        bf16_t* n2 = bf(st.slot_tensor(mb, l, L_N2));
+        bf16_t* gu = bf(st.slot_tensor(mb, l, L_GU));
+        bf16_t* sw = bf(st.slot_tensor(mb, l, L_S));
+        void* out = (l == d.n_layers - 1) ? y : st.slot_tensor(mb, l + 1, L_X);
+
+        ZB_TRY(rmsnorm_fwd(xl, cbf(w[4]), n1, r1, T, H, d.rms_eps, s));
+        ZB_TRY(gemm_bf16(nt(T, QKV, H, n1, H, w[0], H, qkv, QKV), s));
+        ZB_TRY(attn_fwd(qkv, a, lse, T, d.n_heads, d.n_kv_heads, s));
+        GemmDesc go = nt(T, H, QD, a, QD, w[1], QD, h1, H, EPI_RESID);
+        go.R = xl;
+        go.ldr = H;
+        ZB_TRY(gemm_bf16(go, s));
+        ZB_TRY(rmsnorm_fwd(h1, cbf(w[5]), n2, r2, T, H, d.rms_eps, s));
+        GemmDesc gg = nt(T, 2 * F, H, n2, H, w[2], H, gu, 2 * F, EPI_SWIGLU_FWD);
+        gg.C2 = sw;
+        gg.ldc2 = F;
+        gg.half_n = F;
+        ZB_TRY(gemm_bf16(gg, s));
+        GemmDesc gd = nt(T, H, F, sw, F, w[3], F, out, H, EPI_RESID);
+        gd.R = h1;
+        gd.ldr = H;
+        ZB_TRY(gemm_bf16(gd, s));
+    }
+    return ZB_OK;
+}
+
+int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipStream_t s) {
+    const zb_stage_desc& d = st.desc;
+    const int T = d.tokens, H = d.hidden, F = d.ffn;
+    if (d.kind == ZB_LINEAR) {
+        void* dys = st.slot_tensor(mb, 0, LIN_DY);
+        ZB_TRY(copy_bytes(dys, dy, (size_t)T * F * (d.dtype == ZB_F32 ? 4 : 2), s));
+        return linear_gemm(st, nn(T, H, F, dys, F, st.w[0], H, dx, H), s);
+    }
+    if (d.kind == ZB_MLP_GELU) {
+        void* dys = st.slot_tensor(mb, 0, MLP_DY);
+        void* a = st.slot_tensor(mb, 0, MLP_A);
+        void* da = st.slot_tensor(mb, 0, MLP_DA);
+        ZB_TRY(copy_bytes(dys, dy, (size_t)T * H * 2, s));
+        GemmDesc g2 = nn(T, F, H, dys, H, st.w[1], F, da, F, EPI_GELU_BWD);
+        g2.R = a;
+        g2.ldr = F;
+        ZB_TRY(gemm_bf16(g2, s));
+        return gemm_bf16(nn(T, H, F, da, F, st.w[0], H, dx, H), s);
+    }
+    const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
+    bf16_t* da = bf(st.scratch_b);
+    float* delta = reinterpret_cast<float*>(st.scratch_b + ((size_t)T * QD * 2 + 255) / 256 * 256);
+    for (int l = d.n_layers - 1; l >= 0; --l) {
+        void* const* w = &st.w[6 * l];
+        bf16_t* xl = bf(st.slot_tensor(mb, l, L_X));
+        float* r1 = static_cast<float*>(st.slot_tensor(mb, l, L_R1));
+        bf16_t* qkv = bf(st.slot_tensor(mb, l, L_QKV));
+        bf16_t* a = bf(st.slot_tensor(mb, l, L_A));
+        float* lse = static_cast<float*>(st.slot_tensor(mb, l, L_LSE));
+        bf16_t* h1 = bf(st.slot_tensor(mb, l, L_H1));
+        float* r2 = static_cast<float*>(st.slot_tensor(mb, l, L_R2));
+        bf16_t* gu = bf(st.slot_tensor(mb, l, L_GU));
+        bf16_t* dout = bf(st.slot_tensor(mb, l, L_DOUT));
+        bf16_t* dgu = bf(st.slot_tensor(mb, l, L_DGU));
+        bf16_t* dn2 = bf(st.slot_tensor(mb, l, L_DN2));
+        bf16_t* dh1 = bf(st.slot_tensor(mb, l, L_DH1));
+        bf16_t* dqkv = bf(st.slot_tensor(mb, l, L_DQKV));
+        bf16_t* dn1 = bf(st.slot_tensor(mb, l, L_DN1));
+        void* dest = (l == 0) ? dx : st.slot_tensor(mb, l - 1, L_DOUT);
+        if (l == d.n_layers - 1) ZB_TRY(copy_bytes(dout, dy, (size_t)T * H * 2, s));
+
+        GemmDesc gd = nn(T, F, H, dout, H, w[3], F, dgu, 2 * F, EPI_SWIGLU_BWD);
+        gd.R = gu;
+        gd.ldr = 2 * F;
+        gd.half_n = F;
+        ZB_TRY(gemm_bf16(gd, s));
+        ZB_TRY(gemm_bf16(nn(T, H, 2 * F, dgu, 2 * F, w[2], H, dn2, H), s));
+        ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, dout, dh1, T, H, s));
+        ZB_TRY(gemm_bf16(nn(T, QD, H, dh1, H, w[1], QD, da, QD), s));
+        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, T, d.n_heads, d.n_kv_heads, s));
+        ZB_TRY(gemm_bf16(nn(T, H, QKV, dqkv, QKV, w[0], H, dn1, H), s));
+        ZB_TRY(rmsnorm_bwd(xl, r1, cbf(w[4]), dn1, dh1, bf(dest), T, H, s));
+    }
+    return ZB_OK;
+}
+
+int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s) {
+    const zb_stage_desc& d = st.desc;
+    const int T = d.tokens, H = d.hidden, F = d.ffn;
+    if (d.kind == ZB_LINEAR)
+        return linear_gemm(st, tn(F, H, T, st.slot_tensor(mb, 0, LIN_DY), F, st.slot_tensor(mb, 0, LIN_X), H, st.dw[0]), s);
+    if (d.kind == ZB_MLP_GELU) {
+        ZB_TRY(gemm_bf16(tn(F, H, T, st.slot_tensor(mb, 0, MLP_DA), F, st.slot_tensor(mb, 0, MLP_X), H, st.dw[0]), s));
+        return gemm_bf16(tn(H, F, T, st.slot_tensor(mb, 0, MLP_DY), H, st.slot_tensor(mb, 0, MLP_H), F, st.dw[1]), s);
+    }
+    const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
+    float* part = reinterpret_cast<float*>(st.scratch_w);
+    for (int l = 0; l < d.n_layers; ++l) {
+        float* const* dw = &st.dw[6 * l];
+        ZB_TRY(gemm_bf16(tn(QKV, H, T, st.slot_tensor(mb, l, L_DQKV), QKV, st.slot_tensor(mb, l, L_N1), H, dw[0]), s));
+        ZB_TRY(gemm_bf16(tn(H, QD, T, st.slot_tensor(mb, l, L_DH1), H, st.slot_tensor(mb, l, L_A), QD, dw[1]), s));
+        ZB_TRY(gemm_bf16(tn(2 * F, H, T, st.slot_tensor(mb, l, L_DGU), 2 * F, st.slot_tensor(mb, l, L_N2), H, dw[2]), s));
+        ZB_TRY(gemm_bf16(tn(H, F, T, st.slot_tensor(mb, l, L_DOUT), H, st.slot_tensor(mb, l, L_S), F, dw[3]), s));
+        ZB_TRY(rmsnorm_dgamma(cbf(st.slot_tensor(mb, l, L_X)), static_cast<const float*>(st.slot_tensor(mb, l, L_R1)),
+                              cbf(st.slot_tensor(mb, l, L_DN1)), dw[4], part, T, H, s));
+        ZB_TRY(rmsnorm_dgamma(cbf(st.slot_tensor(mb, l, L_H1)), static_cast<const float*>(st.slot_tensor(mb, l, L_R2)),
+                              cbf(st.slot_tensor(mb, l, L_DN2)), dw[5], part, T, H, s));
+    }
+    return ZB_OK;
+}
+
+}  // namespace zb

@@ -1,0 +1,220 @@
+// Host schedule generator: per-stage op order for GPipe, 1F1B and the
+// memory-limited zero-bubble greedy, by integer-time simulation of the whole
+// p-stage pipeline (the model of "Zero-Bubble Pipeline Parallelism Guide for
+// LLMs", "Mathematical Modeling: Bubble Fractions, Memory Bounds, and
+// Speedups": no communication term, integer op costs).
+//
+// Zero-bubble greedy ("Core Innovation 2" and the Guide's scheduler
+// listing): whenever a stage is idle it takes the ready input-gradient op
+// (B) of the lowest microbatch; otherwise the next forward (F) if fewer than
+// mem_limit microbatches hold stashed activations; otherwise the ready
+// weight-gradient op (W) of the lowest microbatch, which releases that
+// microbatch's stash; otherwise it waits for the next completion.  All
+// completions at a time instant are applied before any stage chooses.  The
+// listing's last-resort rule (a forward regardless of the limit) is left out
+// because it would break the hard ceiling on stashed activations described
+// under "Memory Management & Activation Rollback".
+#include <algorithm>
+#include <cstdint>
+#include <limits>
+#include <queue>
+#include <vector>
+
+#include "../../include/zb.h"
+
+namespace {
+
+constexpr int64_t NOT_DONE = std::numeric_limits<int64_t>::max();
+
+struct Placed {
+    int type;  // ZB_OP_F / ZB_OP_B / ZB_OP_W
+    int mb;
+    int64_t start, end;
+};
+
+struct Pipeline {
+    int p, m;
+    // completion times, NOT_DONE until finished: index stage * m + mb
+    std::vector<int64_t> f_end, b_end, w_end;
+    std::vector<std::vector<Placed>> placed;
+    std::vector<int> peak;
+    Pipeline(int p_, int m_)
+        : p(p_), m(m_), f_end((size_t)p_ * m_, NOT_DONE), b_end((size_t)p_ * m_, NOT_DONE),
+          w_end((size_t)p_ * m_, NOT_DONE), placed(p_), peak(p_, 0) {}
+    int64_t& F(int i, int j) { return f_end[(size_t)i * m + j]; }
+    int64_t& B(int i, int j) { return b_end[(size_t)i * m + j]; }
+    int64_t& W(int i, int j) { return w_end[(size_t)i * m + j]; }
+};
+
+// GPipe / 1F1B: fixed per-stage sequences of F and whole backwards (B then W
+// back to back); each op starts when its stage is free and its inputs exist.
+bool run_fixed(Pipeline& P, bool one_f_one_b, int64_t cF, int64_t cB, int64_t cW) {
+    const int p = P.p, m = P.m;
+    std::vector<std::vector<std::pair<int, int>>> seq(p);  // (is_backward, mb)
+    for (int i = 0; i < p; ++i) {
+        auto& s = seq[i];
+        if (!one_f_one_b) {
+            for (int j = 0; j < m; ++j) s.push_back({0, j});
+            for (int j = 0; j < m; ++j) s.push_back({1, j});
+        } else {
+            const int warm = std::min(p - 1 - i, m);
+            for (int j = 0; j < warm; ++j) s.push_back({0, j});
+            for (int j = warm; j < m; ++j) {
+                s.push_back({0, j});
+                s.push_back({1, j - warm});
+            }
+            for (int j = m - warm; j < m; ++j) s.push_back({1, j});
+        }
+    }
+    std::vector<size_t> next(p, 0);
+    std::vector<int64_t> free_at(p, 0);
+    std::vector<int> active(p, 0);
+    size_t left = (size_t)2 * p * m;
+    while (left > 0) {
+        bool moved = false;
+        for (int i = 0; i < p; ++i) {
+            while (next[i] < seq[i].size()) {
+                const auto [bwd, j] = seq[i][next[i]];
+                int64_t ready;
+                if (!bwd) {
+                    ready = (i == 0) ? 0 : P.F(i - 1, j);
+                } else {
+                    const int64_t down = (i == p - 1) ? 0 : P.W(i + 1, j);  // whole backward downstream
+                    ready = std::max(P.F(i, j), down);
+                }
+                if (ready == NOT_DONE) break;
+                const int64_t st = std::max(ready, free_at[i]);
+                if (!bwd) {
+                    P.F(i, j) = st + cF;
+                    free_at[i] = st + cF;
+                    P.placed[i].push_back({ZB_OP_F, j, st, st + cF});
+                    P.peak[i] = std::max(P.peak[i], ++active[i]);
+                } else {
+                    P.B(i, j) = st + cB;
+                    P.W(i, j) = st + cB + cW;
+                    free_at[i] = st + cB + cW;
+                    P.placed[i].push_back({ZB_OP_B, j, st, st + cB});
+                    P.placed[i].push_back({ZB_OP_W, j, st + cB, st + cB + cW});
+                    --active[i];
+                }
+                ++next[i];
+                --left;
+                moved = true;
+            }
+        }
+        if (!moved) return false;
+    }
+    return true;
+}
+
+bool run_greedy(Pipeline& P, int M, int64_t cF, int64_t cB, int64_t cW) {
+    const int p = P.p, m = P.m;
+    struct Running { int64_t end; int type, stage, mb; };
+    auto later = [](const Running& a, const Running& b) { return a.end > b.end; };
+    std::priority_queue<Running, std::vector<Running>, decltype(later)> heap(later);
+    std::vector<char> busy(p, 0);
+    std::vector<int> active(p, 0), next_f(p, 0);
+    std::vector<std::vector<char>> b_started(p, std::vector<char>(m, 0)), w_started(p, std::vector<char>(m, 0));
+    int64_t now = 0;
+    size_t finished = 0;
+    const size_t total = (size_t)3 * p * m;
+    while (true) {
+        while (!heap.empty() && heap.top().end == now) {
+            const Running r = heap.top();
+            heap.pop();
+            if (r.type == ZB_OP_F) P.F(r.stage, r.mb) = r.end;
+            else if (r.type == ZB_OP_B) P.B(r.stage, r.mb) = r.end;
+            else P.W(r.stage, r.mb) = r.end;
+            busy[r.stage] = 0;
+            ++finished;
+        }
+        if (finished == total) break;
+        for (int i = 0; i < p; ++i) {
+            if (busy[i]) continue;
+            int type = -1, mb = -1;
+            for (int j = 0; j < m && type < 0; ++j)
+                if (!b_started[i][j] && P.F(i, j) != NOT_DONE && (i == p - 1 || P.B(i + 1, j) != NOT_DONE)) {
+                    type = ZB_OP_B;
+                    mb = j;
+                }
+            if (type < 0 && active[i] < M && next_f[i] < m &&
+                (i == 0 || P.F(i - 1, next_f[i]) != NOT_DONE)) {
+                type = ZB_OP_F;
+                mb = next_f[i];
+            }
+            if (type < 0)
+                for (int j = 0; j < m && type < 0; ++j)
+                    if (!w_started[i][j] && P.B(i, j) != NOT_DONE) {
+                        type = ZB_OP_W;
+                        mb = j;
+                    }
+            if (type < 0) continue;
+            int64_t cost;
+            if (type == ZB_OP_F) {
+                ++next_f[i];
+                P.peak[i] = std::max(P.peak[i], ++active[i]);
+                cost = cF;
+            } else if (type == ZB_OP_B) {
+                b_started[i][mb] = 1;
+                cost = cB;
+            } else {
+                w_started[i][mb] = 1;
+                --active[i];
+                cost = cW;
+            }
+            busy[i] = 1;
+            heap.push({now + cost, type, i, mb});
+            P.placed[i].push_back({type, mb, now, now + cost});
+        }
+        if (heap.empty()) return false;  // nothing can run: limit too small
+        now = heap.top().end;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" int32_t zb_schedule_generate(int32_t kind, int32_t p, int32_t m, int32_t mem_limit, int32_t cF,
+                                        int32_t cB, int32_t cW, int32_t stage, zb_op* ops, int64_t* start,
+                                        int64_t* end, int32_t cap, int64_t* arrive_f, int64_t* arrive_b,
+                                        zb_sched_stats* stats) {
+    if (p < 1 || m < 1 || stage < 0 || stage >= p || cF < 1 || cB < 1 || cW < 0) return ZB_EINVAL;
+    if ((ops || start || end) && cap < 3 * m) return ZB_EINVAL;
+    if (kind != ZB_SCHED_GPIPE && kind != ZB_SCHED_1F1B && kind != ZB_SCHED_ZB) return ZB_EINVAL;
+    if ((int64_t)p * m > 1 << 22) return ZB_EINVAL;
+    Pipeline P(p, m);
+    bool ok;
+    if (kind == ZB_SCHED_ZB) {
+        if (mem_limit < 1 || cW < 1) return ZB_EINVAL;
+        ok = run_greedy(P, mem_limit, cF, cB, cW);
+    } else {
+        ok = run_fixed(P, kind == ZB_SCHED_1F1B, cF, cB, cW);
+    }
+    if (!ok) return ZB_EINVAL;
+    const auto& mine = P.placed[stage];
+    for (size_t k = 0; k < mine.size(); ++k) {
+        if (ops) ops[k] = zb_op{mine[k].type, mine[k].mb};
+        if (start) start[k] = mine[k].start;
+        if (end) end[k] = mine[k].end;
+    }
+    for (int j = 0; j < m; ++j) {
+        if (arrive_f) arrive_f[j] = stage == 0 ? 0 : P.F(stage - 1, j);
+        if (arrive_b) {
+            if (stage == p - 1) arrive_b[j] = 0;
+            else arrive_b[j] = (kind == ZB_SCHED_ZB) ? P.B(stage + 1, j) : P.W(stage + 1, j);
+        }
+    }
+    if (stats) {
+        int64_t mk = 0;
+        for (int i = 0; i < p; ++i) mk = std::max(mk, P.placed[i].back().end);
+        int64_t busy = 0;
+        for (const auto& o : mine) busy += o.end - o.start;
+        stats->makespan = mk;
+        stats->busy = busy;
+        stats->first_start = mine.front().start;
+        stats->last_end = mine.back().end;
+        stats->peak_active = P.peak[stage];
+        stats->n_ops = (int32_t)mine.size();
+    }
+    return (int32_t)mine.size();
+}

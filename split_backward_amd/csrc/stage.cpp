@@ -1,0 +1,331 @@
+// The stage object behind the C ABI: stash ring, per-microbatch state
+// machine, and the F / B / W passes of each stage kind.
+//
+// The pass structure follows "Zero-Bubble Pipeline Parallelism Guide for
+// LLMs": F keeps what the backward needs (the listing's saved inputs), B
+// computes the input gradient and keeps the output gradients (saved grad
+// outputs), W consumes both and adds the weight gradient into a fixed fp32
+// buffer, then releases the microbatch's activations ("Memory Management &
+// Activation Rollback").  The stash lives in a ring of R slots in the caller's
+// workspace; microbatch mb uses slot mb % R, which is valid because F and W
+// are both issued in ascending microbatch order, so the live microbatches
+// always form a contiguous range.
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "stage.h"
+
+using namespace zb;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+size_t elem_bytes(int dtype) { return dtype == ZB_F32 ? 4 : 2; }
+
+bool valid_desc(const zb_stage_desc* d, std::string& why) {
+    if (!d) { why = "desc is NULL"; return false; }
+    if (d->tokens < 1 || d->hidden < 1 || d->ffn < 1 || d->ring_slots < 1) { why = "tokens, hidden, ffn, ring_slots must be >= 1"; return false; }
+    if (d->dtype != ZB_F32 && d->dtype != ZB_BF16) { why = "dtype must be ZB_F32 or ZB_BF16"; return false; }
+    if (d->kind == ZB_LINEAR) {
+        if (d->dtype == ZB_BF16 && (d->hidden % 8 || d->ffn % 8)) { why = "bf16 linear needs hidden, ffn multiples of 8"; return false; }
+        return true;
+    }
+    if (d->dtype != ZB_BF16) { why = "only the linear kind supports fp32"; return false; }
+    if (d->hidden % 8 || d->ffn % 8) { why = "hidden and ffn must be multiples of 8"; return false; }
+    if (d->kind == ZB_MLP_GELU) return true;
+    if (d->kind != ZB_LLAMA) { why = "unknown kind"; return false; }
+    if (d->n_layers < 1 || d->n_heads < 1 || d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads) { why = "bad head counts"; return false; }
+    if (d->head_dim != 128) { why = "head_dim must be 128"; return false; }
+    if (d->hidden > 8192) { why = "hidden must be <= 8192"; return false; }
+    if (!(d->rms_eps > 0.f)) { why = "rms_eps must be > 0"; return false; }
+    return true;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- layout --
+
+void Layout::build(const zb_stage_desc& d) {
+    const size_t T = d.tokens, H = d.hidden, F = d.ffn;
+    off.clear();
+    slot_bytes = 0;
+    auto add = [&](int layer, int which, int rows, int cols, int dtype) {
+        Tensor t;
+        t.layer = layer; t.which = which; t.rows = rows; t.cols = cols; t.dtype = dtype;
+        t.offset = slot_bytes;
+        slot_bytes += align_up((size_t)rows * cols * elem_bytes(dtype));
+        off.push_back(t);
+    };
+    if (d.kind == ZB_LINEAR) {
+        add(0, LIN_X, T, H, d.dtype);
+        add(0, LIN_DY, T, F, d.dtype);
+    } else if (d.kind == ZB_MLP_GELU) {
+        add(0, MLP_X, T, H, ZB_BF16);
+        add(0, MLP_A, T, F, ZB_BF16);
+        add(0, MLP_H, T, F, ZB_BF16);
+        add(0, MLP_DY, T, H, ZB_BF16);
+        add(0, MLP_DA, T, F, ZB_BF16);
+    } else {
+        const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim;
+        for (int l = 0; l < d.n_layers; ++l) {
+            add(l, L_X, T, H, ZB_BF16);
+            add(l, L_R1, T, 1, ZB_F32);
+            add(l, L_N1, T, H, ZB_BF16);
+            add(l, L_QKV, T, QD + 2 * KVD, ZB_BF16);
+            add(l, L_A, T, QD, ZB_BF16);
+            add(l, L_LSE, d.n_heads, T, ZB_F32);
+            add(l, L_H1, T, H, ZB_BF16);
+            add(l, L_R2, T, 1, ZB_F32);
+            add(l, L_N2, T, H, ZB_BF16);
+            add(l, L_GU, T, 2 * F, ZB_BF16);
+            add(l, L_S, T, F, ZB_BF16);
+            add(l, L_DOUT, T, H, ZB_BF16);
+            add(l, L_DGU, T, 2 * F, ZB_BF16);
+            add(l, L_DN2, T, H, ZB_BF16);
+            add(l, L_DH1, T, H, ZB_BF16);
+            add(l, L_DQKV, T, QD + 2 * KVD, ZB_BF16);
+            add(l, L_DN1, T, H, ZB_BF16);
+        }
+    }
+    // per-pass scratch (not per slot)
+    scratch_b = 0;
+    scratch_w = 0;
+    if (d.kind == ZB_LLAMA) {
+        const size_t QD = (size_t)d.n_heads * d.head_dim;
+        scratch_b = align_up(T * QD * 2) + align_up((size_t)d.n_heads * T * 4);  // da + delta
+        scratch_w = align_up(rmsnorm_dgamma_scratch_floats(d.tokens, d.hidden) * 4);
+    }
+    stamps_bytes = align_up(sizeof(uint64_t) * (3 * (size_t)MAX_RUN_OPS + 8));
+    ring_bytes = slot_bytes * d.ring_slots;
+    total = ring_bytes + scratch_b + scratch_w + stamps_bytes;
+}
+
+const Layout::Tensor* Layout::find(int layer, int which) const {
+    for (const auto& t : off)
+        if (t.layer == layer && t.which == which) return &t;
+    return nullptr;
+}
+
+// ----------------------------------------------------------------- stage ---
+
+zb_stage::~zb_stage() {
+    for (auto& s : slots) {
+        if (s.evF) (void)hipEventDestroy(s.evF);
+        if (s.evB) (void)hipEventDestroy(s.evB);
+        if (s.evW) (void)hipEventDestroy(s.evW);
+    }
+    for (auto& e : chain) if (e) (void)hipEventDestroy(e);
+}
+
+void* zb_stage::slot_tensor(int mb, int layer, int which) const {
+    const Layout::Tensor* t = lay.find(layer, which);
+    if (!t) return nullptr;
+    return ws + (size_t)(mb % desc.ring_slots) * lay.slot_bytes + t->offset;
+}
+
+// Make `s` wait for the last op of kind k (scratch of that pass is shared),
+// and for `dep` (the microbatch's previous op) if it was recorded.
+int32_t zb_stage::order_after(int k, hipEvent_t dep, bool dep_valid, hipStream_t s) {
+    if (chain_valid[k]) ZB_HIP(hipStreamWaitEvent(s, chain[k], 0));
+    if (dep_valid) ZB_HIP(hipStreamWaitEvent(s, dep, 0));
+    return ZB_OK;
+}
+
+int32_t zb_stage::finish(int k, hipEvent_t ev, hipStream_t s) {
+    ZB_HIP(hipEventRecord(ev, s));
+    ZB_HIP(hipEventRecord(chain[k], s));
+    chain_valid[k] = true;
+    return ZB_OK;
+}
+
+// ------------------------------------------------------------- C ABI -------
+
+extern "C" int32_t zb_stage_num_weights(const zb_stage_desc* d) {
+    std::string why;
+    if (!valid_desc(d, why)) return fail(ZB_EINVAL, why);
+    if (d->kind == ZB_LINEAR) return 1;
+    if (d->kind == ZB_MLP_GELU) return 2;
+    return 6 * d->n_layers;
+}
+
+extern "C" size_t zb_stage_workspace_bytes(const zb_stage_desc* d) {
+    std::string why;
+    if (!valid_desc(d, why)) {
+        set_error(why);
+        return 0;
+    }
+    Layout l;
+    l.build(*d);
+    return l.total;
+}
+
+extern "C" int32_t zb_stage_create(const zb_stage_desc* d, void* const* weights, float* const* dw, void* workspace,
+                                   size_t ws_bytes, zb_stage** out) {
+    std::string why;
+    if (!out) return fail(ZB_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!valid_desc(d, why)) return fail(ZB_EINVAL, why);
+    if (!weights || !dw || !workspace) return fail(ZB_EINVAL, "weights, dw and workspace must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % ALIGN) return fail(ZB_EINVAL, "workspace must be 256-byte aligned");
+    const int nw = zb_stage_num_weights(d);
+    for (int i = 0; i < nw; ++i)
+        if (!weights[i] || !dw[i]) return fail(ZB_EINVAL, "NULL weight or dW pointer " + std::to_string(i));
+    auto st = new zb_stage();
+    st->desc = *d;
+    st->lay.build(*d);
+    if (ws_bytes < st->lay.total) {
+        const size_t need = st->lay.total;
+        delete st;
+        return fail(ZB_ENOMEM, "workspace too small: need " + std::to_string(need) + " bytes");
+    }
+    st->w.assign(weights, weights + nw);
+    st->dw.assign(dw, dw + nw);
+    st->ws = static_cast<char*>(workspace);
+    st->scratch_b = st->ws + st->lay.ring_bytes;
+    st->scratch_w = st->scratch_b + st->lay.scratch_b;
+    st->stamps = reinterpret_cast<uint64_t*>(st->scratch_w + st->lay.scratch_w);
+    st->slots.resize(d->ring_slots);
+    auto mk = [&](hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming); };
+    for (auto& s : st->slots) {
+        if (mk(&s.evF) != hipSuccess || mk(&s.evB) != hipSuccess || mk(&s.evW) != hipSuccess) {
+            delete st;
+            return fail(ZB_EHIP, "hipEventCreate failed");
+        }
+    }
+    for (auto& e : st->chain)
+        if (mk(&e) != hipSuccess) {
+            delete st;
+            return fail(ZB_EHIP, "hipEventCreate failed");
+        }
+    *out = st;
+    return ZB_OK;
+}
+
+extern "C" void zb_stage_destroy(zb_stage* st) { delete st; }
+
+extern "C" int32_t zb_fwd(zb_stage* st, int32_t mb, const void* x, void* y, void* stream) {
+    if (!st || !x || !y || mb < 0) return fail(ZB_EINVAL, "zb_fwd: bad argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mb != st->next_f) return fail(ZB_ESTATE, "zb_fwd: F must be issued in ascending microbatch order; expected mb " + std::to_string(st->next_f));
+    Slot& sl = st->slots[mb % st->desc.ring_slots];
+    if (sl.mb >= 0 && !sl.w_issued)
+        return fail(ZB_ERING_FULL, "zb_fwd: ring slot still holds microbatch " + std::to_string(sl.mb) + " (its W has not been issued)");
+    int32_t rc = st->order_after(PASS_F, sl.evW, sl.w_event_valid, s);
+    if (rc) return rc;
+    rc = run_forward(*st, mb, x, y, s);
+    if (rc) return rc;
+    sl.mb = mb;
+    sl.b_issued = sl.w_issued = false;
+    rc = st->finish(PASS_F, sl.evF, s);
+    if (rc) return rc;
+    ++st->next_f;
+    return ZB_OK;
+}
+
+extern "C" int32_t zb_bwd_input(zb_stage* st, int32_t mb, const void* dy, void* dx, void* stream) {
+    if (!st || !dy || !dx || mb < 0) return fail(ZB_EINVAL, "zb_bwd_input: bad argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Slot& sl = st->slots[mb % st->desc.ring_slots];
+    if (sl.mb != mb || sl.b_issued) return fail(ZB_ESTATE, "zb_bwd_input: needs F(mb) issued and B(mb) not yet issued");
+    int32_t rc = st->order_after(PASS_B, sl.evF, true, s);
+    if (rc) return rc;
+    rc = run_backward_input(*st, mb, dy, dx, s);
+    if (rc) return rc;
+    sl.b_issued = true;
+    return st->finish(PASS_B, sl.evB, s);
+}
+
+extern "C" int32_t zb_bwd_weight_accum(zb_stage* st, int32_t mb, void* stream) {
+    if (!st || mb < 0) return fail(ZB_EINVAL, "zb_bwd_weight_accum: bad argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Slot& sl = st->slots[mb % st->desc.ring_slots];
+    if (sl.mb != mb || !sl.b_issued || sl.w_issued) return fail(ZB_ESTATE, "zb_bwd_weight_accum: needs B(mb) issued and W(mb) not yet issued");
+    if (mb != st->next_w) return fail(ZB_ESTATE, "zb_bwd_weight_accum: W must be issued in ascending microbatch order; expected mb " + std::to_string(st->next_w));
+    int32_t rc = st->order_after(PASS_W, sl.evB, true, s);
+    if (rc) return rc;
+    rc = run_backward_weight(*st, mb, s);
+    if (rc) return rc;
+    sl.w_issued = true;
+    sl.w_event_valid = true;
+    ++st->next_w;
+    return st->finish(PASS_W, sl.evW, s);
+}
+
+extern "C" int32_t zb_stage_zero_grad(zb_stage* st, void* stream) {
+    if (!st) return fail(ZB_EINVAL, "zb_stage_zero_grad: NULL stage");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (auto& sl : st->slots)
+        if (sl.mb >= 0 && !sl.w_issued) return fail(ZB_ESTATE, "zb_stage_zero_grad: microbatch " + std::to_string(sl.mb) + " still in flight");
+    if (st->chain_valid[PASS_W]) ZB_HIP(hipStreamWaitEvent(s, st->chain[PASS_W], 0));
+    const zb_stage_desc& d = st->desc;
+    const int nw = zb_stage_num_weights(&d);
+    for (int i = 0; i < nw; ++i) {
+        const size_t n = weight_elems(d, i);
+        int32_t rc = fill_f32(st->dw[i], n, 0.f, s);
+        if (rc) return rc;
+    }
+    ZB_HIP(hipEventRecord(st->chain[PASS_W], s));
+    st->chain_valid[PASS_W] = true;
+    for (auto& sl : st->slots) sl.mb = -1;
+    st->next_f = st->next_w = 0;
+    return ZB_OK;
+}
+
+extern "C" int32_t zb_stage_stash_tensor(zb_stage* st, int32_t mb, int32_t layer, int32_t which, void** ptr,
+                                         int32_t* rows, int32_t* cols, int32_t* dtype) {
+    if (!st || mb < 0 || !ptr) return fail(ZB_EINVAL, "zb_stage_stash_tensor: bad argument");
+    const Layout::Tensor* t = st->lay.find(layer, which);
+    if (!t) return fail(ZB_EINVAL, "zb_stage_stash_tensor: no such tensor");
+    if (st->slots[mb % st->desc.ring_slots].mb != mb) return fail(ZB_ESTATE, "zb_stage_stash_tensor: microbatch not resident");
+    *ptr = st->slot_tensor(mb, layer, which);
+    if (rows) *rows = t->rows;
+    if (cols) *cols = t->cols;
+    if (dtype) *dtype = t->dtype;
+    return ZB_OK;
+}
+
+size_t zb::weight_elems(const zb_stage_desc& d, int i) {
+    const size_t H = d.hidden, F = d.ffn;
+    if (d.kind == ZB_LINEAR) return H * F;
+    if (d.kind == ZB_MLP_GELU) return H * F;
+    const size_t QD = (size_t)d.n_heads * d.head_dim, KVD = (size_t)d.n_kv_heads * d.head_dim;
+    switch (i % 6) {
+        case 0: return (QD + 2 * KVD) * H;
+        case 1: return H * QD;
+        case 2: return 2 * F * H;
+        case 3: return H * F;
+        default: return H;
+    }
+}
+
+extern "C" int32_t zb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda,
+                           int32_t a_kmajor, const void* B, int64_t ldb, int32_t b_kmajor, void* C, int64_t ldc,
+                           int32_t out_f32, int32_t accumulate, void* stream) {
+    if (!A || !B || !C || M < 1 || N < 1 || K < 1) return fail(ZB_EINVAL, "zb_gemm: bad argument");
+    GemmDesc g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.a_kmajor = a_kmajor;
+    g.B = B; g.ldb = ldb; g.b_kmajor = b_kmajor;
+    g.C = C; g.ldc = ldc;
+    const int64_t minlda = a_kmajor ? K : M, minldb = b_kmajor ? K : N;
+    if (lda < minlda || ldb < minldb || ldc < N) return fail(ZB_EINVAL, "zb_gemm: leading dimension too small");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == ZB_F32) {
+        if (!out_f32) return fail(ZB_EINVAL, "zb_gemm: fp32 GEMM writes fp32");
+        return gemm_f32(g, accumulate, s);
+    }
+    if (dtype != ZB_BF16) return fail(ZB_EINVAL, "zb_gemm: bad dtype");
+    if (out_f32) {
+        if (!accumulate) return fail(ZB_EINVAL, "zb_gemm: bf16 with fp32 output accumulates (C += A.B)");
+        g.epi = EPI_ACCUM_F32;
+    } else {
+        if (accumulate) return fail(ZB_EINVAL, "zb_gemm: bf16 output does not accumulate");
+        g.epi = EPI_STORE;
+    }
+    return gemm_bf16(g, s);
+}

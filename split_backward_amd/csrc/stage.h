@@ -1,0 +1,69 @@
+// Internal definition of the stage object shared by the C ABI, the passes
+// and the executor.
+#pragma once
+
+#include <array>
+#include <vector>
+
+#include "common.h"
+
+namespace zb {
+
+constexpr int MAX_RUN_OPS = 4096;  // executor stamp capacity (ops per run)
+
+// Stash tensor indices (the "which" argument of zb_stage_stash_tensor).
+enum { LIN_X = 0, LIN_DY = 1 };
+enum { MLP_X = 0, MLP_A = 1, MLP_H = 2, MLP_DY = 3, MLP_DA = 4 };
+enum {
+    L_X = 0, L_R1, L_N1, L_QKV, L_A, L_LSE, L_H1, L_R2, L_N2, L_GU, L_S,  // kept by F
+    L_DOUT, L_DGU, L_DN2, L_DH1, L_DQKV, L_DN1                            // kept by B
+};
+enum { PASS_F = 0, PASS_B = 1, PASS_W = 2 };
+
+struct Layout {
+    struct Tensor {
+        int layer, which, rows, cols, dtype;
+        size_t offset;  // within a slot
+    };
+    std::vector<Tensor> off;
+    size_t slot_bytes = 0, ring_bytes = 0, scratch_b = 0, scratch_w = 0, stamps_bytes = 0, total = 0;
+    void build(const zb_stage_desc& d);
+    const Tensor* find(int layer, int which) const;
+};
+
+struct Slot {
+    int mb = -1;  // resident microbatch, -1 = free
+    bool b_issued = false, w_issued = false;
+    bool w_event_valid = false;  // evW was recorded at least once
+    hipEvent_t evF = nullptr, evB = nullptr, evW = nullptr;
+};
+
+size_t weight_elems(const zb_stage_desc& d, int i);
+
+}  // namespace zb
+
+struct zb_stage {
+    zb_stage_desc desc{};
+    zb::Layout lay;
+    std::vector<void*> w;
+    std::vector<float*> dw;
+    char* ws = nullptr;
+    char* scratch_b = nullptr;
+    char* scratch_w = nullptr;
+    uint64_t* stamps = nullptr;
+    std::vector<zb::Slot> slots;
+    std::array<hipEvent_t, 3> chain{};     // last op of each pass (scratch reuse order)
+    std::array<bool, 3> chain_valid{};
+    int next_f = 0, next_w = 0;
+
+    ~zb_stage();
+    void* slot_tensor(int mb, int layer, int which) const;
+    int32_t order_after(int pass, hipEvent_t dep, bool dep_valid, hipStream_t s);
+    int32_t finish(int pass, hipEvent_t ev, hipStream_t s);
+};
+
+namespace zb {
+int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s);
+int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipStream_t s);
+int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s);
+}  // namespace zb

@@ -1,0 +1,184 @@
+"""GPU parity: libzb's F / B / W against the fp64 oracle, element by element,
+on the same seeded inputs (through the C ABI via the Python binding).
+
+Tolerances (relative Frobenius error per tensor, max over tensors):
+* fp32 linear stage: 1e-5.
+* bf16 stages (bf16 operands and stored activations, fp32 accumulation):
+  2e-2.
+* bare GEMM with bf16 output: 2.5e-3 -- the only error is the final
+  round-to-nearest to bf16 (relative error <= 2^-9 = 1.95e-3 per element)
+  plus fp32 accumulation error (~1e-6 at these K).
+* bare GEMM accumulating into fp32: 1e-5 (inputs are exact bf16 values; only
+  fp32 accumulation rounding remains).
+"""
+import numpy as np
+import pytest
+import torch
+
+import split_backward_amd as zb
+import synth
+from oracle import dense as od
+from tests.gpu_helpers import make_stage, max_rel, run_both, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    zb.lib()  # loud failure if the library was not built
+
+
+# ------------------------------------------------------------- bare GEMM ---
+
+def _bf16(name, shape, seed, std=1.0):
+    return synth.make_tensor(name, seed, shape, std, "bf16")
+
+
+@pytest.mark.parametrize("M,N,K", [(264, 136, 72), (512, 512, 512), (8, 8, 8), (1000, 24, 64), (256, 776, 1032)])
+def test_gemm_nt_bf16(M, N, K):
+    """F form: C = A . B^T with both operands K-contiguous."""
+    a, b = _bf16("a", (M, K), 11), _bf16("b", (N, K), 12)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    zb.gemm(to_dev(a), to_dev(b), c, a_kmajor=True, b_kmajor=True, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    assert od.rel_fro(to_f64(c), a.f64 @ b.f64.T) <= 2.5e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(264, 136, 72), (512, 512, 512), (8, 8, 8), (300, 1032, 24)])
+def test_gemm_nn_bf16(M, N, K):
+    """B form: C = A . W with W stored [K, N] (N contiguous)."""
+    a, w = _bf16("a", (M, K), 13), _bf16("w", (K, N), 14)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    zb.gemm(to_dev(a), to_dev(w), c, a_kmajor=True, b_kmajor=False, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    assert od.rel_fro(to_f64(c), a.f64 @ w.f64) <= 2.5e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(264, 136, 72), (512, 512, 512), (8, 8, 8), (136, 1032, 296)])
+def test_gemm_tn_accumulate_f32(M, N, K):
+    """W form: dW[M,N] += dY[K,M]^T . X[K,N], fp32 in place, twice."""
+    dy, x = _bf16("dy", (K, M), 15), _bf16("x", (K, N), 16)
+    c0 = synth.normal(17, (M, N), 1.0).astype(np.float32)
+    c = torch.from_numpy(c0.copy()).cuda()
+    for _ in range(2):
+        zb.gemm(to_dev(dy), to_dev(x), c, a_kmajor=False, b_kmajor=False, M=M, N=N, K=K, accumulate=True)
+    torch.cuda.synchronize()
+    ref = c0.astype(np.float64) + 2.0 * (dy.f64.T @ x.f64)
+    assert od.rel_fro(to_f64(c), ref) <= F32_TOL
+
+
+def test_gemm_fp32_all_layouts():
+    M, N, K = 200, 136, 72
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = rng.standard_normal((K, N)).astype(np.float32)
+    A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    ref = a.astype(np.float64) @ b.astype(np.float64)
+    for ak in (True, False):
+        for bk in (True, False):
+            Ad = A if ak else A.t().contiguous()
+            Bd = B.t().contiguous() if bk else B
+            c = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+            zb.gemm(Ad, Bd, c, a_kmajor=ak, b_kmajor=bk, M=M, N=N, K=K)
+            torch.cuda.synchronize()
+            assert od.rel_fro(to_f64(c), ref) <= F32_TOL, (ak, bk)
+
+
+# ---------------------------------------------------------------- stages ---
+
+def test_linear_fp32_workload_parity():
+    """fp32 linear layer X[128x256] W[256x256], m = 2, deferred W."""
+    wl = synth.WORKLOADS["linear_f32"]
+    gpu, orc, _ = run_both(wl["shape"], wl["m"])
+    r = max_rel(gpu, orc)
+    assert max(r.values()) <= F32_TOL, r
+
+
+def test_linear_fp32_ragged_parity():
+    shape = synth.StageShape("linear", 200, 136, 72, dtype="f32")
+    gpu, orc, _ = run_both(shape, 3, ring=3)
+    r = max_rel(gpu, orc)
+    assert max(r.values()) <= F32_TOL, r
+
+
+def test_linear_bf16_ragged_parity():
+    shape = synth.StageShape("linear", 296, 136, 520)
+    gpu, orc, _ = run_both(shape, 3)
+    r = max_rel(gpu, orc)
+    assert max(r.values()) <= BF16_TOL, r
+
+
+@pytest.mark.parametrize("kind_shape", [
+    synth.StageShape("linear", 128, 256, 256, dtype="f32"),
+    synth.StageShape("mlp", 296, 136, 520),
+])
+def test_deferred_equals_immediate_bitwise(kind_shape):
+    """F0 F1 B0 B1 W0 W1 == F0 B0 W0 F1 B1 W1 on the GPU, bit for bit: the W
+    kernel adds each microbatch into dW in issue order, without atomics."""
+    g1, _, _ = run_both(kind_shape, 2, order="deferred")
+    g2, _, _ = run_both(kind_shape, 2, order="immediate")
+    for k in ("y", "dx", "dw"):
+        for a, b in zip(g1[k], g2[k]):
+            assert np.array_equal(a, b), k
+
+
+def test_mlp_ragged_parity():
+    shape = synth.StageShape("mlp", 296, 136, 520)
+    gpu, orc, _ = run_both(shape, 3)
+    r = max_rel(gpu, orc)
+    assert max(r.values()) <= BF16_TOL, r
+
+
+def test_mlp_full_width_parity():
+    """GPT MLP at its full shape (s=2048, h=1024, ffn=4096), 2 microbatches."""
+    shape = synth.WORKLOADS["gpt_mlp_h1024"]["shape"]
+    gpu, orc, _ = run_both(shape, 2)
+    r = max_rel(gpu, orc)
+    assert max(r.values()) <= BF16_TOL, r
+
+
+@pytest.mark.parametrize("shape", [
+    synth.StageShape("llama", 256, 256, 344, n_layers=2, n_heads=2, n_kv_heads=1, head_dim=128),
+    synth.StageShape("llama", 384, 512, 1032, n_layers=1, n_heads=4, n_kv_heads=2, head_dim=128),
+    synth.StageShape("llama", 128, 384, 256, n_layers=1, n_heads=3, n_kv_heads=3, head_dim=128),
+])
+def test_llama_small_parity(shape):
+    gpu, orc, _ = run_both(shape, 2)
+    r = max_rel(gpu, orc)
+    assert max(r.values()) <= BF16_TOL, r
+
+
+# ------------------------------------------------------------ state errors --
+
+def test_stage_state_machine_errors():
+    shape = synth.StageShape("linear", 64, 64, 64)
+    st, _ = make_stage(shape, ring=2)
+    x = to_dev(synth.make_x(shape, 0))
+    dy = to_dev(synth.make_dy(shape, 0))
+    with pytest.raises(zb.ZbError) as e:
+        st.bwd_input(0, dy)
+    assert e.value.code == zb.ESTATE
+    st.fwd(0, x)
+    with pytest.raises(zb.ZbError) as e:
+        st.bwd_weight(0)
+    assert e.value.code == zb.ESTATE
+    with pytest.raises(zb.ZbError) as e:
+        st.fwd(2, x)              # out of order
+    assert e.value.code == zb.ESTATE
+    st.fwd(1, x)
+    with pytest.raises(zb.ZbError) as e:
+        st.fwd(2, x)              # ring of 2 is full: W(0) not issued
+    assert e.value.code == zb.ERING_FULL
+    st.bwd_input(0, dy)
+    with pytest.raises(zb.ZbError) as e:
+        st.bwd_input(0, dy)       # twice
+    assert e.value.code == zb.ESTATE
+    st.bwd_weight(0)
+    st.fwd(2, x)                  # slot freed by W(0)
+    with pytest.raises(zb.ZbError) as e:
+        st.zero_grad()            # microbatches 1 and 2 still in flight
+    assert e.value.code == zb.ESTATE
+    torch.cuda.synchronize()

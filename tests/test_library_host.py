@@ -1,0 +1,137 @@
+"""Host-side tests of libzb (no GPU): the library loads and exports every
+symbol include/zb.h declares, the schedule generator matches the oracle
+simulator bit for bit, and argument validation rejects bad calls before
+anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import split_backward_amd as zb
+from oracle.schedule import simulate
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "zb.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(zb_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = zb.lib()
+    declared = _declared_symbols()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(zb.EXPORTS)
+
+
+def test_version_string():
+    assert b"gfx950" in zb.lib().zb_version()
+
+
+def _grid():
+    for p in (1, 2, 3, 5, 8, 12, 16):
+        for m in (1, 2, 7, 16, 33, 48):
+            for kind in ("gpipe", "1f1b", "zb"):
+                Ms = sorted({p, p + 1, (3 * p) // 2, 2 * p}) if kind == "zb" else [0]
+                for M in Ms:
+                    yield kind, p, m, M
+
+
+@pytest.mark.parametrize("costs", [(1, 1, 1), (2, 3, 1)])
+def test_generator_matches_oracle_bit_exact(costs):
+    n = 0
+    for kind, p, m, M in _grid():
+        if p * m > 400 and costs != (1, 1, 1):
+            continue
+        ref = simulate(kind, p, m, M=M, costs=costs)
+        for stage in sorted({0, p // 2, p - 1}):
+            got = zb.schedule_generate(kind, p, m, M, costs, stage)
+            assert got["ops"] == ref.order(stage), (kind, p, m, M, stage)
+            assert got["start"] == [o.start for o in ref.ops[stage]]
+            assert got["end"] == [o.end for o in ref.ops[stage]]
+            assert got["arrive_f"] == ref.arrive_f[stage]
+            assert got["arrive_b"] == ref.arrive_b[stage]
+            assert got["makespan"] == ref.makespan
+            assert got["busy"] == ref.stats[stage].busy
+            assert got["peak_active"] == ref.stats[stage].peak_active
+            n += 1
+    assert n > 100
+
+
+def test_generator_headline_stage():
+    """Stage 3 of p=8, m=16: 1F1B and ZB(2p) orders and windows."""
+    one = zb.schedule_generate("1f1b", 8, 16, 0, (1, 1, 1), 3)
+    z16 = zb.schedule_generate("zb", 8, 16, 16, (1, 1, 1), 3)
+    assert one["makespan"] == 69 and z16["makespan"] == 55
+    assert (one["first_start"], one["last_end"]) == (3, 63)
+    assert (z16["first_start"], z16["last_end"]) == (3, 51)
+    assert z16["busy"] == z16["last_end"] - z16["first_start"]  # zero in-window idle
+
+
+def test_generator_rejects_bad_arguments():
+    L = zb.lib()
+    assert L.zb_schedule_generate(zb.SCHED_ZB, 4, 8, 0, 1, 1, 1, 0, None, None, None, 0, None, None, None) == zb.EINVAL
+    assert L.zb_schedule_generate(zb.SCHED_ZB, 4, 8, 4, 1, 1, 0, 0, None, None, None, 0, None, None, None) == zb.EINVAL
+    assert L.zb_schedule_generate(zb.SCHED_1F1B, 4, 8, 0, 1, 1, 1, 4, None, None, None, 0, None, None, None) == zb.EINVAL
+    ops = (zb.Op * 3)()
+    assert L.zb_schedule_generate(zb.SCHED_1F1B, 4, 8, 0, 1, 1, 1, 0, ops, None, None, 3, None, None, None) == zb.EINVAL
+    assert L.zb_schedule_generate(9, 4, 8, 0, 1, 1, 1, 0, None, None, None, 0, None, None, None) == zb.EINVAL
+    # memory limit 1 with p = 3 still makes progress (one microbatch at a time)
+    assert L.zb_schedule_generate(zb.SCHED_ZB, 3, 4, 1, 1, 1, 1, 0, None, None, None, 0, None, None, None) == 12
+
+
+def _desc(**kw):
+    base = dict(kind=zb.LLAMA, dtype=zb.BF16, n_layers=4, tokens=4096, hidden=4096, ffn=11008, n_heads=32,
+                n_kv_heads=32, head_dim=128, rms_eps=1e-5, ring_slots=16)
+    base.update(kw)
+    return zb.StageDesc(*[base[f] for f, _ in zb.StageDesc._fields_])
+
+
+def test_workspace_sizes_and_weight_counts():
+    L = zb.lib()
+    d = _desc()
+    assert L.zb_stage_num_weights(ctypes.byref(d)) == 24
+    ws = L.zb_stage_workspace_bytes(ctypes.byref(d))
+    # 16 slots of 4 layers of stash, roughly 1.06 GB per layer per microbatch
+    assert 60e9 < ws < 75e9
+    lin = _desc(kind=zb.LINEAR, dtype=zb.F32, n_layers=1, tokens=128, hidden=256, ffn=256, ring_slots=2)
+    assert L.zb_stage_num_weights(ctypes.byref(lin)) == 1
+    assert L.zb_stage_workspace_bytes(ctypes.byref(lin)) >= 2 * (128 * 256 * 4 * 2)
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=64), dict(n_kv_heads=5), dict(ring_slots=0), dict(hidden=4100),
+                                 dict(dtype=zb.F32), dict(tokens=0), dict(kind=7)])
+def test_invalid_descs_rejected(bad):
+    L = zb.lib()
+    d = _desc(**bad)
+    assert L.zb_stage_workspace_bytes(ctypes.byref(d)) == 0
+    assert L.zb_stage_num_weights(ctypes.byref(d)) == zb.EINVAL
+    assert len(zb.last_error()) > 5
+
+
+def test_gemm_rejects_bad_shapes_before_launch():
+    L = zb.lib()
+    fake = ctypes.c_void_p(0x1000)
+    # K not a multiple of 8 (bf16 vector loads)
+    assert L.zb_gemm(zb.BF16, 64, 64, 12, fake, 16, 1, fake, 16, 1, fake, 64, 0, 0, None) == zb.EINVAL
+    # leading dimension smaller than the row
+    assert L.zb_gemm(zb.BF16, 64, 64, 64, fake, 32, 1, fake, 64, 1, fake, 64, 0, 0, None) == zb.EINVAL
+    # bf16 output cannot accumulate
+    assert L.zb_gemm(zb.BF16, 64, 64, 64, fake, 64, 1, fake, 64, 1, fake, 64, 0, 1, None) == zb.EINVAL
+    # empty shape
+    assert L.zb_gemm(zb.BF16, 0, 64, 64, fake, 64, 1, fake, 64, 1, fake, 64, 0, 0, None) == zb.EINVAL
+    assert L.zb_gemm(zb.F32, 8, 8, 8, None, 8, 1, fake, 8, 1, fake, 8, 1, 0, None) == zb.EINVAL
+
+
+def test_compute_calls_reject_null_stage():
+    L = zb.lib()
+    assert L.zb_fwd(None, 0, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == zb.EINVAL
+    assert L.zb_bwd_input(None, 0, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == zb.EINVAL
+    assert L.zb_bwd_weight_accum(None, 0, None) == zb.EINVAL
+    assert L.zb_stage_zero_grad(None, None) == zb.EINVAL
