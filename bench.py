@@ -1,0 +1,259 @@
+"""Benchmark of the split-backward stage on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b_stage4]
+
+A step is one whole iteration of the stage's hot path over one batch: the
+dW buffers are cleared, then F, B and W run for every microbatch in the
+zero-bubble order (memory limit 2p) that the library's generator produces
+for stage 3 of an emulated 8-stage pipeline, back to back on one stream with
+all inputs already in HBM.  `value` = linear-layer FLOPs of F + B + W
+(2*M*N*K per product, attention and RMSNorm excluded from the count but not
+from the time) / wall time of the step.
+
+Extra fields on the JSON line:
+* roofline: the W-pass GEMM kernel (the kernel with the largest share of the
+  step time), its algorithmic flops / its average launch time, the launches
+  replayed on the benchmark stream and timed with HIP events.
+* cpu_baseline: the fp64 oracle timed on this host on a bounded sample
+  (one decoder layer, one microbatch, 256 tokens, full widths).
+* executor: the stage replayed with emulated arrivals (device-clock waits)
+  for the 1F1B and zero-bubble orders; in-window idle fraction of each.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+
+
+def linear_flops_per_mb(s) -> float:
+    """2*M*N*K of every linear product of F, B and W for one microbatch."""
+    T, H, F = s.tokens, s.hidden, s.ffn
+    if s.kind == "linear":
+        return 3 * 2.0 * T * H * F
+    if s.kind == "mlp":
+        return 3 * 2 * 2.0 * T * H * F
+    qkv = s.q_dim + 2 * s.kv_dim
+    per_pass = 2.0 * T * H * (qkv + s.q_dim + 2 * F + F)
+    return 3 * per_pass * s.n_layers
+
+
+def w_pass_gemms(s):
+    """(M, N, K) of the W-pass products of one microbatch."""
+    T, H, F = s.tokens, s.hidden, s.ffn
+    if s.kind == "llama":
+        qkv = s.q_dim + 2 * s.kv_dim
+        return [(qkv, H, T), (H, s.q_dim, T), (2 * F, H, T), (H, F, T)] * s.n_layers
+    if s.kind == "mlp":
+        return [(F, H, T), (H, F, T)]
+    return [(F, H, T)]
+
+
+def make_inputs(shape, m, device):
+    import torch
+    from tests.gpu_helpers import to_dev
+    import synth
+    xs = [to_dev(synth.make_x(shape, j), device) for j in range(m)]
+    dys = [to_dev(synth.make_dy(shape, j), device) for j in range(m)]
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    out_w = shape.ffn if shape.kind == "linear" else shape.hidden
+    ys = [torch.empty((shape.tokens, out_w), dtype=dt, device=device) for _ in range(m)]
+    dxs = [torch.empty((shape.tokens, shape.hidden), dtype=dt, device=device) for _ in range(m)]
+    return xs, ys, dys, dxs
+
+
+def time_w_kernel(shape, device, reps=5):
+    """Average launch time of the W-pass GEMM kernel at the step's shapes,
+    launched through the C ABI on the current stream, timed with events."""
+    import torch
+    import split_backward_amd as zb
+    gem = w_pass_gemms(shape)
+    bufs = []
+    for (M, N, K) in gem:
+        A = torch.randn((K, M), device=device).to(torch.bfloat16)
+        B = torch.randn((K, N), device=device).to(torch.bfloat16)
+        C = torch.zeros((M, N), device=device, dtype=torch.float32)
+        bufs.append((A, B, C, M, N, K))
+
+    def once():
+        for A, B, C, M, N, K in bufs:
+            zb.gemm(A, B, C, a_kmajor=False, b_kmajor=False, M=M, N=N, K=K, accumulate=True)
+
+    once()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        once()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    launches = reps * len(gem)
+    flops = reps * sum(2.0 * M * N * K for M, N, K in gem)
+    avg_ms = ms_total / launches
+    achieved = flops / (ms_total * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel": "gemm_bf16_kernel<false,false,EPI_ACCUM_F32> (W pass: dW += dY^T X, fp32 in place)",
+            "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
+
+
+def cpu_baseline(shape):
+    """fp64 oracle on a bounded sample: one decoder layer (or the whole
+    stage for the small kinds), one microbatch, F + B + W."""
+    import numpy as np
+    import synth
+    from oracle import dense as od
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    if shape.kind == "llama":
+        sample = synth.StageShape("llama", 256, shape.hidden, shape.ffn, n_layers=1, n_heads=shape.n_heads,
+                                  n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim)
+        desc = f"one decoder layer, one microbatch, 256 tokens, h={shape.hidden}, ffn={shape.ffn}"
+    elif shape.kind == "mlp":
+        sample = synth.StageShape("mlp", 512, shape.hidden, shape.ffn)
+        desc = f"one microbatch, 512 tokens, h={shape.hidden}, ffn={shape.ffn}"
+    else:
+        sample = shape
+        desc = "one microbatch of the full shape"
+    w = synth.make_weights(sample)
+    dims = od.LlamaDims(sample.hidden, sample.ffn, sample.n_heads, sample.n_kv_heads, sample.head_dim) \
+        if sample.kind == "llama" else None
+    x = synth.make_x(sample, 0).f64
+    dy = synth.make_dy(sample, 0).f64
+    reps, t_total = 0, 0.0
+    while t_total < 8.0 and reps < 50:
+        st = od.Stage(sample.kind, [t.f64 for t in w], dims, sample.n_layers)
+        t0 = time.perf_counter()
+        st.fwd(0, x)
+        st.bwd_input(0, dy)
+        st.bwd_weight(0)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    flops = reps * linear_flops_per_mb(sample)
+    return {"value": round(flops / t_total / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{desc}; fp64 numpy; {reps} repetitions in {t_total:.1f} s"}
+
+
+def executor_idle(stage, shape, m, xs, ys, dys, dxs, unit_ms):
+    """Replay stage 3 of an emulated p=8 pipeline with arrivals from the
+    generator at costs 1:1:1; returns in-window idle of each order."""
+    import torch
+    import split_backward_amd as zb
+    out = {}
+    for name, kind, M in (("1f1b", "1f1b", 0), ("zb_M16", "zb", 16), ("zb_M8", "zb", 8)):
+        if M > stage.desc.ring_slots:
+            continue
+        g = zb.schedule_generate(kind, 8, m, M, (1, 1, 1), 3)
+        stage.zero_grad()
+        torch.cuda.synchronize()
+        r = stage.run_schedule(g["ops"], g["arrive_f"], g["arrive_b"], unit_ms, xs, ys, dys, dxs,
+                               mode=zb.EXEC_ORDERED)
+        out[name] = {"in_window_idle": round(r["in_window_idle"], 5), "window_ms": round(r["window_ms"], 2),
+                     "busy_ms": round(r["busy_ms"], 2),
+                     "predicted_window_units": g["last_end"] - g["first_start"],
+                     "predicted_in_window_idle": round(1 - g["busy"] / (g["last_end"] - g["first_start"]), 5),
+                     "stage_end_ms": round(r["t_last_end_ms"], 2)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama7b_stage4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-executor", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import split_backward_amd as zb
+    import synth
+    from tests.gpu_helpers import to_dev
+
+    wl = synth.WORKLOADS[args.workload]
+    shape, m = wl["shape"], wl["m"]
+    ring = wl.get("ring", m)
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    weights = [to_dev(w, device) for w in synth.make_weights(shape)]
+    stage = zb.Stage(shape.kind, shape.tokens, shape.hidden, shape.ffn, weights, dtype=shape.dtype,
+                     n_layers=shape.n_layers, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
+                     head_dim=shape.head_dim if shape.kind == "llama" else 128, ring_slots=ring)
+    xs, ys, dys, dxs = make_inputs(shape, m, device)
+    # zero-bubble order of stage 3 in an emulated 8-stage pipeline, memory limit min(2p, ring)
+    order = zb.schedule_generate("zb", 8, m, min(16, ring), (1, 1, 1), 3)["ops"]
+
+    def step():
+        stage.zero_grad()
+        for t, j in order:
+            if t == "F":
+                stage.fwd(j, xs[j], ys[j])
+            elif t == "B":
+                stage.bwd_input(j, dys[j], dxs[j])
+            else:
+                stage.bwd_weight(j)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    flops = linear_flops_per_mb(shape) * m
+    tflops = flops / dt / 1e12
+
+    # per-pass unit time (for the executor's arrival unit u = mean of F, B, W)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stage.zero_grad()
+    ev[0].record()
+    stage.fwd(0, xs[0], ys[0])
+    ev[1].record()
+    stage.bwd_input(0, dys[0], dxs[0])
+    ev[2].record()
+    stage.bwd_weight(0)
+    ev[3].record()
+    torch.cuda.synchronize()
+    t_f, t_b, t_w = (ev[i].elapsed_time(ev[i + 1]) for i in range(3))
+    unit_ms = (t_f + t_b + t_w) / 3.0
+
+    roof = time_w_kernel(shape, device)
+    extra = {}
+    if shape.kind == "llama" and not args.no_executor:
+        extra["executor_p8_stage3"] = executor_idle(stage, shape, m, xs, ys, dys, dxs, unit_ms)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(shape)
+
+    line = {
+        "metric": "stage F+B+W TFLOP/s (bf16) and % MFMA peak; stage idle fraction vs 1F1B",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": shape.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": shape.tokens, "hidden": shape.hidden, "ffn": shape.ffn,
+                   "n_layers": shape.n_layers, "n_heads": shape.n_heads, "n_kv_heads": shape.n_kv_heads,
+                   "microbatches": m, "ring_slots": ring, "order": "zero-bubble greedy, M=min(16, ring), stage 3 of p=8"},
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "pass_ms": {"F": round(t_f, 3), "B": round(t_b, 3), "W": round(t_w, 3)},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
