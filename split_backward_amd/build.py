@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libzb.so")
 
-SOURCES = ["errors.cpp", "gemm.hip", "norm.hip", "attention.hip", "stage.cpp", "passes.cpp",
+SOURCES = ["errors.cpp", "gemm.hip", "gemm_v2.hip", "norm.hip", "attention.hip", "stage.cpp", "passes.cpp",
            "schedule.cpp", "executor.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -59,6 +59,10 @@ struct GemmDesc {
 };
 
 int32_t gemm_bf16(const GemmDesc& d, hipStream_t s);
+// Direct-to-LDS kernel; sets *handled = false (and does nothing) when an
+// operand is too large for one buffer range or the epilogue cannot use
+// vector accesses (the first-generation kernel then runs).
+int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled);
 int32_t gemm_f32(const GemmDesc& d, int accumulate, hipStream_t s);
 
 // ------------------------------------------------- elementwise / norms ----

@@ -22,6 +22,8 @@
 // ("Core Innovation 1"): GeLU(tanh) forward and backward, SwiGLU forward
 // (paired gate/up tiles) and backward, the residual add and the in-place fp32
 // weight-gradient accumulation of the W pass.
+#include <cstdlib>
+
 #include "common.h"
 
 namespace zb {
@@ -340,6 +342,12 @@ int32_t gemm_bf16(const GemmDesc& d, hipStream_t s) {
         return fail(ZB_EINVAL, "gemm_bf16: operands must be 16-byte aligned");
     const bool paired = d.epi == EPI_SWIGLU_FWD;
     if (paired && (!d.b_kmajor || d.half_n <= 0)) return fail(ZB_EINVAL, "gemm_bf16: bad SwiGLU pairing");
+    static const bool force_v1 = getenv("ZB_GEMM_V1") != nullptr;
+    if (!force_v1) {
+        bool handled = false;
+        const int32_t rc = gemm_bf16_v2(d, s, &handled);
+        if (handled || rc != ZB_OK) return rc;
+    }
     const int tiles_m = (d.M + BM - 1) / BM;
     const int tiles_n = paired ? (d.half_n + BN / 2 - 1) / (BN / 2) : (d.N + BN - 1) / BN;
     if (d.a_kmajor && d.b_kmajor) return launch_epi<true, true>(d, s, tiles_m, tiles_n);

@@ -1,0 +1,470 @@
+// bf16 GEMM, second generation: direct-to-LDS operand staging.
+//
+// Workgroup tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each
+// wave owning a 128 x 128 sub-tile = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
+// (256 fp32 accumulators per lane, held in AGPRs).
+//
+// Operands go HBM -> LDS with buffer_load ... lds (16 bytes per lane): no
+// VGPR staging, no ds_write, and out-of-range rows / columns / k read as zero
+// through the buffer range check.  Each operand keeps its HBM orientation in
+// LDS:
+//   K-contiguous operand  -> LDS [256 rows][64 k], 128-byte rows, 16-byte
+//                            chunks XOR-swizzled by the row; an MFMA fragment
+//                            (8 consecutive k of one row) is one ds_read_b128.
+//   M/N-contiguous operand -> LDS [64 k][256 cols], 512-byte rows, 32-byte
+//                            pieces XOR-swizzled by k; a fragment is two
+//                            ds_read_b64_tr_b16, the gfx950 LDS transpose
+//                            read (in each 16-lane group, output lane i,
+//                            slot s takes element i%4 of the load of lane
+//                            4s + i/4), so the lane receives 8 consecutive k
+//                            of its column.
+// Four LDS stages of 32-k tiles (128 KB): the DMA of k-tiles t+1..t+3 is in
+// flight while tile t is multiplied (three tiles of prefetch hide HBM latency
+// with one wave per SIMD), and fragments of the next 16-k step are read while
+// the MFMAs of the current step issue.  DMA addressing costs no VALU: each
+// lane's offset is fixed once, and the buffer base advances in scalar
+// registers from tile to tile.
+#include "common.h"
+
+namespace zb {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, STAGES = 4;
+constexpr int TILE_BYTES = 256 * BK * 2;  // 16 KB per operand tile
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+constexpr int DMA_PER_TILE = 2 * (TILE_BYTES / 1024) / 4;  // per wave, A + B
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 16-byte chunk swizzle of a K-contiguous tile (64-byte rows): the rows a
+// ds_read_b128 serves together (8 or 16 lanes) hit distinct bank windows.
+__device__ __forceinline__ int key_km(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 32-byte piece swizzle of an M/N-contiguous tile row k: the 4 rows a 16-lane
+// group reads in one transpose instruction land in 4 distinct 32-byte bank
+// windows (and the 8 pieces of a 32-lane half in 8), conflict-free for both
+// 32 and 64 four-byte banks.  Depends only on k & 3, so it is the same for
+// every 16-k step and the step offsets fold into the instruction offset.
+__device__ __forceinline__ int key_mn(int k) { return ((k & 3) << 1) | ((k >> 1) & 1); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // any offset >= the buffer size reads as zero
+
+// ---- DMA of one operand tile (4 instructions per wave, 1 KB each) ---------
+// Per-lane byte offsets relative to the tile's first k are computed once;
+// rows / columns outside the operand get OOB.  K-contiguous: instruction i of
+// wave w covers tile rows 16b..16b+15 with b = 4i + w.  `k_lim` (elements,
+// relative to the tile's first k) marks k beyond K as OOB; a full tile passes
+// BK and needs no check.
+template <bool PAIRED>
+__device__ __forceinline__ void dma_offsets_kmaj(uint32_t (&off)[4], int64_t ld, int row0, int rows_total,
+                                                 int half_n, int k_lim, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = i * 4 + wave;
+        const int r = b * 16 + (lane >> 2);
+        const int kc = (lane & 3) ^ key_km(r);
+        int grow;
+        bool ok;
+        if (PAIRED) {
+            const int rr = row0 + (r & 127);
+            ok = rr < half_n;
+            grow = (r < 128) ? rr : half_n + rr;
+        } else {
+            grow = row0 + r;
+            ok = grow < rows_total;
+        }
+        off[i] = (ok && kc * 8 < k_lim) ? (uint32_t)(((int64_t)grow * ld + kc * 8) * 2) : OOB;
+    }
+}
+
+// M/N-contiguous: instruction i of wave w covers k rows 2b, 2b+1 (b = 4i + w);
+// k beyond K falls past the end of the (advanced) buffer range.
+__device__ __forceinline__ void dma_offsets_mnmaj(uint32_t (&off)[4], int64_t ld, int col0, int cols_total, int lane,
+                                                  int wave) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = i * 4 + wave;
+        const int k = b * 2 + (lane >> 5);
+        const int piece = ((lane & 31) >> 1) ^ key_mn(k);  // logical 32-byte piece at this slot
+        const int col = piece * 16 + (lane & 1) * 8;
+        const int gc = col0 + col;
+        off[i] = (gc < cols_total) ? (uint32_t)(((int64_t)k * ld + gc) * 2) : OOB;
+    }
+}
+
+__device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rs, lds_void* tile, const uint32_t (&off)[4],
+                                          int wave) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = i * 4 + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((__attribute__((address_space(3))) char*)tile + b * 1024),
+                                                 16, off[i], 0, 0, 0);
+    }
+}
+
+// ---- fragment reads ------------------------------------------------------
+// K-contiguous tile: row `row`, k step kk, lane group g = lane/32.
+__device__ __forceinline__ bf16x8 frag_kmaj(const lds_void* tile, int row, int kk, int g) {
+    const int chunk = (kk * 2 + g) ^ key_km(row);
+    return *(const lds_bf16x8*)((const __attribute__((address_space(3))) char*)tile + row * (BK * 2) + chunk * 16);
+}
+
+// M/N-contiguous tile ([BK][256], 512-byte rows): 32-wide block `blk` (0..7), k step kk.
+// The two transpose reads are issued as inline asm: the compiler cannot tell
+// the intrinsic form from the in-flight LDS DMA of later stages and would wait
+// for all of it.  The caller waits for the results with lds_wait().
+__device__ __forceinline__ bf16x8 frag_mnmaj(const lds_void* tile, int blk, int kk, int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int s = j >> 2, q = j & 3;
+    const int piece = (blk * 2 + (G & 1)) ^ key_mn(s);  // k & 3 == s for both reads
+    const int r0 = (G >> 1) * 8 + s;                     // row within the 16-k step
+    const uint32_t addr = (uint32_t)(uintptr_t)tile + kk * 16 * 512 + r0 * 512 + piece * 32 + q * 8;
+    u32x2 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(addr));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(hi) : "v"(addr));
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Wait for every outstanding LDS read; the fragments become outputs of the
+// wait so no use of them is scheduled above it.
+__device__ __forceinline__ void lds_wait(bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+
+// Scheduling pattern for one 16-k step: 8 slots, each holding its share of
+// the RD LDS reads followed by 2 MFMAs.
+template <int RD, int SLOT>
+__device__ __forceinline__ void interleave_reads_mfma() {
+    if constexpr (SLOT < 8) {
+        constexpr int n = ((SLOT + 1) * RD) / 8 - (SLOT * RD) / 8;
+        if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        interleave_reads_mfma<RD, SLOT + 1>();
+    }
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies: that
+// fence waits for every outstanding load, including the DMA of tiles that are
+// meant to stay in flight.  Callers wait for exactly the tile they need
+// (s_waitcnt vmcnt(n)) first; every LDS read of the stage being recycled has
+// been consumed by an MFMA, so it has completed.
+__device__ __forceinline__ void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ float gelu_tanh_f(float a) {
+    const float c = 0.7978845608028654f, k = 0.044715f;
+    return 0.5f * a * (1.f + tanhf(c * (a + k * a * a * a)));
+}
+__device__ __forceinline__ float gelu_tanh_grad_f(float a) {
+    const float c = 0.7978845608028654f, k = 0.044715f;
+    const float t = tanhf(c * (a + k * a * a * a));
+    return 0.5f * (1.f + t) + 0.5f * a * (1.f - t * t) * c * (1.f + 3.f * k * a * a);
+}
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int nwg = tiles_m * tiles_n;
+    const int xcd = bid & 7, local = bid >> 3;
+    const int q = nwg >> 3, r = nwg & 7;
+    const int tile = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+    constexpr int G = 4;
+    const int per_group = G * tiles_n;
+    const int group = tile / per_group;
+    const int first_m = group * G;
+    const int gsize = min(tiles_m - first_m, G);
+    const int in_group = tile - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+template <bool A_KMAJ, bool B_KMAJ, int EPI>
+__global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, uint32_t a_bytes,
+                                                       uint32_t b_bytes) {
+    constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int g = lane >> 5, lrow = lane & 31;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = PAIRED ? tn * (BN / 2) : tn * BN;
+    const int nk = (d.K + BK - 1) / BK;
+    const int k_tail = d.K - (nk - 1) * BK;  // k extent of the last tile (1..BK)
+
+    uint32_t offa[4], offb[4];
+    if (A_KMAJ) dma_offsets_kmaj<false>(offa, d.lda, m0, d.M, 0, BK, lane, wave);
+    else dma_offsets_mnmaj(offa, d.lda, m0, d.M, lane, wave);
+    if (B_KMAJ) dma_offsets_kmaj<PAIRED>(offb, d.ldb, n0, d.N, d.half_n, BK, lane, wave);
+    else dma_offsets_mnmaj(offb, d.ldb, n0, d.N, lane, wave);
+    // Byte step of the buffer base per k-tile.
+    const int64_t step_a = A_KMAJ ? BK * 2 : (int64_t)BK * d.lda * 2;
+    const int64_t step_b = B_KMAJ ? BK * 2 : (int64_t)BK * d.ldb * 2;
+
+    auto dma_tile = [&](int kt) {
+        char* st = smem + (kt % STAGES) * STAGE_BYTES;
+        const uint32_t adv_a = (uint32_t)(kt * step_a), adv_b = (uint32_t)(kt * step_b);
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(static_cast<const char*>(d.A) + adv_a, a_bytes - adv_a);
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(static_cast<const char*>(d.B) + adv_b, b_bytes - adv_b);
+        if (kt == nk - 1 && k_tail < BK) {  // partial last tile: mask k >= K on K-contiguous operands
+            uint32_t ta[4], tb[4];
+            if (A_KMAJ) dma_offsets_kmaj<false>(ta, d.lda, m0, d.M, 0, k_tail, lane, wave);
+            else dma_offsets_mnmaj(ta, d.lda, m0, d.M, lane, wave);
+            if (B_KMAJ) dma_offsets_kmaj<PAIRED>(tb, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
+            else dma_offsets_mnmaj(tb, d.ldb, n0, d.N, lane, wave);
+            dma_issue(ra, (lds_void*)st, ta, wave);
+            dma_issue(rb, (lds_void*)(st + TILE_BYTES), tb, wave);
+        } else {
+            dma_issue(ra, (lds_void*)st, offa, wave);
+            dma_issue(rb, (lds_void*)(st + TILE_BYTES), offb, wave);
+        }
+    };
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    auto frag_a = [&](const lds_void* ta, int mi, int kk) -> bf16x8 {
+        if (A_KMAJ) return frag_kmaj(ta, wm * 128 + mi * 32 + lrow, kk, g);
+        return frag_mnmaj(ta, wm * 4 + mi, kk, lane);
+    };
+    auto frag_b = [&](const lds_void* tb, int ni, int kk) -> bf16x8 {
+        if (B_KMAJ) {
+            const int row = PAIRED ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + lrow) : (wn * 128 + ni * 32 + lrow);
+            return frag_kmaj(tb, row, kk, g);
+        }
+        return frag_mnmaj(tb, wn * 4 + ni, kk, lane);
+    };
+
+    constexpr int RD_A = A_KMAJ ? 1 : 2, RD_B = B_KMAJ ? 1 : 2;
+    constexpr int RD = 4 * (RD_A + RD_B);  // LDS read instructions per 16-k step
+
+    // Prologue: tiles 0..2 in flight, wait for tile 0.
+    const int pre = nk < STAGES - 1 ? nk : STAGES - 1;
+    for (int t = 0; t < pre; ++t) dma_tile(t);
+    if (pre >= 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (pre == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    workgroup_barrier();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+        const lds_void* ta = (const lds_void*)st;
+        const lds_void* tb = (const lds_void*)(st + TILE_BYTES);
+        bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+        // region 1: fragments of k step 0 (their LDS latency overlaps the DMA issue)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fa0[i] = frag_a(ta, i, 0);
+            fb0[i] = frag_b(tb, i, 0);
+        }
+        if (kt + STAGES - 1 < nk) dma_tile(kt + STAGES - 1);  // into the stage freed by the last barrier
+        __builtin_amdgcn_sched_barrier(0);
+        if (!A_KMAJ || !B_KMAJ) lds_wait(fa0, fb0);
+        // region 2: fragments of k step 1 interleaved with the MFMAs of step 0
+        // (with transpose reads: all reads first, then the MFMAs)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fa1[i] = frag_a(ta, i, 1);
+            fb1[i] = frag_b(tb, i, 1);
+        }
+        if (!A_KMAJ || !B_KMAJ) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mi], fb0[ni], acc[mi][ni], 0, 0, 0);
+        if (A_KMAJ && B_KMAJ) interleave_reads_mfma<RD, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (!A_KMAJ || !B_KMAJ) lds_wait(fa1, fb1);
+        // region 3: MFMAs of step 1
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // tile kt+1 must have landed; later tiles may stay in flight
+        if (kt + 3 < nk) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (kt + 2 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        workgroup_barrier();
+    }
+
+    // ---- epilogue ---------------------------------------------------------
+    // The accumulators of a 32-row block (mi) go through the wave's own LDS
+    // region (the k-tile stages are free now) so that each lane then owns 4
+    // consecutive columns of a row: global traffic is 16-byte (fp32) or
+    // 8-byte (bf16) per lane, and every global load of a block is issued
+    // before any of its values is needed.  Same-wave LDS accesses are ordered,
+    // so no barrier is needed.  (Unaligned leading dimensions or widths not
+    // divisible by 4 are routed to the first-generation kernel instead.)
+    constexpr int P = 132;  // floats per staged row: 128 + 4 padding
+    float* stage = reinterpret_cast<float*>(smem) + wave * 32 * P;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int rbase = m0 + wm * 128 + mi * 32;
+        if (!PAIRED) {
+            const int c4 = (lane & 31) * 4;
+            const int gcol = n0 + wn * 128 + c4;
+            const bool col_ok = gcol < d.N;
+            constexpr int IT = 16;  // rows 2*it + lane/32
+            floatx4 cin[IT];
+            u32x2 rin[IT], rin2[IT];
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int row = rbase + 2 * it + (lane >> 5);
+                if (row < d.M && col_ok) {
+                    if (EPI == EPI_ACCUM_F32)
+                        cin[it] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(d.C) + (int64_t)row * d.ldc + gcol);
+                    if (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD)
+                        rin[it] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16_t*>(d.R) + (int64_t)row * d.ldr + gcol);
+                    if (EPI == EPI_SWIGLU_BWD)
+                        rin2[it] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16_t*>(d.R) + (int64_t)row * d.ldr + d.half_n + gcol);
+                }
+            }
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    stage[((r >> 2) * 8 + g * 4 + (r & 3)) * P + ni * 32 + lrow] = acc[mi][ni][r];
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int lr = 2 * it + (lane >> 5);
+                const int row = rbase + lr;
+                if (row >= d.M || !col_ok) continue;
+                const floatx4 v = *reinterpret_cast<const floatx4*>(stage + lr * P + c4);
+                if (EPI == EPI_ACCUM_F32) {
+                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(d.C) + (int64_t)row * d.ldc + gcol) = cin[it] + v;
+                    continue;
+                }
+                float o[4], o2[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = v[e];
+                    const uint32_t rw = (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD) ? rin[it][e >> 1] : 0u;
+                    const float rv = (e & 1) ? __uint_as_float(rw & 0xffff0000u) : __uint_as_float(rw << 16);
+                    if (EPI == EPI_STORE) o[e] = x;
+                    else if (EPI == EPI_RESID) o[e] = x + rv;
+                    else if (EPI == EPI_GELU_FWD) { o[e] = x; o2[e] = gelu_tanh_f(x); }
+                    else if (EPI == EPI_GELU_BWD) o[e] = x * gelu_tanh_grad_f(rv);
+                    else if (EPI == EPI_SWIGLU_BWD) {
+                        const uint32_t uw = rin2[it][e >> 1];
+                        const float u = (e & 1) ? __uint_as_float(uw & 0xffff0000u) : __uint_as_float(uw << 16);
+                        const float sg = sigmoid_f(rv);
+                        o[e] = x * u * sg * (1.f + rv * (1.f - sg));
+                        o2[e] = x * rv * sg;
+                    }
+                }
+                auto pack4 = [](const float (&f)[4]) {
+                    return u32x2{uint32_t(f2bf(f[0])) | (uint32_t(f2bf(f[1])) << 16),
+                                 uint32_t(f2bf(f[2])) | (uint32_t(f2bf(f[3])) << 16)};
+                };
+                bf16_t* crow = reinterpret_cast<bf16_t*>(d.C) + (int64_t)row * d.ldc;
+                *reinterpret_cast<u32x2*>(crow + gcol) = pack4(o);
+                if (EPI == EPI_GELU_FWD)
+                    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(d.C2) + (int64_t)row * d.ldc2 + gcol) = pack4(o2);
+                if (EPI == EPI_SWIGLU_BWD) *reinterpret_cast<u32x2*>(crow + d.half_n + gcol) = pack4(o2);
+            }
+        } else {
+            // paired SwiGLU forward: staged columns 0..63 are gate, 64..127 up
+            const int c4 = (lane & 15) * 4;
+            const int gcol = n0 + wn * 64 + c4;
+            const bool col_ok = gcol < d.half_n;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    stage[((r >> 2) * 8 + g * 4 + (r & 3)) * P + ni * 32 + lrow] = acc[mi][ni][r];
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int lr = 4 * it + (lane >> 4);
+                const int row = rbase + lr;
+                if (row >= d.M || !col_ok) continue;
+                const floatx4 gv = *reinterpret_cast<const floatx4*>(stage + lr * P + c4);
+                const floatx4 uv = *reinterpret_cast<const floatx4*>(stage + lr * P + 64 + c4);
+                float og[4], ou[4], os[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    og[e] = gv[e];
+                    ou[e] = uv[e];
+                    os[e] = gv[e] * sigmoid_f(gv[e]) * uv[e];
+                }
+                auto pack4 = [](const float (&f)[4]) {
+                    return u32x2{uint32_t(f2bf(f[0])) | (uint32_t(f2bf(f[1])) << 16),
+                                 uint32_t(f2bf(f[2])) | (uint32_t(f2bf(f[3])) << 16)};
+                };
+                bf16_t* crow = reinterpret_cast<bf16_t*>(d.C) + (int64_t)row * d.ldc;
+                *reinterpret_cast<u32x2*>(crow + gcol) = pack4(og);
+                *reinterpret_cast<u32x2*>(crow + d.half_n + gcol) = pack4(ou);
+                *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(d.C2) + (int64_t)row * d.ldc2 + gcol) = pack4(os);
+            }
+        }
+    }
+}
+
+template <bool AK, bool BKM>
+int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, uint32_t ab, uint32_t bb) {
+    dim3 grid(tiles_m * tiles_n), block(NTHR);
+    switch (d.epi) {
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E>), grid, block, 0, s, d, tiles_m, tiles_n, ab, bb); break;
+        ZB_CASE(EPI_STORE)
+        ZB_CASE(EPI_RESID)
+        ZB_CASE(EPI_ACCUM_F32)
+        ZB_CASE(EPI_GELU_FWD)
+        ZB_CASE(EPI_GELU_BWD)
+        ZB_CASE(EPI_SWIGLU_FWD)
+        ZB_CASE(EPI_SWIGLU_BWD)
+#undef ZB_CASE
+        default: return fail(ZB_EINVAL, "gemm: unknown epilogue");
+    }
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+}  // namespace
+
+// Bytes spanned by an operand: rows x ld elements (last row counted to its
+// logical end).  Must stay below 2^31 for the buffer range check.
+static uint64_t span_bytes(int64_t rows, int64_t ld, int64_t cols) { return (uint64_t)((rows - 1) * ld + cols) * 2; }
+
+int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
+    *handled = false;
+    const bool paired = d.epi == EPI_SWIGLU_FWD;
+    const uint64_t ab = d.a_kmajor ? span_bytes(d.M, d.lda, d.K) : span_bytes(d.K, d.lda, d.M);
+    const uint64_t bb = d.b_kmajor ? span_bytes(d.N, d.ldb, d.K) : span_bytes(d.K, d.ldb, d.N);
+    if (ab >= OOB || bb >= OOB) return ZB_OK;  // too large for one buffer range: caller uses the first kernel
+    // 16-byte (fp32) / 8-byte (bf16) epilogue accesses need widths and leading
+    // dimensions divisible by 4 and aligned base pointers.
+    auto al = [](const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+    const bool has_r = d.epi == EPI_RESID || d.epi == EPI_GELU_BWD || d.epi == EPI_SWIGLU_BWD;
+    const bool has_c2 = d.epi == EPI_GELU_FWD || paired;
+    bool vec = (d.N % 4 == 0) && (d.ldc % 4 == 0) && al(d.C, d.epi == EPI_ACCUM_F32 ? 16 : 8);
+    if (has_r) vec = vec && (d.ldr % 4 == 0) && al(d.R, 8);
+    if (has_c2) vec = vec && (d.ldc2 % 4 == 0) && al(d.C2, 8);
+    if (d.epi == EPI_SWIGLU_BWD || paired) vec = vec && (d.half_n % 4 == 0);
+    if (!vec) return ZB_OK;  // caller uses the first-generation kernel
+    *handled = true;
+    const int tiles_m = (d.M + BM - 1) / BM;
+    const int tiles_n = paired ? (d.half_n + BN / 2 - 1) / (BN / 2) : (d.N + BN - 1) / BN;
+    const uint32_t a32 = (uint32_t)ab, b32 = (uint32_t)bb;
+    if (d.a_kmajor && d.b_kmajor) return launch_v2<true, true>(d, s, tiles_m, tiles_n, a32, b32);
+    if (d.a_kmajor && !d.b_kmajor) return launch_v2<true, false>(d, s, tiles_m, tiles_n, a32, b32);
+    if (!d.a_kmajor && !d.b_kmajor) return launch_v2<false, false>(d, s, tiles_m, tiles_n, a32, b32);
+    return launch_v2<false, true>(d, s, tiles_m, tiles_n, a32, b32);
+}
+
+}  // namespace zb
