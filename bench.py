@@ -101,7 +101,7 @@ def time_w_kernel(shape, device, reps=5):
     achieved = flops / (ms_total * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-            "kernel": "gemm_bf16_kernel<false,false,EPI_ACCUM_F32> (W pass: dW += dY^T X, fp32 in place)",
+            "kernel": "gemm_v2_kernel<false,false,EPI_ACCUM_F32> (W pass: dW += dY^T X, fp32 in place)",
             "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
 
 
