@@ -5,17 +5,25 @@
 //   dP = do v^T,  dS = P (dP - rowsum(do o)),  dq = dS k / sqrt(d),
 //   dk = dS^T q / sqrt(d),  dv = P^T do   (dk, dv summed over each KV group)
 //
-// CDNA4 design.  Every product is a v_mfma_f32_32x32x16_bf16.  The forward and
-// the dq kernel compute the TRANSPOSED score block S^T = K Q^T, so each lane
-// owns one query column: the softmax row statistics are per-lane scalars
-// (combined with the partner lane 32 away), and the probabilities already sit
-// in the B-operand layout of the next product O^T += V^T P^T.  The MFMA
-// reduction index of that product is the key index in the order the score
-// accumulator holds it; the V^T operand is read from a transposed LDS tile in
-// the same order, so no shuffle of P is needed.  The dk/dv kernel owns a key
-// block per workgroup and sweeps the query blocks, accumulating dK^T and dV^T
-// in registers, so the backward needs no atomics and is deterministic.
-// Softmax runs in fp32 in the base-2 domain; the stashed row statistic is
+// CDNA4 design.  Every product is a v_mfma_f32_32x32x16_bf16.
+// * Tiles of K, V (forward, dq) and of Q, dO (dk/dv) are DMA'd HBM -> LDS
+//   with buffer_load ... lds in their natural [rows][128 d] layout (256-byte
+//   rows, 16-byte chunks XOR-swizzled by the row), double buffered.
+// * Operands whose reduction index is the row of such a tile (V^T in o,
+//   K^T in dq, dO^T and Q^T in dv / dk) are read with the gfx950 transpose
+//   read ds_read_b64_tr_b16; the row addresses are chosen so the lane receives
+//   the keys (or queries) in exactly the order the score accumulator holds
+//   them (8(s/4) + 4g + s%4 within a 16-row step), so probabilities go from
+//   the accumulator into the next MFMA without any shuffle.
+// * The forward and dq kernels compute the transposed score block S^T = K Q^T:
+//   each lane owns one query column, so softmax statistics are per-lane
+//   scalars combined with the partner lane 32 away.  The forward rescales its
+//   running output only when a row maximum grows by more than 2^8 (exact:
+//   output and normaliser always share one reference maximum), and skips the
+//   rescale entirely when no lane of the wave needs it.
+// * The dk/dv kernel owns a key block per workgroup and sweeps query blocks,
+//   accumulating dK^T and dV^T in registers: no atomics, deterministic.
+// Softmax runs in fp32 in base 2; the stashed row statistic is
 // lse2 = max + log2(sum) of the scaled scores.
 #include "common.h"
 
@@ -24,6 +32,12 @@ namespace {
 
 constexpr int D = 128;          // head dim
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_TAU = 8.0f;  // log2 growth of a row max tolerated without rescaling
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+constexpr uint32_t OOB = 0x80000000u;
 
 __device__ __forceinline__ floatx16 zero16() {
     floatx16 z;
@@ -32,77 +46,121 @@ __device__ __forceinline__ floatx16 zero16() {
     return z;
 }
 
+// 2^x with the hardware instruction alone: results below 2^-126 flush to
+// zero, which is harmless for softmax weights (exp2f adds a denormal range
+// fix-up of four more instructions per call).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ floatx16 mfma(const bf16x8& a, const bf16x8& b, const floatx16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Pack 8 fp32 into a bf16x8 operand.
-__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
-                                              float a7) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Accumulator slots [8h, 8h+8) of a 32x32 block as a bf16 operand: slot s of
+// lane group g holds row 16h + 8(s/4) + 4g + s%4 of the block.
+__device__ __forceinline__ bf16x8 acc_half_to_bf16(const floatx16& c, int half) {
+    const int b = half * 8;
     bf16x8 v;
-    v[0] = (__bf16)a0; v[1] = (__bf16)a1; v[2] = (__bf16)a2; v[3] = (__bf16)a3;
-    v[4] = (__bf16)a4; v[5] = (__bf16)a5; v[6] = (__bf16)a6; v[7] = (__bf16)a7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)c[b + i];
     return v;
 }
 
-// Accumulator slots [8h, 8h+8) of a 32x32 block as a bf16 B/A operand.  Slot s
-// of lane group g holds reduction index 16h' + 8(s/4) + 4g + s%4 relative to
-// the block (h' = half), matching the C layout rows (r/4)*8 + 4g + r%4.
-__device__ __forceinline__ bf16x8 acc_half_to_bf16(const floatx16& c, int half) {
-    const int b = half * 8;
-    return pack_bf16x8(c[b], c[b + 1], c[b + 2], c[b + 3], c[b + 4], c[b + 5], c[b + 6], c[b + 7]);
+// ---- [rows][128] tiles in LDS ---------------------------------------------
+// 256-byte rows of 16 chunks (16 B); chunk c of row r sits at c ^ swz(r).
+// With b_i the bits of r, swz = (b0^b1^b3, b0, b1, b2) is a bijection of the
+// low 4 row bits (row reads: 8 or 16 consecutive rows at one chunk hit
+// distinct bank windows), and for the 4 consecutive rows a 16-lane group of a
+// transpose read touches, bits (2,1) and bits (3,2) of swz are bijections of
+// (b1, b0), so their 32-byte pieces also hit distinct windows for 32 and 64
+// four-byte banks.  It depends on r & 15 only.
+__device__ __forceinline__ int swz(int r) {
+    const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
+    return ((b0 ^ b1 ^ b3) << 3) | (b0 << 2) | (b1 << 1) | b2;
 }
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
 
-// ---- LDS tile helpers ----------------------------------------------------
-// Row-major tile with 128 bf16 (256 B) per row, 16-byte chunks swizzled by row.
-__device__ __forceinline__ int rm_off(int row, int chunk) { return row * D + ((chunk ^ (row & 7)) << 3); }
-// Transposed tile [128 d][NK keys] with NK*2 bytes per row, 8-byte units swizzled.
-template <int NK>
-__device__ __forceinline__ int tr_off(int d, int unit) {
-    constexpr int UNITS = NK / 4;
-    return d * NK + ((unit ^ (d & (UNITS - 1) & 15)) << 2);
-}
-
-// Operand read from a transposed tile: row d, keys 16*step + {4g..4g+3} and
-// 16*step + 8 + {4g..4g+3}.
-template <int NK>
-__device__ __forceinline__ bf16x8 read_tr_operand(const bf16_t* t, int d, int step, int g) {
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(t + tr_off<NK>(d, 4 * step + g));
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(t + tr_off<NK>(d, 4 * step + 2 + g));
-    u32x4 v{lo[0], lo[1], hi[0], hi[1]};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-// Write a 4 (rows = keys) x 8 (d) register block transposed into a [128][NK] tile.
-template <int NK>
-__device__ __forceinline__ void store_tr_block(const u32x4 (&reg)[4], bf16_t* t, int key0, int d0) {
+// DMA of `rows` rows (multiple of 16) starting at global row `row0` of a
+// [*, ld] bf16 matrix, columns col0..col0+127, into `tile`.  Each wave
+// instruction writes 1 KB = 4 rows; instruction i of wave w covers rows
+// 4(nw*i + w) .. +3.  Rows >= rows_total read as zero.
+template <int ROWS, int NW>
+__device__ __forceinline__ void dma_rows(const bf16_t* base, int64_t ld, int row0, int rows_total, int col0,
+                                         lds_void* tile, int lane, int wave) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, 0x7fffffff);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = reg[0][w], a1 = reg[1][w], a2 = reg[2][w], a3 = reg[3][w];
-        const u32x2 lo{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        const u32x2 hi{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        const int d = d0 + 2 * w;
-        *reinterpret_cast<u32x2*>(t + tr_off<NK>(d, key0 / 4)) = lo;
-        *reinterpret_cast<u32x2*>(t + tr_off<NK>(d + 1, key0 / 4)) = hi;
+    for (int i = 0; i < ROWS / 4 / NW; ++i) {
+        const int b = NW * i + wave;
+        const int r = b * 4 + (lane >> 4);
+        const int chunk = (lane & 15) ^ swz(r);
+        const int grow = row0 + r;
+        const uint32_t off = grow < rows_total ? (uint32_t)(((int64_t)grow * ld + col0 + chunk * 8) * 2) : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((lds_char*)tile + b * 1024), 16, off, 0, 0, 0);
     }
 }
 
+// Row fragment: row `row`, 8 consecutive d at 16 kk + 8 g.
+__device__ __forceinline__ bf16x8 frag_row(const lds_void* tile, int row, int kk, int g) {
+    return *(const lds_bf16x8*)((const lds_char*)tile + tile_off(row, kk * 2 + g));
+}
+
+// Transposed fragment: column d = dblk*32 + lane%32 of the tile, reduction
+// over tile rows 16 t + 8(s/4) + 4g + s%4 (slot s, g = lane/32), i.e. the
+// score-accumulator order.  Two ds_read_b64_tr_b16: in each 16-lane group
+// the lane j reads 4 columns at row offset j/4; output lane i, slot s takes
+// column i of the row read by lane 4s + i/4.  The row's low 4 bits do not
+// depend on t, so the per-lane byte offsets of (dblk, lo/hi) are computed
+// once (tr_bases) and t enters as the instruction's immediate offset.
+struct TrBases {
+    uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ TrBases tr_bases(int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int s = j >> 2, q = j & 3;
+    const int row_lo = (G >> 1) * 4 + s, row_hi = row_lo + 8;
+    TrBases b;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int d = db * 32 + (G & 1) * 16 + q * 4;
+        b.lo[db] = row_lo * 256 + (((d >> 3) ^ swz(row_lo)) << 4) + (d & 7) * 2;
+        b.hi[db] = row_hi * 256 + (((d >> 3) ^ swz(row_hi)) << 4) + (d & 7) * 2;
+    }
+    return b;
+}
+template <int T16>
+__device__ __forceinline__ bf16x8 frag_tr(uint32_t tile, const TrBases& b, int db) {
+    u32x2 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(tile + b.lo[db]), "i"(T16 * 4096));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(tile + b.hi[db]), "i"(T16 * 4096));
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Wait for all LDS reads; `v` becomes an output so its uses stay below.
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8 (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // ======================================================== forward ========
 constexpr int FQ = 128, FKV = 64, FTHR = 256;
+constexpr int KV_TILE = FKV * D * 2;  // 16 KB
 
-struct FwdSmem {
-    bf16_t k[2][FKV * D];
-    bf16_t vt[2][D * FKV];
-};
-
-__global__ __launch_bounds__(FTHR) void attn_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ o,
-                                                        float* __restrict__ lse, int T, int nq, int nkv) {
-    __shared__ __attribute__((aligned(16))) FwdSmem sm;
+__global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ o,
+                                                           float* __restrict__ lse, int T, int nq, int nkv) {
+    __shared__ __attribute__((aligned(1024))) char sm[2][2 * KV_TILE];  // [stage][K | V]
     const int ld = (nq + 2 * nkv) * D;
     const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
-    const int nqb = T / FQ;
-    const int qb = nqb - 1 - blockIdx.x;  // heaviest (longest causal range) first
+    const int qb = gridDim.x - 1 - blockIdx.x;  // longest causal range first
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, col = lane & 31;
     const int qw0 = qb * FQ + wave * 32;
@@ -119,99 +177,82 @@ __global__ __launch_bounds__(FTHR) void attn_fwd_kernel(const bf16_t* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i) oacc[i] = zero16();
     float m = -INFINITY, l = 0.f;
+    const TrBases trb = tr_bases(lane);
     const float c = LOG2E / sqrtf((float)D);
 
-    const int nkb = (qb * FQ + FQ) / FKV;  // key blocks up to the diagonal
-    u32x4 rk[4], rv[4];
-    auto fetch = [&](int kb) {
-        const int k0 = kb * FKV;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cidx = tid + i * FTHR;  // 1024 chunks of 16 B
-            const int r = cidx >> 4, ch = cidx & 15;
-            rk[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(k0 + r) * ld + ch * 8);
-        }
-        const int kg = tid >> 4, dq = tid & 15;  // 4 keys x 8 d per thread
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            rv[r] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(k0 + kg * 4 + r) * ld + dq * 8);
+    const int nkb = (qb * FQ + FQ) / FKV;
+    auto dma = [&](int kb) {
+        char* st = sm[kb & 1];
+        dma_rows<FKV, 4>(kbase, ld, kb * FKV, T, 0, (lds_void*)st, lane, wave);
+        dma_rows<FKV, 4>(vbase, ld, kb * FKV, T, 0, (lds_void*)(st + KV_TILE), lane, wave);
     };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cidx = tid + i * FTHR;
-            const int r = cidx >> 4, ch = cidx & 15;
-            *reinterpret_cast<u32x4*>(sm.k[buf] + rm_off(r, ch)) = rk[i];
-        }
-        store_tr_block<FKV>(rv, sm.vt[buf], (tid >> 4) * 4, (tid & 15) * 8);
-    };
-
-    fetch(0);
-    stash(0);
-    __syncthreads();
+    dma(0);
     for (int kb = 0; kb < nkb; ++kb) {
-        const int cur = kb & 1;
-        if (kb + 1 < nkb) fetch(kb + 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wg_barrier();  // tile kb landed for every wave; the other stage is free
+        if (kb + 1 < nkb) dma(kb + 1);
         const int k0 = kb * FKV;
-        if (k0 <= qw0 + 31) {  // some key of this block is visible to the wave
-            const bf16_t* kt = sm.k[cur];
-            floatx16 s[2];
+        if (k0 > qw0 + 31) continue;  // every key of this block is in the future of every query of the wave
+        const lds_void* kt = (const lds_void*)sm[kb & 1];
+        const lds_void* vt = (const lds_void*)(sm[kb & 1] + KV_TILE);
+        floatx16 s[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                s[j] = zero16();
+        for (int j = 0; j < 2; ++j) {
+            s[j] = zero16();
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int row = j * 32 + col;
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + rm_off(row, kk * 2 + g));
-                    s[j] = mfma(a, qf[kk], s[j]);
-                }
-            }
-            // scale, mask, running max
-            float mx = -INFINITY;
-            const bool diag = (k0 + FKV - 1 > qw0);
+            for (int kk = 0; kk < 8; ++kk) s[j] = mfma(frag_row(kt, j * 32 + col, kk, g), qf[kk], s[j]);
+        }
+        if (k0 + FKV - 1 > qw0) {  // diagonal block: mask keys after the query
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float v = s[j][r] * c;
-                    if (diag) {
-                        const int key = k0 + j * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                        if (key > q) v = -INFINITY;
-                    }
-                    s[j][r] = v;
-                    mx = fmaxf(mx, v);
+                    const int key = k0 + j * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    if (key > q) s[j][r] = -INFINITY;
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mnew = fmaxf(m, mx);
-            const float alpha = exp2f(m - mnew);
-            float rs = 0.f;
+        }
+        float mx = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = exp2f(s[j][r] - mnew);
-                    s[j][r] = p;
-                    rs += p;
-                }
-            rs += __shfl_xor(rs, 32, 64);
-            l = l * alpha + rs;
-            m = mnew;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+        const bool grow = mx > m + RESCALE_TAU;
+        if (__any(grow)) {  // rare after the first block
+            const float mnew = grow ? mx : m;
+            const float alpha = fast_exp2(m - mnew);
+            l *= alpha;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
-            bf16x8 pb[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) pb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
-            const bf16_t* vt = sm.vt[cur];
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    oacc[db] = mfma(read_tr_operand<FKV>(vt, db * 32 + col, t, g), pb[t], oacc[db]);
+            m = mnew;
         }
-        if (kb + 1 < nkb) stash(cur ^ 1);
-        __syncthreads();
+        float rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(s[j][r], c, -m));
+                s[j][r] = p;
+                rs += p;
+            }
+        l += rs + __shfl_xor(rs, 32, 64);
+        bf16x8 pb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
+        const uint32_t vaddr = (uint32_t)(uintptr_t)vt;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            bf16x8 vf[4];
+            vf[0] = frag_tr<0>(vaddr, trb, db);
+            vf[1] = frag_tr<1>(vaddr, trb, db);
+            vf[2] = frag_tr<2>(vaddr, trb, db);
+            vf[3] = frag_tr<3>(vaddr, trb, db);
+            lds_wait(vf);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) oacc[db] = mfma(vf[t], pb[t], oacc[db]);
+        }
     }
     const float inv = 1.f / l;
 #pragma unroll
@@ -247,22 +288,16 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restric
 // ====================================================== dq kernel ========
 // Per (query block of 128, query head).  Mirrors the forward: S^T = K Q^T,
 // dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
-struct DqSmem {
-    bf16_t k[2][FKV * D];
-    bf16_t v[2][FKV * D];
-    bf16_t kt[2][D * FKV];
-};
-
-__global__ __launch_bounds__(FTHR) void attn_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dout,
-                                                       const float* __restrict__ lse, const float* __restrict__ delta,
-                                                       bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
-    extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
-    DqSmem& sm = *reinterpret_cast<DqSmem*>(dyn_smem);
+__global__ __launch_bounds__(FTHR, 1) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
+                                                          const bf16_t* __restrict__ dout,
+                                                          const float* __restrict__ lse,
+                                                          const float* __restrict__ delta,
+                                                          bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
+    __shared__ __attribute__((aligned(1024))) char sm[2][2 * KV_TILE];
     const int ld = (nq + 2 * nkv) * D;
     const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
-    const int nqb = T / FQ;
-    const int qb = nqb - 1 - blockIdx.x;
+    const int qb = gridDim.x - 1 - blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, col = lane & 31;
     const int qw0 = qb * FQ + wave * 32;
@@ -284,79 +319,61 @@ __global__ __launch_bounds__(FTHR) void attn_dq_kernel(const bf16_t* __restrict_
     floatx16 dacc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dacc[i] = zero16();
+    const TrBases trb = tr_bases(lane);
 
     const int nkb = (qb * FQ + FQ) / FKV;
-    u32x4 rk[4], rv[4], rt[4];
-    auto fetch = [&](int kb) {
-        const int k0 = kb * FKV;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cidx = tid + i * FTHR;
-            const int r = cidx >> 4, ch = cidx & 15;
-            rk[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(k0 + r) * ld + ch * 8);
-            rv[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(k0 + r) * ld + ch * 8);
-        }
-        const int kg = tid >> 4, dq = tid & 15;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            rt[r] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(k0 + kg * 4 + r) * ld + dq * 8);
+    auto dma = [&](int kb) {
+        char* st = sm[kb & 1];
+        dma_rows<FKV, 4>(kbase, ld, kb * FKV, T, 0, (lds_void*)st, lane, wave);
+        dma_rows<FKV, 4>(vbase, ld, kb * FKV, T, 0, (lds_void*)(st + KV_TILE), lane, wave);
     };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cidx = tid + i * FTHR;
-            const int r = cidx >> 4, ch = cidx & 15;
-            *reinterpret_cast<u32x4*>(sm.k[buf] + rm_off(r, ch)) = rk[i];
-            *reinterpret_cast<u32x4*>(sm.v[buf] + rm_off(r, ch)) = rv[i];
-        }
-        store_tr_block<FKV>(rt, sm.kt[buf], (tid >> 4) * 4, (tid & 15) * 8);
-    };
-
-    fetch(0);
-    stash(0);
-    __syncthreads();
+    dma(0);
     for (int kb = 0; kb < nkb; ++kb) {
-        const int cur = kb & 1;
-        if (kb + 1 < nkb) fetch(kb + 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wg_barrier();
+        if (kb + 1 < nkb) dma(kb + 1);
         const int k0 = kb * FKV;
-        if (k0 <= qw0 + 31) {
-            floatx16 s[2], dp[2];
+        if (k0 > qw0 + 31) continue;
+        const lds_void* kt = (const lds_void*)sm[kb & 1];
+        const lds_void* vt = (const lds_void*)(sm[kb & 1] + KV_TILE);
+        floatx16 s[2], dp[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                s[j] = zero16();
-                dp[j] = zero16();
-                const int row = j * 32 + col;
+        for (int j = 0; j < 2; ++j) {
+            s[j] = zero16();
+            dp[j] = zero16();
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sm.k[cur] + rm_off(row, kk * 2 + g));
-                    s[j] = mfma(ak, qf[kk], s[j]);
-                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(sm.v[cur] + rm_off(row, kk * 2 + g));
-                    dp[j] = mfma(av, dof[kk], dp[j]);
-                }
+            for (int kk = 0; kk < 8; ++kk) {
+                s[j] = mfma(frag_row(kt, j * 32 + col, kk, g), qf[kk], s[j]);
+                dp[j] = mfma(frag_row(vt, j * 32 + col, kk, g), dof[kk], dp[j]);
             }
-            const bool diag = (k0 + FKV - 1 > qw0);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = exp2f(s[j][r] * c - lq);
-                    if (diag) {
-                        const int key = k0 + j * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                        if (key > q) p = 0.f;
-                    }
-                    s[j][r] = p * (dp[j][r] - dq_delta);  // dS^T
-                }
-            bf16x8 sb[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    dacc[db] = mfma(read_tr_operand<FKV>(sm.kt[cur], db * 32 + col, t, g), sb[t], dacc[db]);
         }
-        if (kb + 1 < nkb) stash(cur ^ 1);
-        __syncthreads();
+        const bool diag = (k0 + FKV - 1 > qw0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(s[j][r], c, -lq));
+                if (diag) {
+                    const int key = k0 + j * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    if (key > q) p = 0.f;
+                }
+                s[j][r] = p * (dp[j][r] - dq_delta);  // dS^T
+            }
+        bf16x8 sb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
+        const uint32_t kaddr = (uint32_t)(uintptr_t)kt;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            bf16x8 kf[4];
+            kf[0] = frag_tr<0>(kaddr, trb, db);
+            kf[1] = frag_tr<1>(kaddr, trb, db);
+            kf[2] = frag_tr<2>(kaddr, trb, db);
+            kf[3] = frag_tr<3>(kaddr, trb, db);
+            lds_wait(kf);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dacc[db] = mfma(kf[t], sb[t], dacc[db]);
+        }
     }
     const float scale = 1.f / sqrtf((float)D);
 #pragma unroll
@@ -378,32 +395,24 @@ __global__ __launch_bounds__(FTHR) void attn_dq_kernel(const bf16_t* __restrict_
 //   S = Q K^T, P = exp2(S c - lse2), dP = dO V^T, dS = P (dP - delta),
 //   dV^T += dO^T P,  dK^T += Q^T dS.
 constexpr int BKV = 128, BQB = 32;
+constexpr int Q_TILE = BQB * D * 2;  // 8 KB
 
-struct DkvSmem {
-    bf16_t q[2][BQB * D];
-    bf16_t dO[2][BQB * D];
-    bf16_t qt[2][D * BQB];
-    bf16_t dot[2][D * BQB];
-    float lse[2][BQB];
-    float delta[2][BQB];
-};
-
-__global__ __launch_bounds__(FTHR) void attn_dkv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dout,
-                                                        const float* __restrict__ lse, const float* __restrict__ delta,
-                                                        bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
-    extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
-    DkvSmem& sm = *reinterpret_cast<DkvSmem*>(dyn_smem);
+__global__ __launch_bounds__(FTHR, 1) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
+                                                           const bf16_t* __restrict__ dout,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ delta,
+                                                           bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
+    __shared__ __attribute__((aligned(1024))) char sm[2][2 * Q_TILE];  // [stage][Q | dO]
+    __shared__ float sl[2][2][BQB];                                     // [stage][lse | delta]
     const int ld = (nq + 2 * nkv) * D;
     const int ldo = nq * D;
     const int grp = blockIdx.y;
     const int rep = nq / nkv;
-    const int nkb = T / BKV;
-    const int kb = blockIdx.x;  // low key blocks have the most query blocks; launch them first
+    const int kb = blockIdx.x;  // low key blocks have the most query blocks; launched first
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, col = lane & 31;
     const int kw0 = kb * BKV + wave * 32;
     const int key = kw0 + col;
-    (void)nkb;
 
     bf16x8 kf[8], vf[8];
 #pragma unroll
@@ -418,81 +427,98 @@ __global__ __launch_bounds__(FTHR) void attn_dkv_kernel(const bf16_t* __restrict
         dv[i] = zero16();
     }
     const float c = LOG2E / sqrtf((float)D);
+    const TrBases trb = tr_bases(lane);
     const int qb0 = (kb * BKV) / BQB;
     const int nqb = T / BQB;
     const int per_head = nqb - qb0;
     const int total = per_head * rep;
 
-    u32x4 rq[4];
-    float rl = 0.f;
     auto fetch = [&](int it) {
         const int hh = grp * rep + it / per_head;
         const int q0 = (qb0 + it % per_head) * BQB;
-        // threads 0..127: Q block (4 rows x 8 d); 128..255: dO block
-        const int t = tid & 127;
-        const int rg = t >> 4, dq = t & 15;  // rows 4rg..4rg+3, d 8dq..8dq+7
-        if (tid < 128) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                rq[r] = *reinterpret_cast<const u32x4*>(qkv + (int64_t)(q0 + rg * 4 + r) * ld + hh * D + dq * 8);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                rq[r] = *reinterpret_cast<const u32x4*>(dout + (int64_t)(q0 + rg * 4 + r) * ldo + hh * D + dq * 8);
+        char* st = sm[it & 1];
+        dma_rows<BQB, 4>(qkv + hh * D, ld, q0, T, 0, (lds_void*)st, lane, wave);
+        dma_rows<BQB, 4>(dout + hh * D, ldo, q0, T, 0, (lds_void*)(st + Q_TILE), lane, wave);
+        if (wave == 0 && lane < BQB) {  // the row statistics of the block: 32 floats each (32 lanes write)
+            const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (int64_t)hh * T + q0, BQB * 4);
+            const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (int64_t)hh * T + q0, BQB * 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)&sl[it & 1][0][0], 4, lane * 4, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)&sl[it & 1][1][0], 4, lane * 4, 0, 0, 0);
         }
-        if (tid < BQB) rl = lse[(int64_t)hh * T + q0 + tid];
-        else if (tid >= 64 && tid < 64 + BQB) rl = delta[(int64_t)hh * T + q0 + tid - 64];
-    };
-    auto stash = [&](int buf) {
-        const int t = tid & 127;
-        const int rg = t >> 4, dq = t & 15;
-        bf16_t* rowt = tid < 128 ? sm.q[buf] : sm.dO[buf];
-        bf16_t* trt = tid < 128 ? sm.qt[buf] : sm.dot[buf];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(rowt + rm_off(rg * 4 + r, dq)) = rq[r];
-        store_tr_block<BQB>(rq, trt, rg * 4, dq * 8);
-        if (tid < BQB) sm.lse[buf][tid] = rl;
-        else if (tid >= 64 && tid < 64 + BQB) sm.delta[buf][tid - 64] = rl;
     };
 
     fetch(0);
-    stash(0);
-    __syncthreads();
     for (int it = 0; it < total; ++it) {
-        const int cur = it & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wg_barrier();
         if (it + 1 < total) fetch(it + 1);
         const int q0 = (qb0 + it % per_head) * BQB;
-        if (q0 + BQB - 1 >= kw0) {  // some query of the block sees some key of the wave
-            floatx16 s = zero16(), dp = zero16();
+        if (q0 + BQB - 1 < kw0) continue;  // every query of the block precedes every key of the wave
+        const lds_void* qt = (const lds_void*)sm[it & 1];
+        const lds_void* ot = (const lds_void*)(sm[it & 1] + Q_TILE);
+        // Fragment reads as asm (explicit waits): the compiler would otherwise
+        // wait for the DMA of the next block, issued just above, before them.
+        floatx16 s = zero16(), dp = zero16();
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sm.q[cur] + rm_off(col, kk * 2 + g));
-                s = mfma(aq, kf[kk], s);
-                const bf16x8 ad = *reinterpret_cast<const bf16x8*>(sm.dO[cur] + rm_off(col, kk * 2 + g));
-                dp = mfma(ad, vf[kk], dp);
+        for (int half = 0; half < 2; ++half) {
+            bf16x8 fr[8];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const int kk = half * 4 + k4;
+                const uint32_t ro = tile_off(col, kk * 2 + g);
+                asm volatile("ds_read_b128 %0, %1" : "=v"(fr[k4]) : "v"((uint32_t)(uintptr_t)qt + ro));
+                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fr[4 + k4]) : "v"((uint32_t)(uintptr_t)qt + ro), "i"(Q_TILE));
             }
-            const bool diag = (q0 < kw0 + 31);
+            lds_wait(fr);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qr = (r >> 2) * 8 + g * 4 + (r & 3);
-                float p = exp2f(s[r] * c - sm.lse[cur][qr]);
-                if (diag && key > q0 + qr) p = 0.f;
-                s[r] = p;
-                dp[r] = p * (dp[r] - sm.delta[cur][qr]);
-            }
-            const bf16x8 p0 = acc_half_to_bf16(s, 0), p1 = acc_half_to_bf16(s, 1);
-            const bf16x8 s0 = acc_half_to_bf16(dp, 0), s1 = acc_half_to_bf16(dp, 1);
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const int d = db * 32 + col;
-                dv[db] = mfma(read_tr_operand<BQB>(sm.dot[cur], d, 0, g), p0, dv[db]);
-                dv[db] = mfma(read_tr_operand<BQB>(sm.dot[cur], d, 1, g), p1, dv[db]);
-                dk[db] = mfma(read_tr_operand<BQB>(sm.qt[cur], d, 0, g), s0, dk[db]);
-                dk[db] = mfma(read_tr_operand<BQB>(sm.qt[cur], d, 1, g), s1, dk[db]);
+            for (int k4 = 0; k4 < 4; ++k4) {
+                s = mfma(fr[k4], kf[half * 4 + k4], s);
+                dp = mfma(fr[4 + k4], vf[half * 4 + k4], dp);
             }
         }
-        if (it + 1 < total) stash(cur ^ 1);
-        __syncthreads();
+        const bool diag = (q0 < kw0 + 31);
+        // row statistics of the accumulator rows (r/4)*8 + 4g + r%4: four
+        // 16-byte reads each, issued as asm (see frag_tr) and waited for here
+        floatx4 lsv[4], dsv[4];
+        {
+            const uint32_t lb = (uint32_t)(uintptr_t)&sl[it & 1][0][0] + g * 16;
+            const uint32_t db = (uint32_t)(uintptr_t)&sl[it & 1][1][0] + g * 16;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(lsv[rb]) : "v"(lb), "i"(rb * 32));
+                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dsv[rb]) : "v"(db), "i"(rb * 32));
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) asm volatile("" : "+v"(lsv[rb]), "+v"(dsv[rb]));
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) asm volatile("" : "+v"(lsv[rb]), "+v"(dsv[rb]));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qr = (r >> 2) * 8 + g * 4 + (r & 3);
+            float p = fast_exp2(fmaf(s[r], c, -lsv[r >> 2][r & 3]));
+            if (diag && key > q0 + qr) p = 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - dsv[r >> 2][r & 3]);
+        }
+        const bf16x8 p0 = acc_half_to_bf16(s, 0), p1 = acc_half_to_bf16(s, 1);
+        const bf16x8 s0 = acc_half_to_bf16(dp, 0), s1 = acc_half_to_bf16(dp, 1);
+        const uint32_t oaddr = (uint32_t)(uintptr_t)ot, qaddr = (uint32_t)(uintptr_t)qt;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            bf16x8 fo[2], fq[2];
+            fo[0] = frag_tr<0>(oaddr, trb, db);
+            fo[1] = frag_tr<1>(oaddr, trb, db);
+            fq[0] = frag_tr<0>(qaddr, trb, db);
+            fq[1] = frag_tr<1>(qaddr, trb, db);
+            lds_wait(fo);
+            lds_wait(fq);
+            dv[db] = mfma(fo[0], p0, dv[db]);
+            dv[db] = mfma(fo[1], p1, dv[db]);
+            dk[db] = mfma(fq[0], s0, dk[db]);
+            dk[db] = mfma(fq[1], s1, dk[db]);
+        }
     }
     const float scale = 1.f / sqrtf((float)D);
 #pragma unroll
@@ -526,19 +552,9 @@ int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf1
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
     hipLaunchKernelGGL(attn_delta_kernel, dim3((T * nq + 3) / 4), dim3(256), 0, s, o, dout, delta, T, nq);
     ZB_HIP(hipGetLastError());
-    static bool attr_set = false;
-    if (!attr_set) {
-        ZB_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(attn_dq_kernel),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(DqSmem)));
-        ZB_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(attn_dkv_kernel),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(DkvSmem)));
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(attn_dq_kernel, dim3(T / FQ, nq), dim3(FTHR), sizeof(DqSmem), s, qkv, dout, lse, delta, dqkv, T,
-                       nq, nkv);
+    hipLaunchKernelGGL(attn_dq_kernel, dim3(T / FQ, nq), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
     ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(attn_dkv_kernel, dim3(T / BKV, nkv), dim3(FTHR), sizeof(DkvSmem), s, qkv, dout, lse, delta,
-                       dqkv, T, nq, nkv);
+    hipLaunchKernelGGL(attn_dkv_kernel, dim3(T / BKV, nkv), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
