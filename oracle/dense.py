@@ -409,3 +409,45 @@ def rel_fro(got: np.ndarray, ref: np.ndarray) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+# ====================================================== sampled attention ===
+# Single rows / columns of the causal attention at full sequence length,
+# each from its plain definition in fp64 (the same formulas as attn_fwd /
+# attn_bwd, restricted to what one output entry depends on).
+
+def attn_rows_fwd(q, k, v, h: int, rows, n_q: int, n_kv: int, d: int):
+    """Output rows o[t, head h] and their log-sum-exp for query rows `rows`."""
+    g = _kv_of(h, n_q, n_kv)
+    scale = 1.0 / math.sqrt(d)
+    kh = np.asarray(k[:, g * d:(g + 1) * d], np.float64)
+    vh = np.asarray(v[:, g * d:(g + 1) * d], np.float64)
+    out, lse = [], []
+    for t in rows:
+        s = (kh[:t + 1] @ np.asarray(q[t, h * d:(h + 1) * d], np.float64)) * scale
+        mx = np.max(s)
+        e = np.exp(s - mx)
+        out.append((e / e.sum()) @ vh[:t + 1])
+        lse.append(mx + math.log(e.sum()))
+    return np.array(out), np.array(lse)
+
+
+def attn_head_bwd(q, k, v, do, h: int, n_q: int, n_kv: int, d: int):
+    """Full backward of one query head (all rows): (dq_h, dk_part, dv_part)
+    where dk_part / dv_part are this head's contributions to its KV group."""
+    g = _kv_of(h, n_q, n_kv)
+    qh = np.asarray(q[:, h * d:(h + 1) * d], np.float64)
+    kh = np.asarray(k[:, g * d:(g + 1) * d], np.float64)
+    vh = np.asarray(v[:, g * d:(g + 1) * d], np.float64)
+    doh = np.asarray(do[:, h * d:(h + 1) * d], np.float64)
+    T = qh.shape[0]
+    scale = 1.0 / math.sqrt(d)
+    s = (qh @ kh.T) * scale
+    s = np.where(np.tril(np.ones((T, T), dtype=bool)), s, -np.inf)
+    s = s - np.max(s, axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    o = p @ vh
+    dp = doh @ vh.T
+    ds = p * (dp - np.sum(doh * o, axis=1, keepdims=True))
+    return (ds @ kh) * scale, (ds.T @ qh) * scale, p.T @ doh

@@ -258,8 +258,12 @@ class Stage:
     def run_schedule(self, ops, arrive_f, arrive_b, unit_ms: float, xs, ys, dys, dxs, mode: int = EXEC_ORDERED,
                      hi_stream=None, lo_stream=None):
         n = len(ops)
-        opa = (Op * n)(*[Op({"F": OP_F, "B": OP_B, "W": OP_W}[t], j) for t, j in ops])
         m = len(xs)
+        if not (len(ys) == len(dys) == len(dxs) == m and len(arrive_f) >= m and len(arrive_b) >= m):
+            raise ValueError("xs, ys, dys, dxs and the arrival lists need one entry per microbatch")
+        if any(j < 0 or j >= m for _, j in ops):
+            raise ValueError("op microbatch outside the given per-microbatch lists")
+        opa = (Op * n)(*[Op({"F": OP_F, "B": OP_B, "W": OP_W}[t], j) for t, j in ops])
         af = (ctypes.c_double * m)(*[float(a) for a in arrive_f])
         ab = (ctypes.c_double * m)(*[float(a) for a in arrive_b])
         P = lambda ts: (ctypes.c_void_p * m)(*[_ptr(t) for t in ts])

@@ -357,3 +357,38 @@ def test_stage_accumulates_over_microbatches(kind):
     if kind == "linear":
         big = od.linear_bwd_weight(np.concatenate(xs_), np.concatenate(gs))
         assert od.rel_fro(st.grad[0], big) < 1e-13
+
+
+@pytest.mark.parametrize("nq,nkv", [(4, 2), (2, 2)])
+def test_sampled_attention_helpers_match_torch(nq, nkv):
+    """Row-wise forward and per-head backward (used for full-size sampled
+    checks) against torch SDPA / autograd in fp64."""
+    T, d = 9, 4
+    q, k, v, do = rnd(T, nq * d), rnd(T, nkv * d), rnd(T, nkv * d), rnd(T, nq * d)
+    tq = torch.tensor(q.reshape(T, nq, d).transpose(1, 0, 2)[None], requires_grad=True)
+    tk = torch.tensor(k.reshape(T, nkv, d).transpose(1, 0, 2)[None], requires_grad=True)
+    tv = torch.tensor(v.reshape(T, nkv, d).transpose(1, 0, 2)[None], requires_grad=True)
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=nq != nkv)
+    (to * torch.tensor(do.reshape(T, nq, d).transpose(1, 0, 2)[None])).sum().backward()
+    for h in range(nq):
+        rows = [0, 3, T - 1]
+        o, _ = od.attn_rows_fwd(q, k, v, h, rows, nq, nkv, d)
+        assert np.max(np.abs(o - to[0, h].detach().numpy()[rows])) < 1e-13
+    dk_sum = np.zeros((T, nkv * d))
+    dv_sum = np.zeros((T, nkv * d))
+    for h in range(nq):
+        dq, dkp, dvp = od.attn_head_bwd(q, k, v, do, h, nq, nkv, d)
+        assert np.max(np.abs(dq - tq.grad[0, h].numpy())) < 1e-12
+        g = (h * nkv) // nq
+        dk_sum[:, g * d:(g + 1) * d] += dkp
+        dv_sum[:, g * d:(g + 1) * d] += dvp
+    assert np.max(np.abs(dk_sum - tk.grad[0].numpy().transpose(1, 0, 2).reshape(T, nkv * d))) < 1e-12
+    assert np.max(np.abs(dv_sum - tv.grad[0].numpy().transpose(1, 0, 2).reshape(T, nkv * d))) < 1e-12
+
+
+def test_gemm_entries_brute_force():
+    a, b = rnd(5, 7), rnd(6, 7)
+    rows, cols = [0, 4, 2], [5, 0, 3]
+    got = od.gemm_nt_entries(a, b, rows, cols)
+    for i, (r, c) in enumerate(zip(rows, cols)):
+        assert abs(got[i] - sum(a[r, k] * b[c, k] for k in range(7))) < 1e-13
