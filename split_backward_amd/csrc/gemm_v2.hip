@@ -18,10 +18,11 @@
 //                            slot s takes element i%4 of the load of lane
 //                            4s + i/4), so the lane receives 8 consecutive k
 //                            of its column.
-// Four LDS stages of 32-k tiles (128 KB): the DMA of k-tiles t+1..t+3 is in
-// flight while tile t is multiplied (three tiles of prefetch hide HBM latency
-// with one wave per SIMD), and fragments of the next 16-k step are read while
-// the MFMAs of the current step issue.  DMA addressing costs no VALU: each
+// Four LDS stages of 32-k tiles (128 KB): the DMA of the next k-tiles is in
+// flight while tile t is multiplied (about four tiles of prefetch hide HBM
+// latency with one wave per SIMD), fragments of the next 16-k step are read
+// while the MFMAs of the current step issue, and the per-tile barrier sits in
+// the middle of a tile so fragment reads never wait behind it.  DMA addressing costs no VALU: each
 // lane's offset is fixed once, and the buffer base advances in scalar
 // registers from tile to tile.
 #include "common.h"
@@ -150,6 +151,23 @@ __device__ __forceinline__ void interleave_reads_mfma() {
     }
 }
 
+// Region B of the main loop: RD fragment reads, then ND DMA loads, spread
+// over the 16 MFMAs of the step (reads first: they come before the DMA in
+// program order and must stay there).
+template <int RD, int ND, int SLOT>
+__device__ __forceinline__ void interleave_reads_dma_mfma() {
+    if constexpr (SLOT < 16) {
+        constexpr int T = RD + ND;
+        constexpr int lo = (SLOT * T) / 16, hi = ((SLOT + 1) * T) / 16;
+        constexpr int nr = (hi < RD ? hi : RD) - (lo < RD ? lo : RD);
+        constexpr int nd = (hi - lo) - nr;
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+        if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x020, nd, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        interleave_reads_dma_mfma<RD, ND, SLOT + 1>();
+    }
+}
+
 // Workgroup barrier without the memory fence __syncthreads() implies: that
 // fence waits for every outstanding load, including the DMA of tiles that are
 // meant to stay in flight.  Callers wait for exactly the tile they need
@@ -210,11 +228,14 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
 
     auto dma_tile = [&](int kt) {
         char* st = smem + (kt % STAGES) * STAGE_BYTES;
-        const uint32_t adv_a = (uint32_t)(kt * step_a), adv_b = (uint32_t)(kt * step_b);
+        // A tile past the end of K gets an empty range: its loads read zeros,
+        // fetch nothing, and keep the per-iteration DMA count uniform.
+        const bool live = kt < nk;
+        const uint32_t adv_a = live ? (uint32_t)(kt * step_a) : 0u, adv_b = live ? (uint32_t)(kt * step_b) : 0u;
         const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(static_cast<const char*>(d.A) + adv_a, a_bytes - adv_a);
+            make_rsrc(static_cast<const char*>(d.A) + adv_a, live ? a_bytes - adv_a : 0u);
         const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(static_cast<const char*>(d.B) + adv_b, b_bytes - adv_b);
+            make_rsrc(static_cast<const char*>(d.B) + adv_b, live ? b_bytes - adv_b : 0u);
         if (kt == nk - 1 && k_tail < BK) {  // partial last tile: mask k >= K on K-contiguous operands
             uint32_t ta[4], tb[4];
             if (A_KMAJ) dma_offsets_kmaj<false>(ta, d.lda, m0, d.M, 0, k_tail, lane, wave);
@@ -252,30 +273,38 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
     constexpr int RD_A = A_KMAJ ? 1 : 2, RD_B = B_KMAJ ? 1 : 2;
     constexpr int RD = 4 * (RD_A + RD_B);  // LDS read instructions per 16-k step
 
-    // Prologue: tiles 0..2 in flight, wait for tile 0.
-    const int pre = nk < STAGES - 1 ? nk : STAGES - 1;
-    for (int t = 0; t < pre; ++t) dma_tile(t);
-    if (pre >= 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (pre == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Software pipeline across tiles.  Iteration kt:
+    //   region A: MFMAs of k step 0 of tile kt, while the step-1 fragments of
+    //             tile kt are read;
+    //   every read of tile kt has completed and tile kt+1 has landed, then a
+    //             barrier (mid-tile, so no wave idles at a tile boundary);
+    //   region B: MFMAs of step 1 of tile kt, while the step-0 fragments of
+    //             tile kt+1 are read and the DMA of tile kt+4 is issued into
+    //             the stage tile kt just vacated.
+    // Every iteration issues the same DMA count (tiles past K are empty), so
+    // the waits are constants: after region A of iteration kt the DMA of
+    // tiles kt+2 and kt+3 (16 loads per wave) may stay in flight.
+#pragma unroll
+    for (int t = 0; t < STAGES; ++t) dma_tile(t);
+    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // tile 0 landed
     workgroup_barrier();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-        const lds_void* ta = (const lds_void*)st;
-        const lds_void* tb = (const lds_void*)(st + TILE_BYTES);
-        bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-        // region 1: fragments of k step 0 (their LDS latency overlaps the DMA issue)
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    {
+        const lds_void* ta = (const lds_void*)smem;
+        const lds_void* tb = (const lds_void*)(smem + TILE_BYTES);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             fa0[i] = frag_a(ta, i, 0);
             fb0[i] = frag_b(tb, i, 0);
         }
-        if (kt + STAGES - 1 < nk) dma_tile(kt + STAGES - 1);  // into the stage freed by the last barrier
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+        const lds_void* ta = (const lds_void*)st;
+        const lds_void* tb = (const lds_void*)(st + TILE_BYTES);
         __builtin_amdgcn_sched_barrier(0);
         if (!A_KMAJ || !B_KMAJ) lds_wait(fa0, fb0);
-        // region 2: fragments of k step 1 interleaved with the MFMAs of step 0
-        // (with transpose reads: all reads first, then the MFMAs)
+        // region A
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             fa1[i] = frag_a(ta, i, 1);
@@ -289,20 +318,33 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mi], fb0[ni], acc[mi][ni], 0, 0, 0);
         if (A_KMAJ && B_KMAJ) interleave_reads_mfma<RD, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        if (!A_KMAJ || !B_KMAJ) lds_wait(fa1, fb1);
-        // region 3: MFMAs of step 1
+        lds_wait(fa1, fb1);  // tile kt fully read: its stage may be overwritten
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // tile kt+1 landed
+        workgroup_barrier();
+        // region B (the fragments read past the last tile are never used)
+        {
+            const char* sn = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
+            const lds_void* na = (const lds_void*)sn;
+            const lds_void* nb = (const lds_void*)(sn + TILE_BYTES);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fa0[i] = frag_a(na, i, 0);
+                fb0[i] = frag_b(nb, i, 0);
+            }
+        }
+        dma_tile(kt + STAGES);  // into the stage tile kt vacated
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        // tile kt+1 must have landed; later tiles may stay in flight
-        if (kt + 3 < nk) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (kt + 2 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        workgroup_barrier();
+        if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, 8, 0>();
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // The empty tiles' DMA still writes (zeros) into the stages, and every
+    // wave must be done with them before the epilogue reuses the memory.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    workgroup_barrier();
 
     // ---- epilogue ---------------------------------------------------------
     // The accumulators of a 32-row block (mi) go through the wave's own LDS
