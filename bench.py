@@ -13,7 +13,9 @@ from the time) / wall time of the step.
 Extra fields on the JSON line:
 * roofline: the W-pass GEMM kernel (the kernel with the largest share of the
   step time), its algorithmic flops / its average launch time, the launches
-  replayed on the benchmark stream and timed with HIP events.
+  replayed on the benchmark stream and timed with HIP events.  `traffic` is
+  the HBM bytes per launch from the committed --pmc summary, or null when
+  that summary was taken on other kernel sources.
 * cpu_baseline: the fp64 oracle timed on this host on a bounded sample
   (one decoder layer, one microbatch, 256 tokens, full widths).
 * executor_p8_stage3: the stage replayed with emulated arrivals (device-clock
@@ -70,9 +72,10 @@ def make_inputs(shape, m, device):
     return xs, ys, dys, dxs
 
 
-def time_w_kernel(shape, device, reps=5):
-    """Average launch time of the W-pass GEMM kernel at the step's shapes,
-    launched through the C ABI on the current stream, timed with events."""
+def w_kernel_launches(shape, device):
+    """Buffers and a closure that launches the W-pass GEMM kernel once per
+    product of the stage (dW += dY^T X at the step's shapes, fp32 in place),
+    through the C ABI on the current stream."""
     import torch
     import split_backward_amd as zb
     gem = w_pass_gemms(shape)
@@ -87,6 +90,46 @@ def time_w_kernel(shape, device, reps=5):
         for A, B, C, M, N, K in bufs:
             zb.gemm(A, B, C, a_kmajor=False, b_kmajor=False, M=M, N=N, K=K, accumulate=True)
 
+    return gem, once
+
+
+W_KERNEL = "gemm_v2_kernel<false,false,EPI_ACCUM_F32>"
+W_KERNEL_SOURCES = ("split_backward_amd/csrc/gemm_v2.hip", "split_backward_amd/csrc/common.h")
+TRAFFIC_SUMMARY = "profiles/gemm_w_kernel_hbm_traffic_llama7b_stage4.md"
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in W_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per W-kernel launch from the committed rocprofv3 --pmc
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the same counters' reading
+    for a copy kernel of known size), or None when the summary is missing or
+    was taken on other kernel sources."""
+    import re
+    try:
+        with open(os.path.join(ROOT, TRAFFIC_SUMMARY)) as fh:
+            txt = fh.read()
+    except OSError:
+        return None
+    mh = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    mb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not mh or not mb or mh.group(1) != kernel_source_hash():
+        return None
+    return float(mb.group(1))
+
+
+def time_w_kernel(shape, device, reps=5):
+    """Average launch time of the W-pass GEMM kernel at the step's shapes,
+    launched through the C ABI on the current stream, timed with events."""
+    import torch
+    gem, once = w_kernel_launches(shape, device)
     once()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -100,10 +143,31 @@ def time_w_kernel(shape, device, reps=5):
     flops = reps * sum(2.0 * M * N * K for M, N, K in gem)
     avg_ms = ms_total / launches
     achieved = flops / (ms_total * 1e-3) / 1e12
+    algo_bytes = sum(2 * K * (M + N) + 2 * 4 * M * N for M, N, K in gem) / len(gem)
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-            "kernel": "gemm_v2_kernel<false,false,EPI_ACCUM_F32> (W pass: dW += dY^T X, fp32 in place)",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes_per_launch": algo_bytes,
+            "kernel": W_KERNEL + " (W pass: dW += dY^T X, fp32 in place)",
             "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
+
+
+def traffic_probe(shape, device):
+    """Workload for the rocprofv3 --pmc passes: a copy of known size (1 GiB
+    read, 1 GiB written, elementwise negation) three times, then the W-pass
+    launches twice.  Prints the kernel-source hash the counters belong to."""
+    import torch
+    n = 1 << 28  # fp32 elements = 1 GiB
+    src = torch.ones(n, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    gem, once = w_kernel_launches(shape, device)
+    for _ in range(2):
+        once()
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": True, "copy_bytes_each_way": 4 * n, "w_launches": 2 * len(gem),
+                      "shapes_MNK": gem, "kernel_source_sha256": kernel_source_hash()}), flush=True)
 
 
 def cpu_baseline(shape):
@@ -191,6 +255,8 @@ def main():
     ap.add_argument("--workload", default="llama7b_stage4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-executor", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run the copy + W-kernel workload that the --pmc passes count")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -206,6 +272,9 @@ def main():
     ring = wl.get("ring", m)
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.traffic_probe:
+        traffic_probe(shape, device)
+        return
     weights = [to_dev(w, device) for w in synth.make_weights(shape)]
     stage = zb.Stage(shape.kind, shape.tokens, shape.hidden, shape.ffn, weights, dtype=shape.dtype,
                      n_layers=shape.n_layers, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
