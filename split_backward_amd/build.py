@@ -28,9 +28,16 @@ CFLAGS = ["-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-x", "hip",
           "-Wno-unused-result"]
 
 
+# Per-source extra flags.  The attention kernels keep their MFMA
+# accumulators in ordinary VGPRs: with the default heuristic the register
+# allocator splits them between the VGPR and AGPR files and copies them back
+# and forth on every loop iteration.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         msg = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -86,11 +86,13 @@ __device__ __forceinline__ uint32_t tile_off(int row, int chunk) { return row * 
 // DMA of `rows` rows (multiple of 16) starting at global row `row0` of a
 // [*, ld] bf16 matrix, columns col0..col0+127, into `tile`.  Each wave
 // instruction writes 1 KB = 4 rows; instruction i of wave w covers rows
-// 4(nw*i + w) .. +3.  Rows >= rows_total read as zero.
+// 4(nw*i + w) .. +3.  Rows >= rows_total read as zero.  A call that is not
+// `live` issues the same instructions over an empty range (zeros, no memory
+// traffic), which keeps every wave's count of outstanding loads uniform.
 template <int ROWS, int NW>
 __device__ __forceinline__ void dma_rows(const bf16_t* base, int64_t ld, int row0, int rows_total, int col0,
-                                         lds_void* tile, int lane, int wave) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, 0x7fffffff);
+                                         lds_void* tile, int lane, int wave, bool live = true) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, live ? 0x7fffffffu : 0u);
 #pragma unroll
     for (int i = 0; i < ROWS / 4 / NW; ++i) {
         const int b = NW * i + wave;
@@ -146,6 +148,45 @@ __device__ __forceinline__ void lds_wait(bf16x8 (&v)[N]) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+// s_waitcnt lgkmcnt(N) (N a compile-time count of LDS reads allowed to stay
+// in flight); the fragments passed become outputs of the wait so their uses
+// stay below it.  Only LDS reads issued by this code are outstanding where
+// it is used (no scalar memory loads), so the in-order count is exact.
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt");
+    if constexpr (N == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
+    else if constexpr (N == 3) asm volatile("s_waitcnt lgkmcnt(3)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt lgkmcnt(6)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+    else static_assert(N == 0, "unsupported lgkmcnt");
+}
+template <typename F>
+__device__ __forceinline__ void pin(F& f) {
+    asm volatile("" : "+v"(f));
+}
+template <int N, typename... F>
+__device__ __forceinline__ void lds_wait_keep(F&... f) {
+    (pin(f), ...);
+    lgkm_wait<N>();
+    (pin(f), ...);
+}
+
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else static_assert(N == 0, "unsupported vmcnt");
 }
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -288,12 +329,14 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restric
 // ====================================================== dq kernel ========
 // Per (query block of 128, query head).  Mirrors the forward: S^T = K Q^T,
 // dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
-__global__ __launch_bounds__(FTHR, 1) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
+// Two workgroups per CU as in the dk/dv kernel (64 KB of LDS each).
+constexpr int DQ_STAGES = 2;
+__global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
                                                           const bf16_t* __restrict__ dout,
                                                           const float* __restrict__ lse,
                                                           const float* __restrict__ delta,
                                                           bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
-    __shared__ __attribute__((aligned(1024))) char sm[2][2 * KV_TILE];
+    __shared__ __attribute__((aligned(1024))) char sm[DQ_STAGES][2 * KV_TILE];
     const int ld = (nq + 2 * nkv) * D;
     const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
@@ -322,29 +365,48 @@ __global__ __launch_bounds__(FTHR, 1) void attn_dq_kernel(const bf16_t* __restri
     const TrBases trb = tr_bases(lane);
 
     const int nkb = (qb * FQ + FQ) / FKV;
+    // Ring of DQ_STAGES K/V blocks: the DMA of blocks kb+1 .. kb+DQ_STAGES-1
+    // is issued while block kb is used (8 loads per wave per block; blocks
+    // past the last are empty).
     auto dma = [&](int kb) {
-        char* st = sm[kb & 1];
-        dma_rows<FKV, 4>(kbase, ld, kb * FKV, T, 0, (lds_void*)st, lane, wave);
-        dma_rows<FKV, 4>(vbase, ld, kb * FKV, T, 0, (lds_void*)(st + KV_TILE), lane, wave);
+        char* st = sm[kb % DQ_STAGES];
+        const bool live = kb < nkb;
+        dma_rows<FKV, 4>(kbase, ld, kb * FKV, T, 0, (lds_void*)st, lane, wave, live);
+        dma_rows<FKV, 4>(vbase, ld, kb * FKV, T, 0, (lds_void*)(st + KV_TILE), lane, wave, live);
     };
-    dma(0);
+#pragma unroll
+    for (int t = 0; t < DQ_STAGES - 1; ++t) dma(t);
     for (int kb = 0; kb < nkb; ++kb) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        vm_wait<8 * (DQ_STAGES - 2)>();  // block kb landed
         wg_barrier();
-        if (kb + 1 < nkb) dma(kb + 1);
+        dma(kb + DQ_STAGES - 1);  // into the stage block kb-1 used
         const int k0 = kb * FKV;
         if (k0 > qw0 + 31) continue;
-        const lds_void* kt = (const lds_void*)sm[kb & 1];
-        const lds_void* vt = (const lds_void*)(sm[kb & 1] + KV_TILE);
+        const lds_void* kt = (const lds_void*)sm[kb % DQ_STAGES];
+        const lds_void* vt = (const lds_void*)(sm[kb % DQ_STAGES] + KV_TILE);
         floatx16 s[2], dp[2];
+        s[0] = s[1] = dp[0] = dp[1] = zero16();
+        {
+            // K and V row fragments of step (j, kk) + 1 are read while step (j, kk) multiplies
+            const uint32_t ka = (uint32_t)(uintptr_t)kt;
+            bf16x8 fk[2], fv[2];
+            auto rd = [&](int st, int slot) {
+                const uint32_t ro = tile_off((st >> 3) * 32 + col, (st & 7) * 2 + g);
+                asm volatile("ds_read_b128 %0, %1" : "=v"(fk[slot]) : "v"(ka + ro));
+                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fv[slot]) : "v"(ka + ro), "i"(KV_TILE));
+            };
+            rd(0, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            s[j] = zero16();
-            dp[j] = zero16();
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                s[j] = mfma(frag_row(kt, j * 32 + col, kk, g), qf[kk], s[j]);
-                dp[j] = mfma(frag_row(vt, j * 32 + col, kk, g), dof[kk], dp[j]);
+            for (int st = 0; st < 16; ++st) {
+                const int cur = st & 1, j = st >> 3, kk = st & 7;
+                if (st + 1 < 16) {
+                    rd(st + 1, cur ^ 1);
+                    lds_wait_keep<2>(fk[cur], fv[cur]);
+                } else {
+                    lds_wait_keep<0>(fk[cur], fv[cur]);
+                }
+                s[j] = mfma(fk[cur], qf[kk], s[j]);
+                dp[j] = mfma(fv[cur], dof[kk], dp[j]);
             }
         }
         const bool diag = (k0 + FKV - 1 > qw0);
@@ -363,18 +425,31 @@ __global__ __launch_bounds__(FTHR, 1) void attn_dq_kernel(const bf16_t* __restri
 #pragma unroll
         for (int t = 0; t < 4; ++t) sb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
         const uint32_t kaddr = (uint32_t)(uintptr_t)kt;
+        {
+            // K^T fragments of d block db, read one block ahead (8 reads each)
+            bf16x8 kf[2][4];
+            auto rd = [&](int db) {
+                kf[db & 1][0] = frag_tr<0>(kaddr, trb, db);
+                kf[db & 1][1] = frag_tr<1>(kaddr, trb, db);
+                kf[db & 1][2] = frag_tr<2>(kaddr, trb, db);
+                kf[db & 1][3] = frag_tr<3>(kaddr, trb, db);
+            };
+            rd(0);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            bf16x8 kf[4];
-            kf[0] = frag_tr<0>(kaddr, trb, db);
-            kf[1] = frag_tr<1>(kaddr, trb, db);
-            kf[2] = frag_tr<2>(kaddr, trb, db);
-            kf[3] = frag_tr<3>(kaddr, trb, db);
-            lds_wait(kf);
+            for (int db = 0; db < 4; ++db) {
+                bf16x8(&cur)[4] = kf[db & 1];
+                if (db + 1 < 4) {
+                    rd(db + 1);
+                    lds_wait_keep<8>(cur[0], cur[1], cur[2], cur[3]);
+                } else {
+                    lds_wait_keep<0>(cur[0], cur[1], cur[2], cur[3]);
+                }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) dacc[db] = mfma(kf[t], sb[t], dacc[db]);
+                for (int t = 0; t < 4; ++t) dacc[db] = mfma(cur[t], sb[t], dacc[db]);
+            }
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the empty trailing blocks still write LDS
     const float scale = 1.f / sqrtf((float)D);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -396,14 +471,20 @@ __global__ __launch_bounds__(FTHR, 1) void attn_dq_kernel(const bf16_t* __restri
 //   dV^T += dO^T P,  dK^T += Q^T dS.
 constexpr int BKV = 128, BQB = 32;
 constexpr int Q_TILE = BQB * D * 2;  // 8 KB
+// Two workgroups per CU (two waves per SIMD, at most 256 registers per
+// lane, 64.5 KB of LDS each): one workgroup's softmax, barrier and LDS
+// latency overlap the other's MFMAs.  Double-buffered query blocks suffice
+// with that overlap.
+constexpr int KV_STAGES = 2;
 
-__global__ __launch_bounds__(FTHR, 1) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
+__global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
                                                            const bf16_t* __restrict__ dout,
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ delta,
                                                            bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
-    __shared__ __attribute__((aligned(1024))) char sm[2][2 * Q_TILE];  // [stage][Q | dO]
-    __shared__ float sl[2][2][BQB];                                     // [stage][lse | delta]
+    __shared__ __attribute__((aligned(1024))) char sm[KV_STAGES][2 * Q_TILE];  // [stage][Q | dO]
+    __shared__ __attribute__((aligned(1024))) char svt[BKV * D * 2];           // V rows of the block
+    __shared__ float sl[KV_STAGES][2][BQB];                                     // [stage][lse | delta]
     const int ld = (nq + 2 * nkv) * D;
     const int ldo = nq * D;
     const int grp = blockIdx.y;
@@ -414,12 +495,13 @@ __global__ __launch_bounds__(FTHR, 1) void attn_dkv_kernel(const bf16_t* __restr
     const int kw0 = kb * BKV + wave * 32;
     const int key = kw0 + col;
 
-    bf16x8 kf[8], vf[8];
+    // K rows of the wave's keys stay in registers; V rows of the block's 128
+    // keys go to LDS once (8 loads per wave, waited for with the first block).
+    bf16x8 kf[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < 8; ++kk)
         kf[kk] = *reinterpret_cast<const bf16x8*>(qkv + (int64_t)key * ld + nq * D + grp * D + kk * 16 + g * 8);
-        vf[kk] = *reinterpret_cast<const bf16x8*>(qkv + (int64_t)key * ld + (nq + nkv) * D + grp * D + kk * 16 + g * 8);
-    }
+    dma_rows<BKV, 4>(qkv + (nq + nkv) * D + grp * D, ld, kb * BKV, T, 0, (lds_void*)svt, lane, wave);
     floatx16 dk[4], dv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -433,93 +515,116 @@ __global__ __launch_bounds__(FTHR, 1) void attn_dkv_kernel(const bf16_t* __restr
     const int per_head = nqb - qb0;
     const int total = per_head * rep;
 
+    // Ring of KV_STAGES query blocks: the DMA of blocks it+1 .. it+KV_STAGES-1
+    // is issued while block it is used.  Every wave issues 6 loads per block
+    // (2 + 2 DMA of Q and dO, and the 32 row statistics of lse and delta,
+    // written identically by each wave's lanes 0..31); blocks past the last
+    // are empty.
     auto fetch = [&](int it) {
-        const int hh = grp * rep + it / per_head;
-        const int q0 = (qb0 + it % per_head) * BQB;
-        char* st = sm[it & 1];
-        dma_rows<BQB, 4>(qkv + hh * D, ld, q0, T, 0, (lds_void*)st, lane, wave);
-        dma_rows<BQB, 4>(dout + hh * D, ldo, q0, T, 0, (lds_void*)(st + Q_TILE), lane, wave);
-        if (wave == 0 && lane < BQB) {  // the row statistics of the block: 32 floats each (32 lanes write)
-            const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (int64_t)hh * T + q0, BQB * 4);
-            const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (int64_t)hh * T + q0, BQB * 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)&sl[it & 1][0][0], 4, lane * 4, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)&sl[it & 1][1][0], 4, lane * 4, 0, 0, 0);
+        const bool live = it < total;
+        const int itc = live ? it : 0;
+        const int hh = grp * rep + itc / per_head;
+        const int q0 = (qb0 + itc % per_head) * BQB;
+        char* st = sm[it % KV_STAGES];
+        dma_rows<BQB, 4>(qkv + hh * D, ld, q0, T, 0, (lds_void*)st, lane, wave, live);
+        dma_rows<BQB, 4>(dout + hh * D, ldo, q0, T, 0, (lds_void*)(st + Q_TILE), lane, wave, live);
+        if (lane < BQB) {
+            const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (int64_t)hh * T + q0, live ? BQB * 4 : 0);
+            const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (int64_t)hh * T + q0, live ? BQB * 4 : 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)&sl[it % KV_STAGES][0][0], 4, lane * 4, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)&sl[it % KV_STAGES][1][0], 4, lane * 4, 0, 0, 0);
         }
     };
 
-    fetch(0);
+#pragma unroll
+    for (int t = 0; t < KV_STAGES - 1; ++t) fetch(t);
     for (int it = 0; it < total; ++it) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        vm_wait<6 * (KV_STAGES - 2)>();  // block it landed
         wg_barrier();
-        if (it + 1 < total) fetch(it + 1);
+        fetch(it + KV_STAGES - 1);  // into the stage block it-1 used
         const int q0 = (qb0 + it % per_head) * BQB;
         if (q0 + BQB - 1 < kw0) continue;  // every query of the block precedes every key of the wave
-        const lds_void* qt = (const lds_void*)sm[it & 1];
-        const lds_void* ot = (const lds_void*)(sm[it & 1] + Q_TILE);
+        const int stg = it % KV_STAGES;
+        const lds_void* qt = (const lds_void*)sm[stg];
+        const lds_void* ot = (const lds_void*)(sm[stg] + Q_TILE);
         // Fragment reads as asm (explicit waits): the compiler would otherwise
         // wait for the DMA of the next block, issued just above, before them.
         floatx16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            bf16x8 fr[8];
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const int kk = half * 4 + k4;
+        {
+            const uint32_t qa = (uint32_t)(uintptr_t)qt, va = (uint32_t)(uintptr_t)svt + wave * 32 * 256;
+            // Q, dO and V row fragments of k step kk + 1 are read while step kk multiplies
+            bf16x8 fq[2], fo[2], fv[2];
+            auto rd = [&](int kk, int slot) {
                 const uint32_t ro = tile_off(col, kk * 2 + g);
-                asm volatile("ds_read_b128 %0, %1" : "=v"(fr[k4]) : "v"((uint32_t)(uintptr_t)qt + ro));
-                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fr[4 + k4]) : "v"((uint32_t)(uintptr_t)qt + ro), "i"(Q_TILE));
-            }
-            lds_wait(fr);
+                asm volatile("ds_read_b128 %0, %1" : "=v"(fq[slot]) : "v"(qa + ro));
+                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fo[slot]) : "v"(qa + ro), "i"(Q_TILE));
+                asm volatile("ds_read_b128 %0, %1" : "=v"(fv[slot]) : "v"(va + ro));
+            };
+            rd(0, 0);
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                s = mfma(fr[k4], kf[half * 4 + k4], s);
-                dp = mfma(fr[4 + k4], vf[half * 4 + k4], dp);
+            for (int kk = 0; kk < 8; ++kk) {
+                const int cur = kk & 1;
+                if (kk + 1 < 8) {
+                    rd(kk + 1, cur ^ 1);
+                    lds_wait_keep<3>(fq[cur], fo[cur], fv[cur]);
+                } else {
+                    lds_wait_keep<0>(fq[cur], fo[cur], fv[cur]);
+                }
+                s = mfma(fq[cur], kf[kk], s);
+                dp = mfma(fo[cur], fv[cur], dp);
             }
         }
         const bool diag = (q0 < kw0 + 31);
-        // row statistics of the accumulator rows (r/4)*8 + 4g + r%4: four
-        // 16-byte reads each, issued as asm (see frag_tr) and waited for here
-        floatx4 lsv[4], dsv[4];
-        {
-            const uint32_t lb = (uint32_t)(uintptr_t)&sl[it & 1][0][0] + g * 16;
-            const uint32_t db = (uint32_t)(uintptr_t)&sl[it & 1][1][0] + g * 16;
+        // row statistics of the accumulator rows (r/4)*8 + 4g + r%4, 16-byte
+        // reads issued as asm (see frag_tr), two row groups at a time
+        const uint32_t lb = (uint32_t)(uintptr_t)&sl[stg][0][0] + g * 16;
+        const uint32_t db = (uint32_t)(uintptr_t)&sl[stg][1][0] + g * 16;
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(lsv[rb]) : "v"(lb), "i"(rb * 32));
-                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dsv[rb]) : "v"(db), "i"(rb * 32));
+        for (int rb = 0; rb < 4; ++rb) {
+            floatx4 lsv, dsv;
+            asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(lsv) : "v"(lb), "i"(rb * 32));
+            asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dsv) : "v"(db), "i"(rb * 32));
+            lds_wait_keep<0>(lsv, dsv);
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int r = rb * 4 + r4;
+                const int qr = rb * 8 + g * 4 + r4;
+                float p = fast_exp2(fmaf(s[r], c, -lsv[r4]));
+                if (diag && key > q0 + qr) p = 0.f;
+                s[r] = p;
+                dp[r] = p * (dp[r] - dsv[r4]);
             }
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) asm volatile("" : "+v"(lsv[rb]), "+v"(dsv[rb]));
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) asm volatile("" : "+v"(lsv[rb]), "+v"(dsv[rb]));
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qr = (r >> 2) * 8 + g * 4 + (r & 3);
-            float p = fast_exp2(fmaf(s[r], c, -lsv[r >> 2][r & 3]));
-            if (diag && key > q0 + qr) p = 0.f;
-            s[r] = p;
-            dp[r] = p * (dp[r] - dsv[r >> 2][r & 3]);
         }
         const bf16x8 p0 = acc_half_to_bf16(s, 0), p1 = acc_half_to_bf16(s, 1);
         const bf16x8 s0 = acc_half_to_bf16(dp, 0), s1 = acc_half_to_bf16(dp, 1);
         const uint32_t oaddr = (uint32_t)(uintptr_t)ot, qaddr = (uint32_t)(uintptr_t)qt;
+        {
+            // dO^T and Q^T fragments of d block db, read one block ahead
+            bf16x8 fr[2][4];
+            auto rd = [&](int db) {
+                fr[db & 1][0] = frag_tr<0>(oaddr, trb, db);
+                fr[db & 1][1] = frag_tr<1>(oaddr, trb, db);
+                fr[db & 1][2] = frag_tr<0>(qaddr, trb, db);
+                fr[db & 1][3] = frag_tr<1>(qaddr, trb, db);
+            };
+            rd(0);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            bf16x8 fo[2], fq[2];
-            fo[0] = frag_tr<0>(oaddr, trb, db);
-            fo[1] = frag_tr<1>(oaddr, trb, db);
-            fq[0] = frag_tr<0>(qaddr, trb, db);
-            fq[1] = frag_tr<1>(qaddr, trb, db);
-            lds_wait(fo);
-            lds_wait(fq);
-            dv[db] = mfma(fo[0], p0, dv[db]);
-            dv[db] = mfma(fo[1], p1, dv[db]);
-            dk[db] = mfma(fq[0], s0, dk[db]);
-            dk[db] = mfma(fq[1], s1, dk[db]);
+            for (int db = 0; db < 4; ++db) {
+                bf16x8(&cur)[4] = fr[db & 1];
+                if (db + 1 < 4) {
+                    rd(db + 1);
+                    lds_wait_keep<8>(cur[0], cur[1], cur[2], cur[3]);
+                } else {
+                    lds_wait_keep<0>(cur[0], cur[1], cur[2], cur[3]);
+                }
+                dv[db] = mfma(cur[0], p0, dv[db]);
+                dv[db] = mfma(cur[1], p1, dv[db]);
+                dk[db] = mfma(cur[2], s0, dk[db]);
+                dk[db] = mfma(cur[3], s1, dk[db]);
+            }
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the empty trailing blocks still write LDS
     const float scale = 1.f / sqrtf((float)D);
 #pragma unroll
     for (int db = 0; db < 4; ++db)

@@ -30,7 +30,10 @@
 namespace zb {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, STAGES = 4;
+#ifndef ZB_STAGES
+#define ZB_STAGES 4
+#endif
+constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, STAGES = ZB_STAGES;
 constexpr int TILE_BYTES = 256 * BK * 2;  // 16 KB per operand tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr int DMA_PER_TILE = 2 * (TILE_BYTES / 1024) / 4;  // per wave, A + B
@@ -42,7 +45,11 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // 16-byte chunk swizzle of a K-contiguous tile (64-byte rows): the rows a
 // ds_read_b128 serves together (8 or 16 lanes) hit distinct bank windows.
+#ifdef ZB_KEYKM
+__device__ __forceinline__ int key_km(int row) { return (row >> ZB_KEYKM) & 3; }
+#else
 __device__ __forceinline__ int key_km(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+#endif
 // 32-byte piece swizzle of an M/N-contiguous tile row k: the 4 rows a 16-lane
 // group reads in one transpose instruction land in 4 distinct 32-byte bank
 // windows (and the 8 pieces of a 32-lane half in 8), conflict-free for both
@@ -168,6 +175,34 @@ __device__ __forceinline__ void interleave_reads_dma_mfma() {
     }
 }
 
+// Front-loaded variant: PER of the NR reads then ND DMA loads before each of
+// the NM MFMAs until they run out.
+template <int NR, int ND, int PER, int NM, int SLOT>
+__device__ __forceinline__ void front_mfma() {
+    if constexpr (SLOT < NM) {
+        constexpr int lo = SLOT * PER, hi = (SLOT + 1) * PER;
+        constexpr int T = NR + ND;
+        constexpr int a = lo < T ? lo : T, b = hi < T ? hi : T;
+        constexpr int nr = (b < NR ? b : NR) - (a < NR ? a : NR);
+        constexpr int nd = (b - a) - nr;
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+        if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x020, nd, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        front_mfma<NR, ND, PER, NM, SLOT + 1>();
+    }
+}
+
+// Wait until at most N buffer loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N == 0 || N == 8 || N == 16 || N == 24 || N == 32, "vmcnt");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+}
+
 // Workgroup barrier without the memory fence __syncthreads() implies: that
 // fence waits for every outstanding load, including the DMA of tiles that are
 // meant to stay in flight.  Callers wait for exactly the tile they need
@@ -286,7 +321,7 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
     // tiles kt+2 and kt+3 (16 loads per wave) may stay in flight.
 #pragma unroll
     for (int t = 0; t < STAGES; ++t) dma_tile(t);
-    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // tile 0 landed
+    wait_vm<(STAGES - 1) * DMA_PER_TILE>();  // tile 0 landed
     workgroup_barrier();
     bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
     {
@@ -316,10 +351,14 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mi], fb0[ni], acc[mi][ni], 0, 0, 0);
+#ifdef ZB_FRONT
+        if (A_KMAJ && B_KMAJ) front_mfma<RD, 0, ZB_FRONT, 16, 0>();
+#else
         if (A_KMAJ && B_KMAJ) interleave_reads_mfma<RD, 0>();
+#endif
         __builtin_amdgcn_sched_barrier(0);
         lds_wait(fa1, fb1);  // tile kt fully read: its stage may be overwritten
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // tile kt+1 landed
+        wait_vm<(STAGES - 2) * DMA_PER_TILE>();  // tile kt+1 landed
         workgroup_barrier();
         // region B (the fragments read past the last tile are never used)
         {
@@ -338,7 +377,11 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
+#ifdef ZB_FRONT
+        if (A_KMAJ && B_KMAJ) front_mfma<RD, 8, ZB_FRONT, 16, 0>();
+#else
         if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, 8, 0>();
+#endif
     }
     __builtin_amdgcn_sched_barrier(0);
     // The empty tiles' DMA still writes (zeros) into the stages, and every
