@@ -5,7 +5,9 @@
 //   dP = do v^T,  dS = P (dP - rowsum(do o)),  dq = dS k / sqrt(d),
 //   dk = dS^T q / sqrt(d),  dv = P^T do   (dk, dv summed over each KV group)
 //
-// CDNA4 design.  Every product is a v_mfma_f32_32x32x16_bf16.
+// CDNA4 design.  Every product is a v_mfma_f32_32x32x16_bf16.  The wave
+// index is read into a scalar register so that LDS DMA destinations (M0) are
+// computed by scalar instructions.
 // * Tiles of K, V (forward, dq) and of Q, dO (dk/dv) are DMA'd HBM -> LDS
 //   with buffer_load ... lds in their natural [rows][128 d] layout (256-byte
 //   rows, 16-byte chunks XOR-swizzled by the row), double buffered.
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restr
     const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
     const int qb = gridDim.x - 1 - blockIdx.x;  // longest causal range first
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int qw0 = qb * FQ + wave * 32;
     const int q = qw0 + col;
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restri
     const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
     const int qb = gridDim.x - 1 - blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int qw0 = qb * FQ + wave * 32;
     const int q = qw0 + col;
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restr
     const int grp = blockIdx.y;
     const int rep = nq / nkv;
     const int kb = blockIdx.x;  // low key blocks have the most query blocks; launched first
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int kw0 = kb * BKV + wave * 32;
     const int key = kw0 + col;

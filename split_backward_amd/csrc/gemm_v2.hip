@@ -30,10 +30,7 @@
 namespace zb {
 namespace {
 
-#ifndef ZB_STAGES
-#define ZB_STAGES 4
-#endif
-constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, STAGES = ZB_STAGES;
+constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, STAGES = 4;
 constexpr int TILE_BYTES = 256 * BK * 2;  // 16 KB per operand tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr int DMA_PER_TILE = 2 * (TILE_BYTES / 1024) / 4;  // per wave, A + B
@@ -45,11 +42,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // 16-byte chunk swizzle of a K-contiguous tile (64-byte rows): the rows a
 // ds_read_b128 serves together (8 or 16 lanes) hit distinct bank windows.
-#ifdef ZB_KEYKM
-__device__ __forceinline__ int key_km(int row) { return (row >> ZB_KEYKM) & 3; }
-#else
 __device__ __forceinline__ int key_km(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-#endif
 // 32-byte piece swizzle of an M/N-contiguous tile row k: the 4 rows a 16-lane
 // group reads in one transpose instruction land in 4 distinct 32-byte bank
 // windows (and the 8 pieces of a 32-lane half in 8), conflict-free for both
@@ -175,28 +168,12 @@ __device__ __forceinline__ void interleave_reads_dma_mfma() {
     }
 }
 
-// Front-loaded variant: PER of the NR reads then ND DMA loads before each of
-// the NM MFMAs until they run out.
-template <int NR, int ND, int PER, int NM, int SLOT>
-__device__ __forceinline__ void front_mfma() {
-    if constexpr (SLOT < NM) {
-        constexpr int lo = SLOT * PER, hi = (SLOT + 1) * PER;
-        constexpr int T = NR + ND;
-        constexpr int a = lo < T ? lo : T, b = hi < T ? hi : T;
-        constexpr int nr = (b < NR ? b : NR) - (a < NR ? a : NR);
-        constexpr int nd = (b - a) - nr;
-        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
-        if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x020, nd, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        front_mfma<NR, ND, PER, NM, SLOT + 1>();
-    }
-}
-
 // Wait until at most N buffer loads of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-    static_assert(N == 0 || N == 8 || N == 16 || N == 24 || N == 32, "vmcnt");
+    static_assert(N == 0 || N == 8 || N == 16 || N == 20 || N == 24 || N == 32, "vmcnt");
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
     else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
@@ -242,7 +219,9 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index as a scalar: every LDS address derived from it (the DMA
+    // destinations in M0) is then computed by scalar instructions.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 5, lrow = lane & 31;
     int tm, tn;
@@ -261,7 +240,8 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
     const int64_t step_a = A_KMAJ ? BK * 2 : (int64_t)BK * d.lda * 2;
     const int64_t step_b = B_KMAJ ? BK * 2 : (int64_t)BK * d.ldb * 2;
 
-    auto dma_tile = [&](int kt) {
+    // part 0: the A tile only, 1: the B tile only, 2: both.
+    auto dma_tile = [&](int kt, int part = 2) {
         char* st = smem + (kt % STAGES) * STAGE_BYTES;
         // A tile past the end of K gets an empty range: its loads read zeros,
         // fetch nothing, and keep the per-iteration DMA count uniform.
@@ -277,11 +257,11 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
             else dma_offsets_mnmaj(ta, d.lda, m0, d.M, lane, wave);
             if (B_KMAJ) dma_offsets_kmaj<PAIRED>(tb, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
             else dma_offsets_mnmaj(tb, d.ldb, n0, d.N, lane, wave);
-            dma_issue(ra, (lds_void*)st, ta, wave);
-            dma_issue(rb, (lds_void*)(st + TILE_BYTES), tb, wave);
+            if (part != 1) dma_issue(ra, (lds_void*)st, ta, wave);
+            if (part != 0) dma_issue(rb, (lds_void*)(st + TILE_BYTES), tb, wave);
         } else {
-            dma_issue(ra, (lds_void*)st, offa, wave);
-            dma_issue(rb, (lds_void*)(st + TILE_BYTES), offb, wave);
+            if (part != 1) dma_issue(ra, (lds_void*)st, offa, wave);
+            if (part != 0) dma_issue(rb, (lds_void*)(st + TILE_BYTES), offb, wave);
         }
     };
 
@@ -306,6 +286,12 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
     };
 
     constexpr int RD_A = A_KMAJ ? 1 : 2, RD_B = B_KMAJ ? 1 : 2;
+    // With an M/N-contiguous operand (transpose reads, twice the LDS read
+    // instructions) the DMA of a tile is split: its A half is issued in
+    // region B, its B half in the next region A, which spreads the address
+    // unit's work over the whole tile.  Both-K-contiguous kernels measure
+    // faster with the whole tile in region B.
+    constexpr bool SPLIT_DMA = !A_KMAJ || !B_KMAJ;
     constexpr int RD = 4 * (RD_A + RD_B);  // LDS read instructions per 16-k step
 
     // Software pipeline across tiles.  Iteration kt:
@@ -315,13 +301,22 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
     //             barrier (mid-tile, so no wave idles at a tile boundary);
     //   region B: MFMAs of step 1 of tile kt, while the step-0 fragments of
     //             tile kt+1 are read and the DMA of tile kt+4 is issued into
-    //             the stage tile kt just vacated.
+    //             the stage tile kt just vacated (with SPLIT_DMA its A half;
+    //             the B half follows in region A of iteration kt+1, when that
+    //             stage is still free).
     // Every iteration issues the same DMA count (tiles past K are empty), so
     // the waits are constants: after region A of iteration kt the DMA of
     // tiles kt+2 and kt+3 (16 loads per wave) may stay in flight.
+    if (SPLIT_DMA) {
 #pragma unroll
-    for (int t = 0; t < STAGES; ++t) dma_tile(t);
-    wait_vm<(STAGES - 1) * DMA_PER_TILE>();  // tile 0 landed
+        for (int t = 0; t < STAGES - 1; ++t) dma_tile(t);
+        dma_tile(STAGES - 1, 0);
+        wait_vm<(STAGES - 1) * DMA_PER_TILE - DMA_PER_TILE / 2>();  // tile 0 landed
+    } else {
+#pragma unroll
+        for (int t = 0; t < STAGES; ++t) dma_tile(t);
+        wait_vm<(STAGES - 1) * DMA_PER_TILE>();  // tile 0 landed
+    }
     workgroup_barrier();
     bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
     {
@@ -351,15 +346,13 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mi], fb0[ni], acc[mi][ni], 0, 0, 0);
-#ifdef ZB_FRONT
-        if (A_KMAJ && B_KMAJ) front_mfma<RD, 0, ZB_FRONT, 16, 0>();
-#else
+        if (SPLIT_DMA) dma_tile(kt + STAGES - 1, 1);  // B half of tile kt+3
         if (A_KMAJ && B_KMAJ) interleave_reads_mfma<RD, 0>();
-#endif
         __builtin_amdgcn_sched_barrier(0);
         lds_wait(fa1, fb1);  // tile kt fully read: its stage may be overwritten
         wait_vm<(STAGES - 2) * DMA_PER_TILE>();  // tile kt+1 landed
         workgroup_barrier();
+
         // region B (the fragments read past the last tile are never used)
         {
             const char* sn = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
@@ -371,17 +364,13 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
                 fb0[i] = frag_b(nb, i, 0);
             }
         }
-        dma_tile(kt + STAGES);  // into the stage tile kt vacated
+        dma_tile(kt + STAGES, SPLIT_DMA ? 0 : 2);  // into the stage tile kt vacated
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
-#ifdef ZB_FRONT
-        if (A_KMAJ && B_KMAJ) front_mfma<RD, 8, ZB_FRONT, 16, 0>();
-#else
         if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, 8, 0>();
-#endif
     }
     __builtin_amdgcn_sched_barrier(0);
     // The empty tiles' DMA still writes (zeros) into the stages, and every
