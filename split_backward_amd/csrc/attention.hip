@@ -160,6 +160,7 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait() {
     static_assert(N >= 0 && N <= 15, "lgkmcnt");
     if constexpr (N == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    else if constexpr (N == 1) asm volatile("s_waitcnt lgkmcnt(1)" ::: "memory");
     else if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory");
     else if constexpr (N == 3) asm volatile("s_waitcnt lgkmcnt(3)" ::: "memory");
     else if constexpr (N == 4) asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
@@ -239,11 +240,26 @@ __global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restr
         const lds_void* kt = (const lds_void*)sm[kb & 1];
         const lds_void* vt = (const lds_void*)(sm[kb & 1] + KV_TILE);
         floatx16 s[2];
+        s[0] = s[1] = zero16();
+        {
+            // K row fragment of step (j, kk) + 1 is read while step (j, kk) multiplies
+            const uint32_t ka = (uint32_t)(uintptr_t)kt;
+            bf16x8 fk[2];
+            auto rd = [&](int st, int slot) {
+                asm volatile("ds_read_b128 %0, %1" : "=v"(fk[slot]) : "v"(ka + tile_off((st >> 3) * 32 + col, (st & 7) * 2 + g)));
+            };
+            rd(0, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            s[j] = zero16();
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) s[j] = mfma(frag_row(kt, j * 32 + col, kk, g), qf[kk], s[j]);
+            for (int st = 0; st < 16; ++st) {
+                const int cur = st & 1;
+                if (st + 1 < 16) {
+                    rd(st + 1, cur ^ 1);
+                    lds_wait_keep<1>(fk[cur]);
+                } else {
+                    lds_wait_keep<0>(fk[cur]);
+                }
+                s[st >> 3] = mfma(fk[cur], qf[st & 7], s[st >> 3]);
+            }
         }
         if (k0 + FKV - 1 > qw0) {  // diagonal block: mask keys after the query
 #pragma unroll
@@ -285,16 +301,28 @@ __global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restr
 #pragma unroll
         for (int t = 0; t < 4; ++t) pb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
         const uint32_t vaddr = (uint32_t)(uintptr_t)vt;
+        {
+            // V^T fragments of d block db + 1 are read while block db multiplies
+            bf16x8 vf[2][4];
+            auto rd = [&](int db) {
+                vf[db & 1][0] = frag_tr<0>(vaddr, trb, db);
+                vf[db & 1][1] = frag_tr<1>(vaddr, trb, db);
+                vf[db & 1][2] = frag_tr<2>(vaddr, trb, db);
+                vf[db & 1][3] = frag_tr<3>(vaddr, trb, db);
+            };
+            rd(0);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            bf16x8 vf[4];
-            vf[0] = frag_tr<0>(vaddr, trb, db);
-            vf[1] = frag_tr<1>(vaddr, trb, db);
-            vf[2] = frag_tr<2>(vaddr, trb, db);
-            vf[3] = frag_tr<3>(vaddr, trb, db);
-            lds_wait(vf);
+            for (int db = 0; db < 4; ++db) {
+                bf16x8(&cur)[4] = vf[db & 1];
+                if (db + 1 < 4) {
+                    rd(db + 1);
+                    lds_wait_keep<8>(cur[0], cur[1], cur[2], cur[3]);
+                } else {
+                    lds_wait_keep<0>(cur[0], cur[1], cur[2], cur[3]);
+                }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) oacc[db] = mfma(vf[t], pb[t], oacc[db]);
+                for (int t = 0; t < 4; ++t) oacc[db] = mfma(cur[t], pb[t], oacc[db]);
+            }
         }
     }
     const float inv = 1.f / l;
