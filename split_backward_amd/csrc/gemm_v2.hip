@@ -215,7 +215,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
 
 template <bool A_KMAJ, bool B_KMAJ, int EPI>
 __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, uint32_t a_bytes,
-                                                       uint32_t b_bytes) {
+                                                       uint32_t b_bytes, uint32_t c_bytes) {
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
@@ -373,9 +373,33 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
         if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, 8, 0>();
     }
     __builtin_amdgcn_sched_barrier(0);
+    // fp32 accumulate: the old dW values of the first 32-row block are
+    // loaded now (16 loads per wave), so their latency overlaps the drain below.
+    const int c4 = (lane & 31) * 4;
+    const int gcol = n0 + wn * 128 + c4;
+    const bool col_ok = gcol < d.N;
+    floatx4 cin[2][16];
+    // Buffer loads, one per row group whether or not it is inside C (outside
+    // reads as zero), so every wave issues exactly 16 per block: the counted
+    // wait below relies on it.  The launcher guarantees C spans < 2 GiB.
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(d.C, c_bytes);
+    auto load_block = [&](int mi, floatx4 (&dst)[16]) {
+        const int rbase = m0 + wm * 128 + mi * 32;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int row = rbase + 2 * it + (lane >> 5);
+            const uint32_t off = (row < d.M && col_ok) ? (uint32_t)(((int64_t)row * d.ldc + gcol) * 4) : OOB;
+            dst[it] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
+        }
+    };
     // The empty tiles' DMA still writes (zeros) into the stages, and every
     // wave must be done with them before the epilogue reuses the memory.
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    if constexpr (EPI == EPI_ACCUM_F32) {
+        load_block(0, cin[0]);
+        asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");  // all DMA done; dW loads in flight
+    } else {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    }
     workgroup_barrier();
 
     // ---- epilogue ---------------------------------------------------------
@@ -388,6 +412,29 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
     // divisible by 4 are routed to the first-generation kernel instead.)
     constexpr int P = 132;  // floats per staged row: 128 + 4 padding
     float* stage = reinterpret_cast<float*>(smem) + wave * 32 * P;
+    if constexpr (EPI == EPI_ACCUM_F32) {
+        // dW += acc: the old values of block mi+1 are loaded while block mi
+        // is added and stored, so at most one HBM round trip is exposed.
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi + 1 < 4) load_block(mi + 1, cin[(mi + 1) & 1]);
+            const int rbase = m0 + wm * 128 + mi * 32;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    stage[((r >> 2) * 8 + g * 4 + (r & 3)) * P + ni * 32 + lrow] = acc[mi][ni][r];
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int lr = 2 * it + (lane >> 5);
+                const int row = rbase + lr;
+                const uint32_t off = (row < d.M && col_ok) ? (uint32_t)(((int64_t)row * d.ldc + gcol) * 4) : OOB;
+                const floatx4 v = *reinterpret_cast<const floatx4*>(stage + lr * P + c4) + cin[mi & 1][it];
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);  // dropped outside C
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int rbase = m0 + wm * 128 + mi * 32;
@@ -491,10 +538,10 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
 }
 
 template <bool AK, bool BKM>
-int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, uint32_t ab, uint32_t bb) {
+int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, uint32_t ab, uint32_t bb, uint32_t cb) {
     dim3 grid(tiles_m * tiles_n), block(NTHR);
     switch (d.epi) {
-#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E>), grid, block, 0, s, d, tiles_m, tiles_n, ab, bb); break;
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E>), grid, block, 0, s, d, tiles_m, tiles_n, ab, bb, cb); break;
         ZB_CASE(EPI_STORE)
         ZB_CASE(EPI_RESID)
         ZB_CASE(EPI_ACCUM_F32)
@@ -520,7 +567,9 @@ int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
     const bool paired = d.epi == EPI_SWIGLU_FWD;
     const uint64_t ab = d.a_kmajor ? span_bytes(d.M, d.lda, d.K) : span_bytes(d.K, d.lda, d.M);
     const uint64_t bb = d.b_kmajor ? span_bytes(d.N, d.ldb, d.K) : span_bytes(d.K, d.ldb, d.N);
-    if (ab >= OOB || bb >= OOB) return ZB_OK;  // too large for one buffer range: caller uses the first kernel
+    // fp32 accumulate reads C through a buffer range as well
+    const uint64_t cb = d.epi == EPI_ACCUM_F32 ? (uint64_t)((int64_t)(d.M - 1) * d.ldc + d.N) * 4 : 0;
+    if (ab >= OOB || bb >= OOB || cb >= OOB) return ZB_OK;  // too large for one buffer range: caller uses the first kernel
     // 16-byte (fp32) / 8-byte (bf16) epilogue accesses need widths and leading
     // dimensions divisible by 4 and aligned base pointers.
     auto al = [](const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
@@ -534,11 +583,11 @@ int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
     *handled = true;
     const int tiles_m = (d.M + BM - 1) / BM;
     const int tiles_n = paired ? (d.half_n + BN / 2 - 1) / (BN / 2) : (d.N + BN - 1) / BN;
-    const uint32_t a32 = (uint32_t)ab, b32 = (uint32_t)bb;
-    if (d.a_kmajor && d.b_kmajor) return launch_v2<true, true>(d, s, tiles_m, tiles_n, a32, b32);
-    if (d.a_kmajor && !d.b_kmajor) return launch_v2<true, false>(d, s, tiles_m, tiles_n, a32, b32);
-    if (!d.a_kmajor && !d.b_kmajor) return launch_v2<false, false>(d, s, tiles_m, tiles_n, a32, b32);
-    return launch_v2<false, true>(d, s, tiles_m, tiles_n, a32, b32);
+    const uint32_t a32 = (uint32_t)ab, b32 = (uint32_t)bb, c32 = (uint32_t)cb;
+    if (d.a_kmajor && d.b_kmajor) return launch_v2<true, true>(d, s, tiles_m, tiles_n, a32, b32, c32);
+    if (d.a_kmajor && !d.b_kmajor) return launch_v2<true, false>(d, s, tiles_m, tiles_n, a32, b32, c32);
+    if (!d.a_kmajor && !d.b_kmajor) return launch_v2<false, false>(d, s, tiles_m, tiles_n, a32, b32, c32);
+    return launch_v2<false, true>(d, s, tiles_m, tiles_n, a32, b32, c32);
 }
 
 }  // namespace zb
