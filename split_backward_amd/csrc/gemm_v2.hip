@@ -435,28 +435,29 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
         }
         return;
     }
+    // Epilogues that read a bf16 input (residual, activation input): the
+    // rows of block mi+1 are loaded while block mi is computed and stored.
+    constexpr bool HAS_R = EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD;
+    constexpr int IT = 16;  // rows 2*it + lane/32 of a 32-row block
+    u32x2 rin[2][IT], rin2[2][IT];
+    auto load_r = [&](int mi, int buf) {
+        const int rbase = m0 + wm * 128 + mi * 32;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int row = rbase + 2 * it + (lane >> 5);
+            if (row < d.M && col_ok) {
+                const bf16_t* rrow = reinterpret_cast<const bf16_t*>(d.R) + (int64_t)row * d.ldr;
+                rin[buf][it] = *reinterpret_cast<const u32x2*>(rrow + gcol);
+                if (EPI == EPI_SWIGLU_BWD) rin2[buf][it] = *reinterpret_cast<const u32x2*>(rrow + d.half_n + gcol);
+            }
+        }
+    };
+    if (HAS_R && !PAIRED) load_r(0, 0);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int rbase = m0 + wm * 128 + mi * 32;
         if (!PAIRED) {
-            const int c4 = (lane & 31) * 4;
-            const int gcol = n0 + wn * 128 + c4;
-            const bool col_ok = gcol < d.N;
-            constexpr int IT = 16;  // rows 2*it + lane/32
-            floatx4 cin[IT];
-            u32x2 rin[IT], rin2[IT];
-#pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                const int row = rbase + 2 * it + (lane >> 5);
-                if (row < d.M && col_ok) {
-                    if (EPI == EPI_ACCUM_F32)
-                        cin[it] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(d.C) + (int64_t)row * d.ldc + gcol);
-                    if (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD)
-                        rin[it] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16_t*>(d.R) + (int64_t)row * d.ldr + gcol);
-                    if (EPI == EPI_SWIGLU_BWD)
-                        rin2[it] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16_t*>(d.R) + (int64_t)row * d.ldr + d.half_n + gcol);
-                }
-            }
+            if (HAS_R && mi + 1 < 4) load_r(mi + 1, (mi + 1) & 1);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -468,22 +469,18 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
                 const int row = rbase + lr;
                 if (row >= d.M || !col_ok) continue;
                 const floatx4 v = *reinterpret_cast<const floatx4*>(stage + lr * P + c4);
-                if (EPI == EPI_ACCUM_F32) {
-                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(d.C) + (int64_t)row * d.ldc + gcol) = cin[it] + v;
-                    continue;
-                }
                 float o[4], o2[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float x = v[e];
-                    const uint32_t rw = (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD) ? rin[it][e >> 1] : 0u;
+                    const uint32_t rw = HAS_R ? rin[mi & 1][it][e >> 1] : 0u;
                     const float rv = (e & 1) ? __uint_as_float(rw & 0xffff0000u) : __uint_as_float(rw << 16);
                     if (EPI == EPI_STORE) o[e] = x;
                     else if (EPI == EPI_RESID) o[e] = x + rv;
                     else if (EPI == EPI_GELU_FWD) { o[e] = x; o2[e] = gelu_tanh_f(x); }
                     else if (EPI == EPI_GELU_BWD) o[e] = x * gelu_tanh_grad_f(rv);
                     else if (EPI == EPI_SWIGLU_BWD) {
-                        const uint32_t uw = rin2[it][e >> 1];
+                        const uint32_t uw = rin2[mi & 1][it][e >> 1];
                         const float u = (e & 1) ? __uint_as_float(uw & 0xffff0000u) : __uint_as_float(uw << 16);
                         const float sg = sigmoid_f(rv);
                         o[e] = x * u * sg * (1.f + rv * (1.f - sg));
