@@ -111,34 +111,67 @@ __global__ __launch_bounds__(RT) void rms_bwd_kernel(const bf16_t* __restrict__ 
     }
 }
 
-// dgamma partials: block (column pair block, row chunk of DG_ROWS rows).
-constexpr int DG_ROWS = 64;
+// dgamma partials.  Block (column block of 512, row chunk of DG_ROWS rows):
+// each lane owns 8 consecutive columns (16-byte loads of x and dn), each of
+// the 4 waves a quarter of the chunk's rows with all its loads in flight;
+// the waves' sums are combined in LDS in a fixed order (deterministic).
+constexpr int DG_ROWS = 64, DG_WROWS = DG_ROWS / 4;
 __global__ __launch_bounds__(256) void dgamma_partial_kernel(const bf16_t* __restrict__ x, const float* __restrict__ r,
                                                              const bf16_t* __restrict__ dn, float* __restrict__ part,
                                                              int T, int H) {
-    const int col = (blockIdx.x * 256 + threadIdx.x) * 2;
-    const int t0 = blockIdx.y * DG_ROWS;
-    if (col >= H) return;
-    float s0 = 0.f, s1 = 0.f;
-    const int t1 = min(T, t0 + DG_ROWS);
-    for (int t = t0; t < t1; ++t) {
-        const uint32_t xv = *reinterpret_cast<const uint32_t*>(x + (int64_t)t * H + col);
-        const uint32_t dv = *reinterpret_cast<const uint32_t*>(dn + (int64_t)t * H + col);
-        const float rt = r[t];
-        s0 += __uint_as_float(dv << 16) * (__uint_as_float(xv << 16) * rt);
-        s1 += __uint_as_float(dv & 0xffff0000u) * (__uint_as_float(xv & 0xffff0000u) * rt);
+    __shared__ float red[4][512];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c0 = blockIdx.x * 512 + lane * 8;
+    const int t0 = blockIdx.y * DG_ROWS + wave * DG_WROWS;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (c0 < H) {
+        u32x4 xv[DG_WROWS], dv[DG_WROWS];
+        float rv[DG_WROWS];
+#pragma unroll
+        for (int i = 0; i < DG_WROWS; ++i) {
+            const int t = t0 + i;
+            if (t < T) {
+                xv[i] = *reinterpret_cast<const u32x4*>(x + (int64_t)t * H + c0);
+                dv[i] = *reinterpret_cast<const u32x4*>(dn + (int64_t)t * H + c0);
+                rv[i] = r[t];
+            } else {
+                xv[i] = dv[i] = u32x4{0, 0, 0, 0};
+                rv[i] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < DG_WROWS; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t xw = xv[i][e], dw = dv[i][e];
+                acc[2 * e] += __uint_as_float(dw << 16) * (__uint_as_float(xw << 16) * rv[i]);
+                acc[2 * e + 1] += __uint_as_float(dw & 0xffff0000u) * (__uint_as_float(xw & 0xffff0000u) * rv[i]);
+            }
     }
-    part[(int64_t)blockIdx.y * H + col] = s0;
-    part[(int64_t)blockIdx.y * H + col + 1] = s1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = acc[e];
+    __syncthreads();
+    for (int j = threadIdx.x; j < 512; j += 256) {
+        const int col = blockIdx.x * 512 + j;
+        if (col < H) part[(int64_t)blockIdx.y * H + col] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+    }
 }
 
+// dgamma += sum of the chunk partials, chunks in ascending order; four
+// independent partial sums per column keep the loads in flight.
 __global__ __launch_bounds__(256) void dgamma_reduce_kernel(const float* __restrict__ part, float* __restrict__ dgamma,
                                                             int nchunks, int H) {
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= H) return;
-    float s = 0.f;
-    for (int c = 0; c < nchunks; ++c) s += part[(int64_t)c * H + col];
-    dgamma[col] += s;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 4 <= nchunks; c += 4)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s[k] += part[(int64_t)(c + k) * H + col];
+    for (; c < nchunks; ++c) s[0] += part[(int64_t)c * H + col];
+    dgamma[col] += (s[0] + s[1]) + (s[2] + s[3]);
 }
 
 __global__ void fill_f32_kernel(float* p, size_t n, float v) {
@@ -203,9 +236,9 @@ size_t rmsnorm_dgamma_scratch_floats(int T, int H) { return (size_t)((T + DG_ROW
 
 int32_t rmsnorm_dgamma(const bf16_t* x, const float* r, const bf16_t* dn, float* dgamma, float* scratch, int T,
                        int H, hipStream_t s) {
-    if (H % 2 || T <= 0) return fail(ZB_EINVAL, "dgamma: bad shape");
+    if (H % 8 || T <= 0) return fail(ZB_EINVAL, "dgamma: hidden size must be a multiple of 8");
     const int nch = (T + DG_ROWS - 1) / DG_ROWS;
-    hipLaunchKernelGGL(dgamma_partial_kernel, dim3((H / 2 + 255) / 256, nch), dim3(256), 0, s, x, r, dn, scratch, T, H);
+    hipLaunchKernelGGL(dgamma_partial_kernel, dim3((H + 511) / 512, nch), dim3(256), 0, s, x, r, dn, scratch, T, H);
     ZB_HIP(hipGetLastError());
     hipLaunchKernelGGL(dgamma_reduce_kernel, dim3((H + 255) / 256), dim3(256), 0, s, scratch, dgamma, nch, H);
     ZB_HIP(hipGetLastError());
