@@ -198,13 +198,13 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 constexpr int FQ = 128, FKV = 64, FTHR = 256;
 constexpr int KV_TILE = FKV * D * 2;  // 16 KB
 
-__global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ o,
-                                                           float* __restrict__ lse, int T, int nq, int nkv) {
-    __shared__ __attribute__((aligned(1024))) char sm[2][2 * KV_TILE];  // [stage][K | V]
+// One query block qb (128 queries) of head blockIdx.y.
+__device__ __forceinline__ void attn_fwd_block(int qb, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
+                                               bf16_t* __restrict__ o, float* __restrict__ lse, int T, int nq,
+                                               int nkv) {
     const int ld = (nq + 2 * nkv) * D;
     const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
-    const int qb = gridDim.x - 1 - blockIdx.x;  // longest causal range first
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int qw0 = qb * FQ + wave * 32;
@@ -339,6 +339,20 @@ __global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restr
     if (g == 0) lse[(int64_t)h * T + q] = m + log2f(l);
 }
 
+// Causal query blocks differ in length up to nb-fold: each workgroup runs
+// block nb-1-x and then its mirror x, so every workgroup does the same work
+// and the two resident per CU finish together.
+__global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ o,
+                                                           float* __restrict__ lse, int T, int nq, int nkv) {
+    __shared__ __attribute__((aligned(1024))) char sm[2][2 * KV_TILE];  // [stage][K | V]
+    const int nb = T / FQ;
+    const int a = nb - 1 - (int)blockIdx.x, b = (int)blockIdx.x;
+    for (int pass = 0; pass < (b < a ? 2 : 1); ++pass) {
+        if (pass) wg_barrier();  // every wave is done with the stages
+        attn_fwd_block(pass ? b : a, sm, qkv, o, lse, T, nq, nkv);
+    }
+}
+
 // ===================================================== delta = rowsum(do o)
 __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
                                                          float* __restrict__ delta, int T, int nq) {
@@ -361,16 +375,13 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restric
 // dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
 // Two workgroups per CU as in the dk/dv kernel (64 KB of LDS each).
 constexpr int DQ_STAGES = 2;
-__global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
-                                                          const bf16_t* __restrict__ dout,
-                                                          const float* __restrict__ lse,
-                                                          const float* __restrict__ delta,
-                                                          bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
-    __shared__ __attribute__((aligned(1024))) char sm[DQ_STAGES][2 * KV_TILE];
+__device__ __forceinline__ void attn_dq_block(int qb, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
+                                              const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+                                              const float* __restrict__ delta, bf16_t* __restrict__ dqkv, int T,
+                                              int nq, int nkv) {
     const int ld = (nq + 2 * nkv) * D;
     const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
-    const int qb = gridDim.x - 1 - blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int qw0 = qb * FQ + wave * 32;
@@ -493,6 +504,21 @@ __global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restri
         }
 }
 
+// Paired query blocks as in the forward kernel.
+__global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
+                                                          const bf16_t* __restrict__ dout,
+                                                          const float* __restrict__ lse,
+                                                          const float* __restrict__ delta,
+                                                          bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
+    __shared__ __attribute__((aligned(1024))) char sm[DQ_STAGES][2 * KV_TILE];
+    const int nb = T / FQ;
+    const int a = nb - 1 - (int)blockIdx.x, b = (int)blockIdx.x;
+    for (int pass = 0; pass < (b < a ? 2 : 1); ++pass) {
+        if (pass) wg_barrier();
+        attn_dq_block(pass ? b : a, sm, qkv, dout, lse, delta, dqkv, T, nq, nkv);
+    }
+}
+
 // ===================================================== dk / dv kernel ====
 // Per (key block of 128, KV head).  Each wave owns 32 keys (K and V rows in
 // registers as B operands).  Sweeps the query heads of the group and the
@@ -507,19 +533,14 @@ constexpr int Q_TILE = BQB * D * 2;  // 8 KB
 // with that overlap.
 constexpr int KV_STAGES = 2;
 
-__global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
-                                                           const bf16_t* __restrict__ dout,
-                                                           const float* __restrict__ lse,
-                                                           const float* __restrict__ delta,
-                                                           bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
-    __shared__ __attribute__((aligned(1024))) char sm[KV_STAGES][2 * Q_TILE];  // [stage][Q | dO]
-    __shared__ __attribute__((aligned(1024))) char svt[BKV * D * 2];           // V rows of the block
-    __shared__ float sl[KV_STAGES][2][BQB];                                     // [stage][lse | delta]
+__device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], char* svt, float (*sl)[2][BQB],
+                                               const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dout,
+                                               const float* __restrict__ lse, const float* __restrict__ delta,
+                                               bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
     const int ld = (nq + 2 * nkv) * D;
     const int ldo = nq * D;
     const int grp = blockIdx.y;
     const int rep = nq / nkv;
-    const int kb = blockIdx.x;  // low key blocks have the most query blocks; launched first
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int kw0 = kb * BKV + wave * 32;
@@ -671,13 +692,31 @@ __global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restr
         }
 }
 
+// Key block kb sweeps the query blocks at or after it: pairs kb with its
+// mirror so every workgroup does the same work.
+__global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
+                                                           const bf16_t* __restrict__ dout,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ delta,
+                                                           bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
+    __shared__ __attribute__((aligned(1024))) char sm[KV_STAGES][2 * Q_TILE];  // [stage][Q | dO]
+    __shared__ __attribute__((aligned(1024))) char svt[BKV * D * 2];           // V rows of the block
+    __shared__ float sl[KV_STAGES][2][BQB];                                     // [stage][lse | delta]
+    const int nb = T / BKV;
+    const int a = (int)blockIdx.x, b = nb - 1 - (int)blockIdx.x;  // a: the longer sweep
+    for (int pass = 0; pass < (b > a ? 2 : 1); ++pass) {
+        if (pass) wg_barrier();
+        attn_dkv_block(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, T, nq, nkv);
+    }
+}
+
 bool shapes_ok(int T, int nq, int nkv) { return T > 0 && T % FQ == 0 && nq > 0 && nkv > 0 && nq % nkv == 0; }
 
 }  // namespace
 
 int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s) {
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3(T / FQ, nq), dim3(FTHR), 0, s, qkv, o, lse, T, nq, nkv);
+    hipLaunchKernelGGL(attn_fwd_kernel, dim3((T / FQ + 1) / 2, nq), dim3(FTHR), 0, s, qkv, o, lse, T, nq, nkv);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
@@ -687,9 +726,9 @@ int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf1
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
     hipLaunchKernelGGL(attn_delta_kernel, dim3((T * nq + 3) / 4), dim3(256), 0, s, o, dout, delta, T, nq);
     ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(attn_dq_kernel, dim3(T / FQ, nq), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
+    hipLaunchKernelGGL(attn_dq_kernel, dim3((T / FQ + 1) / 2, nq), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
     ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(attn_dkv_kernel, dim3(T / BKV, nkv), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
+    hipLaunchKernelGGL(attn_dkv_kernel, dim3((T / BKV + 1) / 2, nkv), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
