@@ -86,14 +86,14 @@ def w_kernel_launches(shape, device):
         C = torch.zeros((M, N), device=device, dtype=torch.float32)
         bufs.append((A, B, C, M, N, K))
 
-    def once():
-        for A, B, C, M, N, K in bufs:
-            zb.gemm(A, B, C, a_kmajor=False, b_kmajor=False, M=M, N=N, K=K, accumulate=True)
+    def once():  # the W pass's products in one grouped launch, as the stage issues them
+        zb.gemm_wgrad_group([b[0] for b in bufs], [b[1] for b in bufs], [b[2] for b in bufs],
+                            [b[3] for b in bufs], [b[4] for b in bufs], [b[5] for b in bufs])
 
     return gem, once
 
 
-W_KERNEL = "gemm_v2_kernel<false,false,EPI_ACCUM_F32>"
+W_KERNEL = "gemm_v2_group_kernel<false,false,EPI_ACCUM_F32>"
 W_KERNEL_SOURCES = ("split_backward_amd/csrc/gemm_v2.hip", "split_backward_amd/csrc/common.h")
 TRAFFIC_SUMMARY = "profiles/gemm_w_kernel_hbm_traffic_llama7b_stage4.md"
 
@@ -139,16 +139,16 @@ def time_w_kernel(shape, device, reps=5):
     e1.record()
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
-    launches = reps * len(gem)
+    launches = reps * ((len(gem) + 15) // 16)  # 16 products per grouped launch
     flops = reps * sum(2.0 * M * N * K for M, N, K in gem)
     avg_ms = ms_total / launches
     achieved = flops / (ms_total * 1e-3) / 1e12
-    algo_bytes = sum(2 * K * (M + N) + 2 * 4 * M * N for M, N, K in gem) / len(gem)
+    algo_bytes = sum(2 * K * (M + N) + 2 * 4 * M * N for M, N, K in gem) / ((len(gem) + 15) // 16)
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": algo_bytes,
-            "kernel": W_KERNEL + " (W pass: dW += dY^T X, fp32 in place)",
+            "kernel": W_KERNEL + " (W pass: dW += dY^T X for every product of a microbatch, fp32 in place)",
             "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
 
 
@@ -166,7 +166,7 @@ def traffic_probe(shape, device):
     for _ in range(2):
         once()
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_probe": True, "copy_bytes_each_way": 4 * n, "w_launches": 2 * len(gem),
+    print(json.dumps({"traffic_probe": True, "copy_bytes_each_way": 4 * n, "w_launches": 2 * ((len(gem) + 15) // 16),
                       "shapes_MNK": gem, "kernel_source_sha256": kernel_source_hash()}), flush=True)
 
 

@@ -233,6 +233,20 @@ int32_t zb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K,
                 const void* B, int64_t ldb, int32_t b_kmajor,
                 void* C, int64_t ldc, int32_t out_f32, int32_t accumulate, void* stream);
 
+/* A group of weight-gradient products in one launch ([Guide] "Core
+ * Innovation 1": W is each layer's weight gradient, and the products of one
+ * microbatch are independent of each other once B has run).  For i < count:
+ *   C_i[M_i, N_i] (fp32) += opA_i(A_i)[M_i, K_i] . opB_i(B_i)[K_i, N_i]
+ * with bf16 A_i, B_i, the same operand orientations (a_kmajor, b_kmajor, as
+ * in zb_gemm) for every product, and host arrays of length count (1..256).
+ * Each product obeys zb_gemm's rules; the C_i must not overlap.  Products
+ * that do not fit the single-launch kernel run one launch each.  The result
+ * is bit-identical to count zb_gemm calls.  Errors: ZB_EINVAL. */
+int32_t zb_gemm_wgrad_group(int32_t count, const int32_t* M, const int32_t* N, const int32_t* K,
+                            const void* const* A, const int64_t* lda, int32_t a_kmajor,
+                            const void* const* B, const int64_t* ldb, int32_t b_kmajor,
+                            void* const* C, const int64_t* ldc, void* stream);
+
 /* Thread-local description of the last error (never NULL). */
 const char* zb_last_error(void);
 

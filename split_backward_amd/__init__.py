@@ -83,6 +83,7 @@ _PROTOS = {
                                      ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _vp, _i32,
                                      ctypes.POINTER(RunStats), ctypes.POINTER(ctypes.c_double)]),
     "zb_gemm": (_i32, [_i32, _i32, _i32, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _vp]),
+    "zb_gemm_wgrad_group": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp]),
     "zb_last_error": (ctypes.c_char_p, []),
     "zb_version": (ctypes.c_char_p, []),
 }
@@ -291,3 +292,26 @@ def gemm(A, B, C, *, a_kmajor: bool, b_kmajor: bool, M: int, N: int, K: int, acc
     check(lib().zb_gemm(dt, M, N, K, _ptr(A), lda, int(a_kmajor), _ptr(B), ldb, int(b_kmajor), _ptr(C), ldc,
                         out_f32, int(accumulate), _stream_ptr(stream)))
     return C
+
+
+def gemm_wgrad_group(As, Bs, Cs, Ms, Ns, Ks, a_kmajor=False, b_kmajor=False, stream=None):
+    """C_i (fp32) += opA_i . opB_i for every i in one grouped launch
+    (zb_gemm_wgrad_group); bf16 A_i, B_i with one orientation for all."""
+    import torch
+    n = len(As)
+    if not (len(Bs) == len(Cs) == len(Ms) == len(Ns) == len(Ks) == n):
+        raise ValueError("gemm_wgrad_group: list lengths differ")
+    for t in list(As) + list(Bs):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("gemm_wgrad_group: A and B are bf16")
+    for t in Cs:
+        if t.dtype != torch.float32:
+            raise ValueError("gemm_wgrad_group: C is fp32")
+    i32 = ctypes.c_int32 * n
+    i64 = ctypes.c_int64 * n
+    vp = ctypes.c_void_p * n
+    check(lib().zb_gemm_wgrad_group(n, i32(*Ms), i32(*Ns), i32(*Ks), vp(*[a.data_ptr() for a in As]),
+                                    i64(*[a.stride(0) for a in As]), int(a_kmajor),
+                                    vp(*[b.data_ptr() for b in Bs]), i64(*[b.stride(0) for b in Bs]), int(b_kmajor),
+                                    vp(*[c.data_ptr() for c in Cs]), i64(*[c.stride(0) for c in Cs]),
+                                    _stream_ptr(stream)))

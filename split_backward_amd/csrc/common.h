@@ -64,6 +64,9 @@ int32_t gemm_bf16(const GemmDesc& d, hipStream_t s);
 // vector accesses (the first-generation kernel then runs).
 int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled);
 int32_t gemm_f32(const GemmDesc& d, int accumulate, hipStream_t s);
+// n independent products of one layout and epilogue in a single launch when
+// every one fits the direct-to-LDS kernel (else one gemm_bf16 each).
+int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s);
 
 // ------------------------------------------------- elementwise / norms ----
 int32_t fill_f32(float* p, size_t n, float v, hipStream_t s);

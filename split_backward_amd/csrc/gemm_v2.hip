@@ -213,19 +213,18 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
     tn = in_group / gsize;
 }
 
+// One 256x256 output tile (tm, tn) of the product `d`; `smem` is the
+// workgroup's 128 KB of LDS.
 template <bool A_KMAJ, bool B_KMAJ, int EPI>
-__global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, uint32_t a_bytes,
-                                                       uint32_t b_bytes, uint32_t c_bytes) {
+__device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, uint32_t a_bytes, uint32_t b_bytes,
+                                             uint32_t c_bytes, char* smem) {
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
     // wave index as a scalar: every LDS address derived from it (the DMA
     // destinations in M0) is then computed by scalar instructions.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 5, lrow = lane & 31;
-    int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM;
     const int n0 = PAIRED ? tn * (BN / 2) : tn * BN;
     const int nk = (d.K + BK - 1) / BK;
@@ -534,6 +533,46 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, 
     }
 }
 
+template <bool A_KMAJ, bool B_KMAJ, int EPI>
+__global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, uint32_t a_bytes,
+                                                       uint32_t b_bytes, uint32_t c_bytes) {
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI>(d, tm, tn, a_bytes, b_bytes, c_bytes, smem);
+}
+
+// Up to GROUP_MAX independent products of one layout and epilogue in one
+// launch (the W pass of a whole stage: every weight gradient of every layer).
+// Product g owns workgroups [off[g], off[g+1]); each range is a multiple of 8
+// so that a workgroup's XCD (blockIdx & 7) is the same in the product's own
+// numbering, and the padding workgroups of a range exit at once.
+constexpr int GROUP_MAX = 16;
+struct GemmGroup {
+    GemmDesc d[GROUP_MAX];
+    int tiles_m[GROUP_MAX], tiles_n[GROUP_MAX];
+    uint32_t a_bytes[GROUP_MAX], b_bytes[GROUP_MAX], c_bytes[GROUP_MAX];
+    int off[GROUP_MAX + 1];
+    int n;
+};
+static_assert(sizeof(GemmGroup) <= 3072, "kernel argument block");
+
+template <bool A_KMAJ, bool B_KMAJ, int EPI>
+__global__ __launch_bounds__(NTHR) void gemm_v2_group_kernel(GemmGroup grp) {
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    const int bid = blockIdx.x;
+    int g = 0;
+    while (g + 1 < grp.n && bid >= grp.off[g + 1]) ++g;
+    const int local = bid - grp.off[g];
+    const int nwg = grp.tiles_m[g] * grp.tiles_n[g];
+    const int q = nwg >> 3, r = nwg & 7, xcd = local & 7;
+    if ((local >> 3) >= (xcd < r ? q + 1 : q)) return;  // padding workgroup
+    int tm, tn;
+    tile_of(local, grp.tiles_m[g], grp.tiles_n[g], tm, tn);
+    const GemmDesc d = grp.d[g];  // a value copy: its fields stay in scalar registers
+    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI>(d, tm, tn, grp.a_bytes[g], grp.b_bytes[g], grp.c_bytes[g], smem);
+}
+
 template <bool AK, bool BKM>
 int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, uint32_t ab, uint32_t bb, uint32_t cb) {
     dim3 grid(tiles_m * tiles_n), block(NTHR);
@@ -559,32 +598,107 @@ int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, ui
 // logical end).  Must stay below 2^31 for the buffer range check.
 static uint64_t span_bytes(int64_t rows, int64_t ld, int64_t cols) { return (uint64_t)((rows - 1) * ld + cols) * 2; }
 
-int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
-    *handled = false;
+namespace {
+// Whether the direct-to-LDS kernel can run `d`, and its buffer spans and grid.
+struct V2Plan {
+    bool ok;
+    uint32_t a32, b32, c32;
+    int tiles_m, tiles_n;
+};
+V2Plan plan_v2(const GemmDesc& d) {
+    V2Plan p{};
     const bool paired = d.epi == EPI_SWIGLU_FWD;
     const uint64_t ab = d.a_kmajor ? span_bytes(d.M, d.lda, d.K) : span_bytes(d.K, d.lda, d.M);
     const uint64_t bb = d.b_kmajor ? span_bytes(d.N, d.ldb, d.K) : span_bytes(d.K, d.ldb, d.N);
     // fp32 accumulate reads C through a buffer range as well
     const uint64_t cb = d.epi == EPI_ACCUM_F32 ? (uint64_t)((int64_t)(d.M - 1) * d.ldc + d.N) * 4 : 0;
-    if (ab >= OOB || bb >= OOB || cb >= OOB) return ZB_OK;  // too large for one buffer range: caller uses the first kernel
+    if (ab >= OOB || bb >= OOB || cb >= OOB) return p;  // too large for one buffer range
     // 16-byte (fp32) / 8-byte (bf16) epilogue accesses need widths and leading
     // dimensions divisible by 4 and aligned base pointers.
-    auto al = [](const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+    auto al = [](const void* q, int a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
     const bool has_r = d.epi == EPI_RESID || d.epi == EPI_GELU_BWD || d.epi == EPI_SWIGLU_BWD;
     const bool has_c2 = d.epi == EPI_GELU_FWD || paired;
     bool vec = (d.N % 4 == 0) && (d.ldc % 4 == 0) && al(d.C, d.epi == EPI_ACCUM_F32 ? 16 : 8);
     if (has_r) vec = vec && (d.ldr % 4 == 0) && al(d.R, 8);
     if (has_c2) vec = vec && (d.ldc2 % 4 == 0) && al(d.C2, 8);
     if (d.epi == EPI_SWIGLU_BWD || paired) vec = vec && (d.half_n % 4 == 0);
-    if (!vec) return ZB_OK;  // caller uses the first-generation kernel
+    if (!vec) return p;
+    p.ok = true;
+    p.a32 = (uint32_t)ab;
+    p.b32 = (uint32_t)bb;
+    p.c32 = (uint32_t)cb;
+    p.tiles_m = (d.M + BM - 1) / BM;
+    p.tiles_n = paired ? (d.half_n + BN / 2 - 1) / (BN / 2) : (d.N + BN - 1) / BN;
+    return p;
+}
+
+template <bool AK, bool BKM>
+int32_t launch_group(const GemmGroup& g, int epi, hipStream_t s) {
+    dim3 grid(g.off[g.n]), block(NTHR);
+    switch (epi) {
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_group_kernel<AK, BKM, E>), grid, block, 0, s, g); break;
+        ZB_CASE(EPI_STORE)
+        ZB_CASE(EPI_RESID)
+        ZB_CASE(EPI_ACCUM_F32)
+        ZB_CASE(EPI_GELU_FWD)
+        ZB_CASE(EPI_GELU_BWD)
+        ZB_CASE(EPI_SWIGLU_FWD)
+        ZB_CASE(EPI_SWIGLU_BWD)
+#undef ZB_CASE
+        default: return fail(ZB_EINVAL, "gemm: unknown epilogue");
+    }
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+}  // namespace
+
+int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
+    *handled = false;
+    const V2Plan p = plan_v2(d);
+    if (!p.ok) return ZB_OK;  // caller uses the first-generation kernel
     *handled = true;
-    const int tiles_m = (d.M + BM - 1) / BM;
-    const int tiles_n = paired ? (d.half_n + BN / 2 - 1) / (BN / 2) : (d.N + BN - 1) / BN;
-    const uint32_t a32 = (uint32_t)ab, b32 = (uint32_t)bb, c32 = (uint32_t)cb;
-    if (d.a_kmajor && d.b_kmajor) return launch_v2<true, true>(d, s, tiles_m, tiles_n, a32, b32, c32);
-    if (d.a_kmajor && !d.b_kmajor) return launch_v2<true, false>(d, s, tiles_m, tiles_n, a32, b32, c32);
-    if (!d.a_kmajor && !d.b_kmajor) return launch_v2<false, false>(d, s, tiles_m, tiles_n, a32, b32, c32);
-    return launch_v2<false, true>(d, s, tiles_m, tiles_n, a32, b32, c32);
+    if (d.a_kmajor && d.b_kmajor) return launch_v2<true, true>(d, s, p.tiles_m, p.tiles_n, p.a32, p.b32, p.c32);
+    if (d.a_kmajor && !d.b_kmajor) return launch_v2<true, false>(d, s, p.tiles_m, p.tiles_n, p.a32, p.b32, p.c32);
+    if (!d.a_kmajor && !d.b_kmajor) return launch_v2<false, false>(d, s, p.tiles_m, p.tiles_n, p.a32, p.b32, p.c32);
+    return launch_v2<false, true>(d, s, p.tiles_m, p.tiles_n, p.a32, p.b32, p.c32);
+}
+
+int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s) {
+    if (n <= 0) return ZB_OK;
+    bool grouped = n <= GROUP_MAX && getenv("ZB_GEMM_V1") == nullptr;
+    GemmGroup g{};
+    g.n = n;
+    g.off[0] = 0;
+    for (int i = 0; i < n && grouped; ++i) {
+        const GemmDesc& d = ds[i];
+        const V2Plan p = plan_v2(d);
+        // same layout and epilogue for every product; each must be valid for the single-product path too
+        grouped = p.ok && d.a_kmajor == ds[0].a_kmajor && d.b_kmajor == ds[0].b_kmajor && d.epi == ds[0].epi &&
+                  d.M > 0 && d.N > 0 && d.K > 0 && d.K % 8 == 0 && d.lda % 8 == 0 && d.ldb % 8 == 0 &&
+                  (d.a_kmajor || d.M % 8 == 0) && (d.b_kmajor || d.N % 8 == 0) &&
+                  ((reinterpret_cast<uintptr_t>(d.A) | reinterpret_cast<uintptr_t>(d.B)) & 15) == 0 &&
+                  (d.epi != EPI_SWIGLU_FWD || (d.b_kmajor && d.half_n > 0));
+        if (!grouped) break;
+        g.d[i] = d;
+        g.tiles_m[i] = p.tiles_m;
+        g.tiles_n[i] = p.tiles_n;
+        g.a_bytes[i] = p.a32;
+        g.b_bytes[i] = p.b32;
+        g.c_bytes[i] = p.c32;
+        g.off[i + 1] = g.off[i] + ((p.tiles_m * p.tiles_n + 7) & ~7);
+    }
+    if (!grouped) {  // one launch per product (validated there)
+        for (int i = 0; i < n; ++i) {
+            const int32_t rc = gemm_bf16(ds[i], s);
+            if (rc != ZB_OK) return rc;
+        }
+        return ZB_OK;
+    }
+    const bool ak = ds[0].a_kmajor, bk = ds[0].b_kmajor;
+    if (ak && bk) return launch_group<true, true>(g, ds[0].epi, s);
+    if (ak && !bk) return launch_group<true, false>(g, ds[0].epi, s);
+    if (!ak && !bk) return launch_group<false, false>(g, ds[0].epi, s);
+    return launch_group<false, true>(g, ds[0].epi, s);
 }
 
 }  // namespace zb

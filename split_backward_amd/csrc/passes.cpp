@@ -7,6 +7,9 @@
 #include "common.h"
 #include "stage.h"
 
+#include <algorithm>
+#include <vector>
+
 namespace zb {
 namespace {
 
@@ -170,18 +173,31 @@ int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s) {
     const int T = d.tokens, H = d.hidden, F = d.ffn;
     if (d.kind == ZB_LINEAR)
         return linear_gemm(st, tn(F, H, T, st.slot_tensor(mb, 0, LIN_DY), F, st.slot_tensor(mb, 0, LIN_X), H, st.dw[0]), s);
+    // Every weight-gradient product of the microbatch is independent of the
+    // others (distinct dW buffers, stashed operands): they run as one grouped
+    // launch (16 products at most per launch), so the partial last round of
+    // one product's tiles overlaps the next product's tiles.
+    constexpr int GROUP = 16;
     if (d.kind == ZB_MLP_GELU) {
-        ZB_TRY(gemm_bf16(tn(F, H, T, st.slot_tensor(mb, 0, MLP_DA), F, st.slot_tensor(mb, 0, MLP_X), H, st.dw[0]), s));
-        return gemm_bf16(tn(H, F, T, st.slot_tensor(mb, 0, MLP_DY), H, st.slot_tensor(mb, 0, MLP_H), F, st.dw[1]), s);
+        const GemmDesc g[2] = {tn(F, H, T, st.slot_tensor(mb, 0, MLP_DA), F, st.slot_tensor(mb, 0, MLP_X), H, st.dw[0]),
+                               tn(H, F, T, st.slot_tensor(mb, 0, MLP_DY), H, st.slot_tensor(mb, 0, MLP_H), F, st.dw[1])};
+        return gemm_bf16_group(g, 2, s);
     }
     const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
     float* part = reinterpret_cast<float*>(st.scratch_w);
+    std::vector<GemmDesc> g;
+    g.reserve(4 * d.n_layers);
     for (int l = 0; l < d.n_layers; ++l) {
         float* const* dw = &st.dw[6 * l];
-        ZB_TRY(gemm_bf16(tn(QKV, H, T, st.slot_tensor(mb, l, L_DQKV), QKV, st.slot_tensor(mb, l, L_N1), H, dw[0]), s));
-        ZB_TRY(gemm_bf16(tn(H, QD, T, st.slot_tensor(mb, l, L_DH1), H, st.slot_tensor(mb, l, L_A), QD, dw[1]), s));
-        ZB_TRY(gemm_bf16(tn(2 * F, H, T, st.slot_tensor(mb, l, L_DGU), 2 * F, st.slot_tensor(mb, l, L_N2), H, dw[2]), s));
-        ZB_TRY(gemm_bf16(tn(H, F, T, st.slot_tensor(mb, l, L_DOUT), H, st.slot_tensor(mb, l, L_S), F, dw[3]), s));
+        g.push_back(tn(QKV, H, T, st.slot_tensor(mb, l, L_DQKV), QKV, st.slot_tensor(mb, l, L_N1), H, dw[0]));
+        g.push_back(tn(H, QD, T, st.slot_tensor(mb, l, L_DH1), H, st.slot_tensor(mb, l, L_A), QD, dw[1]));
+        g.push_back(tn(2 * F, H, T, st.slot_tensor(mb, l, L_DGU), 2 * F, st.slot_tensor(mb, l, L_N2), H, dw[2]));
+        g.push_back(tn(H, F, T, st.slot_tensor(mb, l, L_DOUT), H, st.slot_tensor(mb, l, L_S), F, dw[3]));
+    }
+    for (size_t i = 0; i < g.size(); i += GROUP)
+        ZB_TRY(gemm_bf16_group(&g[i], (int)std::min<size_t>(GROUP, g.size() - i), s));
+    for (int l = 0; l < d.n_layers; ++l) {
+        float* const* dw = &st.dw[6 * l];
         ZB_TRY(rmsnorm_dgamma(cbf(st.slot_tensor(mb, l, L_X)), static_cast<const float*>(st.slot_tensor(mb, l, L_R1)),
                               cbf(st.slot_tensor(mb, l, L_DN1)), dw[4], part, T, H, s));
         ZB_TRY(rmsnorm_dgamma(cbf(st.slot_tensor(mb, l, L_H1)), static_cast<const float*>(st.slot_tensor(mb, l, L_R2)),

@@ -329,3 +329,33 @@ extern "C" int32_t zb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const
     }
     return gemm_bf16(g, s);
 }
+
+extern "C" int32_t zb_gemm_wgrad_group(int32_t count, const int32_t* M, const int32_t* N, const int32_t* K,
+                                       const void* const* A, const int64_t* lda, int32_t a_kmajor,
+                                       const void* const* B, const int64_t* ldb, int32_t b_kmajor, void* const* C,
+                                       const int64_t* ldc, void* stream) {
+    if (count < 1 || count > 256 || !M || !N || !K || !A || !lda || !B || !ldb || !C || !ldc)
+        return fail(ZB_EINVAL, "zb_gemm_wgrad_group: bad argument");
+    std::vector<GemmDesc> g(count);
+    for (int i = 0; i < count; ++i) {
+        if (!A[i] || !B[i] || !C[i] || M[i] < 1 || N[i] < 1 || K[i] < 1)
+            return fail(ZB_EINVAL, "zb_gemm_wgrad_group: bad product");
+        const int64_t minlda = a_kmajor ? K[i] : M[i], minldb = b_kmajor ? K[i] : N[i];
+        if (lda[i] < minlda || ldb[i] < minldb || ldc[i] < N[i])
+            return fail(ZB_EINVAL, "zb_gemm_wgrad_group: leading dimension too small");
+        GemmDesc& d = g[i];
+        d = GemmDesc{};
+        d.M = M[i]; d.N = N[i]; d.K = K[i];
+        d.A = A[i]; d.lda = lda[i]; d.a_kmajor = a_kmajor;
+        d.B = B[i]; d.ldb = ldb[i]; d.b_kmajor = b_kmajor;
+        d.C = C[i]; d.ldc = ldc[i];
+        d.epi = EPI_ACCUM_F32;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    constexpr int GROUP = 16;  // products per launch
+    for (int i = 0; i < count; i += GROUP) {
+        const int32_t rc = gemm_bf16_group(&g[i], std::min(GROUP, count - i), s);
+        if (rc != ZB_OK) return rc;
+    }
+    return ZB_OK;
+}

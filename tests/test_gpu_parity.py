@@ -70,6 +70,36 @@ def test_gemm_tn_accumulate_f32(M, N, K):
     assert od.rel_fro(to_f64(c), ref) <= F32_TOL
 
 
+def test_wgrad_group_matches_single_launches_and_oracle():
+    """Grouped W-pass launch: 18 products (two launches of at most 16, one
+    ragged in every dimension, one too wide for 16-byte epilogue accesses so
+    it takes the fallback kernel) equal the single launches bit for bit, and
+    the oracle within the fp32-accumulate tolerance."""
+    shapes = [(264, 136, 72), (512, 512, 512), (8, 8, 8), (136, 1032, 296), (1024, 256, 64), (40, 264, 24)] * 3
+    padded = 5  # C with leading dimension N + 2: no 16-byte epilogue, first-generation kernel inside the group call
+    As, Bs, C1, C2, refs = [], [], [], [], []
+    for i, (M, N, K) in enumerate(shapes):
+        dy, x = _bf16(f"gdy{i}", (K, M), 40 + i), _bf16(f"gx{i}", (K, N), 80 + i)
+        c0 = synth.normal(120 + i, (M, N), 1.0).astype(np.float32)
+        As.append(to_dev(dy)); Bs.append(to_dev(x))
+        for lst in (C1, C2):
+            if i == padded:
+                big = torch.zeros((M, N + 2), dtype=torch.float32, device="cuda")
+                big[:, :N] = torch.from_numpy(c0)
+                lst.append(big[:, :N])
+            else:
+                lst.append(torch.from_numpy(c0.copy()).cuda())
+        refs.append(c0.astype(np.float64) + dy.f64.T @ x.f64)
+    Ms, Ns, Ks = [s_[0] for s_ in shapes], [s_[1] for s_ in shapes], [s_[2] for s_ in shapes]
+    zb.gemm_wgrad_group(As, Bs, C1, Ms, Ns, Ks)
+    for A, B, C, (M, N, K) in zip(As, Bs, C2, shapes):
+        zb.gemm(A, B, C, a_kmajor=False, b_kmajor=False, M=M, N=N, K=K, accumulate=True, ldc=C.stride(0))
+    torch.cuda.synchronize()
+    for i, (c1, c2, ref) in enumerate(zip(C1, C2, refs)):
+        assert torch.equal(c1, c2), i
+        assert od.rel_fro(to_f64(c1), ref) <= F32_TOL, i
+
+
 def test_gemm_fp32_all_layouts():
     M, N, K = 200, 136, 72
     rng = np.random.default_rng(5)
