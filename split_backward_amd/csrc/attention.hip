@@ -353,32 +353,15 @@ __global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restr
     }
 }
 
-// ===================================================== delta = rowsum(do o)
-__global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
-                                                         float* __restrict__ delta, int T, int nq) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (q, h) pair
-    const int lane = threadIdx.x & 63;
-    if (row >= T * nq) return;
-    const int q = row / nq, h = row % nq;
-    const int64_t base = (int64_t)q * nq * D + h * D + lane * 2;
-    const uint32_t ov = *reinterpret_cast<const uint32_t*>(o + base);
-    const uint32_t dv = *reinterpret_cast<const uint32_t*>(dout + base);
-    float s = __uint_as_float(ov << 16) * __uint_as_float(dv << 16) +
-              __uint_as_float(ov & 0xffff0000u) * __uint_as_float(dv & 0xffff0000u);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (lane == 0) delta[(int64_t)h * T + q] = s;
-}
-
 // ====================================================== dq kernel ========
 // Per (query block of 128, query head).  Mirrors the forward: S^T = K Q^T,
 // dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
 // Two workgroups per CU as in the dk/dv kernel (64 KB of LDS each).
 constexpr int DQ_STAGES = 2;
 __device__ __forceinline__ void attn_dq_block(int qb, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
-                                              const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-                                              const float* __restrict__ delta, bf16_t* __restrict__ dqkv, int T,
-                                              int nq, int nkv) {
+                                              const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+                                              const float* __restrict__ lse, float* __restrict__ delta,
+                                              bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
     const int ld = (nq + 2 * nkv) * D;
     const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
@@ -397,7 +380,18 @@ __device__ __forceinline__ void attn_dq_block(int qb, char (*sm)[2 * KV_TILE], c
         dof[kk] = *reinterpret_cast<const bf16x8*>(dout + (int64_t)q * ldo + h * D + kk * 16 + g * 8);
     }
     const float lq = lse[(int64_t)h * T + q];
-    const float dq_delta = delta[(int64_t)h * T + q];
+    // delta = rowsum(dO o) of the lane's query: half of the row's 128 products
+    // in each of the lanes q and q+32; stored for the dk/dv kernel.
+    float dsum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + (int64_t)q * ldo + h * D + kk * 16 + g * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsum = fmaf((float)ov[e], (float)dof[kk][e], dsum);
+    }
+    dsum += __shfl_xor(dsum, 32, 64);
+    const float dq_delta = dsum;
+    if (g == 0) delta[(int64_t)h * T + q] = dsum;
     const float c = LOG2E / sqrtf((float)D);
 
     floatx16 dacc[4];
@@ -506,16 +500,17 @@ __device__ __forceinline__ void attn_dq_block(int qb, char (*sm)[2 * KV_TILE], c
 
 // Paired query blocks as in the forward kernel.
 __global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
+                                                          const bf16_t* __restrict__ o,
                                                           const bf16_t* __restrict__ dout,
                                                           const float* __restrict__ lse,
-                                                          const float* __restrict__ delta,
+                                                          float* __restrict__ delta,
                                                           bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
     __shared__ __attribute__((aligned(1024))) char sm[DQ_STAGES][2 * KV_TILE];
     const int nb = T / FQ;
     const int a = nb - 1 - (int)blockIdx.x, b = (int)blockIdx.x;
     for (int pass = 0; pass < (b < a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();
-        attn_dq_block(pass ? b : a, sm, qkv, dout, lse, delta, dqkv, T, nq, nkv);
+        attn_dq_block(pass ? b : a, sm, qkv, o, dout, lse, delta, dqkv, T, nq, nkv);
     }
 }
 
@@ -724,9 +719,9 @@ int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nk
 int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout, bf16_t* dqkv, float* delta,
                  int T, int nq, int nkv, hipStream_t s) {
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
-    hipLaunchKernelGGL(attn_delta_kernel, dim3((T * nq + 3) / 4), dim3(256), 0, s, o, dout, delta, T, nq);
-    ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(attn_dq_kernel, dim3((T / FQ + 1) / 2, nq), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
+    // the dq kernel also computes delta = rowsum(dO o), which the dk/dv kernel reads
+    hipLaunchKernelGGL(attn_dq_kernel, dim3((T / FQ + 1) / 2, nq), dim3(FTHR), 0, s, qkv, o, dout, lse, delta, dqkv, T,
+                       nq, nkv);
     ZB_HIP(hipGetLastError());
     hipLaunchKernelGGL(attn_dkv_kernel, dim3((T / BKV + 1) / 2, nkv), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
     ZB_HIP(hipGetLastError());
