@@ -8,7 +8,8 @@ zero-bubble order (memory limit 2p) that the library's generator produces
 for stage 3 of an emulated 8-stage pipeline, back to back on one stream with
 all inputs already in HBM.  `value` = linear-layer FLOPs of F + B + W
 (2*M*N*K per product, attention and RMSNorm excluded from the count but not
-from the time) / wall time of the step.
+from the time) / wall time of the step; `tflops_incl_attention` adds the
+causal attention core's algorithmic flops to the numerator.
 
 Extra fields on the JSON line:
 * roofline: the W-pass GEMM kernel (the kernel with the largest share of the
@@ -46,6 +47,16 @@ def linear_flops_per_mb(s) -> float:
     qkv = s.q_dim + 2 * s.kv_dim
     per_pass = 2.0 * T * H * (qkv + s.q_dim + 2 * F + F)
     return 3 * per_pass * s.n_layers
+
+
+def attention_flops_per_mb(s) -> float:
+    """Algorithmic flops of the causal attention core for one microbatch:
+    forward 2 products over the causal half (4*T^2*d*heads/2), backward 2.5x
+    the forward (5 products).  Not in `value`; reported beside it."""
+    if s.kind != "llama":
+        return 0.0
+    fwd = 4.0 * s.tokens * s.tokens * s.head_dim * s.n_heads / 2
+    return 3.5 * fwd * s.n_layers
 
 
 def w_pass_gemms(s):
@@ -332,6 +343,7 @@ def main():
                    "n_layers": shape.n_layers, "n_heads": shape.n_heads, "n_kv_heads": shape.n_kv_heads,
                    "microbatches": m, "ring_slots": ring, "order": "zero-bubble greedy, M=min(16, ring), stage 3 of p=8"},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tflops_incl_attention": round((flops + attention_flops_per_mb(shape) * m) / dt / 1e12, 2),
         "pass_ms": {"F": round(t_f, 3), "B": round(t_b, 3), "W": round(t_w, 3)},
         "roofline": roof, "cpu_baseline": cpu,
     }
