@@ -187,16 +187,31 @@ __device__ __forceinline__ void wait_vm() {
 // been consumed by an MFMA, so it has completed.
 __device__ __forceinline__ void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Branch-free activations for the epilogues (results are rounded to bf16):
+// tanh(y) = 1 - 2 / (e^{2y} + 1) and sigmoid(z) = 1 / (1 + e^{-z}), with the
+// hardware base-2 exponential and reciprocal.  At large |y| the exponential
+// saturates to 0 or inf and the reciprocal to 1/1 or 0, so the limits -1, 1
+// (tanh) and 0, 1 (sigmoid) come out exactly.
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float tanh_f(float y) { return 1.f - 2.f * __builtin_amdgcn_rcpf(exp_f(2.f * y) + 1.f); }
 __device__ __forceinline__ float gelu_tanh_f(float a) {
     const float c = 0.7978845608028654f, k = 0.044715f;
-    return 0.5f * a * (1.f + tanhf(c * (a + k * a * a * a)));
+    return 0.5f * a * (1.f + tanh_f(c * (a + k * a * a * a)));
 }
 __device__ __forceinline__ float gelu_tanh_grad_f(float a) {
     const float c = 0.7978845608028654f, k = 0.044715f;
-    const float t = tanhf(c * (a + k * a * a * a));
+    const float t = tanh_f(c * (a + k * a * a * a));
     return 0.5f * (1.f + t) + 0.5f * a * (1.f - t * t) * c * (1.f + 3.f * k * a * a);
 }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.f + exp_f(-z)); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Four floats -> four bf16 (round to nearest even), two per conversion instruction.
+__device__ __forceinline__ u32x2 pack_bf16x4(const float (&f)[4]) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[0], f[1]}, bf16x2_t)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[2], f[3]}, bf16x2_t))};
+}
 
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int nwg = tiles_m * tiles_n;
@@ -213,11 +228,19 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
     tn = in_group / gsize;
 }
 
+// Byte lengths of the buffer ranges through which a product's operands are
+// read and its outputs written (A, B, C, the epilogue input R, the second
+// output C2).  Each is below 2^31: an offset at or past a range reads zero or
+// drops the store, which is how rows and columns outside the matrices are
+// handled without branches.
+struct BufSpans {
+    uint32_t a, b, c, r, c2;
+};
+
 // One 256x256 output tile (tm, tn) of the product `d`; `smem` is the
 // workgroup's 128 KB of LDS.
 template <bool A_KMAJ, bool B_KMAJ, int EPI>
-__device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, uint32_t a_bytes, uint32_t b_bytes,
-                                             uint32_t c_bytes, char* smem) {
+__device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
 
     // wave index as a scalar: every LDS address derived from it (the DMA
@@ -247,9 +270,9 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
         const bool live = kt < nk;
         const uint32_t adv_a = live ? (uint32_t)(kt * step_a) : 0u, adv_b = live ? (uint32_t)(kt * step_b) : 0u;
         const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(static_cast<const char*>(d.A) + adv_a, live ? a_bytes - adv_a : 0u);
+            make_rsrc(static_cast<const char*>(d.A) + adv_a, live ? sp.a - adv_a : 0u);
         const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(static_cast<const char*>(d.B) + adv_b, live ? b_bytes - adv_b : 0u);
+            make_rsrc(static_cast<const char*>(d.B) + adv_b, live ? sp.b - adv_b : 0u);
         if (kt == nk - 1 && k_tail < BK) {  // partial last tile: mask k >= K on K-contiguous operands
             uint32_t ta[4], tb[4];
             if (A_KMAJ) dma_offsets_kmaj<false>(ta, d.lda, m0, d.M, 0, k_tail, lane, wave);
@@ -372,16 +395,16 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
         if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, 8, 0>();
     }
     __builtin_amdgcn_sched_barrier(0);
-    // fp32 accumulate: the old dW values of the first 32-row block are
-    // loaded now (16 loads per wave), so their latency overlaps the drain below.
     const int c4 = (lane & 31) * 4;
     const int gcol = n0 + wn * 128 + c4;
     const bool col_ok = gcol < d.N;
     floatx4 cin[2][16];
-    // Buffer loads, one per row group whether or not it is inside C (outside
-    // reads as zero), so every wave issues exactly 16 per block: the counted
-    // wait below relies on it.  The launcher guarantees C spans < 2 GiB.
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(d.C, c_bytes);
+    // Every epilogue access is a buffer access, issued whether or not its row
+    // and columns are inside the matrix (outside, the offset is OOB: loads
+    // read zero, stores are dropped).  The code is then free of branches and
+    // the compiler counts outstanding loads exactly, so a wait for a block's
+    // inputs does not also wait for the stores issued before it.
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(d.C, sp.c);
     auto load_block = [&](int mi, floatx4 (&dst)[16]) {
         const int rbase = m0 + wm * 128 + mi * 32;
 #pragma unroll
@@ -391,11 +414,37 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
             dst[it] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
         }
     };
+    // Epilogues that read a bf16 input (residual, activation input): the
+    // rows of block mi+1 are loaded while block mi is computed and stored.
+    constexpr bool HAS_R = EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD;
+    constexpr int IT = 16;  // rows 2*it + lane/32 of a 32-row block
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(d.R, HAS_R ? sp.r : 0u);
+    u32x2 rin[2][IT], rin2[2][IT];
+    auto load_r = [&](int mi, int buf) {
+        const int rbase = m0 + wm * 128 + mi * 32;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int row = rbase + 2 * it + (lane >> 5);
+            const bool ok = row < d.M && col_ok;
+            const int64_t e = (int64_t)row * d.ldr + gcol;
+            rin[buf][it] = __builtin_amdgcn_raw_buffer_load_b64(rr, ok ? (uint32_t)(e * 2) : OOB, 0, 0);
+            if (EPI == EPI_SWIGLU_BWD)
+                rin2[buf][it] = __builtin_amdgcn_raw_buffer_load_b64(rr, ok ? (uint32_t)((e + d.half_n) * 2) : OOB, 0, 0);
+        }
+    };
     // The empty tiles' DMA still writes (zeros) into the stages, and every
-    // wave must be done with them before the epilogue reuses the memory.
+    // wave must be done with them before the epilogue reuses the memory.  The
+    // first block's epilogue inputs are requested before that wait, so their
+    // latency overlaps the drain.
     if constexpr (EPI == EPI_ACCUM_F32) {
         load_block(0, cin[0]);
         asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");  // all DMA done; dW loads in flight
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        load_r(0, 0);
+        asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
+    } else if constexpr (HAS_R) {
+        load_r(0, 0);
+        asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
     } else {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     }
@@ -434,24 +483,8 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
         }
         return;
     }
-    // Epilogues that read a bf16 input (residual, activation input): the
-    // rows of block mi+1 are loaded while block mi is computed and stored.
-    constexpr bool HAS_R = EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD;
-    constexpr int IT = 16;  // rows 2*it + lane/32 of a 32-row block
-    u32x2 rin[2][IT], rin2[2][IT];
-    auto load_r = [&](int mi, int buf) {
-        const int rbase = m0 + wm * 128 + mi * 32;
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const int row = rbase + 2 * it + (lane >> 5);
-            if (row < d.M && col_ok) {
-                const bf16_t* rrow = reinterpret_cast<const bf16_t*>(d.R) + (int64_t)row * d.ldr;
-                rin[buf][it] = *reinterpret_cast<const u32x2*>(rrow + gcol);
-                if (EPI == EPI_SWIGLU_BWD) rin2[buf][it] = *reinterpret_cast<const u32x2*>(rrow + d.half_n + gcol);
-            }
-        }
-    };
-    if (HAS_R && !PAIRED) load_r(0, 0);
+    constexpr bool HAS_C2 = EPI == EPI_GELU_FWD || PAIRED;
+    const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(d.C2, HAS_C2 ? sp.c2 : 0u);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int rbase = m0 + wm * 128 + mi * 32;
@@ -466,7 +499,7 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
             for (int it = 0; it < IT; ++it) {
                 const int lr = 2 * it + (lane >> 5);
                 const int row = rbase + lr;
-                if (row >= d.M || !col_ok) continue;
+                const bool ok = row < d.M && col_ok;
                 const floatx4 v = *reinterpret_cast<const floatx4*>(stage + lr * P + c4);
                 float o[4], o2[4];
 #pragma unroll
@@ -481,20 +514,20 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
                     else if (EPI == EPI_SWIGLU_BWD) {
                         const uint32_t uw = rin2[mi & 1][it][e >> 1];
                         const float u = (e & 1) ? __uint_as_float(uw & 0xffff0000u) : __uint_as_float(uw << 16);
-                        const float sg = sigmoid_f(rv);
-                        o[e] = x * u * sg * (1.f + rv * (1.f - sg));
-                        o2[e] = x * rv * sg;
+                        // dg = ds u sg (1 + g (1 - sg)) = ds u (sg + a - a sg), du = ds a, a = g sg
+                        const float sg = sigmoid_f(rv), a = rv * sg;
+                        o[e] = x * u * fmaf(-a, sg, a + sg);
+                        o2[e] = x * a;
                     }
                 }
-                auto pack4 = [](const float (&f)[4]) {
-                    return u32x2{uint32_t(f2bf(f[0])) | (uint32_t(f2bf(f[1])) << 16),
-                                 uint32_t(f2bf(f[2])) | (uint32_t(f2bf(f[3])) << 16)};
-                };
-                bf16_t* crow = reinterpret_cast<bf16_t*>(d.C) + (int64_t)row * d.ldc;
-                *reinterpret_cast<u32x2*>(crow + gcol) = pack4(o);
+                const int64_t ec = (int64_t)row * d.ldc + gcol;
+                __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(o), rc, ok ? (uint32_t)(ec * 2) : OOB, 0, 0);
                 if (EPI == EPI_GELU_FWD)
-                    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(d.C2) + (int64_t)row * d.ldc2 + gcol) = pack4(o2);
-                if (EPI == EPI_SWIGLU_BWD) *reinterpret_cast<u32x2*>(crow + d.half_n + gcol) = pack4(o2);
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        pack_bf16x4(o2), rc2, ok ? (uint32_t)(((int64_t)row * d.ldc2 + gcol) * 2) : OOB, 0, 0);
+                if (EPI == EPI_SWIGLU_BWD)
+                    __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(o2), rc, ok ? (uint32_t)((ec + d.half_n) * 2) : OOB, 0,
+                                                          0);
             }
         } else {
             // paired SwiGLU forward: staged columns 0..63 are gate, 64..127 up
@@ -510,7 +543,7 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
             for (int it = 0; it < 8; ++it) {
                 const int lr = 4 * it + (lane >> 4);
                 const int row = rbase + lr;
-                if (row >= d.M || !col_ok) continue;
+                const bool ok = row < d.M && col_ok;
                 const floatx4 gv = *reinterpret_cast<const floatx4*>(stage + lr * P + c4);
                 const floatx4 uv = *reinterpret_cast<const floatx4*>(stage + lr * P + 64 + c4);
                 float og[4], ou[4], os[4];
@@ -520,26 +553,22 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
                     ou[e] = uv[e];
                     os[e] = gv[e] * sigmoid_f(gv[e]) * uv[e];
                 }
-                auto pack4 = [](const float (&f)[4]) {
-                    return u32x2{uint32_t(f2bf(f[0])) | (uint32_t(f2bf(f[1])) << 16),
-                                 uint32_t(f2bf(f[2])) | (uint32_t(f2bf(f[3])) << 16)};
-                };
-                bf16_t* crow = reinterpret_cast<bf16_t*>(d.C) + (int64_t)row * d.ldc;
-                *reinterpret_cast<u32x2*>(crow + gcol) = pack4(og);
-                *reinterpret_cast<u32x2*>(crow + d.half_n + gcol) = pack4(ou);
-                *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(d.C2) + (int64_t)row * d.ldc2 + gcol) = pack4(os);
+                const int64_t ec = (int64_t)row * d.ldc + gcol;
+                __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(og), rc, ok ? (uint32_t)(ec * 2) : OOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(ou), rc, ok ? (uint32_t)((ec + d.half_n) * 2) : OOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    pack_bf16x4(os), rc2, ok ? (uint32_t)(((int64_t)row * d.ldc2 + gcol) * 2) : OOB, 0, 0);
             }
         }
     }
 }
 
 template <bool A_KMAJ, bool B_KMAJ, int EPI>
-__global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, uint32_t a_bytes,
-                                                       uint32_t b_bytes, uint32_t c_bytes) {
+__global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, BufSpans sp) {
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI>(d, tm, tn, a_bytes, b_bytes, c_bytes, smem);
+    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI>(d, tm, tn, sp, smem);
 }
 
 // Up to GROUP_MAX independent products of one layout and epilogue in one
@@ -551,7 +580,7 @@ constexpr int GROUP_MAX = 16;
 struct GemmGroup {
     GemmDesc d[GROUP_MAX];
     int tiles_m[GROUP_MAX], tiles_n[GROUP_MAX];
-    uint32_t a_bytes[GROUP_MAX], b_bytes[GROUP_MAX], c_bytes[GROUP_MAX];
+    BufSpans sp[GROUP_MAX];
     int off[GROUP_MAX + 1];
     int n;
 };
@@ -570,14 +599,15 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_group_kernel(GemmGroup grp) {
     int tm, tn;
     tile_of(local, grp.tiles_m[g], grp.tiles_n[g], tm, tn);
     const GemmDesc d = grp.d[g];  // a value copy: its fields stay in scalar registers
-    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI>(d, tm, tn, grp.a_bytes[g], grp.b_bytes[g], grp.c_bytes[g], smem);
+    const BufSpans sp = grp.sp[g];
+    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI>(d, tm, tn, sp, smem);
 }
 
 template <bool AK, bool BKM>
-int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, uint32_t ab, uint32_t bb, uint32_t cb) {
+int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, const BufSpans& sp) {
     dim3 grid(tiles_m * tiles_n), block(NTHR);
     switch (d.epi) {
-#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E>), grid, block, 0, s, d, tiles_m, tiles_n, ab, bb, cb); break;
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E>), grid, block, 0, s, d, tiles_m, tiles_n, sp); break;
         ZB_CASE(EPI_STORE)
         ZB_CASE(EPI_RESID)
         ZB_CASE(EPI_ACCUM_F32)
@@ -602,7 +632,7 @@ namespace {
 // Whether the direct-to-LDS kernel can run `d`, and its buffer spans and grid.
 struct V2Plan {
     bool ok;
-    uint32_t a32, b32, c32;
+    BufSpans sp;
     int tiles_m, tiles_n;
 };
 V2Plan plan_v2(const GemmDesc& d) {
@@ -610,23 +640,28 @@ V2Plan plan_v2(const GemmDesc& d) {
     const bool paired = d.epi == EPI_SWIGLU_FWD;
     const uint64_t ab = d.a_kmajor ? span_bytes(d.M, d.lda, d.K) : span_bytes(d.K, d.lda, d.M);
     const uint64_t bb = d.b_kmajor ? span_bytes(d.N, d.ldb, d.K) : span_bytes(d.K, d.ldb, d.N);
-    // fp32 accumulate reads C through a buffer range as well
-    const uint64_t cb = d.epi == EPI_ACCUM_F32 ? (uint64_t)((int64_t)(d.M - 1) * d.ldc + d.N) * 4 : 0;
-    if (ab >= OOB || bb >= OOB || cb >= OOB) return p;  // too large for one buffer range
+    const bool has_r = d.epi == EPI_RESID || d.epi == EPI_GELU_BWD || d.epi == EPI_SWIGLU_BWD;
+    const bool has_c2 = d.epi == EPI_GELU_FWD || paired;
+    // Row widths touched by the epilogue: [g | u] and [dg | du] rows hold
+    // their second half half_n elements after the first.
+    const int64_t c_w = paired ? 2 * (int64_t)d.half_n : d.epi == EPI_SWIGLU_BWD ? (int64_t)d.half_n + d.N : d.N;
+    const int64_t r_w = d.epi == EPI_SWIGLU_BWD ? (int64_t)d.half_n + d.N : d.N;
+    const int64_t c2_w = paired ? d.half_n : d.N;
+    const uint64_t cb = d.epi == EPI_ACCUM_F32 ? (uint64_t)((int64_t)(d.M - 1) * d.ldc + d.N) * 4
+                                               : span_bytes(d.M, d.ldc, c_w);
+    const uint64_t rb = has_r ? span_bytes(d.M, d.ldr, r_w) : 0;
+    const uint64_t c2b = has_c2 ? span_bytes(d.M, d.ldc2, c2_w) : 0;
+    if (ab >= OOB || bb >= OOB || cb >= OOB || rb >= OOB || c2b >= OOB) return p;  // too large for one buffer range
     // 16-byte (fp32) / 8-byte (bf16) epilogue accesses need widths and leading
     // dimensions divisible by 4 and aligned base pointers.
     auto al = [](const void* q, int a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
-    const bool has_r = d.epi == EPI_RESID || d.epi == EPI_GELU_BWD || d.epi == EPI_SWIGLU_BWD;
-    const bool has_c2 = d.epi == EPI_GELU_FWD || paired;
     bool vec = (d.N % 4 == 0) && (d.ldc % 4 == 0) && al(d.C, d.epi == EPI_ACCUM_F32 ? 16 : 8);
     if (has_r) vec = vec && (d.ldr % 4 == 0) && al(d.R, 8);
     if (has_c2) vec = vec && (d.ldc2 % 4 == 0) && al(d.C2, 8);
     if (d.epi == EPI_SWIGLU_BWD || paired) vec = vec && (d.half_n % 4 == 0);
     if (!vec) return p;
     p.ok = true;
-    p.a32 = (uint32_t)ab;
-    p.b32 = (uint32_t)bb;
-    p.c32 = (uint32_t)cb;
+    p.sp = BufSpans{(uint32_t)ab, (uint32_t)bb, (uint32_t)cb, (uint32_t)rb, (uint32_t)c2b};
     p.tiles_m = (d.M + BM - 1) / BM;
     p.tiles_n = paired ? (d.half_n + BN / 2 - 1) / (BN / 2) : (d.N + BN - 1) / BN;
     return p;
@@ -657,10 +692,10 @@ int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
     const V2Plan p = plan_v2(d);
     if (!p.ok) return ZB_OK;  // caller uses the first-generation kernel
     *handled = true;
-    if (d.a_kmajor && d.b_kmajor) return launch_v2<true, true>(d, s, p.tiles_m, p.tiles_n, p.a32, p.b32, p.c32);
-    if (d.a_kmajor && !d.b_kmajor) return launch_v2<true, false>(d, s, p.tiles_m, p.tiles_n, p.a32, p.b32, p.c32);
-    if (!d.a_kmajor && !d.b_kmajor) return launch_v2<false, false>(d, s, p.tiles_m, p.tiles_n, p.a32, p.b32, p.c32);
-    return launch_v2<false, true>(d, s, p.tiles_m, p.tiles_n, p.a32, p.b32, p.c32);
+    if (d.a_kmajor && d.b_kmajor) return launch_v2<true, true>(d, s, p.tiles_m, p.tiles_n, p.sp);
+    if (d.a_kmajor && !d.b_kmajor) return launch_v2<true, false>(d, s, p.tiles_m, p.tiles_n, p.sp);
+    if (!d.a_kmajor && !d.b_kmajor) return launch_v2<false, false>(d, s, p.tiles_m, p.tiles_n, p.sp);
+    return launch_v2<false, true>(d, s, p.tiles_m, p.tiles_n, p.sp);
 }
 
 int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s) {
@@ -682,9 +717,7 @@ int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s) {
         g.d[i] = d;
         g.tiles_m[i] = p.tiles_m;
         g.tiles_n[i] = p.tiles_n;
-        g.a_bytes[i] = p.a32;
-        g.b_bytes[i] = p.b32;
-        g.c_bytes[i] = p.c32;
+        g.sp[i] = p.sp;
         g.off[i + 1] = g.off[i] + ((p.tiles_m * p.tiles_n + 7) & ~7);
     }
     if (!grouped) {  // one launch per product (validated there)
