@@ -155,10 +155,15 @@ def time_w_kernel(shape, device, reps=5):
     avg_ms = ms_total / launches
     achieved = flops / (ms_total * 1e-3) / 1e12
     algo_bytes = sum(2 * K * (M + N) + 2 * 4 * M * N for M, N, K in gem) / ((len(gem) + 15) // 16)
+    traffic = measured_traffic()
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": algo_bytes,
+            # stash reads (dY, X) and the fp32 dW read-modify-write per launch,
+            # over the launch time; and the measured HBM traffic over the same time
+            "stash_and_dw_GBps": round(algo_bytes / (avg_ms * 1e-3) / 1e9, 1),
+            "hbm_GBps": round(traffic / (avg_ms * 1e-3) / 1e9, 1) if traffic else None,
             "kernel": W_KERNEL + " (W pass: dW += dY^T X for every product of a microbatch, fp32 in place)",
             "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
 

@@ -33,7 +33,6 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, STAGES = 4;
 constexpr int TILE_BYTES = 256 * BK * 2;  // 16 KB per operand tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-constexpr int DMA_PER_TILE = 2 * (TILE_BYTES / 1024) / 4;  // per wave, A + B
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
@@ -56,17 +55,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 
 constexpr uint32_t OOB = 0x80000000u;  // any offset >= the buffer size reads as zero
 
-// ---- DMA of one operand tile (4 instructions per wave, 1 KB each) ---------
+// ---- DMA of one operand tile (NI instructions per wave, 1 KB each) --------
 // Per-lane byte offsets relative to the tile's first k are computed once;
 // rows / columns outside the operand get OOB.  K-contiguous: instruction i of
-// wave w covers tile rows 16b..16b+15 with b = 4i + w.  `k_lim` (elements,
-// relative to the tile's first k) marks k beyond K as OOB; a full tile passes
-// BK and needs no check.
-template <bool PAIRED>
-__device__ __forceinline__ void dma_offsets_kmaj(uint32_t (&off)[4], int64_t ld, int row0, int rows_total,
+// wave w covers tile rows 16b..16b+15 with b = 4i + w (NI = 4: 256 rows,
+// NI = 2: 128 rows).  `k_lim` (elements, relative to the tile's first k)
+// marks k beyond K as OOB; a full tile passes BK and needs no check.
+template <bool PAIRED, int NI>
+__device__ __forceinline__ void dma_offsets_kmaj(uint32_t (&off)[NI], int64_t ld, int row0, int rows_total,
                                                  int half_n, int k_lim, int lane, int wave) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NI; ++i) {
         const int b = i * 4 + wave;
         const int r = b * 16 + (lane >> 2);
         const int kc = (lane & 3) ^ key_km(r);
@@ -99,14 +98,20 @@ __device__ __forceinline__ void dma_offsets_mnmaj(uint32_t (&off)[4], int64_t ld
     }
 }
 
+// Instruction i of wave w writes LDS bytes [1024 b, 1024 b + 1024), b = 4i + w.
+__device__ __forceinline__ void dma_issue_one(__amdgpu_buffer_rsrc_t rs, lds_void* tile, uint32_t off, int b) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((__attribute__((address_space(3))) char*)tile + b * 1024),
+                                             16, off, 0, 0, 0);
+}
 __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rs, lds_void* tile, const uint32_t (&off)[4],
                                           int wave) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int b = i * 4 + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((__attribute__((address_space(3))) char*)tile + b * 1024),
-                                                 16, off[i], 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) dma_issue_one(rs, tile, off[i], i * 4 + wave);
+}
+__device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rs, lds_void* tile, const uint32_t (&off)[2],
+                                          int wave) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma_issue_one(rs, tile, off[i], i * 4 + wave);
 }
 
 // ---- fragment reads ------------------------------------------------------
@@ -134,45 +139,54 @@ __device__ __forceinline__ bf16x8 frag_mnmaj(const lds_void* tile, int blk, int 
 
 // Wait for every outstanding LDS read; the fragments become outputs of the
 // wait so no use of them is scheduled above it.
-__device__ __forceinline__ void lds_wait(bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+template <int NA>
+__device__ __forceinline__ void lds_wait(bf16x8 (&a)[NA], bf16x8 (&b)[4]) {
+    if constexpr (NA == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
 }
 
-// Scheduling pattern for one 16-k step: 8 slots, each holding its share of
-// the RD LDS reads followed by 2 MFMAs.
-template <int RD, int SLOT>
+// Scheduling pattern for one 16-k step of NM MFMAs: NM/2 slots, each
+// holding its share of the RD LDS reads followed by 2 MFMAs.
+template <int RD, int NM, int SLOT>
 __device__ __forceinline__ void interleave_reads_mfma() {
-    if constexpr (SLOT < 8) {
-        constexpr int n = ((SLOT + 1) * RD) / 8 - (SLOT * RD) / 8;
+    constexpr int NS = NM / 2;
+    if constexpr (SLOT < NS) {
+        constexpr int n = ((SLOT + 1) * RD) / NS - (SLOT * RD) / NS;
         if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        interleave_reads_mfma<RD, SLOT + 1>();
+        interleave_reads_mfma<RD, NM, SLOT + 1>();
     }
 }
 
 // Region B of the main loop: RD fragment reads, then ND DMA loads, spread
-// over the 16 MFMAs of the step (reads first: they come before the DMA in
+// over the NM MFMAs of the step (reads first: they come before the DMA in
 // program order and must stay there).
-template <int RD, int ND, int SLOT>
+template <int RD, int ND, int NM, int SLOT>
 __device__ __forceinline__ void interleave_reads_dma_mfma() {
-    if constexpr (SLOT < 16) {
+    if constexpr (SLOT < NM) {
         constexpr int T = RD + ND;
-        constexpr int lo = (SLOT * T) / 16, hi = ((SLOT + 1) * T) / 16;
+        constexpr int lo = (SLOT * T) / NM, hi = ((SLOT + 1) * T) / NM;
         constexpr int nr = (hi < RD ? hi : RD) - (lo < RD ? lo : RD);
         constexpr int nd = (hi - lo) - nr;
         if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
         if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x020, nd, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        interleave_reads_dma_mfma<RD, ND, SLOT + 1>();
+        interleave_reads_dma_mfma<RD, ND, NM, SLOT + 1>();
     }
 }
 
 // Wait until at most N buffer loads of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-    static_assert(N == 0 || N == 8 || N == 16 || N == 20 || N == 24 || N == 32, "vmcnt");
+    static_assert(N == 0 || N == 8 || N == 12 || N == 14 || N == 16 || N == 18 || N == 20 || N == 24 || N == 32,
+                  "vmcnt");
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
     else if constexpr (N == 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
     else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -237,26 +251,31 @@ struct BufSpans {
     uint32_t a, b, c, r, c2;
 };
 
-// One 256x256 output tile (tm, tn) of the product `d`; `smem` is the
-// workgroup's 128 KB of LDS.
-template <bool A_KMAJ, bool B_KMAJ, int EPI>
+// One TBM x 256 output tile (tm, tn) of the product `d`; `smem` is the
+// workgroup's 128 KB of LDS.  TBM = 256: each wave computes 128 x 128;
+// TBM = 128 (K-contiguous A only): each wave computes 64 x 128, for tiles
+// that would otherwise leave most of the chip idle in a launch's last round.
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM = BM>
 __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
+    static_assert(TBM == BM || (TBM == BM / 2 && A_KMAJ), "half-height tiles need a K-contiguous A");
+    constexpr int MI = TBM / 64;  // 32-row A fragments per wave; also A DMA instructions per wave
+    constexpr int DPT = MI + 4;   // DMA instructions per wave per k-tile
 
     // wave index as a scalar: every LDS address derived from it (the DMA
     // destinations in M0) is then computed by scalar instructions.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 5, lrow = lane & 31;
-    const int m0 = tm * BM;
+    const int m0 = tm * TBM;
     const int n0 = PAIRED ? tn * (BN / 2) : tn * BN;
     const int nk = (d.K + BK - 1) / BK;
     const int k_tail = d.K - (nk - 1) * BK;  // k extent of the last tile (1..BK)
 
-    uint32_t offa[4], offb[4];
-    if (A_KMAJ) dma_offsets_kmaj<false>(offa, d.lda, m0, d.M, 0, BK, lane, wave);
+    uint32_t offa[MI], offb[4];
+    if constexpr (A_KMAJ) dma_offsets_kmaj<false, MI>(offa, d.lda, m0, d.M, 0, BK, lane, wave);
     else dma_offsets_mnmaj(offa, d.lda, m0, d.M, lane, wave);
-    if (B_KMAJ) dma_offsets_kmaj<PAIRED>(offb, d.ldb, n0, d.N, d.half_n, BK, lane, wave);
+    if constexpr (B_KMAJ) dma_offsets_kmaj<PAIRED, 4>(offb, d.ldb, n0, d.N, d.half_n, BK, lane, wave);
     else dma_offsets_mnmaj(offb, d.ldb, n0, d.N, lane, wave);
     // Byte step of the buffer base per k-tile.
     const int64_t step_a = A_KMAJ ? BK * 2 : (int64_t)BK * d.lda * 2;
@@ -274,10 +293,10 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
         const __amdgpu_buffer_rsrc_t rb =
             make_rsrc(static_cast<const char*>(d.B) + adv_b, live ? sp.b - adv_b : 0u);
         if (kt == nk - 1 && k_tail < BK) {  // partial last tile: mask k >= K on K-contiguous operands
-            uint32_t ta[4], tb[4];
-            if (A_KMAJ) dma_offsets_kmaj<false>(ta, d.lda, m0, d.M, 0, k_tail, lane, wave);
+            uint32_t ta[MI], tb[4];
+            if constexpr (A_KMAJ) dma_offsets_kmaj<false, MI>(ta, d.lda, m0, d.M, 0, k_tail, lane, wave);
             else dma_offsets_mnmaj(ta, d.lda, m0, d.M, lane, wave);
-            if (B_KMAJ) dma_offsets_kmaj<PAIRED>(tb, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
+            if constexpr (B_KMAJ) dma_offsets_kmaj<PAIRED, 4>(tb, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
             else dma_offsets_mnmaj(tb, d.ldb, n0, d.N, lane, wave);
             if (part != 1) dma_issue(ra, (lds_void*)st, ta, wave);
             if (part != 0) dma_issue(rb, (lds_void*)(st + TILE_BYTES), tb, wave);
@@ -287,16 +306,16 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
         }
     };
 
-    floatx16 acc[4][4];
+    floatx16 acc[MI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     auto frag_a = [&](const lds_void* ta, int mi, int kk) -> bf16x8 {
-        if (A_KMAJ) return frag_kmaj(ta, wm * 128 + mi * 32 + lrow, kk, g);
+        if (A_KMAJ) return frag_kmaj(ta, wm * (TBM / 2) + mi * 32 + lrow, kk, g);
         return frag_mnmaj(ta, wm * 4 + mi, kk, lane);
     };
     auto frag_b = [&](const lds_void* tb, int ni, int kk) -> bf16x8 {
@@ -314,7 +333,8 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     // unit's work over the whole tile.  Both-K-contiguous kernels measure
     // faster with the whole tile in region B.
     constexpr bool SPLIT_DMA = !A_KMAJ || !B_KMAJ;
-    constexpr int RD = 4 * (RD_A + RD_B);  // LDS read instructions per 16-k step
+    constexpr int RD = MI * RD_A + 4 * RD_B;  // LDS read instructions per 16-k step
+    constexpr int NM = MI * 4;                // MFMAs per wave per 16-k step
 
     // Software pipeline across tiles.  Iteration kt:
     //   region A: MFMAs of k step 0 of tile kt, while the step-1 fragments of
@@ -333,20 +353,20 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
 #pragma unroll
         for (int t = 0; t < STAGES - 1; ++t) dma_tile(t);
         dma_tile(STAGES - 1, 0);
-        wait_vm<(STAGES - 1) * DMA_PER_TILE - DMA_PER_TILE / 2>();  // tile 0 landed
+        wait_vm<(STAGES - 2) * DPT + MI>();  // tile 0 landed (tiles 1, 2 and the A half of 3 may not)
     } else {
 #pragma unroll
         for (int t = 0; t < STAGES; ++t) dma_tile(t);
-        wait_vm<(STAGES - 1) * DMA_PER_TILE>();  // tile 0 landed
+        wait_vm<(STAGES - 1) * DPT>();  // tile 0 landed
     }
     workgroup_barrier();
-    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    bf16x8 fa0[MI], fb0[4], fa1[MI], fb1[4];
     {
         const lds_void* ta = (const lds_void*)smem;
         const lds_void* tb = (const lds_void*)(smem + TILE_BYTES);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            fa0[i] = frag_a(ta, i, 0);
+            if (i < MI) fa0[i] = frag_a(ta, i, 0);
             fb0[i] = frag_b(tb, i, 0);
         }
     }
@@ -359,20 +379,20 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
         // region A
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            fa1[i] = frag_a(ta, i, 1);
+            if (i < MI) fa1[i] = frag_a(ta, i, 1);
             fb1[i] = frag_b(tb, i, 1);
         }
         if (!A_KMAJ || !B_KMAJ) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mi], fb0[ni], acc[mi][ni], 0, 0, 0);
         if (SPLIT_DMA) dma_tile(kt + STAGES - 1, 1);  // B half of tile kt+3
-        if (A_KMAJ && B_KMAJ) interleave_reads_mfma<RD, 0>();
+        if (A_KMAJ && B_KMAJ) interleave_reads_mfma<RD, NM, 0>();
         __builtin_amdgcn_sched_barrier(0);
         lds_wait(fa1, fb1);  // tile kt fully read: its stage may be overwritten
-        wait_vm<(STAGES - 2) * DMA_PER_TILE>();  // tile kt+1 landed
+        wait_vm<(STAGES - 2) * DPT>();  // tile kt+1 landed
         workgroup_barrier();
 
         // region B (the fragments read past the last tile are never used)
@@ -382,17 +402,17 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
             const lds_void* nb = (const lds_void*)(sn + TILE_BYTES);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                fa0[i] = frag_a(na, i, 0);
+                if (i < MI) fa0[i] = frag_a(na, i, 0);
                 fb0[i] = frag_b(nb, i, 0);
             }
         }
         dma_tile(kt + STAGES, SPLIT_DMA ? 0 : 2);  // into the stage tile kt vacated
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
-        if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, 8, 0>();
+        if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, DPT, NM, 0>();
     }
     __builtin_amdgcn_sched_barrier(0);
     const int c4 = (lane & 31) * 4;
@@ -406,7 +426,7 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     // inputs does not also wait for the stores issued before it.
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(d.C, sp.c);
     auto load_block = [&](int mi, floatx4 (&dst)[16]) {
-        const int rbase = m0 + wm * 128 + mi * 32;
+        const int rbase = m0 + wm * (TBM / 2) + mi * 32;
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
             const int row = rbase + 2 * it + (lane >> 5);
@@ -421,7 +441,7 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(d.R, HAS_R ? sp.r : 0u);
     u32x2 rin[2][IT], rin2[2][IT];
     auto load_r = [&](int mi, int buf) {
-        const int rbase = m0 + wm * 128 + mi * 32;
+        const int rbase = m0 + wm * (TBM / 2) + mi * 32;
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int row = rbase + 2 * it + (lane >> 5);
@@ -464,9 +484,9 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
         // dW += acc: the old values of block mi+1 are loaded while block mi
         // is added and stored, so at most one HBM round trip is exposed.
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            if (mi + 1 < 4) load_block(mi + 1, cin[(mi + 1) & 1]);
-            const int rbase = m0 + wm * 128 + mi * 32;
+        for (int mi = 0; mi < MI; ++mi) {
+            if (mi + 1 < MI) load_block(mi + 1, cin[(mi + 1) & 1]);
+            const int rbase = m0 + wm * (TBM / 2) + mi * 32;
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -486,10 +506,10 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     constexpr bool HAS_C2 = EPI == EPI_GELU_FWD || PAIRED;
     const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(d.C2, HAS_C2 ? sp.c2 : 0u);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        const int rbase = m0 + wm * 128 + mi * 32;
+    for (int mi = 0; mi < MI; ++mi) {
+        const int rbase = m0 + wm * (TBM / 2) + mi * 32;
         if (!PAIRED) {
-            if (HAS_R && mi + 1 < 4) load_r(mi + 1, (mi + 1) & 1);
+            if (HAS_R && mi + 1 < MI) load_r(mi + 1, (mi + 1) & 1);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -563,12 +583,14 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     }
 }
 
-template <bool A_KMAJ, bool B_KMAJ, int EPI>
-__global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, BufSpans sp) {
+// Tiles (tm, tn_base + tn) for tm < tiles_m, tn < tiles_n, of height TBM.
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
+__global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, int tn_base,
+                                                       BufSpans sp) {
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI>(d, tm, tn, sp, smem);
+    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn_base + tn, sp, smem);
 }
 
 // Up to GROUP_MAX independent products of one layout and epilogue in one
@@ -600,14 +622,14 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_group_kernel(GemmGroup grp) {
     tile_of(local, grp.tiles_m[g], grp.tiles_n[g], tm, tn);
     const GemmDesc d = grp.d[g];  // a value copy: its fields stay in scalar registers
     const BufSpans sp = grp.sp[g];
-    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI>(d, tm, tn, sp, smem);
+    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI, BM>(d, tm, tn, sp, smem);
 }
 
-template <bool AK, bool BKM>
-int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, const BufSpans& sp) {
+template <bool AK, bool BKM, int TBM>
+int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, int tn_base, const BufSpans& sp) {
     dim3 grid(tiles_m * tiles_n), block(NTHR);
     switch (d.epi) {
-#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E>), grid, block, 0, s, d, tiles_m, tiles_n, sp); break;
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E, TBM>), grid, block, 0, s, d, tiles_m, tiles_n, tn_base, sp); break;
         ZB_CASE(EPI_STORE)
         ZB_CASE(EPI_RESID)
         ZB_CASE(EPI_ACCUM_F32)
@@ -687,15 +709,68 @@ int32_t launch_group(const GemmGroup& g, int epi, hipStream_t s) {
 }
 }  // namespace
 
+namespace {
+int cu_count() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// How the tile columns of a K-contiguous-A product split between 256-row
+// and 128-row tiles.  With one workgroup per CU a launch runs in rounds of
+// `cus` tiles, and a last round with at most half the CUs busy costs as long
+// as a full one.  Columns [0, n_full) use 256-row tiles and fill whole rounds;
+// columns [n_full, tiles_n) use 128-row tiles, twice as many of half the
+// work, so the remainder finishes in about half a round.
+struct TileSplit {
+    int n_full;
+};
+TileSplit split_columns(int tiles_m, int tiles_n, int tiles_m_half, int cus) {
+    const int tiles = tiles_m * tiles_n;
+    if (tiles_m_half * tiles_n <= cus) return {0};  // under one round: all half-height
+    const int rounds = tiles / cus, rem = tiles % cus;
+    if (rem == 0 || rem > cus / 2) return {tiles_n};
+    const int n_full = rounds * cus / tiles_m;
+    if (tiles_m_half * (tiles_n - n_full) > cus) return {tiles_n};
+    return {n_full};
+}
+
+template <bool AK, bool BKM>
+int32_t launch_v2_split(const GemmDesc& d, hipStream_t s, const V2Plan& p) {
+    if constexpr (!AK) {
+        return launch_v2<AK, BKM, BM>(d, s, p.tiles_m, p.tiles_n, 0, p.sp);
+    } else {
+        const int tiles_m_half = (d.M + BM / 2 - 1) / (BM / 2);
+        // ZB_GEMM_FULL_TILES=1 keeps every tile 256 rows high (the results are
+        // the same bit for bit: a tile's height does not change the order in
+        // which any output element is accumulated).
+        const TileSplit t = getenv("ZB_GEMM_FULL_TILES") ? TileSplit{p.tiles_n}
+                                                         : split_columns(p.tiles_m, p.tiles_n, tiles_m_half, cu_count());
+        if (t.n_full > 0) {
+            const int32_t rc = launch_v2<AK, BKM, BM>(d, s, p.tiles_m, t.n_full, 0, p.sp);
+            if (rc != ZB_OK) return rc;
+        }
+        if (t.n_full < p.tiles_n) return launch_v2<AK, BKM, BM / 2>(d, s, tiles_m_half, p.tiles_n - t.n_full, t.n_full, p.sp);
+        return ZB_OK;
+    }
+}
+}  // namespace
+
 int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
     *handled = false;
     const V2Plan p = plan_v2(d);
     if (!p.ok) return ZB_OK;  // caller uses the first-generation kernel
     *handled = true;
-    if (d.a_kmajor && d.b_kmajor) return launch_v2<true, true>(d, s, p.tiles_m, p.tiles_n, p.sp);
-    if (d.a_kmajor && !d.b_kmajor) return launch_v2<true, false>(d, s, p.tiles_m, p.tiles_n, p.sp);
-    if (!d.a_kmajor && !d.b_kmajor) return launch_v2<false, false>(d, s, p.tiles_m, p.tiles_n, p.sp);
-    return launch_v2<false, true>(d, s, p.tiles_m, p.tiles_n, p.sp);
+    if (d.a_kmajor && d.b_kmajor) return launch_v2_split<true, true>(d, s, p);
+    if (d.a_kmajor && !d.b_kmajor) return launch_v2_split<true, false>(d, s, p);
+    if (!d.a_kmajor && !d.b_kmajor) return launch_v2_split<false, false>(d, s, p);
+    return launch_v2_split<false, true>(d, s, p);
 }
 
 int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s) {

@@ -47,6 +47,31 @@ def test_gemm_nt_bf16(M, N, K):
     assert od.rel_fro(to_f64(c), a.f64 @ b.f64.T) <= 2.5e-3
 
 
+@pytest.mark.parametrize("M,N,K,b_kmajor", [
+    (500, 129 * 256 + 40, 64, True),   # 2 x 130 tiles: 256-row tiles fill one round, 128-row tiles the rest
+    (512, 128 * 256, 32, False),       # 2 x 128 tiles, exactly one round: 256-row tiles only
+    (1000, 24, 64, False),             # under one round: 128-row tiles only
+])
+def test_gemm_tile_heights_bitwise_and_parity(M, N, K, b_kmajor, monkeypatch):
+    """Products with a K-contiguous A mix 256-row and 128-row tiles by how
+    the tile count fills the chip's rounds (the cases above are for 256 CUs).
+    The result equals, bit for bit, the one with every tile 256 rows high
+    (ZB_GEMM_FULL_TILES=1), and the oracle's product."""
+    a = _bf16("a", (M, K), 21)
+    b = _bf16("b", (N, K) if b_kmajor else (K, N), 22)
+    outs = []
+    for full in (False, True):
+        if full:
+            monkeypatch.setenv("ZB_GEMM_FULL_TILES", "1")
+        c = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        zb.gemm(to_dev(a), to_dev(b), c, a_kmajor=True, b_kmajor=b_kmajor, M=M, N=N, K=K)
+        torch.cuda.synchronize()
+        outs.append(c.cpu())
+    assert torch.equal(outs[0], outs[1])
+    ref = a.f64 @ (b.f64.T if b_kmajor else b.f64)
+    assert od.rel_fro(to_f64(outs[0]), ref) <= 2.5e-3
+
+
 @pytest.mark.parametrize("M,N,K", [(264, 136, 72), (512, 512, 512), (8, 8, 8), (300, 1032, 24)])
 def test_gemm_nn_bf16(M, N, K):
     """B form: C = A . W with W stored [K, N] (N contiguous)."""
