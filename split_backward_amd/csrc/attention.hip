@@ -531,11 +531,16 @@ constexpr int KV_STAGES = 2;
 __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], char* svt, float (*sl)[2][BQB],
                                                const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dout,
                                                const float* __restrict__ lse, const float* __restrict__ delta,
-                                               bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
+                                               bf16_t* __restrict__ dqkv, float* __restrict__ part, int T, int nq,
+                                               int nkv) {
     const int ld = (nq + 2 * nkv) * D;
     const int ldo = nq * D;
     const int grp = blockIdx.y;
-    const int rep = nq / nkv;
+    // The group's query heads split over gridDim.z workgroups (head subset
+    // blockIdx.z); with more than one, each writes fp32 partial dK, dV to
+    // `part` and attn_dkv_reduce_kernel adds them in subset order.
+    const int rep = nq / nkv / (int)gridDim.z;
+    const int head0 = (grp * (int)gridDim.z + (int)blockIdx.z) * rep;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int kw0 = kb * BKV + wave * 32;
@@ -569,7 +574,7 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
     auto fetch = [&](int it) {
         const bool live = it < total;
         const int itc = live ? it : 0;
-        const int hh = grp * rep + itc / per_head;
+        const int hh = head0 + itc / per_head;
         const int q0 = (qb0 + itc % per_head) * BQB;
         char* st = sm[it % KV_STAGES];
         dma_rows<BQB, 4>(qkv + hh * D, ld, q0, T, 0, (lds_void*)st, lane, wave, live);
@@ -671,6 +676,20 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the empty trailing blocks still write LDS
+    if (part) {  // fp32 partials [subset][key][kv head][dK | dV][D], dK not yet scaled
+        float* pk = part + (((int64_t)blockIdx.z * T + key) * nkv + grp) * 2 * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d = db * 32 + rg * 8 + g * 4;
+                *reinterpret_cast<floatx4*>(pk + d) =
+                    floatx4{dk[db][rg * 4], dk[db][rg * 4 + 1], dk[db][rg * 4 + 2], dk[db][rg * 4 + 3]};
+                *reinterpret_cast<floatx4*>(pk + D + d) =
+                    floatx4{dv[db][rg * 4], dv[db][rg * 4 + 1], dv[db][rg * 4 + 2], dv[db][rg * 4 + 3]};
+            }
+        return;
+    }
     const float scale = 1.f / sqrtf((float)D);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -693,7 +712,8 @@ __global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restr
                                                            const bf16_t* __restrict__ dout,
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ delta,
-                                                           bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
+                                                           bf16_t* __restrict__ dqkv, float* __restrict__ part,
+                                                           int T, int nq, int nkv) {
     __shared__ __attribute__((aligned(1024))) char sm[KV_STAGES][2 * Q_TILE];  // [stage][Q | dO]
     __shared__ __attribute__((aligned(1024))) char svt[BKV * D * 2];           // V rows of the block
     __shared__ float sl[KV_STAGES][2][BQB];                                     // [stage][lse | delta]
@@ -701,11 +721,43 @@ __global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restr
     const int a = (int)blockIdx.x, b = nb - 1 - (int)blockIdx.x;  // a: the longer sweep
     for (int pass = 0; pass < (b > a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();
-        attn_dkv_block(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, T, nq, nkv);
+        attn_dkv_block(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, part, T, nq, nkv);
     }
 }
 
+// dK = scale * sum_z part[z][.][.][0], dV = sum_z part[z][.][.][1], summed in
+// subset order (deterministic); one thread per 4 consecutive elements.
+__global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(const float* __restrict__ part, bf16_t* __restrict__ dqkv,
+                                                              int T, int nq, int nkv, int nsplit) {
+    const int64_t per = (int64_t)T * nkv * 2 * D;  // floats per subset
+    const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i4 >= per) return;
+    floatx4 acc = *reinterpret_cast<const floatx4*>(part + i4);
+    for (int z = 1; z < nsplit; ++z) acc += *reinterpret_cast<const floatx4*>(part + z * per + i4);
+    const int d = (int)(i4 % D);
+    const int which = (int)((i4 / D) % 2);
+    const int grp = (int)((i4 / (2 * D)) % nkv);
+    const int key = (int)(i4 / (2 * D * nkv));
+    const float sc = which == 0 ? 1.f / sqrtf((float)D) : 1.f;
+    u32x2 v;
+    v[0] = uint32_t(f2bf(acc[0] * sc)) | (uint32_t(f2bf(acc[1] * sc)) << 16);
+    v[1] = uint32_t(f2bf(acc[2] * sc)) | (uint32_t(f2bf(acc[3] * sc)) << 16);
+    const int ld = (nq + 2 * nkv) * D;
+    *reinterpret_cast<u32x2*>(dqkv + (int64_t)key * ld + (nq + which * nkv + grp) * D + d) = v;
+}
+
 bool shapes_ok(int T, int nq, int nkv) { return T > 0 && T % FQ == 0 && nq > 0 && nkv > 0 && nq % nkv == 0; }
+
+// Query-head subsets per KV head for the dk/dv kernel: the smallest divisor
+// of the group size that gives at least 512 workgroups (two per CU on a
+// 256-CU part).  A group of 8 query heads per KV head (Llama-70B: 8 KV heads,
+// 16 key-block pairs) would otherwise run 128 workgroups.
+int dkv_split(int T, int nq, int nkv) {
+    const int rep = nq / nkv, wgs = (T / BKV + 1) / 2 * nkv;
+    for (int z = 1; z < rep; ++z)
+        if (rep % z == 0 && wgs * z >= 512) return z;
+    return rep;
+}
 
 }  // namespace
 
@@ -716,15 +768,30 @@ int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nk
     return ZB_OK;
 }
 
+size_t attn_bwd_scratch_bytes(int T, int nq, int nkv) {
+    if (!shapes_ok(T, nq, nkv)) return 0;
+    const int z = dkv_split(T, nq, nkv);
+    return z > 1 ? (size_t)z * T * nkv * 2 * D * 4 : 0;
+}
+
 int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout, bf16_t* dqkv, float* delta,
-                 int T, int nq, int nkv, hipStream_t s) {
+                 float* part, int T, int nq, int nkv, hipStream_t s) {
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
     // the dq kernel also computes delta = rowsum(dO o), which the dk/dv kernel reads
     hipLaunchKernelGGL(attn_dq_kernel, dim3((T / FQ + 1) / 2, nq), dim3(FTHR), 0, s, qkv, o, dout, lse, delta, dqkv, T,
                        nq, nkv);
     ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(attn_dkv_kernel, dim3((T / BKV + 1) / 2, nkv), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv, T, nq, nkv);
+    const int z = dkv_split(T, nq, nkv);
+    if (z > 1 && part == nullptr) return fail(ZB_EINVAL, "attention: missing dk/dv partial scratch");
+    hipLaunchKernelGGL(attn_dkv_kernel, dim3((T / BKV + 1) / 2, nkv, z), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv,
+                       z > 1 ? part : nullptr, T, nq, nkv);
     ZB_HIP(hipGetLastError());
+    if (z > 1) {
+        const int64_t n4 = (int64_t)T * nkv * 2 * D / 4;
+        hipLaunchKernelGGL(attn_dkv_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, part, dqkv, T,
+                           nq, nkv, z);
+        ZB_HIP(hipGetLastError());
+    }
     return ZB_OK;
 }
 

@@ -86,9 +86,12 @@ size_t rmsnorm_dgamma_scratch_floats(int T, int H);
 // Causal GQA attention, head_dim 128.  q/k/v are column blocks of the packed
 // qkv [T, (nq + 2 nkv) * 128] buffer; o [T, nq*128]; lse f32 [nq, T].
 int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s);
-// dqkv [T, (nq + 2 nkv)*128]; delta scratch f32 [nq, T].
+// dqkv [T, (nq + 2 nkv)*128]; delta scratch f32 [nq, T]; part: scratch of
+// attn_bwd_scratch_bytes(T, nq, nkv) bytes (fp32 partial dK, dV when the
+// query heads of a KV head are split over workgroups; nullptr if 0).
+size_t attn_bwd_scratch_bytes(int T, int nq, int nkv);
 int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout,
-                 bf16_t* dqkv, float* delta, int T, int nq, int nkv, hipStream_t s);
+                 bf16_t* dqkv, float* delta, float* part, int T, int nq, int nkv, hipStream_t s);
 
 // --------------------------------------------------------------- timing ---
 int32_t stamp_now(uint64_t* dst, hipStream_t s);

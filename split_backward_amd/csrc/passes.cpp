@@ -134,6 +134,10 @@ int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipSt
     const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
     bf16_t* da = bf(st.scratch_b);
     float* delta = reinterpret_cast<float*>(st.scratch_b + ((size_t)T * QD * 2 + 255) / 256 * 256);
+    float* part = attn_bwd_scratch_bytes(T, d.n_heads, d.n_kv_heads) == 0
+                      ? nullptr
+                      : reinterpret_cast<float*>(reinterpret_cast<char*>(delta) +
+                                                 ((size_t)d.n_heads * T * 4 + 255) / 256 * 256);
     for (int l = d.n_layers - 1; l >= 0; --l) {
         void* const* w = &st.w[6 * l];
         bf16_t* xl = bf(st.slot_tensor(mb, l, L_X));
@@ -161,7 +165,7 @@ int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipSt
         ZB_TRY(gemm_bf16(nn(T, H, 2 * F, dgu, 2 * F, w[2], H, dn2, H), s));
         ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, dout, dh1, T, H, s));
         ZB_TRY(gemm_bf16(nn(T, QD, H, dh1, H, w[1], QD, da, QD), s));
-        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, T, d.n_heads, d.n_kv_heads, s));
+        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, part, T, d.n_heads, d.n_kv_heads, s));
         ZB_TRY(gemm_bf16(nn(T, H, QKV, dqkv, QKV, w[0], H, dn1, H), s));
         ZB_TRY(rmsnorm_bwd(xl, r1, cbf(w[4]), dn1, dh1, bf(dest), T, H, s));
     }

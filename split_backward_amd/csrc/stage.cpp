@@ -97,7 +97,9 @@ void Layout::build(const zb_stage_desc& d) {
     scratch_w = 0;
     if (d.kind == ZB_LLAMA) {
         const size_t QD = (size_t)d.n_heads * d.head_dim;
-        scratch_b = align_up(T * QD * 2) + align_up((size_t)d.n_heads * T * 4);  // da + delta
+        // da + delta + the dk/dv partials of split query-head groups
+        scratch_b = align_up(T * QD * 2) + align_up((size_t)d.n_heads * T * 4) +
+                    align_up(attn_bwd_scratch_bytes(d.tokens, d.n_heads, d.n_kv_heads));
         scratch_w = align_up(rmsnorm_dgamma_scratch_floats(d.tokens, d.hidden) * 4);
     }
     stamps_bytes = align_up(sizeof(uint64_t) * (3 * (size_t)MAX_RUN_OPS + 8));
