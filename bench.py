@@ -118,11 +118,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per W-kernel launch from the committed rocprofv3 --pmc
     summary (FETCH_SIZE + WRITE_SIZE, scaled by the same counters' reading
-    for a copy kernel of known size), or None when the summary is missing or
-    was taken on other kernel sources."""
+    for a copy kernel of known size), or None when the summary is missing,
+    covers another workload or was taken on other kernel sources."""
     import re
     try:
         with open(os.path.join(ROOT, TRAFFIC_SUMMARY)) as fh:
@@ -131,12 +131,13 @@ def measured_traffic():
         return None
     mh = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
     mb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not mh or not mb or mh.group(1) != kernel_source_hash():
+    mw = re.search(r"workload:\s*(\S+)", txt)
+    if not mh or not mb or not mw or mh.group(1) != kernel_source_hash() or mw.group(1) != workload:
         return None
     return float(mb.group(1))
 
 
-def time_w_kernel(shape, device, reps=5):
+def time_w_kernel(shape, workload, device, reps=5):
     """Average launch time of the W-pass GEMM kernel at the step's shapes,
     launched through the C ABI on the current stream, timed with events."""
     import torch
@@ -155,7 +156,7 @@ def time_w_kernel(shape, device, reps=5):
     avg_ms = ms_total / launches
     achieved = flops / (ms_total * 1e-3) / 1e12
     algo_bytes = sum(2 * K * (M + N) + 2 * 4 * M * N for M, N, K in gem) / ((len(gem) + 15) // 16)
-    traffic = measured_traffic()
+    traffic = measured_traffic(workload)
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
@@ -333,7 +334,7 @@ def main():
     torch.cuda.synchronize()
     t_f, t_b, t_w = (ev[i].elapsed_time(ev[i + 1]) for i in range(3))
 
-    roof = time_w_kernel(shape, device)
+    roof = time_w_kernel(shape, args.workload, device)
     extra = {}
     if shape.kind == "llama" and not args.no_executor:
         extra["executor_p8_stage3"] = executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w)
