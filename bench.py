@@ -110,11 +110,17 @@ TRAFFIC_SUMMARY = "profiles/gemm_w_kernel_hbm_traffic_llama7b_stage4.md"
 
 
 def kernel_source_hash() -> str:
+    """sha256 prefix of the W kernel's sources with comments and whitespace
+    removed (a comment edit does not invalidate the measured traffic)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in W_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update("".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

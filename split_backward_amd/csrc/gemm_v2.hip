@@ -1,17 +1,19 @@
 // bf16 GEMM, second generation: direct-to-LDS operand staging.
 //
-// Workgroup tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each
-// wave owning a 128 x 128 sub-tile = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
-// (256 fp32 accumulators per lane, held in AGPRs).
+// Workgroup tile 256 x 256 (k-tiles of 32), 256 threads = 4 waves in a 2 x 2
+// grid, each wave owning a 128 x 128 sub-tile = 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, held in AGPRs).
+// For a K-contiguous A the tile may instead be 128 x 256 (each wave 64 x 128),
+// used where a launch's last round of tiles would leave most CUs idle.
 //
 // Operands go HBM -> LDS with buffer_load ... lds (16 bytes per lane): no
 // VGPR staging, no ds_write, and out-of-range rows / columns / k read as zero
 // through the buffer range check.  Each operand keeps its HBM orientation in
 // LDS:
-//   K-contiguous operand  -> LDS [256 rows][64 k], 128-byte rows, 16-byte
-//                            chunks XOR-swizzled by the row; an MFMA fragment
-//                            (8 consecutive k of one row) is one ds_read_b128.
-//   M/N-contiguous operand -> LDS [64 k][256 cols], 512-byte rows, 32-byte
+//   K-contiguous operand  -> LDS [rows][32 k], 64-byte rows, 16-byte chunks
+//                            XOR-swizzled by the row; an MFMA fragment (8
+//                            consecutive k of one row) is one ds_read_b128.
+//   M/N-contiguous operand -> LDS [32 k][256 cols], 512-byte rows, 32-byte
 //                            pieces XOR-swizzled by k; a fragment is two
 //                            ds_read_b64_tr_b16, the gfx950 LDS transpose
 //                            read (in each 16-lane group, output lane i,
@@ -19,12 +21,12 @@
 //                            4s + i/4), so the lane receives 8 consecutive k
 //                            of its column.
 // Four LDS stages of 32-k tiles (128 KB): the DMA of the next k-tiles is in
-// flight while tile t is multiplied (about four tiles of prefetch hide HBM
-// latency with one wave per SIMD), fragments of the next 16-k step are read
-// while the MFMAs of the current step issue, and the per-tile barrier sits in
-// the middle of a tile so fragment reads never wait behind it.  DMA addressing costs no VALU: each
-// lane's offset is fixed once, and the buffer base advances in scalar
-// registers from tile to tile.
+// flight while tile t is multiplied (three tiles of prefetch hide HBM latency
+// with one wave per SIMD), fragments of the next 16-k step are read while the
+// MFMAs of the current step issue, and the per-tile barrier sits in the
+// middle of a tile so fragment reads never wait behind it.  DMA addressing
+// costs no VALU: each lane's offset is fixed once, and the buffer base
+// advances in scalar registers from tile to tile.
 #include "common.h"
 
 namespace zb {
