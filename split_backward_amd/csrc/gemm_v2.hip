@@ -183,9 +183,10 @@ __device__ __forceinline__ void interleave_reads_dma_mfma() {
 // Wait until at most N buffer loads of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-    static_assert(N == 0 || N == 8 || N == 12 || N == 14 || N == 16 || N == 18 || N == 20 || N == 24 || N == 32,
+    static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 14 || N == 16 || N == 18 || N == 20 || N == 24 || N == 32,
                   "vmcnt");
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
     else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
@@ -257,165 +258,18 @@ struct BufSpans {
 // workgroup's 128 KB of LDS.  TBM = 256: each wave computes 128 x 128;
 // TBM = 128 (K-contiguous A only): each wave computes 64 x 128, for tiles
 // that would otherwise leave most of the chip idle in a launch's last round.
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM = BM>
-__device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
+// Epilogue of a TBM x 256 tile: the accumulators go through LDS (the
+// k-tile stages are free by then) and out with the fused operation EPI.
+// Called once every DMA into LDS has been issued: the waits below count the
+// loads still in flight.
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
+__device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans& sp, floatx16 (&acc)[TBM / 64][4],
+                                              int m0, int n0, char* smem) {
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
-    static_assert(TBM == BM || (TBM == BM / 2 && A_KMAJ), "half-height tiles need a K-contiguous A");
-    constexpr int MI = TBM / 64;  // 32-row A fragments per wave; also A DMA instructions per wave
-    constexpr int DPT = MI + 4;   // DMA instructions per wave per k-tile
-
-    // wave index as a scalar: every LDS address derived from it (the DMA
-    // destinations in M0) is then computed by scalar instructions.
+    constexpr int MI = TBM / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 5, lrow = lane & 31;
-    const int m0 = tm * TBM;
-    const int n0 = PAIRED ? tn * (BN / 2) : tn * BN;
-    const int nk = (d.K + BK - 1) / BK;
-    const int k_tail = d.K - (nk - 1) * BK;  // k extent of the last tile (1..BK)
-
-    uint32_t offa[MI], offb[4];
-    if constexpr (A_KMAJ) dma_offsets_kmaj<false, MI>(offa, d.lda, m0, d.M, 0, BK, lane, wave);
-    else dma_offsets_mnmaj(offa, d.lda, m0, d.M, lane, wave);
-    if constexpr (B_KMAJ) dma_offsets_kmaj<PAIRED, 4>(offb, d.ldb, n0, d.N, d.half_n, BK, lane, wave);
-    else dma_offsets_mnmaj(offb, d.ldb, n0, d.N, lane, wave);
-    // Byte step of the buffer base per k-tile.
-    const int64_t step_a = A_KMAJ ? BK * 2 : (int64_t)BK * d.lda * 2;
-    const int64_t step_b = B_KMAJ ? BK * 2 : (int64_t)BK * d.ldb * 2;
-
-    // part 0: the A tile only, 1: the B tile only, 2: both.
-    auto dma_tile = [&](int kt, int part = 2) {
-        char* st = smem + (kt % STAGES) * STAGE_BYTES;
-        // A tile past the end of K gets an empty range: its loads read zeros,
-        // fetch nothing, and keep the per-iteration DMA count uniform.
-        const bool live = kt < nk;
-        const uint32_t adv_a = live ? (uint32_t)(kt * step_a) : 0u, adv_b = live ? (uint32_t)(kt * step_b) : 0u;
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(static_cast<const char*>(d.A) + adv_a, live ? sp.a - adv_a : 0u);
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(static_cast<const char*>(d.B) + adv_b, live ? sp.b - adv_b : 0u);
-        if (kt == nk - 1 && k_tail < BK) {  // partial last tile: mask k >= K on K-contiguous operands
-            uint32_t ta[MI], tb[4];
-            if constexpr (A_KMAJ) dma_offsets_kmaj<false, MI>(ta, d.lda, m0, d.M, 0, k_tail, lane, wave);
-            else dma_offsets_mnmaj(ta, d.lda, m0, d.M, lane, wave);
-            if constexpr (B_KMAJ) dma_offsets_kmaj<PAIRED, 4>(tb, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
-            else dma_offsets_mnmaj(tb, d.ldb, n0, d.N, lane, wave);
-            if (part != 1) dma_issue(ra, (lds_void*)st, ta, wave);
-            if (part != 0) dma_issue(rb, (lds_void*)(st + TILE_BYTES), tb, wave);
-        } else {
-            if (part != 1) dma_issue(ra, (lds_void*)st, offa, wave);
-            if (part != 0) dma_issue(rb, (lds_void*)(st + TILE_BYTES), offb, wave);
-        }
-    };
-
-    floatx16 acc[MI][4];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    auto frag_a = [&](const lds_void* ta, int mi, int kk) -> bf16x8 {
-        if (A_KMAJ) return frag_kmaj(ta, wm * (TBM / 2) + mi * 32 + lrow, kk, g);
-        return frag_mnmaj(ta, wm * 4 + mi, kk, lane);
-    };
-    auto frag_b = [&](const lds_void* tb, int ni, int kk) -> bf16x8 {
-        if (B_KMAJ) {
-            const int row = PAIRED ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + lrow) : (wn * 128 + ni * 32 + lrow);
-            return frag_kmaj(tb, row, kk, g);
-        }
-        return frag_mnmaj(tb, wn * 4 + ni, kk, lane);
-    };
-
-    constexpr int RD_A = A_KMAJ ? 1 : 2, RD_B = B_KMAJ ? 1 : 2;
-    // With an M/N-contiguous operand (transpose reads, twice the LDS read
-    // instructions) the DMA of a tile is split: its A half is issued in
-    // region B, its B half in the next region A, which spreads the address
-    // unit's work over the whole tile.  Both-K-contiguous kernels measure
-    // faster with the whole tile in region B.
-    constexpr bool SPLIT_DMA = !A_KMAJ || !B_KMAJ;
-    constexpr int RD = MI * RD_A + 4 * RD_B;  // LDS read instructions per 16-k step
-    constexpr int NM = MI * 4;                // MFMAs per wave per 16-k step
-
-    // Software pipeline across tiles.  Iteration kt:
-    //   region A: MFMAs of k step 0 of tile kt, while the step-1 fragments of
-    //             tile kt are read;
-    //   every read of tile kt has completed and tile kt+1 has landed, then a
-    //             barrier (mid-tile, so no wave idles at a tile boundary);
-    //   region B: MFMAs of step 1 of tile kt, while the step-0 fragments of
-    //             tile kt+1 are read and the DMA of tile kt+4 is issued into
-    //             the stage tile kt just vacated (with SPLIT_DMA its A half;
-    //             the B half follows in region A of iteration kt+1, when that
-    //             stage is still free).
-    // Every iteration issues the same DMA count (tiles past K are empty), so
-    // the waits are constants: after region A of iteration kt the DMA of
-    // tiles kt+2 and kt+3 (16 loads per wave) may stay in flight.
-    if (SPLIT_DMA) {
-#pragma unroll
-        for (int t = 0; t < STAGES - 1; ++t) dma_tile(t);
-        dma_tile(STAGES - 1, 0);
-        wait_vm<(STAGES - 2) * DPT + MI>();  // tile 0 landed (tiles 1, 2 and the A half of 3 may not)
-    } else {
-#pragma unroll
-        for (int t = 0; t < STAGES; ++t) dma_tile(t);
-        wait_vm<(STAGES - 1) * DPT>();  // tile 0 landed
-    }
-    workgroup_barrier();
-    bf16x8 fa0[MI], fb0[4], fa1[MI], fb1[4];
-    {
-        const lds_void* ta = (const lds_void*)smem;
-        const lds_void* tb = (const lds_void*)(smem + TILE_BYTES);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i < MI) fa0[i] = frag_a(ta, i, 0);
-            fb0[i] = frag_b(tb, i, 0);
-        }
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-        const lds_void* ta = (const lds_void*)st;
-        const lds_void* tb = (const lds_void*)(st + TILE_BYTES);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!A_KMAJ || !B_KMAJ) lds_wait(fa0, fb0);
-        // region A
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i < MI) fa1[i] = frag_a(ta, i, 1);
-            fb1[i] = frag_b(tb, i, 1);
-        }
-        if (!A_KMAJ || !B_KMAJ) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mi], fb0[ni], acc[mi][ni], 0, 0, 0);
-        if (SPLIT_DMA) dma_tile(kt + STAGES - 1, 1);  // B half of tile kt+3
-        if (A_KMAJ && B_KMAJ) interleave_reads_mfma<RD, NM, 0>();
-        __builtin_amdgcn_sched_barrier(0);
-        lds_wait(fa1, fb1);  // tile kt fully read: its stage may be overwritten
-        wait_vm<(STAGES - 2) * DPT>();  // tile kt+1 landed
-        workgroup_barrier();
-
-        // region B (the fragments read past the last tile are never used)
-        {
-            const char* sn = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
-            const lds_void* na = (const lds_void*)sn;
-            const lds_void* nb = (const lds_void*)(sn + TILE_BYTES);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < MI) fa0[i] = frag_a(na, i, 0);
-                fb0[i] = frag_b(nb, i, 0);
-            }
-        }
-        dma_tile(kt + STAGES, SPLIT_DMA ? 0 : 2);  // into the stage tile kt vacated
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
-        if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, DPT, NM, 0>();
-    }
     __builtin_amdgcn_sched_barrier(0);
     const int c4 = (lane & 31) * 4;
     const int gcol = n0 + wn * 128 + c4;
@@ -585,14 +439,360 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     }
 }
 
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM = BM>
+__device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
+    constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
+    static_assert(TBM == BM || (TBM == BM / 2 && A_KMAJ), "half-height tiles need a K-contiguous A");
+    constexpr int MI = TBM / 64;  // 32-row A fragments per wave; also A DMA instructions per wave
+    constexpr int DPT = MI + 4;   // DMA instructions per wave per k-tile
+
+    // wave index as a scalar: every LDS address derived from it (the DMA
+    // destinations in M0) is then computed by scalar instructions.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int g = lane >> 5, lrow = lane & 31;
+    const int m0 = tm * TBM;
+    const int n0 = PAIRED ? tn * (BN / 2) : tn * BN;
+    const int nk = (d.K + BK - 1) / BK;
+    const int k_tail = d.K - (nk - 1) * BK;  // k extent of the last tile (1..BK)
+
+    uint32_t offa[MI], offb[4];
+    if constexpr (A_KMAJ) dma_offsets_kmaj<false, MI>(offa, d.lda, m0, d.M, 0, BK, lane, wave);
+    else dma_offsets_mnmaj(offa, d.lda, m0, d.M, lane, wave);
+    if constexpr (B_KMAJ) dma_offsets_kmaj<PAIRED, 4>(offb, d.ldb, n0, d.N, d.half_n, BK, lane, wave);
+    else dma_offsets_mnmaj(offb, d.ldb, n0, d.N, lane, wave);
+    // Byte step of the buffer base per k-tile.
+    const int64_t step_a = A_KMAJ ? BK * 2 : (int64_t)BK * d.lda * 2;
+    const int64_t step_b = B_KMAJ ? BK * 2 : (int64_t)BK * d.ldb * 2;
+
+    // part 0: the A tile only, 1: the B tile only, 2: both.
+    auto dma_tile = [&](int kt, int part = 2) {
+        char* st = smem + (kt % STAGES) * STAGE_BYTES;
+        // A tile past the end of K gets an empty range: its loads read zeros,
+        // fetch nothing, and keep the per-iteration DMA count uniform.
+        const bool live = kt < nk;
+        const uint32_t adv_a = live ? (uint32_t)(kt * step_a) : 0u, adv_b = live ? (uint32_t)(kt * step_b) : 0u;
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(static_cast<const char*>(d.A) + adv_a, live ? sp.a - adv_a : 0u);
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(static_cast<const char*>(d.B) + adv_b, live ? sp.b - adv_b : 0u);
+        if (kt == nk - 1 && k_tail < BK) {  // partial last tile: mask k >= K on K-contiguous operands
+            uint32_t ta[MI], tb[4];
+            if constexpr (A_KMAJ) dma_offsets_kmaj<false, MI>(ta, d.lda, m0, d.M, 0, k_tail, lane, wave);
+            else dma_offsets_mnmaj(ta, d.lda, m0, d.M, lane, wave);
+            if constexpr (B_KMAJ) dma_offsets_kmaj<PAIRED, 4>(tb, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
+            else dma_offsets_mnmaj(tb, d.ldb, n0, d.N, lane, wave);
+            if (part != 1) dma_issue(ra, (lds_void*)st, ta, wave);
+            if (part != 0) dma_issue(rb, (lds_void*)(st + TILE_BYTES), tb, wave);
+        } else {
+            if (part != 1) dma_issue(ra, (lds_void*)st, offa, wave);
+            if (part != 0) dma_issue(rb, (lds_void*)(st + TILE_BYTES), offb, wave);
+        }
+    };
+
+    floatx16 acc[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    auto frag_a = [&](const lds_void* ta, int mi, int kk) -> bf16x8 {
+        if (A_KMAJ) return frag_kmaj(ta, wm * (TBM / 2) + mi * 32 + lrow, kk, g);
+        return frag_mnmaj(ta, wm * 4 + mi, kk, lane);
+    };
+    auto frag_b = [&](const lds_void* tb, int ni, int kk) -> bf16x8 {
+        if (B_KMAJ) {
+            const int row = PAIRED ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + lrow) : (wn * 128 + ni * 32 + lrow);
+            return frag_kmaj(tb, row, kk, g);
+        }
+        return frag_mnmaj(tb, wn * 4 + ni, kk, lane);
+    };
+
+    constexpr int RD_A = A_KMAJ ? 1 : 2, RD_B = B_KMAJ ? 1 : 2;
+    // With an M/N-contiguous operand (transpose reads, twice the LDS read
+    // instructions) the DMA of a tile is split: its A half is issued in
+    // region B, its B half in the next region A, which spreads the address
+    // unit's work over the whole tile.  Both-K-contiguous kernels measure
+    // faster with the whole tile in region B.
+    constexpr bool SPLIT_DMA = !A_KMAJ || !B_KMAJ;
+    constexpr int RD = MI * RD_A + 4 * RD_B;  // LDS read instructions per 16-k step
+    constexpr int NM = MI * 4;                // MFMAs per wave per 16-k step
+
+    // Software pipeline across tiles.  Iteration kt:
+    //   region A: MFMAs of k step 0 of tile kt, while the step-1 fragments of
+    //             tile kt are read;
+    //   every read of tile kt has completed and tile kt+1 has landed, then a
+    //             barrier (mid-tile, so no wave idles at a tile boundary);
+    //   region B: MFMAs of step 1 of tile kt, while the step-0 fragments of
+    //             tile kt+1 are read and the DMA of tile kt+4 is issued into
+    //             the stage tile kt just vacated (with SPLIT_DMA its A half;
+    //             the B half follows in region A of iteration kt+1, when that
+    //             stage is still free).
+    // Every iteration issues the same DMA count (tiles past K are empty), so
+    // the waits are constants: after region A of iteration kt the DMA of
+    // tiles kt+2 and kt+3 (16 loads per wave) may stay in flight.
+    if (SPLIT_DMA) {
+#pragma unroll
+        for (int t = 0; t < STAGES - 1; ++t) dma_tile(t);
+        dma_tile(STAGES - 1, 0);
+        wait_vm<(STAGES - 2) * DPT + MI>();  // tile 0 landed (tiles 1, 2 and the A half of 3 may not)
+    } else {
+#pragma unroll
+        for (int t = 0; t < STAGES; ++t) dma_tile(t);
+        wait_vm<(STAGES - 1) * DPT>();  // tile 0 landed
+    }
+    workgroup_barrier();
+    bf16x8 fa0[MI], fb0[4], fa1[MI], fb1[4];
+    {
+        const lds_void* ta = (const lds_void*)smem;
+        const lds_void* tb = (const lds_void*)(smem + TILE_BYTES);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < MI) fa0[i] = frag_a(ta, i, 0);
+            fb0[i] = frag_b(tb, i, 0);
+        }
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+        const lds_void* ta = (const lds_void*)st;
+        const lds_void* tb = (const lds_void*)(st + TILE_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!A_KMAJ || !B_KMAJ) lds_wait(fa0, fb0);
+        // region A
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < MI) fa1[i] = frag_a(ta, i, 1);
+            fb1[i] = frag_b(tb, i, 1);
+        }
+        if (!A_KMAJ || !B_KMAJ) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mi], fb0[ni], acc[mi][ni], 0, 0, 0);
+        if (SPLIT_DMA) dma_tile(kt + STAGES - 1, 1);  // B half of tile kt+3
+        if (A_KMAJ && B_KMAJ) interleave_reads_mfma<RD, NM, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait(fa1, fb1);  // tile kt fully read: its stage may be overwritten
+        wait_vm<(STAGES - 2) * DPT>();  // tile kt+1 landed
+        workgroup_barrier();
+
+        // region B (the fragments read past the last tile are never used)
+        {
+            const char* sn = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
+            const lds_void* na = (const lds_void*)sn;
+            const lds_void* nb = (const lds_void*)(sn + TILE_BYTES);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i < MI) fa0[i] = frag_a(na, i, 0);
+                fb0[i] = frag_b(nb, i, 0);
+            }
+        }
+        dma_tile(kt + STAGES, SPLIT_DMA ? 0 : 2);  // into the stage tile kt vacated
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
+        if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, DPT, NM, 0>();
+    }
+    gemm_epilogue<A_KMAJ, B_KMAJ, EPI, TBM>(d, sp, acc, m0, n0, smem);
+}
+
+// ---- both operands K-contiguous: 64-k parts in a ring of five -------------
+// A 32-k K-contiguous tile row is a 64-byte segment, half a cache line, and
+// its DMA keeps the address unit waiting on the vector L1.  With both
+// operands K-contiguous the k-tile is 64 deep instead: each operand's part
+// of a k-tile (rows x 128 bytes) fills whole lines, and the parts sit in a
+// ring of five 32 KB LDS slots (part p, the A (p even) or B (p odd) half of
+// k-tile p/2, in slot p % 5), so three parts are in flight while a k-tile is
+// multiplied, about the prefetch depth of four 32-k stages.
+// Swizzle of the 16-byte chunks of a 128-byte row (conflict-free b128 reads).
+__device__ __forceinline__ int key8(int row) { return (row >> 1) & 7; }
+
+// Instruction i of wave w covers part rows 8b..8b+7 (b = 4i + w); NI = 8:
+// 256 rows, NI = 4: 128 rows.
+template <bool PAIRED, int NI>
+__device__ __forceinline__ void dma_offsets_k64(uint32_t (&off)[NI], int64_t ld, int row0, int rows_total, int half_n,
+                                                int k_lim, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int b = i * 4 + wave;
+        const int r = b * 8 + (lane >> 3);
+        const int kc = (lane & 7) ^ key8(r);
+        int grow;
+        bool ok;
+        if (PAIRED) {
+            const int rr = row0 + (r & 127);
+            ok = rr < half_n;
+            grow = (r < 128) ? rr : half_n + rr;
+        } else {
+            grow = row0 + r;
+            ok = grow < rows_total;
+        }
+        off[i] = (ok && kc * 8 < k_lim) ? (uint32_t)(((int64_t)grow * ld + kc * 8) * 2) : OOB;
+    }
+}
+
+template <int NI>
+__device__ __forceinline__ void dma_issue_n(__amdgpu_buffer_rsrc_t rs, lds_void* tile, const uint32_t (&off)[NI],
+                                            int wave) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma_issue_one(rs, tile, off[i], i * 4 + wave);
+}
+
+__device__ __forceinline__ bf16x8 frag_k64(const lds_void* tile, int row, int kk, int g) {
+    const int chunk = (kk * 2 + g) ^ key8(row);
+    return *(const lds_bf16x8*)((const __attribute__((address_space(3))) char*)tile + row * 128 + chunk * 16);
+}
+
+constexpr int BK64 = 64, PART_BYTES = 32768, NSLOT = 5;
+
+template <int EPI, int TBM>
+__device__ __forceinline__ void gemm_kk64_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
+    constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
+    constexpr int MI = TBM / 64;
+    constexpr int NA = TBM / 32, NB = 8;  // DMA instructions per wave per part
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int g = lane >> 5, lrow = lane & 31;
+    const int m0 = tm * TBM;
+    const int n0 = PAIRED ? tn * (BN / 2) : tn * BN;
+    const int nk = (d.K + BK64 - 1) / BK64;
+    const int k_tail = d.K - (nk - 1) * BK64;  // k extent of the last k-tile (1..64)
+
+    uint32_t offa[NA], offb[NB], offa_t[NA], offb_t[NB];  // full k-tiles, and the last one
+    dma_offsets_k64<false, NA>(offa, d.lda, m0, d.M, 0, BK64, lane, wave);
+    dma_offsets_k64<false, NA>(offa_t, d.lda, m0, d.M, 0, k_tail, lane, wave);
+    dma_offsets_k64<PAIRED, NB>(offb, d.ldb, n0, d.N, d.half_n, BK64, lane, wave);
+    dma_offsets_k64<PAIRED, NB>(offb_t, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
+    // Part p of the sequence; parts past the last k-tile get an empty range
+    // (zeros, nothing fetched) so every iteration issues the same loads.
+    auto dma_part = [&](int p) {
+        const int kt = p >> 1;
+        char* dst = smem + (p % NSLOT) * PART_BYTES;
+        const bool live = kt < nk, tail = kt == nk - 1;
+        const uint32_t adv = live ? (uint32_t)(kt * BK64 * 2) : 0u;
+        if ((p & 1) == 0) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(d.A) + adv, live ? sp.a - adv : 0u);
+            uint32_t t[NA];
+#pragma unroll
+            for (int i = 0; i < NA; ++i) t[i] = tail ? offa_t[i] : offa[i];
+            dma_issue_n<NA>(rs, (lds_void*)dst, t, wave);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(d.B) + adv, live ? sp.b - adv : 0u);
+            uint32_t t[NB];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) t[i] = tail ? offb_t[i] : offb[i];
+            dma_issue_n<NB>(rs, (lds_void*)dst, t, wave);
+        }
+    };
+
+    floatx16 acc[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    auto frag_a = [&](const lds_void* ta, int mi, int kk) -> bf16x8 {
+        return frag_k64(ta, wm * (TBM / 2) + mi * 32 + lrow, kk, g);
+    };
+    auto frag_b = [&](const lds_void* tb, int ni, int kk) -> bf16x8 {
+        const int row = PAIRED ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + lrow) : (wn * 128 + ni * 32 + lrow);
+        return frag_k64(tb, row, kk, g);
+    };
+    constexpr int RD = MI + 4;  // LDS reads per 16-k step
+    constexpr int NM = MI * 4;  // MFMAs per 16-k step
+
+    // Iteration kt multiplies the four 16-k steps of k-tile kt, each while
+    // the next step's fragments are read.  Before the last step every read
+    // of kt has completed and k-tile kt+1 has landed (the A part of kt+2 may
+    // still be in flight), then a barrier; during the last step the first
+    // fragments of kt+1 are read and parts 2kt+5, 2kt+6 go into the two
+    // slots kt vacated.
+#pragma unroll
+    for (int p = 0; p < NSLOT; ++p) dma_part(p);
+    wait_vm<2 * NA + NB>();  // parts 0 and 1 (k-tile 0) landed
+    workgroup_barrier();
+    bf16x8 fa0[MI], fb0[4], fa1[MI], fb1[4];
+    {
+        const lds_void* ta = (const lds_void*)smem;
+        const lds_void* tb = (const lds_void*)(smem + PART_BYTES);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < MI) fa0[i] = frag_a(ta, i, 0);
+            fb0[i] = frag_b(tb, i, 0);
+        }
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const lds_void* ta = (const lds_void*)(smem + ((2 * kt) % NSLOT) * PART_BYTES);
+        const lds_void* tb = (const lds_void*)(smem + ((2 * kt + 1) % NSLOT) * PART_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < 3; ++st) {
+            bf16x8(&ca)[MI] = (st & 1) ? fa1 : fa0;
+            bf16x8(&cb)[4] = (st & 1) ? fb1 : fb0;
+            bf16x8(&na)[MI] = (st & 1) ? fa0 : fa1;
+            bf16x8(&nb)[4] = (st & 1) ? fb0 : fb1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i < MI) na[i] = frag_a(ta, i, st + 1);
+                nb[i] = frag_b(tb, i, st + 1);
+            }
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[mi], cb[ni], acc[mi][ni], 0, 0, 0);
+            interleave_reads_mfma<RD, NM, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_wait(fa1, fb1);  // every read of k-tile kt has completed: its slots may be overwritten
+        wait_vm<NA>();       // k-tile kt+1 landed
+        workgroup_barrier();
+        {
+            const lds_void* na = (const lds_void*)(smem + ((2 * kt + 2) % NSLOT) * PART_BYTES);
+            const lds_void* nb = (const lds_void*)(smem + ((2 * kt + 3) % NSLOT) * PART_BYTES);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i < MI) fa0[i] = frag_a(na, i, 0);
+                fb0[i] = frag_b(nb, i, 0);
+            }
+        }
+        dma_part(2 * kt + 5);
+        dma_part(2 * kt + 6);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
+        interleave_reads_dma_mfma<RD, NA + NB, NM, 0>();
+    }
+    gemm_epilogue<true, true, EPI, TBM>(d, sp, acc, m0, n0, smem);
+}
+
+// LDS of one workgroup: five 32 KB slots for both-K-contiguous products,
+// four 32 KB stages otherwise (the epilogue reuses the first 68 KB).
+template <bool A_KMAJ, bool B_KMAJ>
+constexpr int gemm_lds_bytes() { return (A_KMAJ && B_KMAJ) ? NSLOT * PART_BYTES : STAGES * STAGE_BYTES; }
+
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
+__device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
+    if constexpr (A_KMAJ && B_KMAJ) gemm_kk64_tile<EPI, TBM>(d, tm, tn, sp, smem);
+    else gemm_v2_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn, sp, smem);
+}
+
 // Tiles (tm, tn_base + tn) for tm < tiles_m, tn < tiles_n, of height TBM.
 template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
 __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, int tn_base,
                                                        BufSpans sp) {
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[gemm_lds_bytes<A_KMAJ, B_KMAJ>()];
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn_base + tn, sp, smem);
+    gemm_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn_base + tn, sp, smem);
 }
 
 // Up to GROUP_MAX independent products of one layout and epilogue in one
@@ -612,7 +812,7 @@ static_assert(sizeof(GemmGroup) <= 3072, "kernel argument block");
 
 template <bool A_KMAJ, bool B_KMAJ, int EPI>
 __global__ __launch_bounds__(NTHR) void gemm_v2_group_kernel(GemmGroup grp) {
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[gemm_lds_bytes<A_KMAJ, B_KMAJ>()];
     const int bid = blockIdx.x;
     int g = 0;
     while (g + 1 < grp.n && bid >= grp.off[g + 1]) ++g;
@@ -624,7 +824,7 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_group_kernel(GemmGroup grp) {
     tile_of(local, grp.tiles_m[g], grp.tiles_n[g], tm, tn);
     const GemmDesc d = grp.d[g];  // a value copy: its fields stay in scalar registers
     const BufSpans sp = grp.sp[g];
-    gemm_v2_tile<A_KMAJ, B_KMAJ, EPI, BM>(d, tm, tn, sp, smem);
+    gemm_tile<A_KMAJ, B_KMAJ, EPI, BM>(d, tm, tn, sp, smem);
 }
 
 template <bool AK, bool BKM, int TBM>
