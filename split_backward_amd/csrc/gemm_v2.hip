@@ -601,14 +601,15 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     gemm_epilogue<A_KMAJ, B_KMAJ, EPI, TBM>(d, sp, acc, m0, n0, smem);
 }
 
-// ---- both operands K-contiguous: 64-k parts in a ring of five -------------
+// ---- K-contiguous A: 64-k parts in a ring of five --------------------------
 // A 32-k K-contiguous tile row is a 64-byte segment, half a cache line, and
-// its DMA keeps the address unit waiting on the vector L1.  With both
-// operands K-contiguous the k-tile is 64 deep instead: each operand's part
-// of a k-tile (rows x 128 bytes) fills whole lines, and the parts sit in a
-// ring of five 32 KB LDS slots (part p, the A (p even) or B (p odd) half of
-// k-tile p/2, in slot p % 5), so three parts are in flight while a k-tile is
-// multiplied, about the prefetch depth of four 32-k stages.
+// its DMA keeps the address unit waiting on the vector L1.  With a
+// K-contiguous A (the F and B passes) the k-tile is 64 deep instead: a
+// K-contiguous part of a k-tile (rows x 128 bytes) fills whole lines (an
+// M/N-contiguous part is 64 rows of 512 bytes).  The parts sit in a ring of
+// five 32 KB LDS slots (part p, the A (p even) or B (p odd) half of k-tile
+// p/2, in slot p % 5), so about three parts are in flight while a k-tile is
+// multiplied, the prefetch depth of four 32-k stages.
 // Swizzle of the 16-byte chunks of a 128-byte row (conflict-free b128 reads).
 __device__ __forceinline__ int key8(int row) { return (row >> 1) & 7; }
 
@@ -650,8 +651,20 @@ __device__ __forceinline__ bf16x8 frag_k64(const lds_void* tile, int row, int kk
 
 constexpr int BK64 = 64, PART_BYTES = 32768, NSLOT = 5;
 
-template <int EPI, int TBM>
-__device__ __forceinline__ void gemm_kk64_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
+__device__ __forceinline__ void dma_offsets_mn64(uint32_t (&off)[8], int64_t ld, int col0, int cols_total, int lane,
+                                                 int wave) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int b = i * 4 + wave;
+        const int k = b * 2 + (lane >> 5);
+        const int piece = ((lane & 31) >> 1) ^ key_mn(k);
+        const int col = piece * 16 + (lane & 1) * 8;
+        const int gc = col0 + col;
+        off[i] = (gc < cols_total) ? (uint32_t)(((int64_t)k * ld + gc) * 2) : OOB;
+    }
+}
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
+__device__ __forceinline__ void gemm_64_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
     constexpr int MI = TBM / 64;
     constexpr int NA = TBM / 32, NB = 8;  // DMA instructions per wave per part
@@ -664,28 +677,39 @@ __device__ __forceinline__ void gemm_kk64_tile(const GemmDesc& d, int tm, int tn
     const int k_tail = d.K - (nk - 1) * BK64;  // k extent of the last k-tile (1..64)
 
     uint32_t offa[NA], offb[NB], offa_t[NA], offb_t[NB];  // full k-tiles, and the last one
-    dma_offsets_k64<false, NA>(offa, d.lda, m0, d.M, 0, BK64, lane, wave);
-    dma_offsets_k64<false, NA>(offa_t, d.lda, m0, d.M, 0, k_tail, lane, wave);
-    dma_offsets_k64<PAIRED, NB>(offb, d.ldb, n0, d.N, d.half_n, BK64, lane, wave);
-    dma_offsets_k64<PAIRED, NB>(offb_t, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
+    if constexpr (A_KMAJ) {
+        dma_offsets_k64<false, NA>(offa, d.lda, m0, d.M, 0, BK64, lane, wave);
+        dma_offsets_k64<false, NA>(offa_t, d.lda, m0, d.M, 0, k_tail, lane, wave);
+    } else {
+        dma_offsets_mn64(offa, d.lda, m0, d.M, lane, wave);
+    }
+    if constexpr (B_KMAJ) {
+        dma_offsets_k64<PAIRED, NB>(offb, d.ldb, n0, d.N, d.half_n, BK64, lane, wave);
+        dma_offsets_k64<PAIRED, NB>(offb_t, d.ldb, n0, d.N, d.half_n, k_tail, lane, wave);
+    } else {
+        dma_offsets_mn64(offb, d.ldb, n0, d.N, lane, wave);
+    }
+    const int64_t step_a = A_KMAJ ? BK64 * 2 : (int64_t)BK64 * d.lda * 2;
+    const int64_t step_b = B_KMAJ ? BK64 * 2 : (int64_t)BK64 * d.ldb * 2;
     // Part p of the sequence; parts past the last k-tile get an empty range
     // (zeros, nothing fetched) so every iteration issues the same loads.
     auto dma_part = [&](int p) {
         const int kt = p >> 1;
         char* dst = smem + (p % NSLOT) * PART_BYTES;
         const bool live = kt < nk, tail = kt == nk - 1;
-        const uint32_t adv = live ? (uint32_t)(kt * BK64 * 2) : 0u;
         if ((p & 1) == 0) {
+            const uint32_t adv = live ? (uint32_t)(kt * step_a) : 0u;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(d.A) + adv, live ? sp.a - adv : 0u);
             uint32_t t[NA];
 #pragma unroll
-            for (int i = 0; i < NA; ++i) t[i] = tail ? offa_t[i] : offa[i];
+            for (int i = 0; i < NA; ++i) t[i] = (A_KMAJ && tail) ? offa_t[i] : offa[i];
             dma_issue_n<NA>(rs, (lds_void*)dst, t, wave);
         } else {
+            const uint32_t adv = live ? (uint32_t)(kt * step_b) : 0u;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(d.B) + adv, live ? sp.b - adv : 0u);
             uint32_t t[NB];
 #pragma unroll
-            for (int i = 0; i < NB; ++i) t[i] = tail ? offb_t[i] : offb[i];
+            for (int i = 0; i < NB; ++i) t[i] = (B_KMAJ && tail) ? offb_t[i] : offb[i];
             dma_issue_n<NB>(rs, (lds_void*)dst, t, wave);
         }
     };
@@ -698,24 +722,32 @@ __device__ __forceinline__ void gemm_kk64_tile(const GemmDesc& d, int tm, int tn
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     auto frag_a = [&](const lds_void* ta, int mi, int kk) -> bf16x8 {
-        return frag_k64(ta, wm * (TBM / 2) + mi * 32 + lrow, kk, g);
+        if constexpr (A_KMAJ) return frag_k64(ta, wm * (TBM / 2) + mi * 32 + lrow, kk, g);
+        else return frag_mnmaj(ta, wm * 4 + mi, kk, lane);
     };
     auto frag_b = [&](const lds_void* tb, int ni, int kk) -> bf16x8 {
-        const int row = PAIRED ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + lrow) : (wn * 128 + ni * 32 + lrow);
-        return frag_k64(tb, row, kk, g);
+        if constexpr (B_KMAJ) {
+            const int row = PAIRED ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + lrow) : (wn * 128 + ni * 32 + lrow);
+            return frag_k64(tb, row, kk, g);
+        } else {
+            return frag_mnmaj(tb, wn * 4 + ni, kk, lane);
+        }
     };
-    constexpr int RD = MI + 4;  // LDS reads per 16-k step
+    constexpr bool KK = A_KMAJ && B_KMAJ;
+    constexpr int RD = MI * (A_KMAJ ? 1 : 2) + 4 * (B_KMAJ ? 1 : 2);  // LDS reads per 16-k step
     constexpr int NM = MI * 4;  // MFMAs per 16-k step
 
     // Iteration kt multiplies the four 16-k steps of k-tile kt, each while
-    // the next step's fragments are read.  Before the last step every read
-    // of kt has completed and k-tile kt+1 has landed (the A part of kt+2 may
-    // still be in flight), then a barrier; during the last step the first
-    // fragments of kt+1 are read and parts 2kt+5, 2kt+6 go into the two
-    // slots kt vacated.
+    // the next step's fragments are read.  During step 0 the A part of
+    // k-tile kt+2 goes into the slot k-tile kt-1's B part left.  Before the
+    // last step every read of kt has completed and k-tile kt+1 has landed
+    // (the A part of kt+2 may still be in flight), then a barrier; during the
+    // last step the first fragments of kt+1 are read and the B part of kt+2
+    // goes into the slot kt's A part left.  Splitting the two parts' DMA
+    // between steps 3 and 0 spreads the address unit's work.
 #pragma unroll
-    for (int p = 0; p < NSLOT; ++p) dma_part(p);
-    wait_vm<2 * NA + NB>();  // parts 0 and 1 (k-tile 0) landed
+    for (int p = 0; p < NSLOT - 1; ++p) dma_part(p);
+    wait_vm<NA + NB>();  // parts 0 and 1 (k-tile 0) landed
     workgroup_barrier();
     bf16x8 fa0[MI], fb0[4], fa1[MI], fb1[4];
     {
@@ -737,17 +769,23 @@ __device__ __forceinline__ void gemm_kk64_tile(const GemmDesc& d, int tm, int tn
             bf16x8(&cb)[4] = (st & 1) ? fb1 : fb0;
             bf16x8(&na)[MI] = (st & 1) ? fa0 : fa1;
             bf16x8(&nb)[4] = (st & 1) ? fb0 : fb1;
+            if constexpr (!KK) lds_wait(ca, cb);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (i < MI) na[i] = frag_a(ta, i, st + 1);
                 nb[i] = frag_b(tb, i, st + 1);
             }
+            if constexpr (!KK) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[mi], cb[ni], acc[mi][ni], 0, 0, 0);
-            interleave_reads_mfma<RD, NM, 0>();
+            if (st == 0) dma_part(2 * kt + 4);  // the A part of k-tile kt+2, into the slot kt-1's B part left
+            if constexpr (KK) {
+                if (st == 0) interleave_reads_dma_mfma<RD, NA, NM, 0>();
+                else interleave_reads_mfma<RD, NM, 0>();
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         lds_wait(fa1, fb1);  // every read of k-tile kt has completed: its slots may be overwritten
@@ -762,26 +800,28 @@ __device__ __forceinline__ void gemm_kk64_tile(const GemmDesc& d, int tm, int tn
                 fb0[i] = frag_b(nb, i, 0);
             }
         }
-        dma_part(2 * kt + 5);
-        dma_part(2 * kt + 6);
+        dma_part(2 * kt + 5);  // the B part of k-tile kt+2, into the slot kt's A part left
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
-        interleave_reads_dma_mfma<RD, NA + NB, NM, 0>();
+        if constexpr (KK) interleave_reads_dma_mfma<RD, NB, NM, 0>();
     }
-    gemm_epilogue<true, true, EPI, TBM>(d, sp, acc, m0, n0, smem);
+    gemm_epilogue<A_KMAJ, B_KMAJ, EPI, TBM>(d, sp, acc, m0, n0, smem);
 }
 
-// LDS of one workgroup: five 32 KB slots for both-K-contiguous products,
-// four 32 KB stages otherwise (the epilogue reuses the first 68 KB).
+// LDS of one workgroup: five 32 KB slots for products with a K-contiguous A
+// (64-k parts), four 32 KB stages otherwise (the epilogue reuses the first
+// 68 KB).
 template <bool A_KMAJ, bool B_KMAJ>
-constexpr int gemm_lds_bytes() { return (A_KMAJ && B_KMAJ) ? NSLOT * PART_BYTES : STAGES * STAGE_BYTES; }
+constexpr int gemm_lds_bytes() { return A_KMAJ ? NSLOT * PART_BYTES : STAGES * STAGE_BYTES; }
 
+// Products with a K-contiguous A (the F and B passes) run on 64-k parts;
+// those with an M/N-contiguous A (the W pass) measured faster on 32-k tiles.
 template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
-    if constexpr (A_KMAJ && B_KMAJ) gemm_kk64_tile<EPI, TBM>(d, tm, tn, sp, smem);
+    if constexpr (A_KMAJ) gemm_64_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn, sp, smem);
     else gemm_v2_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn, sp, smem);
 }
 
