@@ -22,6 +22,8 @@ Extra fields on the JSON line:
 * executor_p8_stage3: the stage replayed with emulated arrivals (device-clock
   waits) for the 1F1B and zero-bubble orders; in-window idle of each, beside
   the simulator's prediction (see executor_idle).
+* memory_limit_sweep_p8_stage3: ZB(M) for M = 8 .. 16 replayed the same way,
+  with the stash each order keeps resident at its peak (memory_limit_sweep).
 """
 from __future__ import annotations
 
@@ -253,6 +255,7 @@ def executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w):
             ("zb_M16_u1.1", "zb", 16, (1, 1, 1), 1.1 * unit),
             ("1f1b_measured_costs", "1f1b", 0, mc, q), ("zb_M16_measured_costs", "zb", 16, mc, q),
             ("zb_M16_measured_costs_filler", "zb", 16, mc, q)]
+    runs.insert(5, ("zb_M16_filler", "zb", 16, (1, 1, 1), unit))
     out = {"unit_ms": round(unit, 3), "measured_costs_0.1ms": mc}
     for name, kind, M, costs, u in runs:
         if M > stage.desc.ring_slots:
@@ -268,6 +271,31 @@ def executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w):
                      "predicted_in_window_idle": round(1 - g["busy"] / win, 5),
                      "predicted_stage_end_ms": round(g["last_end"] * u, 2)}
     return out
+
+
+def memory_limit_sweep(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3):
+    """ZB(M) for M = p .. 2p on the GPU (ordered replay, arrivals at costs
+    1:1:1 in units of the mean pass time): measured in-window idle and stage
+    end beside the simulator's, and the stash the order keeps resident at
+    its peak (peak in-flight microbatches x bytes per ring slot)."""
+    import torch
+    import split_backward_amd as zb
+    slot = stage.slot_bytes()
+    rows = []
+    for M in range(p, 2 * p + 1):
+        if M > stage.desc.ring_slots:
+            break
+        g = zb.schedule_generate("zb", p, m, M, (1, 1, 1), stage_idx)
+        stage.zero_grad()
+        torch.cuda.synchronize()
+        r = stage.run_schedule(g["ops"], g["arrive_f"], g["arrive_b"], unit, xs, ys, dys, dxs, mode=zb.EXEC_ORDERED)
+        win = g["last_end"] - g["first_start"]
+        rows.append({"M": M, "in_window_idle": round(r["in_window_idle"], 5),
+                     "predicted_in_window_idle": round(1 - g["busy"] / win, 5),
+                     "stage_end_ms": round(r["t_last_end_ms"], 2), "predicted_stage_end_ms": round(g["last_end"] * unit, 2),
+                     "peak_resident_microbatches": g["peak_active"],
+                     "stash_GiB": round(g["peak_active"] * slot / 2**30, 2)})
+    return {"unit_ms": round(unit, 3), "slot_GiB": round(slot / 2**30, 3), "runs": rows}
 
 
 def main():
@@ -344,6 +372,7 @@ def main():
     extra = {}
     if shape.kind == "llama" and not args.no_executor:
         extra["executor_p8_stage3"] = executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w)
+        extra["memory_limit_sweep_p8_stage3"] = memory_limit_sweep(stage, m, xs, ys, dys, dxs, (t_f + t_b + t_w) / 3.0)
     cpu = None if args.no_cpu_baseline else cpu_baseline(shape)
 
     line = {

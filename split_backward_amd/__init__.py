@@ -219,6 +219,14 @@ class Stage:
             lib().zb_stage_destroy(h)
             self.handle = None
 
+    def slot_bytes(self) -> int:
+        """Bytes of one stash-ring slot (one microbatch's F and B stash):
+        the workspace size's growth per added slot."""
+        L = lib()
+        d1, d2 = StageDesc.from_buffer_copy(self.desc), StageDesc.from_buffer_copy(self.desc)
+        d1.ring_slots, d2.ring_slots = 1, 2
+        return int(L.zb_stage_workspace_bytes(ctypes.byref(d2)) - L.zb_stage_workspace_bytes(ctypes.byref(d1)))
+
     @property
     def act_dtype(self):
         return self.torch.bfloat16 if self.dtype == "bf16" else self.torch.float32

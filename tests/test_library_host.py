@@ -105,6 +105,33 @@ def test_workspace_sizes_and_weight_counts():
     assert L.zb_stage_workspace_bytes(ctypes.byref(lin)) >= 2 * (128 * 256 * 4 * 2)
 
 
+def test_workspace_grows_by_one_slot_per_ring_slot():
+    """The workspace is the stash ring plus fixed scratch, so its size is
+    affine in ring_slots; the bench's stash figures (peak resident
+    microbatches x slot bytes) rely on it."""
+    L = zb.lib()
+    for kw in (dict(), dict(kind=zb.MLP_GELU, n_layers=1, tokens=2048, hidden=1024, ffn=4096),
+               dict(n_layers=2, hidden=8192, ffn=28672, n_heads=64, n_kv_heads=8)):
+        sizes = [L.zb_stage_workspace_bytes(ctypes.byref(_desc(ring_slots=r, **kw))) for r in range(1, 6)]
+        steps = {b - a for a, b in zip(sizes, sizes[1:])}
+        assert len(steps) == 1, kw
+        slot = steps.pop()
+        d = _desc(**kw)
+        T, h, f = d.tokens, d.hidden, d.ffn
+        if d.kind == zb.LLAMA:
+            # per layer, bf16: the F stash x, n1, q|k|v, attention output, h1,
+            # n2, g|u, s and the B stash d_out, dg|du, dn2, dh1, dq|dk|dv,
+            # dn1; fp32: two rms factors per token and the attention lse per
+            # head and token; each tensor 256-byte aligned
+            qd, qkv = d.n_heads * d.head_dim, (d.n_heads + 2 * d.n_kv_heads) * d.head_dim
+            bf16 = d.n_layers * 2 * T * (8 * h + qd + 2 * qkv + 5 * f)
+            f32 = d.n_layers * 4 * T * (2 + d.n_heads)
+            assert bf16 + f32 <= slot < bf16 + f32 + d.n_layers * 17 * 256, kw
+        else:
+            # x, a, gelu(a), dy, da in bf16
+            assert 2 * T * (2 * h + 3 * f) <= slot < 2 * T * (2 * h + 3 * f) + 5 * 256, kw
+
+
 @pytest.mark.parametrize("bad", [dict(head_dim=64), dict(n_kv_heads=5), dict(ring_slots=0), dict(hidden=4100),
                                  dict(dtype=zb.F32), dict(tokens=0), dict(kind=7)])
 def test_invalid_descs_rejected(bad):
