@@ -6,7 +6,8 @@ A step is one whole iteration of the stage's hot path over one batch: the
 dW buffers are cleared, then F, B and W run for every microbatch in the
 zero-bubble order (memory limit 2p) that the library's generator produces
 for stage 3 of an emulated 8-stage pipeline, back to back on one stream with
-all inputs already in HBM.  `value` = linear-layer FLOPs of F + B + W
+all inputs already in HBM.  Adjacent W(j), W(j+1) of the order run as one W
+pass over both microbatches (--no-w-pairs: each on its own).  `value` = linear-layer FLOPs of F + B + W
 (2*M*N*K per product, attention and RMSNorm excluded from the count but not
 from the time) / wall time of the step; `tflops_incl_attention` adds the
 causal attention core's algorithmic flops to the numerator.
@@ -306,6 +307,8 @@ def main():
     ap.add_argument("--workload", default="llama7b_stage4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-executor", action="store_true")
+    ap.add_argument("--no-w-pairs", action="store_true",
+                    help="issue every W on its own instead of pairing adjacent W(j), W(j+1)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the copy + W-kernel workload that the --pmc passes count")
     args = ap.parse_args()
@@ -334,13 +337,29 @@ def main():
     # zero-bubble order of stage 3 in an emulated 8-stage pipeline, memory limit min(2p, ring)
     order = zb.schedule_generate("zb", 8, m, min(16, ring), (1, 1, 1), 3)["ops"]
 
+    # Adjacent W(j), W(j+1) of the order run as one pass over both
+    # microbatches (zb_bwd_weight_accum_pair): the same work in the same
+    # order, with one fp32 read-modify-write of dW for the two.
+    plan, i = [], 0
+    while i < len(order):
+        t, j = order[i]
+        if t == "W" and not args.no_w_pairs and i + 1 < len(order) and order[i + 1] == ("W", j + 1):
+            plan.append(("P", j))
+            i += 2
+        else:
+            plan.append((t, j))
+            i += 1
+    w_pairs = sum(1 for t, _ in plan if t == "P")
+
     def step():
         stage.zero_grad()
-        for t, j in order:
+        for t, j in plan:
             if t == "F":
                 stage.fwd(j, xs[j], ys[j])
             elif t == "B":
                 stage.bwd_input(j, dys[j], dxs[j])
+            elif t == "P":
+                stage.bwd_weight_pair(j)
             else:
                 stage.bwd_weight(j)
 
@@ -382,7 +401,8 @@ def main():
         "dtype": shape.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "tokens": shape.tokens, "hidden": shape.hidden, "ffn": shape.ffn,
                    "n_layers": shape.n_layers, "n_heads": shape.n_heads, "n_kv_heads": shape.n_kv_heads,
-                   "microbatches": m, "ring_slots": ring, "order": "zero-bubble greedy, M=min(16, ring), stage 3 of p=8"},
+                   "microbatches": m, "ring_slots": ring, "order": "zero-bubble greedy, M=min(16, ring), stage 3 of p=8",
+                   "w_pairs": w_pairs},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops_incl_attention": round((flops + attention_flops_per_mb(shape) * m) / dt / 1e12, 2),
         "pass_ms": {"F": round(t_f, 3), "B": round(t_b, 3), "W": round(t_w, 3)},

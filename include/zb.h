@@ -128,6 +128,23 @@ int32_t zb_bwd_input(zb_stage* st, int32_t mb, const void* dy, void* dx, void* s
  * the next W in ascending order. */
 int32_t zb_bwd_weight_accum(zb_stage* st, int32_t mb, void* stream);
 
+/* W for microbatches mb and mb + 1 in one pass.  The weight-gradient pass is
+ * deferrable and needs only the stashed activations and output gradients
+ * (Guide, "Core Innovation 1": the weight gradient does not feed any other
+ * computation), so two ready microbatches may be combined: each product runs
+ * once with K spanning both microbatches' tokens, and dW is read and written
+ * once for the pair instead of twice.  Mathematically equal to
+ * zb_bwd_weight_accum(mb) then zb_bwd_weight_accum(mb + 1); the fp32
+ * rounding differs (the two microbatches' contributions are summed before
+ * they are added to dW), within 1e-5 relative.  RMSNorm dgamma is reduced per
+ * microbatch exactly as by two W calls.  Frees both ring slots once the
+ * device work has completed.  Stages whose products cannot take the
+ * two-segment kernel (fp32 linear stages, tokens not a multiple of 32) run
+ * it as the two single calls.
+ * Errors: ZB_ESTATE unless B was issued and W was not for both microbatches,
+ * or mb is not the next W in ascending order. */
+int32_t zb_bwd_weight_accum_pair(zb_stage* st, int32_t mb, void* stream);
+
 /* Set every dW buffer to 0 (a fill kernel on stream) and reset the
  * microbatch counters for a new iteration.  Errors: ZB_ESTATE if a
  * microbatch is still in flight (F issued, W not). */

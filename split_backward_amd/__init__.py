@@ -72,6 +72,7 @@ _PROTOS = {
     "zb_fwd": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "zb_bwd_input": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "zb_bwd_weight_accum": (_i32, [_vp, _i32, _vp]),
+    "zb_bwd_weight_accum_pair": (_i32, [_vp, _i32, _vp]),
     "zb_stage_zero_grad": (_i32, [_vp, _vp]),
     "zb_stage_stash_tensor": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
                                      ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
@@ -249,6 +250,10 @@ class Stage:
 
     def bwd_weight(self, mb: int, stream=None):
         check(lib().zb_bwd_weight_accum(self.handle, mb, _stream_ptr(stream)))
+
+    def bwd_weight_pair(self, mb: int, stream=None):
+        """W for microbatches mb and mb + 1 in one pass (zb_bwd_weight_accum_pair)."""
+        check(lib().zb_bwd_weight_accum_pair(self.handle, mb, _stream_ptr(stream)))
 
     def zero_grad(self, stream=None):
         check(lib().zb_stage_zero_grad(self.handle, _stream_ptr(stream)))

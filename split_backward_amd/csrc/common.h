@@ -56,6 +56,14 @@ struct GemmDesc {
     const void* R; int64_t ldr;                // residual / stash operand of the epilogue
     void* C2; int64_t ldc2;                    // second output of the epilogue
     int half_n;                                // EPI_SWIGLU_*: width of g (= ffn)
+    // Second K segment (W over two microbatches): with K1 > 0, k < K1 reads
+    // A and B and k >= K1 reads A2 and B2 at row k - K1 (same leading
+    // dimensions, K = 2 * K1).  Only the grouped direct-to-LDS kernel with
+    // both operands M/N-contiguous and EPI_ACCUM_F32 takes it
+    // (gemm_bf16_group_segmented); every other path rejects K1 != 0.
+    int K1;
+    const void* A2;
+    const void* B2;
 };
 
 int32_t gemm_bf16(const GemmDesc& d, hipStream_t s);
@@ -67,6 +75,12 @@ int32_t gemm_f32(const GemmDesc& d, int accumulate, hipStream_t s);
 // n independent products of one layout and epilogue in a single launch when
 // every one fits the direct-to-LDS kernel (else one gemm_bf16 each).
 int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s);
+// The same for products with a second K segment (K1 > 0).  Launches nothing
+// and sets *handled = false unless every product fits one grouped launch of
+// the direct-to-LDS kernel (both operands M/N-contiguous, EPI_ACCUM_F32,
+// K = 2 * K1, K1 a multiple of 32); the caller then issues the segments as
+// separate products.
+int32_t gemm_bf16_group_segmented(const GemmDesc* ds, int n, hipStream_t s, bool* handled);
 
 // ------------------------------------------------- elementwise / norms ----
 int32_t fill_f32(float* p, size_t n, float v, hipStream_t s);

@@ -335,6 +335,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d, int accumulat
 
 int32_t gemm_bf16(const GemmDesc& d, hipStream_t s) {
     if (d.M <= 0 || d.N <= 0 || d.K <= 0) return fail(ZB_EINVAL, "gemm_bf16: empty shape");
+    if (d.K1 != 0) return fail(ZB_EINVAL, "gemm_bf16: a second K segment needs gemm_bf16_group_segmented");
     if (d.K % 8 || d.lda % 8 || d.ldb % 8) return fail(ZB_EINVAL, "gemm_bf16: K and leading dims must be multiples of 8");
     if ((!d.a_kmajor && d.M % 8) || (!d.b_kmajor && d.N % 8))
         return fail(ZB_EINVAL, "gemm_bf16: contiguous M/N extent must be a multiple of 8");
@@ -358,6 +359,7 @@ int32_t gemm_bf16(const GemmDesc& d, hipStream_t s) {
 
 int32_t gemm_f32(const GemmDesc& d, int accumulate, hipStream_t s) {
     if (d.M <= 0 || d.N <= 0 || d.K <= 0) return fail(ZB_EINVAL, "gemm_f32: empty shape");
+    if (d.K1 != 0) return fail(ZB_EINVAL, "gemm_f32: no second K segment");
     dim3 grid((d.N + FT - 1) / FT, (d.M + FT - 1) / FT), block(256);
     hipLaunchKernelGGL(gemm_f32_kernel, grid, block, 0, s, d, accumulate);
     ZB_HIP(hipGetLastError());

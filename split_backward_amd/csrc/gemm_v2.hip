@@ -445,6 +445,7 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     static_assert(TBM == BM || (TBM == BM / 2 && A_KMAJ), "half-height tiles need a K-contiguous A");
     constexpr int MI = TBM / 64;  // 32-row A fragments per wave; also A DMA instructions per wave
     constexpr int DPT = MI + 4;   // DMA instructions per wave per k-tile
+    constexpr bool SEGMENTED = !A_KMAJ && !B_KMAJ && EPI == EPI_ACCUM_F32;
 
     // wave index as a scalar: every LDS address derived from it (the DMA
     // destinations in M0) is then computed by scalar instructions.
@@ -465,17 +466,23 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
     const int64_t step_a = A_KMAJ ? BK * 2 : (int64_t)BK * d.lda * 2;
     const int64_t step_b = B_KMAJ ? BK * 2 : (int64_t)BK * d.ldb * 2;
 
+    // Two K segments (W over two microbatches): k-tiles from K1 / BK on come
+    // from A2 / B2.  K1 is a multiple of BK, so no k-tile straddles them.
+    const int nk1 = (SEGMENTED && d.K1 > 0) ? d.K1 / BK : nk;
+
     // part 0: the A tile only, 1: the B tile only, 2: both.
     auto dma_tile = [&](int kt, int part = 2) {
         char* st = smem + (kt % STAGES) * STAGE_BYTES;
         // A tile past the end of K gets an empty range: its loads read zeros,
         // fetch nothing, and keep the per-iteration DMA count uniform.
         const bool live = kt < nk;
-        const uint32_t adv_a = live ? (uint32_t)(kt * step_a) : 0u, adv_b = live ? (uint32_t)(kt * step_b) : 0u;
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(static_cast<const char*>(d.A) + adv_a, live ? sp.a - adv_a : 0u);
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(static_cast<const char*>(d.B) + adv_b, live ? sp.b - adv_b : 0u);
+        const bool seg2 = SEGMENTED && kt >= nk1;
+        const int ktl = seg2 ? kt - nk1 : kt;
+        const char* base_a = static_cast<const char*>(seg2 ? d.A2 : d.A);
+        const char* base_b = static_cast<const char*>(seg2 ? d.B2 : d.B);
+        const uint32_t adv_a = live ? (uint32_t)(ktl * step_a) : 0u, adv_b = live ? (uint32_t)(ktl * step_b) : 0u;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(base_a + adv_a, live ? sp.a - adv_a : 0u);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(base_b + adv_b, live ? sp.b - adv_b : 0u);
         if (kt == nk - 1 && k_tail < BK) {  // partial last tile: mask k >= K on K-contiguous operands
             uint32_t ta[MI], tb[4];
             if constexpr (A_KMAJ) dma_offsets_kmaj<false, MI>(ta, d.lda, m0, d.M, 0, k_tail, lane, wave);
@@ -902,8 +909,9 @@ struct V2Plan {
 V2Plan plan_v2(const GemmDesc& d) {
     V2Plan p{};
     const bool paired = d.epi == EPI_SWIGLU_FWD;
-    const uint64_t ab = d.a_kmajor ? span_bytes(d.M, d.lda, d.K) : span_bytes(d.K, d.lda, d.M);
-    const uint64_t bb = d.b_kmajor ? span_bytes(d.N, d.ldb, d.K) : span_bytes(d.K, d.ldb, d.N);
+    const int64_t krows = d.K1 > 0 ? d.K1 : d.K;  // k extent of one segment
+    const uint64_t ab = d.a_kmajor ? span_bytes(d.M, d.lda, d.K) : span_bytes(krows, d.lda, d.M);
+    const uint64_t bb = d.b_kmajor ? span_bytes(d.N, d.ldb, d.K) : span_bytes(krows, d.ldb, d.N);
     const bool has_r = d.epi == EPI_RESID || d.epi == EPI_GELU_BWD || d.epi == EPI_SWIGLU_BWD;
     const bool has_c2 = d.epi == EPI_GELU_FWD || paired;
     // Row widths touched by the epilogue: [g | u] and [dg | du] rows hold
@@ -1006,6 +1014,7 @@ int32_t launch_v2_split(const GemmDesc& d, hipStream_t s, const V2Plan& p) {
 
 int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
     *handled = false;
+    if (d.K1 != 0) return fail(ZB_EINVAL, "gemm: a second K segment needs gemm_bf16_group_segmented");
     const V2Plan p = plan_v2(d);
     if (!p.ok) return ZB_OK;  // caller uses the first-generation kernel
     *handled = true;
@@ -1015,8 +1024,35 @@ int32_t gemm_bf16_v2(const GemmDesc& d, hipStream_t s, bool* handled) {
     return launch_v2_split<false, true>(d, s, p);
 }
 
+int32_t gemm_bf16_group_segmented(const GemmDesc* ds, int n, hipStream_t s, bool* handled) {
+    *handled = false;
+    if (n <= 0 || n > GROUP_MAX || getenv("ZB_GEMM_V1")) return ZB_OK;
+    GemmGroup g{};
+    g.n = n;
+    g.off[0] = 0;
+    for (int i = 0; i < n; ++i) {
+        const GemmDesc& d = ds[i];
+        if (d.K1 <= 0 || d.K1 % BK != 0 || d.K != 2 * d.K1 || !d.A2 || !d.B2) return ZB_OK;
+        const V2Plan p = plan_v2(d);
+        const bool ok = p.ok && !d.a_kmajor && !d.b_kmajor && d.epi == EPI_ACCUM_F32 && d.M % 8 == 0 &&
+                        d.N % 8 == 0 && d.lda % 8 == 0 && d.ldb % 8 == 0 &&
+                        ((reinterpret_cast<uintptr_t>(d.A) | reinterpret_cast<uintptr_t>(d.B) |
+                          reinterpret_cast<uintptr_t>(d.A2) | reinterpret_cast<uintptr_t>(d.B2)) & 15) == 0;
+        if (!ok) return ZB_OK;
+        g.d[i] = d;
+        g.tiles_m[i] = p.tiles_m;
+        g.tiles_n[i] = p.tiles_n;
+        g.sp[i] = p.sp;
+        g.off[i + 1] = g.off[i] + ((p.tiles_m * p.tiles_n + 7) & ~7);
+    }
+    *handled = true;
+    return launch_group<false, false>(g, EPI_ACCUM_F32, s);
+}
+
 int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s) {
     if (n <= 0) return ZB_OK;
+    for (int i = 0; i < n; ++i)
+        if (ds[i].K1 != 0) return fail(ZB_EINVAL, "gemm: a second K segment needs gemm_bf16_group_segmented");
     bool grouped = n <= GROUP_MAX && getenv("ZB_GEMM_V1") == nullptr;
     GemmGroup g{};
     g.n = n;

@@ -210,4 +210,87 @@ int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s) {
     return ZB_OK;
 }
 
+// W for microbatches mb and mb + 1 together: each weight-gradient product
+// runs once with K spanning both microbatches' tokens (two K segments, one
+// per ring slot), so dW is read and written once for the pair.  When a
+// product cannot take the two-segment kernel the pair is issued as two
+// ordinary W passes.  The RMSNorm dgamma reductions run per microbatch, in
+// the same order as two W passes.
+int32_t run_backward_weight_pair(zb_stage& st, int mb, hipStream_t s) {
+    const zb_stage_desc& d = st.desc;
+    const int T = d.tokens, H = d.hidden, F = d.ffn;
+    std::vector<GemmDesc> g;
+    auto two = [&](GemmDesc a, const void* dy1, const void* x1) {
+        a.K = 2 * T;
+        a.K1 = T;
+        a.A2 = dy1;
+        a.B2 = x1;
+        g.push_back(a);
+    };
+    const int m1 = mb + 1;
+    if (d.kind == ZB_MLP_GELU && d.dtype == ZB_BF16) {
+        two(tn(F, H, T, st.slot_tensor(mb, 0, MLP_DA), F, st.slot_tensor(mb, 0, MLP_X), H, st.dw[0]),
+            st.slot_tensor(m1, 0, MLP_DA), st.slot_tensor(m1, 0, MLP_X));
+        two(tn(H, F, T, st.slot_tensor(mb, 0, MLP_DY), H, st.slot_tensor(mb, 0, MLP_H), F, st.dw[1]),
+            st.slot_tensor(m1, 0, MLP_DY), st.slot_tensor(m1, 0, MLP_H));
+    } else if (d.kind == ZB_LLAMA) {
+        const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
+        for (int l = 0; l < d.n_layers; ++l) {
+            float* const* dw = &st.dw[6 * l];
+            two(tn(QKV, H, T, st.slot_tensor(mb, l, L_DQKV), QKV, st.slot_tensor(mb, l, L_N1), H, dw[0]),
+                st.slot_tensor(m1, l, L_DQKV), st.slot_tensor(m1, l, L_N1));
+            two(tn(H, QD, T, st.slot_tensor(mb, l, L_DH1), H, st.slot_tensor(mb, l, L_A), QD, dw[1]),
+                st.slot_tensor(m1, l, L_DH1), st.slot_tensor(m1, l, L_A));
+            two(tn(2 * F, H, T, st.slot_tensor(mb, l, L_DGU), 2 * F, st.slot_tensor(mb, l, L_N2), H, dw[2]),
+                st.slot_tensor(m1, l, L_DGU), st.slot_tensor(m1, l, L_N2));
+            two(tn(H, F, T, st.slot_tensor(mb, l, L_DOUT), H, st.slot_tensor(mb, l, L_S), F, dw[3]),
+                st.slot_tensor(m1, l, L_DOUT), st.slot_tensor(m1, l, L_S));
+        }
+    }
+    // The products as segmented groups of at most 16; all must take that path.
+    constexpr int GROUP = 16;
+    bool handled = !g.empty();
+    for (size_t i = 0; i < g.size() && handled; i += GROUP) {
+        // probe each group before launching any, so a fallback issues nothing twice
+        const int n = (int)std::min<size_t>(GROUP, g.size() - i);
+        for (int j = 0; j < n && handled; ++j)
+            handled = g[i + j].K1 % 32 == 0 && g[i + j].M % 8 == 0 && g[i + j].N % 8 == 0;
+    }
+    if (!handled) {
+        ZB_TRY(run_backward_weight(st, mb, s));
+        return run_backward_weight(st, m1, s);
+    }
+    for (size_t i = 0; i < g.size(); i += GROUP) {
+        bool h = false;
+        ZB_TRY(gemm_bf16_group_segmented(&g[i], (int)std::min<size_t>(GROUP, g.size() - i), s, &h));
+        if (!h) {
+            // A group the segmented kernel did not take (operand spans beyond
+            // one buffer range): its products as one-segment products, per
+            // microbatch.
+            for (size_t j = i; j < std::min(g.size(), i + GROUP); ++j) {
+                GemmDesc a = g[j], b = g[j];
+                a.K = b.K = T;
+                a.K1 = b.K1 = 0;
+                a.A2 = a.B2 = b.A2 = b.B2 = nullptr;
+                b.A = g[j].A2;
+                b.B = g[j].B2;
+                ZB_TRY(gemm_bf16(a, s));
+                ZB_TRY(gemm_bf16(b, s));
+            }
+        }
+    }
+    if (d.kind == ZB_LLAMA) {
+        float* part = reinterpret_cast<float*>(st.scratch_w);
+        for (int m : {mb, m1})
+            for (int l = 0; l < d.n_layers; ++l) {
+                float* const* dw = &st.dw[6 * l];
+                ZB_TRY(rmsnorm_dgamma(cbf(st.slot_tensor(m, l, L_X)), static_cast<const float*>(st.slot_tensor(m, l, L_R1)),
+                                      cbf(st.slot_tensor(m, l, L_DN1)), dw[4], part, T, H, s));
+                ZB_TRY(rmsnorm_dgamma(cbf(st.slot_tensor(m, l, L_H1)), static_cast<const float*>(st.slot_tensor(m, l, L_R2)),
+                                      cbf(st.slot_tensor(m, l, L_DN2)), dw[5], part, T, H, s));
+            }
+    }
+    return ZB_OK;
+}
+
 }  // namespace zb

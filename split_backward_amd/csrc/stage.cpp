@@ -258,6 +258,33 @@ extern "C" int32_t zb_bwd_weight_accum(zb_stage* st, int32_t mb, void* stream) {
     return st->finish(PASS_W, sl.evW, s);
 }
 
+extern "C" int32_t zb_bwd_weight_accum_pair(zb_stage* st, int32_t mb, void* stream) {
+    if (!st || mb < 0) return fail(ZB_EINVAL, "zb_bwd_weight_accum_pair: bad argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int R = st->desc.ring_slots;
+    if (R < 2) return fail(ZB_ESTATE, "zb_bwd_weight_accum_pair: a ring of one slot never holds two microbatches");
+    Slot& s0 = st->slots[mb % R];
+    Slot& s1 = st->slots[(mb + 1) % R];
+    for (const Slot* sl : {&s0, &s1})
+        if (sl->mb < 0 || !sl->b_issued || sl->w_issued)
+            return fail(ZB_ESTATE, "zb_bwd_weight_accum_pair: needs B issued and W not yet issued for mb and mb + 1");
+    if (s0.mb != mb || s1.mb != mb + 1)
+        return fail(ZB_ESTATE, "zb_bwd_weight_accum_pair: mb and mb + 1 must both be resident");
+    if (mb != st->next_w) return fail(ZB_ESTATE, "zb_bwd_weight_accum_pair: W must be issued in ascending microbatch order; expected mb " + std::to_string(st->next_w));
+    int32_t rc = st->order_after(PASS_W, s0.evB, true, s);
+    if (rc) return rc;
+    ZB_HIP(hipStreamWaitEvent(s, s1.evB, 0));
+    rc = run_backward_weight_pair(*st, mb, s);
+    if (rc) return rc;
+    for (Slot* sl : {&s0, &s1}) {
+        sl->w_issued = true;
+        sl->w_event_valid = true;
+    }
+    st->next_w += 2;
+    ZB_HIP(hipEventRecord(s1.evW, s));
+    return st->finish(PASS_W, s0.evW, s);
+}
+
 extern "C" int32_t zb_stage_zero_grad(zb_stage* st, void* stream) {
     if (!st) return fail(ZB_EINVAL, "zb_stage_zero_grad: NULL stage");
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -66,4 +66,5 @@ namespace zb {
 int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s);
 int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipStream_t s);
 int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s);
+int32_t run_backward_weight_pair(zb_stage& st, int mb, hipStream_t s);
 }  // namespace zb
