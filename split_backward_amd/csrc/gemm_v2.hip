@@ -605,6 +605,11 @@ __device__ __forceinline__ void gemm_v2_tile(const GemmDesc& d, int tm, int tn, 
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
         if (A_KMAJ && B_KMAJ) interleave_reads_dma_mfma<RD, DPT, NM, 0>();
     }
+    // The last iteration read fragments of a k-tile past K that are never
+    // used.  Waiting for them with the fragments as operands keeps their
+    // registers reserved until the reads have landed, so no later value can
+    // be placed in a register an LDS read is still writing.
+    lds_wait(fa0, fb0);
     gemm_epilogue<A_KMAJ, B_KMAJ, EPI, TBM>(d, sp, acc, m0, n0, smem);
 }
 
@@ -815,6 +820,7 @@ __device__ __forceinline__ void gemm_64_tile(const GemmDesc& d, int tm, int tn, 
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
         if constexpr (KK) interleave_reads_dma_mfma<RD, NB, NM, 0>();
     }
+    lds_wait(fa0, fb0);  // the unused reads of k-tile nk (see the 32-k loop)
     gemm_epilogue<A_KMAJ, B_KMAJ, EPI, TBM>(d, sp, acc, m0, n0, smem);
 }
 
