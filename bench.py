@@ -73,6 +73,23 @@ def w_pass_gemms(s):
     return [(F, H, T)]
 
 
+def issue_plan(order, pair_w=True):
+    """The calls that issue `order` ((type, mb) ops): adjacent W(j), W(j+1)
+    become one ("P", j), a W pass over both microbatches
+    (zb_bwd_weight_accum_pair): the same work in the same order, with one
+    fp32 read-modify-write of dW for the two."""
+    plan, i = [], 0
+    while i < len(order):
+        t, j = order[i]
+        if pair_w and t == "W" and i + 1 < len(order) and tuple(order[i + 1]) == ("W", j + 1):
+            plan.append(("P", j))
+            i += 2
+        else:
+            plan.append((t, j))
+            i += 1
+    return plan
+
+
 def make_inputs(shape, m, device):
     import torch
     from tests.gpu_helpers import to_dev
@@ -337,18 +354,7 @@ def main():
     # zero-bubble order of stage 3 in an emulated 8-stage pipeline, memory limit min(2p, ring)
     order = zb.schedule_generate("zb", 8, m, min(16, ring), (1, 1, 1), 3)["ops"]
 
-    # Adjacent W(j), W(j+1) of the order run as one pass over both
-    # microbatches (zb_bwd_weight_accum_pair): the same work in the same
-    # order, with one fp32 read-modify-write of dW for the two.
-    plan, i = [], 0
-    while i < len(order):
-        t, j = order[i]
-        if t == "W" and not args.no_w_pairs and i + 1 < len(order) and order[i + 1] == ("W", j + 1):
-            plan.append(("P", j))
-            i += 2
-        else:
-            plan.append((t, j))
-            i += 1
+    plan = issue_plan(order, pair_w=not args.no_w_pairs)
     w_pairs = sum(1 for t, _ in plan if t == "P")
 
     def step():

@@ -37,3 +37,20 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stdout
+
+
+def test_issue_plan_pairs_adjacent_w_only():
+    """The bench issues the generator's order as is, except that W(j)
+    directly followed by W(j+1) becomes one pair call; every microbatch's
+    F, B and W appear exactly once and in the order's positions."""
+    import split_backward_amd as zb
+    order = zb.schedule_generate("zb", 8, 16, 16, (1, 1, 1), 3)["ops"]
+    plan = bench.issue_plan(order)
+    assert [("P", 8), ("P", 10), ("P", 12), ("P", 14)] == [op for op in plan if op[0] == "P"]
+    expanded = []
+    for t, j in plan:
+        expanded += [("W", j), ("W", j + 1)] if t == "P" else [(t, j)]
+    assert expanded == [tuple(op) for op in order]
+    assert bench.issue_plan(order, pair_w=False) == [tuple(op) for op in order]
+    # a W followed by a W of a non-adjacent microbatch is not paired
+    assert bench.issue_plan([("W", 0), ("W", 2), ("W", 3)]) == [("W", 0), ("P", 2)]
