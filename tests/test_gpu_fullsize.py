@@ -3,8 +3,9 @@
 1. Full widths (hidden, ffn, heads) with the token count reduced so the fp64
    oracle finishes in seconds: whole-stage parity, element by element.
 2. The exact configuration the benchmark times (all layers, 4096 tokens, the
-   benchmark's ring size): every F / B / W product, the RMSNorms and the
-   attention core are checked on sampled outputs that the oracle recomputes
+   benchmark's ring size, W per microbatch and W over a pair of microbatches):
+   every F / B / W product, the RMSNorms and the attention core are checked
+   on sampled outputs that the oracle recomputes
    one by one in fp64 from the GPU's own stashed operands (the inputs of
    each step), so a wrong tile, epilogue or index anywhere shows up.
 
@@ -92,8 +93,11 @@ def _w_samples(S: Sampler, key, dYs, Xs, dW, tol=5e-3):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["llama7b_stage4", "llama70b_slice2"])
-def test_benchmark_configuration_sampled(name):
+@pytest.mark.parametrize("name,w_pair", [("llama7b_stage4", False), ("llama7b_stage4", True),
+                                         ("llama70b_slice2", False), ("llama70b_slice2", True)])
+def test_benchmark_configuration_sampled(name, w_pair):
+    """w_pair: W of the two microbatches as one pass (two K segments), as the
+    benchmark issues adjacent W ops; otherwise one W per microbatch."""
     wl = synth.WORKLOADS[name]
     shape = wl["shape"]
     ring = wl.get("ring", wl["m"])
@@ -108,8 +112,11 @@ def test_benchmark_configuration_sampled(name):
     st.zero_grad()
     ys = [st.fwd(j, xs[j]) for j in range(m)]
     dxs = [st.bwd_input(j, dys[j]) for j in range(m)]
-    for j in range(m):
-        st.bwd_weight(j)
+    if w_pair:
+        st.bwd_weight_pair(0)
+    else:
+        for j in range(m):
+            st.bwd_weight(j)
     torch.cuda.synchronize()
 
     S = Sampler(7)
