@@ -292,10 +292,11 @@ def executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w):
 
 
 def memory_limit_sweep(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3):
-    """ZB(M) for M = p .. 2p on the GPU (ordered replay, arrivals at costs
-    1:1:1 in units of the mean pass time): measured in-window idle and stage
-    end beside the simulator's, and the stash the order keeps resident at
-    its peak (peak in-flight microbatches x bytes per ring slot)."""
+    """ZB(M) for M = p .. 2p on the GPU (arrivals at costs 1:1:1 in units of
+    the mean pass time), replayed in ordered mode and in filler mode (W on
+    the second stream): measured in-window idle and stage end beside the
+    simulator's, and the stash the order keeps resident at its peak (peak
+    in-flight microbatches x bytes per ring slot)."""
     import torch
     import split_backward_amd as zb
     slot = stage.slot_bytes()
@@ -304,13 +305,19 @@ def memory_limit_sweep(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3):
         if M > stage.desc.ring_slots:
             break
         g = zb.schedule_generate("zb", p, m, M, (1, 1, 1), stage_idx)
-        stage.zero_grad()
-        torch.cuda.synchronize()
-        r = stage.run_schedule(g["ops"], g["arrive_f"], g["arrive_b"], unit, xs, ys, dys, dxs, mode=zb.EXEC_ORDERED)
+        res = {}
+        for mode_name, mode in (("ordered", zb.EXEC_ORDERED), ("filler", zb.EXEC_FILLER)):
+            stage.zero_grad()
+            torch.cuda.synchronize()
+            res[mode_name] = stage.run_schedule(g["ops"], g["arrive_f"], g["arrive_b"], unit, xs, ys, dys, dxs,
+                                                mode=mode)
         win = g["last_end"] - g["first_start"]
-        rows.append({"M": M, "in_window_idle": round(r["in_window_idle"], 5),
+        rows.append({"M": M, "in_window_idle": round(res["ordered"]["in_window_idle"], 5),
+                     "in_window_idle_filler": round(res["filler"]["in_window_idle"], 5),
                      "predicted_in_window_idle": round(1 - g["busy"] / win, 5),
-                     "stage_end_ms": round(r["t_last_end_ms"], 2), "predicted_stage_end_ms": round(g["last_end"] * unit, 2),
+                     "stage_end_ms": round(res["ordered"]["t_last_end_ms"], 2),
+                     "stage_end_ms_filler": round(res["filler"]["t_last_end_ms"], 2),
+                     "predicted_stage_end_ms": round(g["last_end"] * unit, 2),
                      "peak_resident_microbatches": g["peak_active"],
                      "stash_GiB": round(g["peak_active"] * slot / 2**30, 2)})
     return {"unit_ms": round(unit, 3), "slot_GiB": round(slot / 2**30, 3), "runs": rows}
