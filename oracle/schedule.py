@@ -246,3 +246,121 @@ def simulate(kind: str, p: int, m: int, M: int = 0, costs=(1, 1, 1)) -> Result:
         raise ValueError(kind)
     makespan = max(s.last_end for s in stats)
     return Result(kind, p, m, M, (cF, cB, cW), ops, stats, makespan, af, ab)
+
+
+# ---------------------------------------------------------------------------
+# Several iterations back to back (zero-bubble greedy only).
+#
+# Each stage closes iteration `it` with an optimizer op O(it) of cost cO once
+# all of its own W of that iteration have completed; its first F of
+# iteration it+1 waits for that O and for the upstream stage's F, and for
+# nothing else: there is no synchronization across stages between
+# iterations.  [Abstract] says the method bypasses the synchronizations of
+# the optimizer step without describing how; this is the plainest reading
+# (each stage updates its own weights as soon as its own gradients are
+# complete).  Microbatch j of
+# iteration it has the global index g = it*m + j; "lowest microbatch" in the
+# greedy rules is the lowest g, and the memory limit counts in-flight
+# microbatches of any iteration.  Rule 0 (before B, F, W): a ready O.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class IterResult:
+    p: int
+    m: int
+    M: int
+    n_iter: int
+    costs: Tuple[int, int, int]
+    c_opt: int
+    ops: List[List[Op]]                 # per stage; O ops carry the iteration in .mb
+    stats: List[StageStats]
+    makespan: int
+    arrive_f: List[List[int]]           # [stage][g], g = it*m + j
+    arrive_b: List[List[int]]
+
+    def order(self, i: int) -> List[Tuple[str, int]]:
+        return [(o.type, o.mb) for o in self.ops[i]]
+
+
+def simulate_iterations(p: int, m: int, M: int, costs=(1, 1, 1), n_iter: int = 2, c_opt: int = 1) -> IterResult:
+    cF, cB, cW = (int(c) for c in costs)
+    c_opt = int(c_opt)
+    if p < 1 or m < 1 or M < 1 or cF < 1 or cB < 1 or cW < 1 or n_iter < 1 or c_opt < 1:
+        raise ValueError("bad arguments")
+    G = n_iter * m
+    cost = {"F": cF, "B": cB, "W": cW, "O": c_opt}
+    done: Dict[Tuple[str, int, int], int] = {}
+    started = set()
+    w_left = [[m] * n_iter for _ in range(p)]   # W of iteration it still to complete at stage i
+    running: List[Tuple[int, str, int, int]] = []
+    busy_stage = [False] * p
+    active = [0] * p
+    peak = [0] * p
+    ops: List[List[Op]] = [[] for _ in range(p)]
+    t = 0
+    total = p * (3 * G + n_iter)
+    n_done = 0
+    while n_done < total:
+        still = []
+        for (e, ty, i, k) in running:
+            if e == t:
+                done[(ty, i, k)] = e
+                busy_stage[i] = False
+                n_done += 1
+                if ty == "W":
+                    w_left[i][k // m] -= 1
+            else:
+                still.append((e, ty, i, k))
+        running = still
+        for i in range(p):
+            if busy_stage[i]:
+                continue
+            pick = None
+            for it in range(n_iter):                 # rule 0: a ready optimizer step
+                if ("O", i, it) not in started and w_left[i][it] == 0:
+                    pick = ("O", it)
+                    break
+            if pick is None:                         # rule 1: lowest ready B
+                for g in range(G):
+                    if (("B", i, g) not in started and ("F", i, g) in done
+                            and (i == p - 1 or ("B", i + 1, g) in done)):
+                        pick = ("B", g)
+                        break
+            if pick is None and active[i] < M:       # rule 2: lowest ready F
+                for g in range(G):
+                    it = g // m
+                    if (("F", i, g) not in started and (i == 0 or ("F", i - 1, g) in done)
+                            and (it == 0 or ("O", i, it - 1) in done)):
+                        pick = ("F", g)
+                        break
+            if pick is None:                         # rule 3: lowest ready W
+                for g in range(G):
+                    if ("W", i, g) not in started and ("B", i, g) in done:
+                        pick = ("W", g)
+                        break
+            if pick is None:
+                continue
+            ty, k = pick
+            started.add((ty, i, k))
+            if ty == "F":
+                active[i] += 1
+                peak[i] = max(peak[i], active[i])
+            elif ty == "W":
+                active[i] -= 1
+            e = t + cost[ty]
+            running.append((e, ty, i, k))
+            busy_stage[i] = True
+            ops[i].append(Op(ty, k, t, e))
+        if n_done == total:
+            break
+        if not running:
+            raise RuntimeError("zero-bubble greedy deadlocked (memory limit too small?)")
+        t = min(e for (e, _, _, _) in running)
+    stats = []
+    for i in range(p):
+        busy = sum(o.end - o.start for o in ops[i])
+        stats.append(StageStats(busy, ops[i][0].start, ops[i][-1].end, peak[i]))
+    arrive_f = [[done[("F", i - 1, g)] if i > 0 else 0 for g in range(G)] for i in range(p)]
+    arrive_b = [[done[("B", i + 1, g)] if i < p - 1 else 0 for g in range(G)] for i in range(p)]
+    makespan = max(s.last_end for s in stats)
+    return IterResult(p, m, M, n_iter, (cF, cB, cW), c_opt, ops, stats, makespan, arrive_f, arrive_b)

@@ -6,6 +6,7 @@ from fractions import Fraction
 
 import pytest
 
+from oracle import schedule as S
 from oracle.schedule import simulate
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -164,3 +165,108 @@ def test_zb_memory_limit_respected_and_deadlock_free():
         for M in range(p, 2 * p + 1):
             r = simulate("zb", p, 3 * p, M=M)
             assert all(s.peak_active <= M for s in r.stats)
+
+
+# ---------------------------------------------------- several iterations ---
+
+ITER_CASES = [(8, 16, 16, (1, 1, 1), 1, 3), (4, 8, 8, (2, 2, 2), 1, 2), (4, 8, 8, (1, 1, 1), 3, 2),
+              (8, 24, 16, (1, 1, 1), 1, 2), (4, 6, 8, (1, 1, 1), 1, 2), (8, 16, 8, (1, 1, 1), 1, 2),
+              (8, 16, 16, (63, 84, 63), 1, 3), (8, 16, 12, (2, 3, 2), 2, 3), (3, 2, 3, (1, 1, 1), 1, 3),
+              (2, 1, 1, (1, 1, 1), 1, 3)]
+
+
+def _check_iteration_dependencies(r):
+    """Independent of the simulator's bookkeeping: every op once, no overlap
+    on a stage, every dependency ended before its op starts, the memory
+    limit never exceeded."""
+    p, m, n = r.p, r.m, r.n_iter
+    G = n * m
+    end = {}
+    for i in range(p):
+        seen = set()
+        last = 0
+        for o in r.ops[i]:
+            assert o.start >= last, ("overlap", i, o)
+            last = o.end
+            assert (o.type, o.mb) not in seen
+            seen.add((o.type, o.mb))
+            end[(o.type, i, o.mb)] = (o.start, o.end)
+        assert seen == ({(t, g) for t in "FBW" for g in range(G)} | {("O", it) for it in range(n)})
+    for i in range(p):
+        active = 0
+        for o in r.ops[i]:
+            s = o.start
+            if o.type == "F":
+                g, it = o.mb, o.mb // m
+                if i > 0:
+                    assert end[("F", i - 1, g)][1] <= s
+                if it > 0:
+                    assert end[("O", i, it - 1)][1] <= s
+                active += 1
+                assert active <= r.M
+            elif o.type == "B":
+                assert end[("F", i, o.mb)][1] <= s
+                if i < p - 1:
+                    assert end[("B", i + 1, o.mb)][1] <= s
+            elif o.type == "W":
+                assert end[("B", i, o.mb)][1] <= s
+                active -= 1
+            else:
+                for j in range(m):
+                    assert end[("W", i, o.mb * m + j)][1] <= s
+        for g in range(G):
+            if i > 0:
+                assert r.arrive_f[i][g] == end[("F", i - 1, g)][1]
+            if i < p - 1:
+                assert r.arrive_b[i][g] == end[("B", i + 1, g)][1]
+
+
+@pytest.mark.parametrize("p,m,M,costs,c_opt,n", ITER_CASES)
+def test_iterations_dependencies_and_memory(p, m, M, costs, c_opt, n):
+    _check_iteration_dependencies(S.simulate_iterations(p, m, M, costs, n, c_opt))
+
+
+@pytest.mark.parametrize("p,m,M,costs,c_opt,n", ITER_CASES)
+def test_one_iteration_is_the_single_iteration_schedule(p, m, M, costs, c_opt, n):
+    r = S.simulate_iterations(p, m, M, costs, 1, c_opt)
+    single = S.simulate("zb", p, m, M, costs)
+    for i in range(p):
+        got = [(o.type, o.mb, o.start, o.end) for o in r.ops[i]]
+        last_w = single.ops[i][-1].end
+        assert got == [(o.type, o.mb, o.start, o.end) for o in single.ops[i]] + [("O", 0, last_w, last_w + c_opt)]
+
+
+@pytest.mark.parametrize("p,m,M,costs,c_opt,n", ITER_CASES)
+def test_iterations_repeat_with_stage0_period(p, m, M, costs, c_opt, n):
+    """Every stage's iteration k is its iteration 0 shifted by k * T, with
+    T = stage 0's single-iteration end + c_opt (stage 0 starts iteration k+1
+    right after its optimizer step, and nothing else gates it), so the
+    makespan is (n-1) T + makespan(1) + c_opt."""
+    r = S.simulate_iterations(p, m, M, costs, n, c_opt)
+    single = S.simulate("zb", p, m, M, costs)
+    T = single.stats[0].last_end + c_opt
+    for i in range(p):
+        base = [(o.type, o.mb, o.start, o.end) for o in single.ops[i]]
+        for it in range(n):
+            got = [(o.type, o.mb - m * it, o.start - it * T, o.end - it * T) for o in r.ops[i]
+                   if o.type != "O" and m * it <= o.mb < m * (it + 1)]
+            assert got == base, (i, it)
+    assert r.makespan == (n - 1) * T + single.makespan + c_opt
+
+
+@pytest.mark.parametrize("p,m,n", [(8, 16, 2), (8, 16, 3), (4, 8, 3), (8, 24, 2)])
+def test_iterations_tile_without_idle_at_equal_costs(p, m, n):
+    """Equal F, B, W costs, memory limit 2p, m >= 2p: the iterations tile
+    (each stage starts its next iteration's first F exactly when it would
+    otherwise fall idle), so in-window idle stays zero over the whole run."""
+    r = S.simulate_iterations(p, m, 2 * p, (1, 1, 1), n, 1)
+    for s in r.stats:
+        assert s.busy == s.last_end - s.first_start
+
+
+def test_iterations_reject_bad_arguments():
+    for bad in (dict(n_iter=0), dict(c_opt=0), dict(M=0)):
+        kw = dict(p=4, m=8, M=8, costs=(1, 1, 1), n_iter=2, c_opt=1)
+        kw.update(bad)
+        with pytest.raises(ValueError):
+            S.simulate_iterations(**kw)
