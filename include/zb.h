@@ -160,7 +160,8 @@ int32_t zb_stage_stash_tensor(zb_stage* st, int32_t mb, int32_t layer, int32_t w
 /* ------------------------------------------------------------ schedules -- */
 
 /* Op of a per-stage schedule (the Guide scheduler listing's task types). */
-enum { ZB_OP_F = 0, ZB_OP_B = 1, ZB_OP_W = 2 };
+enum { ZB_OP_F = 0, ZB_OP_B = 1, ZB_OP_W = 2,
+       ZB_OP_O = 3 /* optimizer step closing an iteration (zb_schedule_generate_iters) */ };
 typedef struct { int32_t type; int32_t mb; } zb_op;
 
 /* Schedule kinds: GPipe and 1F1B with the backward kept whole (each B is
@@ -197,6 +198,23 @@ int32_t zb_schedule_generate(int32_t kind, int32_t p, int32_t m, int32_t mem_lim
                              int32_t cF, int32_t cB, int32_t cW, int32_t stage,
                              zb_op* ops, int64_t* start, int64_t* end, int32_t cap,
                              int64_t* arrive_f, int64_t* arrive_b, zb_sched_stats* stats);
+
+/* Several iterations of the zero-bubble greedy, back to back.  Each stage
+ * closes iteration it with an optimizer step (op ZB_OP_O, mb = it, cost
+ * c_opt >= 1) as soon as all of its own W of that iteration have completed;
+ * its first F of iteration it+1 waits for that step and for the upstream
+ * F, and for nothing else.  The abstract page "Zero Bubble Pipeline
+ * Parallelism" says the method bypasses the optimizer step's
+ * synchronizations; this is read as no barrier across stages.  A ready step
+ * is taken before any B, F or W; otherwise the rules of ZB above apply with
+ * the global microbatch index g = it * m + j (F, B, W ops carry g).
+ * Outputs as for zb_schedule_generate, with 3 m n_iter + n_iter ops and
+ * arrivals indexed by g (arrive_f / arrive_b of m * n_iter entries).
+ * Returns the number of ops or ZB_EINVAL. */
+int32_t zb_schedule_generate_iters(int32_t p, int32_t m, int32_t mem_limit, int32_t cF, int32_t cB,
+                                   int32_t cW, int32_t c_opt, int32_t n_iter, int32_t stage,
+                                   zb_op* ops, int64_t* start, int64_t* end, int32_t cap,
+                                   int64_t* arrive_f, int64_t* arrive_b, zb_sched_stats* stats);
 
 /* ------------------------------------------------------------- executor -- */
 

@@ -19,13 +19,13 @@ LIB_PATH = os.path.join(HERE, "libzb.so")
 OK, EINVAL, ESTATE, ERING_FULL, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 LINEAR, MLP_GELU, LLAMA = 0, 1, 2
-OP_F, OP_B, OP_W = 0, 1, 2
+OP_F, OP_B, OP_W, OP_O = 0, 1, 2, 3
 SCHED_GPIPE, SCHED_1F1B, SCHED_ZB = 0, 1, 2
 EXEC_ORDERED, EXEC_FILLER = 0, 1
 
 KIND = {"linear": LINEAR, "mlp": MLP_GELU, "llama": LLAMA}
 SCHED = {"gpipe": SCHED_GPIPE, "1f1b": SCHED_1F1B, "zb": SCHED_ZB}
-OPNAME = {OP_F: "F", OP_B: "B", OP_W: "W"}
+OPNAME = {OP_F: "F", OP_B: "B", OP_W: "W", OP_O: "O"}
 
 # stash tensor indices ("which")
 LIN_X, LIN_DY = 0, 1
@@ -79,6 +79,9 @@ _PROTOS = {
     "zb_schedule_generate": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Op),
                                     ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, ctypes.POINTER(_i64),
                                     ctypes.POINTER(_i64), ctypes.POINTER(SchedStats)]),
+    "zb_schedule_generate_iters": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Op),
+                                          ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, ctypes.POINTER(_i64),
+                                          ctypes.POINTER(_i64), ctypes.POINTER(SchedStats)]),
     "zb_stage_run_schedule": (_i32, [_vp, ctypes.POINTER(Op), _i32, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double), ctypes.c_double, ctypes.POINTER(_vp),
                                      ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _vp, _i32,
@@ -132,6 +135,32 @@ def schedule_generate(kind: str, p: int, m: int, mem_limit: int = 0, costs=(1, 1
     stats = SchedStats()
     cnt = lib().zb_schedule_generate(SCHED[kind], p, m, mem_limit, costs[0], costs[1], costs[2], stage, ops, st,
                                      en, n, af, ab, ctypes.byref(stats))
+    check(cnt)
+    return {
+        "ops": [(OPNAME[ops[i].type], ops[i].mb) for i in range(cnt)],
+        "start": list(st[:cnt]), "end": list(en[:cnt]),
+        "arrive_f": list(af), "arrive_b": list(ab),
+        "makespan": stats.makespan, "busy": stats.busy, "first_start": stats.first_start,
+        "last_end": stats.last_end, "peak_active": stats.peak_active,
+    }
+
+
+def schedule_generate_iters(p: int, m: int, mem_limit: int, costs=(1, 1, 1), c_opt: int = 1, n_iter: int = 2,
+                            stage: int = 0) -> dict:
+    """Zero-bubble order of n_iter iterations for one stage, with an
+    optimizer step ("O", iteration) closing each (no GPU needed).  F, B, W
+    ops carry the global microbatch index it * m + j; arrivals are indexed
+    by it."""
+    G = m * n_iter
+    n = 3 * G + n_iter
+    ops = (Op * n)()
+    st = (ctypes.c_int64 * n)()
+    en = (ctypes.c_int64 * n)()
+    af = (ctypes.c_int64 * G)()
+    ab = (ctypes.c_int64 * G)()
+    stats = SchedStats()
+    cnt = lib().zb_schedule_generate_iters(p, m, mem_limit, costs[0], costs[1], costs[2], c_opt, n_iter, stage, ops,
+                                           st, en, n, af, ab, ctypes.byref(stats))
     check(cnt)
     return {
         "ops": [(OPNAME[ops[i].type], ops[i].mb) for i in range(cnt)],

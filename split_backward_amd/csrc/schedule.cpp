@@ -218,3 +218,124 @@ extern "C" int32_t zb_schedule_generate(int32_t kind, int32_t p, int32_t m, int3
     }
     return (int32_t)mine.size();
 }
+
+// ---------------------------------------------------------------------------
+// Several iterations of the zero-bubble greedy.  Each stage runs an optimizer
+// step O(it) (cost c_opt) once all of its own W of iteration it have
+// completed; its F of iteration it+1 waits for that step and for the
+// upstream F only (no synchronization across stages between iterations: the
+// abstract page "Zero Bubble Pipeline Parallelism" states that the method
+// bypasses the optimizer step's synchronizations).  Microbatch j of
+// iteration it is g = it*m + j; "lowest microbatch" is the lowest g and the
+// memory limit counts stashed microbatches of any iteration.  A ready O is
+// taken before any B, F or W.
+extern "C" int32_t zb_schedule_generate_iters(int32_t p, int32_t m, int32_t mem_limit, int32_t cF, int32_t cB,
+                                              int32_t cW, int32_t c_opt, int32_t n_iter, int32_t stage, zb_op* ops,
+                                              int64_t* start, int64_t* end, int32_t cap, int64_t* arrive_f,
+                                              int64_t* arrive_b, zb_sched_stats* stats) {
+    if (p < 1 || m < 1 || n_iter < 1 || stage < 0 || stage >= p || cF < 1 || cB < 1 || cW < 1 || c_opt < 1 ||
+        mem_limit < 1)
+        return ZB_EINVAL;
+    if ((int64_t)p * m * n_iter > 1 << 22) return ZB_EINVAL;
+    const int G = m * n_iter;
+    const int n_stage_ops = 3 * G + n_iter;
+    if ((ops || start || end) && cap < n_stage_ops) return ZB_EINVAL;
+    std::vector<int64_t> Fe((size_t)p * G, NOT_DONE), Be((size_t)p * G, NOT_DONE), Oe((size_t)p * n_iter, NOT_DONE);
+    auto at = [G](int i, int g) { return (size_t)i * G + g; };
+    std::vector<std::vector<char>> b_started(p, std::vector<char>(G, 0)), w_started(p, std::vector<char>(G, 0));
+    std::vector<std::vector<char>> o_started(p, std::vector<char>(n_iter, 0));
+    std::vector<std::vector<int>> w_left(p, std::vector<int>(n_iter, m));
+    std::vector<int> active(p, 0), next_f(p, 0), peak(p, 0);
+    std::vector<char> busy(p, 0);
+    std::vector<std::vector<Placed>> placed(p);
+    struct Running { int64_t end; int type, stage, k; };
+    auto later = [](const Running& a, const Running& b) { return a.end > b.end; };
+    std::priority_queue<Running, std::vector<Running>, decltype(later)> heap(later);
+    int64_t now = 0;
+    size_t finished = 0;
+    const size_t total = (size_t)p * n_stage_ops;
+    while (true) {
+        while (!heap.empty() && heap.top().end == now) {
+            const Running r = heap.top();
+            heap.pop();
+            if (r.type == ZB_OP_F) Fe[at(r.stage, r.k)] = r.end;
+            else if (r.type == ZB_OP_B) Be[at(r.stage, r.k)] = r.end;
+            else if (r.type == ZB_OP_W) --w_left[r.stage][r.k / m];
+            else Oe[(size_t)r.stage * n_iter + r.k] = r.end;
+            busy[r.stage] = 0;
+            ++finished;
+        }
+        if (finished == total) break;
+        for (int i = 0; i < p; ++i) {
+            if (busy[i]) continue;
+            int type = -1, k = -1;
+            for (int it = 0; it < n_iter && type < 0; ++it)
+                if (!o_started[i][it] && w_left[i][it] == 0) {
+                    type = ZB_OP_O;
+                    k = it;
+                }
+            for (int g = 0; g < G && type < 0; ++g)
+                if (!b_started[i][g] && Fe[at(i, g)] != NOT_DONE && (i == p - 1 || Be[at(i + 1, g)] != NOT_DONE)) {
+                    type = ZB_OP_B;
+                    k = g;
+                }
+            if (type < 0 && active[i] < mem_limit && next_f[i] < G) {
+                const int g = next_f[i], it = g / m;
+                if ((i == 0 || Fe[at(i - 1, g)] != NOT_DONE) && (it == 0 || Oe[(size_t)i * n_iter + it - 1] != NOT_DONE)) {
+                    type = ZB_OP_F;
+                    k = g;
+                }
+            }
+            for (int g = 0; g < G && type < 0; ++g)
+                if (!w_started[i][g] && Be[at(i, g)] != NOT_DONE) {
+                    type = ZB_OP_W;
+                    k = g;
+                }
+            if (type < 0) continue;
+            int64_t cost;
+            if (type == ZB_OP_F) {
+                ++next_f[i];
+                peak[i] = std::max(peak[i], ++active[i]);
+                cost = cF;
+            } else if (type == ZB_OP_B) {
+                b_started[i][k] = 1;
+                cost = cB;
+            } else if (type == ZB_OP_W) {
+                w_started[i][k] = 1;
+                --active[i];
+                cost = cW;
+            } else {
+                o_started[i][k] = 1;
+                cost = c_opt;
+            }
+            busy[i] = 1;
+            heap.push({now + cost, type, i, k});
+            placed[i].push_back({type, k, now, now + cost});
+        }
+        if (heap.empty()) return ZB_EINVAL;  // nothing can run: limit too small
+        now = heap.top().end;
+    }
+    const auto& mine = placed[stage];
+    for (size_t q = 0; q < mine.size(); ++q) {
+        if (ops) ops[q] = zb_op{mine[q].type, mine[q].mb};
+        if (start) start[q] = mine[q].start;
+        if (end) end[q] = mine[q].end;
+    }
+    for (int g = 0; g < G; ++g) {
+        if (arrive_f) arrive_f[g] = stage == 0 ? 0 : Fe[at(stage - 1, g)];
+        if (arrive_b) arrive_b[g] = stage == p - 1 ? 0 : Be[at(stage + 1, g)];
+    }
+    if (stats) {
+        int64_t mk = 0;
+        for (int i = 0; i < p; ++i) mk = std::max(mk, placed[i].back().end);
+        int64_t b = 0;
+        for (const auto& o : mine) b += o.end - o.start;
+        stats->makespan = mk;
+        stats->busy = b;
+        stats->first_start = mine.front().start;
+        stats->last_end = mine.back().end;
+        stats->peak_active = peak[stage];
+        stats->n_ops = (int32_t)mine.size();
+    }
+    return (int32_t)mine.size();
+}

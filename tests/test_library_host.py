@@ -162,3 +162,29 @@ def test_compute_calls_reject_null_stage():
     assert L.zb_bwd_input(None, 0, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == zb.EINVAL
     assert L.zb_bwd_weight_accum(None, 0, None) == zb.EINVAL
     assert L.zb_stage_zero_grad(None, None) == zb.EINVAL
+
+
+@pytest.mark.parametrize("p,m,M,costs,c_opt,n", [(8, 16, 16, (1, 1, 1), 1, 3), (4, 8, 8, (2, 3, 2), 2, 2),
+                                                (8, 16, 8, (63, 84, 63), 1, 2), (4, 6, 5, (1, 2, 1), 3, 3),
+                                                (2, 1, 1, (1, 1, 1), 1, 2)])
+def test_iteration_generator_matches_oracle_bit_exact(p, m, M, costs, c_opt, n):
+    from oracle.schedule import simulate_iterations
+    ref = simulate_iterations(p, m, M, costs, n, c_opt)
+    for stage in range(p):
+        g = zb.schedule_generate_iters(p, m, M, costs, c_opt, n, stage)
+        assert g["ops"] == ref.order(stage)
+        assert g["start"] == [o.start for o in ref.ops[stage]]
+        assert g["end"] == [o.end for o in ref.ops[stage]]
+        assert g["arrive_f"] == ref.arrive_f[stage]
+        assert g["arrive_b"] == ref.arrive_b[stage]
+        assert g["makespan"] == ref.makespan
+        assert g["peak_active"] == ref.stats[stage].peak_active
+        assert g["busy"] == ref.stats[stage].busy
+
+
+def test_iteration_generator_rejects_bad_arguments():
+    for bad in (dict(n_iter=0), dict(c_opt=0), dict(mem_limit=0), dict(stage=4)):
+        kw = dict(p=4, m=8, mem_limit=8, costs=(1, 1, 1), c_opt=1, n_iter=2, stage=0)
+        kw.update(bad)
+        with pytest.raises(zb.ZbError):
+            zb.schedule_generate_iters(**kw)
