@@ -157,6 +157,22 @@ int32_t zb_stage_zero_grad(zb_stage* st, void* stream);
 int32_t zb_stage_stash_tensor(zb_stage* st, int32_t mb, int32_t layer, int32_t which,
                               void** ptr, int32_t* rows, int32_t* cols, int32_t* dtype);
 
+/* Optimizer step of the stage, closing an iteration (the op ZB_OP_O of
+ * zb_schedule_generate_iters): for every weight, w -= lr * dW elementwise
+ * (fp32 product and difference, each rounded once, then rounded once to the
+ * weight's type, round to nearest even), after every issued W has completed
+ * on the device; then dW is cleared and the stage is reset for a new
+ * iteration as by zb_stage_zero_grad.  A plain SGD step: the pages name an
+ * optimizer step per iteration but no optimizer.  lr must be finite.
+ * Errors: ZB_EINVAL, ZB_ESTATE if a microbatch is in flight (its W not
+ * issued). */
+int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream);
+
+/* Learning rate of the optimizer steps zb_stage_run_schedule issues for
+ * ZB_OP_O ops (default 0: the weights are left unchanged).  ZB_EINVAL if lr
+ * is not finite. */
+int32_t zb_stage_set_lr(zb_stage* st, float lr);
+
 /* ------------------------------------------------------------ schedules -- */
 
 /* Op of a per-stage schedule (the Guide scheduler listing's task types). */
@@ -244,7 +260,15 @@ typedef struct {
  * Both streams must be default-priority HIP streams (NULL = create and
  * destroy private ones).  op_ms (may be NULL) receives 2*n doubles: start and
  * end of each op in ms since t0.  Blocks until the run has finished.
- * Errors: as the compute calls, plus ZB_EINVAL for a malformed op list. */
+ * Several iterations (ops of zb_schedule_generate_iters): F, B, W ops carry
+ * the global microbatch index g (into x, y, dy, dx and the arrivals, which
+ * then have one entry per microbatch of every iteration); a ZB_OP_O op runs
+ * zb_stage_sgd_step with the rate of zb_stage_set_lr on the high stream,
+ * after every W issued before it, and the next F restarts the stage's own
+ * numbering at 0.
+ * Errors: as the compute calls, plus ZB_EINVAL for a malformed op list (an
+ * op type outside F, B, W, O, a negative index, or an op of an iteration an
+ * optimizer step has already closed), detected before any work is issued. */
 int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t n,
                               const double* arrive_f, const double* arrive_b, double unit_ms,
                               const void* const* x, void* const* y,

@@ -451,3 +451,34 @@ def attn_head_bwd(q, k, v, do, h: int, n_q: int, n_kv: int, d: int):
     dp = doh @ vh.T
     ds = p * (dp - np.sum(doh * o, axis=1, keepdims=True))
     return (ds @ kh) * scale, (ds.T @ qh) * scale, p.T @ doh
+
+
+# ====================================================== optimizer step ====
+# The pages name an optimizer step after each iteration's weight gradients
+# ([Guide] listing: the weight gradient accumulates into weight.grad, which
+# an optimizer then consumes; [Abstract]: the optimizer step) but no
+# optimizer.  The stage applies plain SGD, w <- w - lr * dW, and its result
+# is a rounded value, so here the step is written at the precision the
+# stage defines for it: the product lr * dW and the difference are float32
+# operations (one rounding each), then the weight is rounded once to its
+# storage type.  Unlike the rest of this module this is not fp64: the
+# result is a bf16 / fp32 bit pattern that is compared exactly.
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 values -> nearest bfloat16 values (ties to even), as float64.
+    Finite inputs only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep = u >> 16                       # sign, exponent and top 7 mantissa bits
+    rest = u & 0xFFFF                    # the 16 bits rounded away
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & 1) == 1))
+    r = ((keep + up.astype(np.uint64)) << 16).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def sgd_step(w: np.ndarray, dw: np.ndarray, lr: float, dtype: str) -> np.ndarray:
+    """w - lr * dW as the stage computes it: float32 product, float32
+    difference, then one rounding to dtype ("bf16" or "f32")."""
+    w32 = np.asarray(w, dtype=np.float64).astype(np.float32)  # exact: w is bf16 or fp32
+    t = np.float32(lr) * np.asarray(dw, dtype=np.float32)
+    r = (w32 - t).astype(np.float32)
+    return bf16_round(r) if dtype == "bf16" else r.astype(np.float64)

@@ -74,6 +74,8 @@ _PROTOS = {
     "zb_bwd_weight_accum": (_i32, [_vp, _i32, _vp]),
     "zb_bwd_weight_accum_pair": (_i32, [_vp, _i32, _vp]),
     "zb_stage_zero_grad": (_i32, [_vp, _vp]),
+    "zb_stage_sgd_step": (_i32, [_vp, ctypes.c_float, _vp]),
+    "zb_stage_set_lr": (_i32, [_vp, ctypes.c_float]),
     "zb_stage_stash_tensor": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
                                      ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "zb_schedule_generate": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Op),
@@ -284,6 +286,14 @@ class Stage:
         """W for microbatches mb and mb + 1 in one pass (zb_bwd_weight_accum_pair)."""
         check(lib().zb_bwd_weight_accum_pair(self.handle, mb, _stream_ptr(stream)))
 
+    def sgd_step(self, lr: float, stream=None):
+        """w -= lr * dW for every weight, then zero_grad (zb_stage_sgd_step)."""
+        check(lib().zb_stage_sgd_step(self.handle, lr, _stream_ptr(stream)))
+
+    def set_lr(self, lr: float):
+        """Rate of the optimizer steps the executor runs for "O" ops."""
+        check(lib().zb_stage_set_lr(self.handle, lr))
+
     def zero_grad(self, stream=None):
         check(lib().zb_stage_zero_grad(self.handle, _stream_ptr(stream)))
 
@@ -304,9 +314,9 @@ class Stage:
         m = len(xs)
         if not (len(ys) == len(dys) == len(dxs) == m and len(arrive_f) >= m and len(arrive_b) >= m):
             raise ValueError("xs, ys, dys, dxs and the arrival lists need one entry per microbatch")
-        if any(j < 0 or j >= m for _, j in ops):
+        if any(j < 0 or (t != "O" and j >= m) for t, j in ops):
             raise ValueError("op microbatch outside the given per-microbatch lists")
-        opa = (Op * n)(*[Op({"F": OP_F, "B": OP_B, "W": OP_W}[t], j) for t, j in ops])
+        opa = (Op * n)(*[Op({"F": OP_F, "B": OP_B, "W": OP_W, "O": OP_O}[t], j) for t, j in ops])
         af = (ctypes.c_double * m)(*[float(a) for a in arrive_f])
         ab = (ctypes.c_double * m)(*[float(a) for a in arrive_b])
         P = lambda ts: (ctypes.c_void_p * m)(*[_ptr(t) for t in ts])

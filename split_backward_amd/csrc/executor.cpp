@@ -11,8 +11,10 @@
 //            the GPU executes exactly the generated order.
 //   FILLER:  W waits only for its own B (and F of a reused ring slot waits
 //            for the W that frees it), so W soaks up whatever gaps remain.
-// Each op is bracketed by two clock-stamp kernels; idle time is the part of
-// the stage's window [first op start, last op end] that no op interval covers.
+// Optimizer-step ops (several iterations back to back) run on the high
+// stream after every W issued before them.  Each op is bracketed by two
+// clock-stamp kernels; idle time is the part of the stage's window
+// [first op start, last op end] that no op interval covers.
 #include <algorithm>
 #include <cmath>
 #include <vector>
@@ -49,11 +51,34 @@ extern "C" int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t
         !dx)
         return fail(ZB_EINVAL, "zb_stage_run_schedule: bad argument");
     if (mode != ZB_EXEC_ORDERED && mode != ZB_EXEC_FILLER) return fail(ZB_EINVAL, "zb_stage_run_schedule: bad mode");
+    // F, B and W ops carry a microbatch index into x, y, dy, dx and the
+    // arrivals; an optimizer-step op (ZB_OP_O, from
+    // zb_schedule_generate_iters) closes an iteration and resets the stage,
+    // whose own numbering then starts again at 0 with the next F.  local[k]
+    // is op k's microbatch in the stage's numbering, checked here before any
+    // work is issued.
     int nmb = 0;
-    for (int k = 0; k < n; ++k) {
-        if (ops[k].type < ZB_OP_F || ops[k].type > ZB_OP_W || ops[k].mb < 0)
-            return fail(ZB_EINVAL, "zb_stage_run_schedule: malformed op " + std::to_string(k));
-        nmb = std::max(nmb, ops[k].mb + 1);
+    std::vector<int> local(n, 0);
+    {
+        int base = 0;
+        bool reset = false;
+        for (int k = 0; k < n; ++k) {
+            if (ops[k].type < ZB_OP_F || ops[k].type > ZB_OP_O || ops[k].mb < 0)
+                return fail(ZB_EINVAL, "zb_stage_run_schedule: malformed op " + std::to_string(k));
+            if (ops[k].type == ZB_OP_O) {
+                reset = true;
+                continue;
+            }
+            if (ops[k].type == ZB_OP_F && reset) {
+                base = ops[k].mb;
+                reset = false;
+            }
+            local[k] = ops[k].mb - base;
+            if (local[k] < 0 || reset)
+                return fail(ZB_EINVAL, "zb_stage_run_schedule: op " + std::to_string(k) +
+                                           " belongs to an iteration an optimizer step has closed");
+            nmb = std::max(nmb, ops[k].mb + 1);
+        }
     }
     for (int j = 0; j < nmb; ++j)
         if (!(arrive_f[j] >= 0.0) || !(arrive_b[j] >= 0.0) || arrive_f[j] > 1e6 || arrive_b[j] > 1e6)
@@ -95,7 +120,7 @@ extern "C" int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t
             hipError_t e = hipStreamWaitEvent(s, pool.ev[prev], 0);
             if (e != hipSuccess) { rc = fail(ZB_EHIP, "hipStreamWaitEvent failed"); break; }
         }
-        if (!is_w) {
+        if (op.type == ZB_OP_F || op.type == ZB_OP_B) {
             const double a = op.type == ZB_OP_F ? arrive_f[op.mb] : arrive_b[op.mb];
             const uint64_t delta = (uint64_t)std::llround(a * unit_ms * ticks_per_ms);
             rc = wait_until(t0, delta, wait_end + k, s);
@@ -103,9 +128,10 @@ extern "C" int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t
         }
         rc = stamp_now(stamp + 2 * k, s);
         if (rc) break;
-        if (op.type == ZB_OP_F) rc = zb_fwd(st, op.mb, x[op.mb], y[op.mb], s);
-        else if (op.type == ZB_OP_B) rc = zb_bwd_input(st, op.mb, dy[op.mb], dx[op.mb], s);
-        else rc = zb_bwd_weight_accum(st, op.mb, s);
+        if (op.type == ZB_OP_F) rc = zb_fwd(st, local[k], x[op.mb], y[op.mb], s);
+        else if (op.type == ZB_OP_B) rc = zb_bwd_input(st, local[k], dy[op.mb], dx[op.mb], s);
+        else if (op.type == ZB_OP_W) rc = zb_bwd_weight_accum(st, local[k], s);
+        else rc = zb_stage_sgd_step(st, st->lr, s);  // waits for every W issued on the other stream
         if (rc) break;
         rc = stamp_now(stamp + 2 * k + 1, s);
         if (rc) break;
@@ -132,7 +158,7 @@ extern "C" int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t
             op_ms[2 * k] = iv[k].first;
             op_ms[2 * k + 1] = iv[k].second;
         }
-        if (ops[k].type != ZB_OP_W) {
+        if (ops[k].type == ZB_OP_F || ops[k].type == ZB_OP_B) {
             const double a = (ops[k].type == ZB_OP_F ? arrive_f[ops[k].mb] : arrive_b[ops[k].mb]) * unit_ms;
             late += std::max(0.0, ms(host[1 + 2 * n + k]) - a);
         }

@@ -4,6 +4,8 @@
 //
 // RMSNorm: y = x r g with r = (mean(x^2) + eps)^(-1/2);
 //          dx = r (dy g - xhat mean(dy g xhat)), xhat = x r;  dg = sum_t dy xhat.
+#include <algorithm>
+
 #include "common.h"
 
 namespace zb {
@@ -179,6 +181,49 @@ __global__ void fill_f32_kernel(float* p, size_t n, float v) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
 }
 
+// Optimizer step w -= lr * dW, in fp32 with the product and the difference
+// each rounded once (no fused multiply-add: contraction is switched off in
+// these kernels; the __fmul_rn / __fsub_rn helpers are fused regardless,
+// because they are inlined from headers that allow it), then w
+// rounded once to bf16 (round to nearest even).  Four consecutive elements
+// per thread.
+__global__ void sgd_bf16_kernel(bf16_t* __restrict__ w, const float* __restrict__ dw, size_t n4, float lr) {
+#pragma clang fp contract(off)  // the product and the difference are rounded separately
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const floatx4 d = reinterpret_cast<const floatx4*>(dw)[i];
+        u32x2 v = reinterpret_cast<const u32x2*>(w)[i];
+        float x[4] = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
+                      __uint_as_float(v[1] & 0xffff0000u)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float t = lr * d[e];
+            x[e] = x[e] - t;
+        }
+        v[0] = uint32_t(f2bf(x[0])) | (uint32_t(f2bf(x[1])) << 16);
+        v[1] = uint32_t(f2bf(x[2])) | (uint32_t(f2bf(x[3])) << 16);
+        reinterpret_cast<u32x2*>(w)[i] = v;
+    }
+}
+// The elements past the last full group of four, one per thread.
+__global__ void sgd_bf16_tail_kernel(bf16_t* __restrict__ w, const float* __restrict__ dw, size_t begin, size_t n,
+                                     float lr) {
+#pragma clang fp contract(off)
+    const size_t i = begin + threadIdx.x;
+    if (i < n) {
+        const float t = lr * dw[i];
+        w[i] = f2bf(bf2f(w[i]) - t);
+    }
+}
+__global__ void sgd_f32_kernel(float* __restrict__ w, const float* __restrict__ dw, size_t n, float lr) {
+#pragma clang fp contract(off)
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float t = lr * dw[i];
+        w[i] = w[i] - t;
+    }
+}
+
 __global__ void stamp_kernel(uint64_t* dst) {
     if (threadIdx.x == 0) *dst = wall_clock64();
 }
@@ -251,6 +296,30 @@ int32_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
     ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+int32_t sgd_step(void* w, int dtype, const float* dw, size_t n, float lr, hipStream_t s) {
+    if (n == 0) return ZB_OK;
+    if (dtype == ZB_F32) {
+        size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
+        hipLaunchKernelGGL(sgd_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<float*>(w), dw, n, lr);
+        ZB_HIP(hipGetLastError());
+        return ZB_OK;
+    }
+    if ((reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(dw) & 15))
+        return fail(ZB_EINVAL, "sgd_step: weights must be 8-byte and dW 16-byte aligned");
+    bf16_t* wb = static_cast<bf16_t*>(w);
+    const size_t n4 = n / 4;
+    if (n4 > 0) {
+        size_t blocks = std::min<size_t>((n4 + 255) / 256, 8192);
+        hipLaunchKernelGGL(sgd_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, wb, dw, n4, lr);
+        ZB_HIP(hipGetLastError());
+    }
+    if (n4 * 4 < n) {
+        hipLaunchKernelGGL(sgd_bf16_tail_kernel, dim3(1), dim3(64), 0, s, wb, dw, n4 * 4, n, lr);
+        ZB_HIP(hipGetLastError());
+    }
     return ZB_OK;
 }
 

@@ -11,6 +11,7 @@
 // are both issued in ascending microbatch order, so the live microbatches
 // always form a contiguous range.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -302,6 +303,27 @@ extern "C" int32_t zb_stage_zero_grad(zb_stage* st, void* stream) {
     st->chain_valid[PASS_W] = true;
     for (auto& sl : st->slots) sl.mb = -1;
     st->next_f = st->next_w = 0;
+    return ZB_OK;
+}
+
+extern "C" int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream) {
+    if (!st || !std::isfinite(lr)) return fail(ZB_EINVAL, "zb_stage_sgd_step: bad argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (auto& sl : st->slots)
+        if (sl.mb >= 0 && !sl.w_issued) return fail(ZB_ESTATE, "zb_stage_sgd_step: microbatch " + std::to_string(sl.mb) + " still in flight");
+    if (st->chain_valid[PASS_W]) ZB_HIP(hipStreamWaitEvent(s, st->chain[PASS_W], 0));
+    const zb_stage_desc& d = st->desc;
+    const int nw = zb_stage_num_weights(&d);
+    for (int i = 0; i < nw; ++i) {
+        const int32_t rc = sgd_step(st->w[i], d.dtype, st->dw[i], weight_elems(d, i), lr, s);
+        if (rc) return rc;
+    }
+    return zb_stage_zero_grad(st, stream);
+}
+
+extern "C" int32_t zb_stage_set_lr(zb_stage* st, float lr) {
+    if (!st || !std::isfinite(lr)) return fail(ZB_EINVAL, "zb_stage_set_lr: bad argument");
+    st->lr = lr;
     return ZB_OK;
 }
 

@@ -55,6 +55,7 @@ struct zb_stage {
     std::array<hipEvent_t, 3> chain{};     // last op of each pass (scratch reuse order)
     std::array<bool, 3> chain_valid{};
     int next_f = 0, next_w = 0;
+    float lr = 0.f;  // learning rate of the executor's optimizer-step ops
 
     ~zb_stage();
     void* slot_tensor(int mb, int layer, int which) const;

@@ -392,3 +392,42 @@ def test_gemm_entries_brute_force():
     got = od.gemm_nt_entries(a, b, rows, cols)
     for i, (r, c) in enumerate(zip(rows, cols)):
         assert abs(got[i] - sum(a[r, k] * b[c, k] for k in range(7))) < 1e-13
+
+
+# ------------------------------------------------------- optimizer step ---
+
+def test_bf16_round_matches_torch_conversion():
+    """The oracle's round-to-nearest-even equals torch's float32 -> bfloat16
+    conversion (a library routine) on random values and on constructed ties."""
+    import torch
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    ties = (np.array([1.0, -1.0, 3.0, 0.5], np.float32).view(np.uint32)[:, None]
+            + np.array([0x8000, 0x18000, 0x7FFF, 0x8001], np.uint32)[None, :]).ravel().view(np.float32)
+    for v in (x, ties):
+        ref = torch.from_numpy(v.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+        assert np.array_equal(od.bf16_round(v), ref)
+
+
+def test_bf16_round_ties_to_even():
+    assert od.bf16_round(np.array([1 + 2 ** -8], np.float32))[0] == 1.0             # halfway, even below
+    assert od.bf16_round(np.array([1 + 3 * 2 ** -8], np.float32))[0] == 1 + 2 ** -6  # halfway, even above
+    assert od.bf16_round(np.array([-(1 + 2 ** -8)], np.float32))[0] == -1.0
+    assert od.bf16_round(np.array([1 + 2 ** -8 + 2 ** -20], np.float32))[0] == 1 + 2 ** -7
+
+
+def test_sgd_step_special_cases():
+    rng = np.random.default_rng(4)
+    w = od.bf16_round(rng.standard_normal(4096).astype(np.float32))
+    dw = rng.standard_normal(4096).astype(np.float32)
+    assert np.array_equal(od.sgd_step(w, dw, 0.0, "bf16"), w)                    # lr = 0: unchanged
+    assert od.sgd_step(np.array([1.0]), np.array([0.5]), 0.5, "bf16")[0] == 0.75  # exact
+    assert od.sgd_step(np.array([1.0]), np.array([3.0]), 0.25, "f32")[0] == 0.25
+    # the result is the exact value rounded twice: within half a bf16 unit of it
+    exact = w - np.float64(np.float32(1e-2)) * dw.astype(np.float64)
+    got = od.sgd_step(w, dw, 1e-2, "bf16")
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact))) - 7)
+    assert np.all(np.abs(got - exact) <= 0.5 * ulp * (1 + 2 ** -15))
+    # a step against the gradient lowers a quadratic loss sum(w^2)/2 (dW = w)
+    ww = od.bf16_round(rng.standard_normal(4096).astype(np.float32))
+    assert np.sum(od.sgd_step(ww, ww.astype(np.float32), 0.1, "bf16") ** 2) < np.sum(ww ** 2)
