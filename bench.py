@@ -25,6 +25,8 @@ Extra fields on the JSON line:
   the simulator's prediction (see executor_idle).
 * memory_limit_sweep_p8_stage3: ZB(M) for M = 8 .. 16 replayed the same way,
   with the stash each order keeps resident at its peak (memory_limit_sweep).
+* two_iterations_p8_stage3: two iterations back to back with a per-stage
+  optimizer step between them (multi_iteration).
 """
 from __future__ import annotations
 
@@ -323,6 +325,47 @@ def memory_limit_sweep(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3):
     return {"unit_ms": round(unit, 3), "slot_GiB": round(slot / 2**30, 3), "runs": rows}
 
 
+def multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o, p=8, stage_idx=3, n_iter=2, lr=1e-4):
+    """Two iterations back to back (zb_schedule_generate_iters, M = 2p):
+    each stage runs its optimizer step (SGD, then cleared dW) after its own
+    last W, and its next iteration's F waits only for that step and the
+    upstream F.  Replayed in ordered and filler mode with arrivals at costs
+    1:1:1 (units of a tenth of the mean pass time, the optimizer step rounded
+    to that unit) and at the measured costs (0.1 ms units).  Reports the
+    in-window idle over the whole run, the stage end and the gap between the
+    stage's optimizer step and its next F, each beside the simulator's."""
+    import torch
+    import split_backward_amd as zb
+    u = (t_f + t_b + t_w) / 3.0
+    ys2 = [torch.empty_like(y) for y in ys]
+    dxs2 = [torch.empty_like(d) for d in dxs]
+    X, Y, DY, DX = xs * n_iter, (ys + ys2)[:m * n_iter], dys * n_iter, (dxs + dxs2)[:m * n_iter]
+    q = 0.1
+    cases = [("costs_1:1:1", (10, 10, 10), max(1, int(round(10 * t_o / u))), u / 10),
+             ("measured_costs", tuple(max(1, int(round(t / q))) for t in (t_f, t_b, t_w)), max(1, int(round(t_o / q))), q)]
+    stage.set_lr(lr)
+    out = {"optimizer_step_ms": round(t_o, 3), "n_iter": n_iter, "M": 2 * p}
+    for name, costs, c_opt, unit in cases:
+        g = zb.schedule_generate_iters(p, m, 2 * p, costs, c_opt, n_iter, stage_idx)
+        ops = g["ops"]
+        o_idx = [k for k, (t, _) in enumerate(ops) if t == "O"]
+        pred_gap = (g["start"][o_idx[0] + 1] - g["end"][o_idx[0]]) * unit
+        win = g["last_end"] - g["first_start"]
+        row = {"costs": costs, "c_opt": c_opt, "unit_ms": round(unit, 4),
+               "predicted_in_window_idle": round(1 - g["busy"] / win, 5),
+               "predicted_stage_end_ms": round(g["last_end"] * unit, 2), "predicted_gap_ms": round(pred_gap, 3)}
+        for mode_name, mode in (("ordered", zb.EXEC_ORDERED), ("filler", zb.EXEC_FILLER)):
+            stage.zero_grad()
+            torch.cuda.synchronize()
+            r = stage.run_schedule(ops, g["arrive_f"], g["arrive_b"], unit, X, Y, DY, DX, mode=mode)
+            om = r["op_ms"]
+            row[mode_name] = {"in_window_idle": round(r["in_window_idle"], 5), "stage_end_ms": round(r["t_last_end_ms"], 2),
+                              "gap_ms": round(om[o_idx[0] + 1][0] - om[o_idx[0]][1], 3)}
+        out[name] = row
+    stage.set_lr(0.0)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +448,15 @@ def main():
     if shape.kind == "llama" and not args.no_executor:
         extra["executor_p8_stage3"] = executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w)
         extra["memory_limit_sweep_p8_stage3"] = memory_limit_sweep(stage, m, xs, ys, dys, dxs, (t_f + t_b + t_w) / 3.0)
+        # the optimizer step's own time (SGD over every weight, then dW cleared)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stage.sgd_step(0.0)
+        e0.record()
+        stage.sgd_step(0.0)
+        e1.record()
+        torch.cuda.synchronize()
+        t_o = e0.elapsed_time(e1)
+        extra["two_iterations_p8_stage3"] = multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o)
     cpu = None if args.no_cpu_baseline else cpu_baseline(shape)
 
     line = {
