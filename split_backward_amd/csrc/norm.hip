@@ -205,16 +205,6 @@ __global__ void sgd_bf16_kernel(bf16_t* __restrict__ w, const float* __restrict_
         reinterpret_cast<u32x2*>(w)[i] = v;
     }
 }
-// The elements past the last full group of four, one per thread.
-__global__ void sgd_bf16_tail_kernel(bf16_t* __restrict__ w, const float* __restrict__ dw, size_t begin, size_t n,
-                                     float lr) {
-#pragma clang fp contract(off)
-    const size_t i = begin + threadIdx.x;
-    if (i < n) {
-        const float t = lr * dw[i];
-        w[i] = f2bf(bf2f(w[i]) - t);
-    }
-}
 __global__ void sgd_f32_kernel(float* __restrict__ w, const float* __restrict__ dw, size_t n, float lr) {
 #pragma clang fp contract(off)
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -307,19 +297,14 @@ int32_t sgd_step(void* w, int dtype, const float* dw, size_t n, float lr, hipStr
         ZB_HIP(hipGetLastError());
         return ZB_OK;
     }
-    if ((reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(dw) & 15))
-        return fail(ZB_EINVAL, "sgd_step: weights must be 8-byte and dW 16-byte aligned");
-    bf16_t* wb = static_cast<bf16_t*>(w);
+    // bf16 stages have widths divisible by 8, so every bf16 weight is a
+    // whole number of four-element groups.
+    if ((reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(dw) & 15) || n % 4)
+        return fail(ZB_EINVAL, "sgd_step: bf16 weights need 8-byte alignment, dW 16-byte, a size divisible by 4");
     const size_t n4 = n / 4;
-    if (n4 > 0) {
-        size_t blocks = std::min<size_t>((n4 + 255) / 256, 8192);
-        hipLaunchKernelGGL(sgd_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, wb, dw, n4, lr);
-        ZB_HIP(hipGetLastError());
-    }
-    if (n4 * 4 < n) {
-        hipLaunchKernelGGL(sgd_bf16_tail_kernel, dim3(1), dim3(64), 0, s, wb, dw, n4 * 4, n, lr);
-        ZB_HIP(hipGetLastError());
-    }
+    size_t blocks = std::min<size_t>((n4 + 255) / 256, 8192);
+    hipLaunchKernelGGL(sgd_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<bf16_t*>(w), dw, n4, lr);
+    ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
 
