@@ -326,10 +326,11 @@ def memory_limit_sweep(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3):
 
 
 def multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o, p=8, stage_idx=3, n_iter=2, lr=1e-4):
-    """Two iterations back to back (zb_schedule_generate_iters, M = 2p):
-    each stage runs its optimizer step (SGD, then cleared dW) after its own
-    last W, and its next iteration's F waits only for that step and the
-    upstream F.  Replayed in ordered and filler mode with arrivals at costs
+    """Two iterations back to back (zb_schedule_generate_iters; zero bubble
+    with M = 2p, and 1F1B for comparison): each stage runs its optimizer step
+    (SGD, then cleared dW) after its own last W, and its next iteration's F
+    waits only for that step and the upstream F.  Replayed in ordered mode
+    (and filler mode for the zero-bubble order) with arrivals at costs
     1:1:1 (units of a tenth of the mean pass time, the optimizer step rounded
     to that unit) and at the measured costs (0.1 ms units).  Reports the
     in-window idle over the whole run, the stage end and the gap between the
@@ -346,22 +347,25 @@ def multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o, p=8, stage_i
     stage.set_lr(lr)
     out = {"optimizer_step_ms": round(t_o, 3), "n_iter": n_iter, "M": 2 * p}
     for name, costs, c_opt, unit in cases:
-        g = zb.schedule_generate_iters(p, m, 2 * p, costs, c_opt, n_iter, stage_idx)
-        ops = g["ops"]
-        o_idx = [k for k, (t, _) in enumerate(ops) if t == "O"]
-        pred_gap = (g["start"][o_idx[0] + 1] - g["end"][o_idx[0]]) * unit
-        win = g["last_end"] - g["first_start"]
-        row = {"costs": costs, "c_opt": c_opt, "unit_ms": round(unit, 4),
-               "predicted_in_window_idle": round(1 - g["busy"] / win, 5),
-               "predicted_stage_end_ms": round(g["last_end"] * unit, 2), "predicted_gap_ms": round(pred_gap, 3)}
-        for mode_name, mode in (("ordered", zb.EXEC_ORDERED), ("filler", zb.EXEC_FILLER)):
-            stage.zero_grad()
-            torch.cuda.synchronize()
-            r = stage.run_schedule(ops, g["arrive_f"], g["arrive_b"], unit, X, Y, DY, DX, mode=mode)
-            om = r["op_ms"]
-            row[mode_name] = {"in_window_idle": round(r["in_window_idle"], 5), "stage_end_ms": round(r["t_last_end_ms"], 2),
-                              "gap_ms": round(om[o_idx[0] + 1][0] - om[o_idx[0]][1], 3)}
-        out[name] = row
+        for kind, M, modes in (("zb", 2 * p, (("ordered", zb.EXEC_ORDERED), ("filler", zb.EXEC_FILLER))),
+                               ("1f1b", 0, (("ordered", zb.EXEC_ORDERED),))):
+            g = zb.schedule_generate_iters(p, m, M, costs, c_opt, n_iter, stage_idx, kind=kind)
+            ops = g["ops"]
+            o_idx = [k for k, (t, _) in enumerate(ops) if t == "O"]
+            pred_gap = (g["start"][o_idx[0] + 1] - g["end"][o_idx[0]]) * unit
+            win = g["last_end"] - g["first_start"]
+            row = {"costs": costs, "c_opt": c_opt, "unit_ms": round(unit, 4),
+                   "predicted_in_window_idle": round(1 - g["busy"] / win, 5),
+                   "predicted_stage_end_ms": round(g["last_end"] * unit, 2), "predicted_gap_ms": round(pred_gap, 3)}
+            for mode_name, mode in modes:
+                stage.zero_grad()
+                torch.cuda.synchronize()
+                r = stage.run_schedule(ops, g["arrive_f"], g["arrive_b"], unit, X, Y, DY, DX, mode=mode)
+                om = r["op_ms"]
+                row[mode_name] = {"in_window_idle": round(r["in_window_idle"], 5),
+                                  "stage_end_ms": round(r["t_last_end_ms"], 2),
+                                  "gap_ms": round(om[o_idx[0] + 1][0] - om[o_idx[0]][1], 3)}
+            out[f"{kind}_{name}"] = row
     stage.set_lr(0.0)
     return out
 

@@ -215,19 +215,21 @@ int32_t zb_schedule_generate(int32_t kind, int32_t p, int32_t m, int32_t mem_lim
                              zb_op* ops, int64_t* start, int64_t* end, int32_t cap,
                              int64_t* arrive_f, int64_t* arrive_b, zb_sched_stats* stats);
 
-/* Several iterations of the zero-bubble greedy, back to back.  Each stage
- * closes iteration it with an optimizer step (op ZB_OP_O, mb = it, cost
- * c_opt >= 1) as soon as all of its own W of that iteration have completed;
- * its first F of iteration it+1 waits for that step and for the upstream
- * F, and for nothing else.  The abstract page "Zero Bubble Pipeline
- * Parallelism" says the method bypasses the optimizer step's
- * synchronizations; this is read as no barrier across stages.  A ready step
- * is taken before any B, F or W; otherwise the rules of ZB above apply with
- * the global microbatch index g = it * m + j (F, B, W ops carry g).
- * Outputs as for zb_schedule_generate, with 3 m n_iter + n_iter ops and
- * arrivals indexed by g (arrive_f / arrive_b of m * n_iter entries).
- * Returns the number of ops or ZB_EINVAL. */
-int32_t zb_schedule_generate_iters(int32_t p, int32_t m, int32_t mem_limit, int32_t cF, int32_t cB,
+/* Several iterations back to back (kind ZB_SCHED_ZB or ZB_SCHED_1F1B).
+ * Each stage closes iteration it with an optimizer step (op ZB_OP_O,
+ * mb = it, cost c_opt >= 1) as soon as all of its own W of that iteration
+ * have completed; its first F of iteration it+1 waits for that step and for
+ * the upstream F, and for nothing else.  The abstract page "Zero Bubble
+ * Pipeline Parallelism" says the method bypasses the optimizer step's
+ * synchronizations; this is read as no barrier across stages.
+ *   ZB  : a ready step is taken before any B, F or W; otherwise the rules of
+ *         ZB above apply with the global microbatch index g = it * m + j.
+ *   1F1B: each stage's 1F1B sequence of every iteration, the step after it.
+ * F, B, W ops carry g.  Outputs as for zb_schedule_generate, with
+ * 3 m n_iter + n_iter ops and arrivals indexed by g (arrive_f / arrive_b of
+ * m * n_iter entries; arrive_b the downstream B for ZB, the downstream
+ * whole backward for 1F1B).  Returns the number of ops or ZB_EINVAL. */
+int32_t zb_schedule_generate_iters(int32_t kind, int32_t p, int32_t m, int32_t mem_limit, int32_t cF, int32_t cB,
                                    int32_t cW, int32_t c_opt, int32_t n_iter, int32_t stage,
                                    zb_op* ops, int64_t* start, int64_t* end, int32_t cap,
                                    int64_t* arrive_f, int64_t* arrive_b, zb_sched_stats* stats);

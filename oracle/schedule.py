@@ -282,9 +282,78 @@ class IterResult:
         return [(o.type, o.mb) for o in self.ops[i]]
 
 
-def simulate_iterations(p: int, m: int, M: int, costs=(1, 1, 1), n_iter: int = 2, c_opt: int = 1) -> IterResult:
+def _simulate_1f1b_iterations(p, m, costs, n_iter, c_opt):
+    """1F1B over several iterations: each stage runs its fixed 1F1B sequence
+    of iteration it (microbatches g = it*m + j, whole backwards), then its
+    optimizer step O(it), then the sequence of iteration it+1; an op starts
+    when its stage is free and its inputs exist (the step follows the
+    stage's last backward by sequence order, and the next iteration's F
+    waits for the step the same way)."""
+    cF, cB, cW = costs
+    G = n_iter * m
+    seqs = []
+    for i in range(p):
+        seq = []
+        for it in range(n_iter):
+            seq += [(t, it * m + j) for t, j in _fixed_orders(ONE_F_ONE_B, p, m)[i]] + [("O", it)]
+        seqs.append(seq)
+    end: Dict[Tuple[str, int, int], int] = {}
+    free = [0] * p
+    pos = [0] * p
+    ops: List[List[Op]] = [[] for _ in range(p)]
+    active, peak = [0] * p, [0] * p
+    remaining = sum(len(q) for q in seqs)
+    while remaining:
+        progressed = False
+        for i in range(p):
+            while pos[i] < len(seqs[i]):
+                t, k = seqs[i][pos[i]]
+                if t == "F":
+                    deps, cost = ([("F", i - 1, k)] if i > 0 else []), cF
+                elif t == "BW":
+                    deps, cost = [("F", i, k)] + ([("BW", i + 1, k)] if i < p - 1 else []), cB + cW
+                else:
+                    deps, cost = [], c_opt
+                if any(d not in end for d in deps):
+                    break
+                st = max([free[i]] + [end[d] for d in deps])
+                end[(t, i, k)] = st + cost
+                free[i] = st + cost
+                if t == "F":
+                    ops[i].append(Op("F", k, st, st + cF))
+                    active[i] += 1
+                    peak[i] = max(peak[i], active[i])
+                elif t == "BW":
+                    ops[i].append(Op("B", k, st, st + cB))
+                    ops[i].append(Op("W", k, st + cB, st + cB + cW))
+                    active[i] -= 1
+                else:
+                    ops[i].append(Op("O", k, st, st + cost))
+                pos[i] += 1
+                remaining -= 1
+                progressed = True
+        if not progressed:
+            raise RuntimeError("fixed order deadlocked")
+    stats = [StageStats(sum(o.end - o.start for o in ops[i]), ops[i][0].start, ops[i][-1].end, peak[i])
+             for i in range(p)]
+    arrive_f = [[end[("F", i - 1, g)] if i > 0 else 0 for g in range(G)] for i in range(p)]
+    arrive_b = [[end[("BW", i + 1, g)] if i < p - 1 else 0 for g in range(G)] for i in range(p)]
+    return ops, stats, arrive_f, arrive_b
+
+
+def simulate_iterations(p: int, m: int, M: int, costs=(1, 1, 1), n_iter: int = 2, c_opt: int = 1,
+                        kind: str = ZB) -> IterResult:
+    """Several iterations back to back: kind "zb" (the greedy below, memory
+    limit M) or "1f1b" (fixed sequences, M unused)."""
     cF, cB, cW = (int(c) for c in costs)
     c_opt = int(c_opt)
+    if kind == ONE_F_ONE_B:
+        if p < 1 or m < 1 or cF < 1 or cB < 1 or cW < 0 or n_iter < 1 or c_opt < 1:
+            raise ValueError("bad arguments")
+        ops, stats, af, ab = _simulate_1f1b_iterations(p, m, (cF, cB, cW), n_iter, c_opt)
+        return IterResult(p, m, M, n_iter, (cF, cB, cW), c_opt, ops, stats, max(s.last_end for s in stats), af, ab)
+    if kind != ZB:
+        raise ValueError(kind)
     if p < 1 or m < 1 or M < 1 or cF < 1 or cB < 1 or cW < 1 or n_iter < 1 or c_opt < 1:
         raise ValueError("bad arguments")
     G = n_iter * m

@@ -81,7 +81,7 @@ _PROTOS = {
     "zb_schedule_generate": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Op),
                                     ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, ctypes.POINTER(_i64),
                                     ctypes.POINTER(_i64), ctypes.POINTER(SchedStats)]),
-    "zb_schedule_generate_iters": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Op),
+    "zb_schedule_generate_iters": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Op),
                                           ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, ctypes.POINTER(_i64),
                                           ctypes.POINTER(_i64), ctypes.POINTER(SchedStats)]),
     "zb_stage_run_schedule": (_i32, [_vp, ctypes.POINTER(Op), _i32, ctypes.POINTER(ctypes.c_double),
@@ -148,9 +148,9 @@ def schedule_generate(kind: str, p: int, m: int, mem_limit: int = 0, costs=(1, 1
 
 
 def schedule_generate_iters(p: int, m: int, mem_limit: int, costs=(1, 1, 1), c_opt: int = 1, n_iter: int = 2,
-                            stage: int = 0) -> dict:
-    """Zero-bubble order of n_iter iterations for one stage, with an
-    optimizer step ("O", iteration) closing each (no GPU needed).  F, B, W
+                            stage: int = 0, kind: str = "zb") -> dict:
+    """Zero-bubble (or 1F1B) order of n_iter iterations for one stage, with
+    an optimizer step ("O", iteration) closing each (no GPU needed).  F, B, W
     ops carry the global microbatch index it * m + j; arrivals are indexed
     by it."""
     G = m * n_iter
@@ -161,8 +161,8 @@ def schedule_generate_iters(p: int, m: int, mem_limit: int, costs=(1, 1, 1), c_o
     af = (ctypes.c_int64 * G)()
     ab = (ctypes.c_int64 * G)()
     stats = SchedStats()
-    cnt = lib().zb_schedule_generate_iters(p, m, mem_limit, costs[0], costs[1], costs[2], c_opt, n_iter, stage, ops,
-                                           st, en, n, af, ab, ctypes.byref(stats))
+    cnt = lib().zb_schedule_generate_iters(SCHED[kind], p, m, mem_limit, costs[0], costs[1], costs[2], c_opt, n_iter,
+                                           stage, ops, st, en, n, af, ab, ctypes.byref(stats))
     check(cnt)
     return {
         "ops": [(OPNAME[ops[i].type], ops[i].mb) for i in range(cnt)],

@@ -229,17 +229,112 @@ extern "C" int32_t zb_schedule_generate(int32_t kind, int32_t p, int32_t m, int3
 // iteration it is g = it*m + j; "lowest microbatch" is the lowest g and the
 // memory limit counts stashed microbatches of any iteration.  A ready O is
 // taken before any B, F or W.
-extern "C" int32_t zb_schedule_generate_iters(int32_t p, int32_t m, int32_t mem_limit, int32_t cF, int32_t cB,
-                                              int32_t cW, int32_t c_opt, int32_t n_iter, int32_t stage, zb_op* ops,
-                                              int64_t* start, int64_t* end, int32_t cap, int64_t* arrive_f,
-                                              int64_t* arrive_b, zb_sched_stats* stats) {
-    if (p < 1 || m < 1 || n_iter < 1 || stage < 0 || stage >= p || cF < 1 || cB < 1 || cW < 1 || c_opt < 1 ||
-        mem_limit < 1)
-        return ZB_EINVAL;
+namespace {
+// 1F1B over several iterations: each stage runs its fixed 1F1B sequence of
+// iteration it (whole backwards, microbatches g = it*m + j), then its
+// optimizer step, then iteration it+1; an op starts when its stage is free
+// and its inputs exist.  Fills the stage's ops and the arrival times.
+bool run_fixed_iters(int p, int m, int n_iter, int64_t cF, int64_t cB, int64_t cW, int64_t c_opt,
+                     std::vector<std::vector<Placed>>& placed, std::vector<int>& peak, std::vector<int64_t>& Fe,
+                     std::vector<int64_t>& BWe) {
+    const int G = m * n_iter;
+    enum { S_F = 0, S_BW = 1, S_O = 2 };
+    std::vector<std::vector<std::pair<int, int>>> seq(p);  // (kind, index)
+    for (int i = 0; i < p; ++i) {
+        const int warm = std::min(p - 1 - i, m);
+        for (int it = 0; it < n_iter; ++it) {
+            const int b = it * m;
+            for (int j = 0; j < warm; ++j) seq[i].push_back({S_F, b + j});
+            for (int j = warm; j < m; ++j) {
+                seq[i].push_back({S_F, b + j});
+                seq[i].push_back({S_BW, b + j - warm});
+            }
+            for (int j = m - warm; j < m; ++j) seq[i].push_back({S_BW, b + j});
+            seq[i].push_back({S_O, it});
+        }
+    }
+    auto at = [G](int i, int g) { return (size_t)i * G + g; };
+    std::vector<size_t> next(p, 0);
+    std::vector<int64_t> free_at(p, 0);
+    std::vector<int> active(p, 0);
+    size_t left = 0;
+    for (auto& q : seq) left += q.size();
+    while (left > 0) {
+        bool moved = false;
+        for (int i = 0; i < p; ++i) {
+            while (next[i] < seq[i].size()) {
+                const auto [kind, k] = seq[i][next[i]];
+                int64_t ready = 0;
+                if (kind == S_F) ready = (i == 0) ? 0 : Fe[at(i - 1, k)];
+                else if (kind == S_BW) ready = std::max(Fe[at(i, k)], (i == p - 1) ? int64_t(0) : BWe[at(i + 1, k)]);
+                if (ready == NOT_DONE) break;
+                const int64_t st = std::max(ready, free_at[i]);
+                if (kind == S_F) {
+                    Fe[at(i, k)] = st + cF;
+                    free_at[i] = st + cF;
+                    placed[i].push_back({ZB_OP_F, k, st, st + cF});
+                    peak[i] = std::max(peak[i], ++active[i]);
+                } else if (kind == S_BW) {
+                    BWe[at(i, k)] = st + cB + cW;
+                    free_at[i] = st + cB + cW;
+                    placed[i].push_back({ZB_OP_B, k, st, st + cB});
+                    placed[i].push_back({ZB_OP_W, k, st + cB, st + cB + cW});
+                    --active[i];
+                } else {
+                    free_at[i] = st + c_opt;
+                    placed[i].push_back({ZB_OP_O, k, st, st + c_opt});
+                }
+                ++next[i];
+                --left;
+                moved = true;
+            }
+        }
+        if (!moved) return false;
+    }
+    return true;
+}
+}  // namespace
+
+extern "C" int32_t zb_schedule_generate_iters(int32_t kind, int32_t p, int32_t m, int32_t mem_limit, int32_t cF,
+                                              int32_t cB, int32_t cW, int32_t c_opt, int32_t n_iter, int32_t stage,
+                                              zb_op* ops, int64_t* start, int64_t* end, int32_t cap,
+                                              int64_t* arrive_f, int64_t* arrive_b, zb_sched_stats* stats) {
+    if (kind != ZB_SCHED_ZB && kind != ZB_SCHED_1F1B) return ZB_EINVAL;
+    if (p < 1 || m < 1 || n_iter < 1 || stage < 0 || stage >= p || cF < 1 || cB < 1 || c_opt < 1) return ZB_EINVAL;
+    if (kind == ZB_SCHED_ZB && (cW < 1 || mem_limit < 1)) return ZB_EINVAL;
+    if (cW < 0) return ZB_EINVAL;
     if ((int64_t)p * m * n_iter > 1 << 22) return ZB_EINVAL;
     const int G = m * n_iter;
     const int n_stage_ops = 3 * G + n_iter;
     if ((ops || start || end) && cap < n_stage_ops) return ZB_EINVAL;
+    if (kind == ZB_SCHED_1F1B) {
+        std::vector<std::vector<Placed>> placed(p);
+        std::vector<int> peak(p, 0);
+        std::vector<int64_t> Fe((size_t)p * G, NOT_DONE), BWe((size_t)p * G, NOT_DONE);
+        if (!run_fixed_iters(p, m, n_iter, cF, cB, cW, c_opt, placed, peak, Fe, BWe)) return ZB_EINVAL;
+        const auto& mine = placed[stage];
+        for (size_t q = 0; q < mine.size(); ++q) {
+            if (ops) ops[q] = zb_op{mine[q].type, mine[q].mb};
+            if (start) start[q] = mine[q].start;
+            if (end) end[q] = mine[q].end;
+        }
+        for (int g = 0; g < G; ++g) {
+            if (arrive_f) arrive_f[g] = stage == 0 ? 0 : Fe[(size_t)(stage - 1) * G + g];
+            if (arrive_b) arrive_b[g] = stage == p - 1 ? 0 : BWe[(size_t)(stage + 1) * G + g];
+        }
+        if (stats) {
+            int64_t mk = 0, b = 0;
+            for (int i = 0; i < p; ++i) mk = std::max(mk, placed[i].back().end);
+            for (const auto& o : mine) b += o.end - o.start;
+            stats->makespan = mk;
+            stats->busy = b;
+            stats->first_start = mine.front().start;
+            stats->last_end = mine.back().end;
+            stats->peak_active = peak[stage];
+            stats->n_ops = (int32_t)mine.size();
+        }
+        return (int32_t)mine.size();
+    }
     std::vector<int64_t> Fe((size_t)p * G, NOT_DONE), Be((size_t)p * G, NOT_DONE), Oe((size_t)p * n_iter, NOT_DONE);
     auto at = [G](int i, int g) { return (size_t)i * G + g; };
     std::vector<std::vector<char>> b_started(p, std::vector<char>(G, 0)), w_started(p, std::vector<char>(G, 0));

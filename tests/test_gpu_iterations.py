@@ -71,10 +71,11 @@ def _snapshot(st, ys, dxs):
             [to_f64(d) for d in dxs])
 
 
-@pytest.mark.parametrize("mode", [zb.EXEC_ORDERED, zb.EXEC_FILLER])
-def test_two_iteration_replay_matches_sequential(mode):
-    p, stage, m, M, n_iter = 4, 1, 4, 4, 2
-    g = zb.schedule_generate_iters(p, m, M, (2, 2, 2), 1, n_iter, stage)
+@pytest.mark.parametrize("kind,mode", [("zb", zb.EXEC_ORDERED), ("zb", zb.EXEC_FILLER), ("1f1b", zb.EXEC_ORDERED)])
+def test_two_iteration_replay_matches_sequential(kind, mode):
+    p, stage, m, n_iter = 4, 1, 4, 2
+    g = zb.schedule_generate_iters(p, m, 4 if kind == "zb" else 0, (2, 2, 2), 1, n_iter, stage, kind=kind)
+    M = max(g["peak_active"], 1)  # ring slots
     ops = g["ops"]
     assert [t for t, _ in ops].count("O") == n_iter
     # one set of per-microbatch buffers per iteration (iteration 2 reuses the inputs of iteration 1)

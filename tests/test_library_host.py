@@ -164,14 +164,16 @@ def test_compute_calls_reject_null_stage():
     assert L.zb_stage_zero_grad(None, None) == zb.EINVAL
 
 
+@pytest.mark.parametrize("kind", ["zb", "1f1b"])
 @pytest.mark.parametrize("p,m,M,costs,c_opt,n", [(8, 16, 16, (1, 1, 1), 1, 3), (4, 8, 8, (2, 3, 2), 2, 2),
                                                 (8, 16, 8, (63, 84, 63), 1, 2), (4, 6, 5, (1, 2, 1), 3, 3),
                                                 (2, 1, 1, (1, 1, 1), 1, 2)])
-def test_iteration_generator_matches_oracle_bit_exact(p, m, M, costs, c_opt, n):
+def test_iteration_generator_matches_oracle_bit_exact(kind, p, m, M, costs, c_opt, n):
     from oracle.schedule import simulate_iterations
-    ref = simulate_iterations(p, m, M, costs, n, c_opt)
+    M = M if kind == "zb" else 0
+    ref = simulate_iterations(p, m, M, costs, n, c_opt, kind=kind)
     for stage in range(p):
-        g = zb.schedule_generate_iters(p, m, M, costs, c_opt, n, stage)
+        g = zb.schedule_generate_iters(p, m, M, costs, c_opt, n, stage, kind=kind)
         assert g["ops"] == ref.order(stage)
         assert g["start"] == [o.start for o in ref.ops[stage]]
         assert g["end"] == [o.end for o in ref.ops[stage]]
@@ -183,7 +185,7 @@ def test_iteration_generator_matches_oracle_bit_exact(p, m, M, costs, c_opt, n):
 
 
 def test_iteration_generator_rejects_bad_arguments():
-    for bad in (dict(n_iter=0), dict(c_opt=0), dict(mem_limit=0), dict(stage=4)):
+    for bad in (dict(n_iter=0), dict(c_opt=0), dict(mem_limit=0), dict(stage=4), dict(kind="gpipe")):
         kw = dict(p=4, m=8, mem_limit=8, costs=(1, 1, 1), c_opt=1, n_iter=2, stage=0)
         kw.update(bad)
         with pytest.raises(zb.ZbError):

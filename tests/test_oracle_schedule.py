@@ -181,6 +181,9 @@ def _check_iteration_dependencies(r):
     limit never exceeded."""
     p, m, n = r.p, r.m, r.n_iter
     G = n * m
+    # the gradient a stage sends upstream: after B (zero bubble), after the
+    # whole backward B + W (1F1B, M = 0)
+    down = "W" if r.M == 0 else "B"
     end = {}
     for i in range(p):
         seen = set()
@@ -203,11 +206,11 @@ def _check_iteration_dependencies(r):
                 if it > 0:
                     assert end[("O", i, it - 1)][1] <= s
                 active += 1
-                assert active <= r.M
+                assert r.M == 0 or active <= r.M   # M = 0: 1F1B, no memory limit
             elif o.type == "B":
                 assert end[("F", i, o.mb)][1] <= s
                 if i < p - 1:
-                    assert end[("B", i + 1, o.mb)][1] <= s
+                    assert end[(down, i + 1, o.mb)][1] <= s
             elif o.type == "W":
                 assert end[("B", i, o.mb)][1] <= s
                 active -= 1
@@ -218,32 +221,35 @@ def _check_iteration_dependencies(r):
             if i > 0:
                 assert r.arrive_f[i][g] == end[("F", i - 1, g)][1]
             if i < p - 1:
-                assert r.arrive_b[i][g] == end[("B", i + 1, g)][1]
+                assert r.arrive_b[i][g] == end[(down, i + 1, g)][1]
 
 
-@pytest.mark.parametrize("p,m,M,costs,c_opt,n", ITER_CASES)
-def test_iterations_dependencies_and_memory(p, m, M, costs, c_opt, n):
-    _check_iteration_dependencies(S.simulate_iterations(p, m, M, costs, n, c_opt))
+ITER_KIND_CASES = [("zb",) + c for c in ITER_CASES] + [("1f1b", p, m, 0, costs, c_opt, n) for p, m, _, costs, c_opt, n in ITER_CASES]
 
 
-@pytest.mark.parametrize("p,m,M,costs,c_opt,n", ITER_CASES)
-def test_one_iteration_is_the_single_iteration_schedule(p, m, M, costs, c_opt, n):
-    r = S.simulate_iterations(p, m, M, costs, 1, c_opt)
-    single = S.simulate("zb", p, m, M, costs)
+@pytest.mark.parametrize("kind,p,m,M,costs,c_opt,n", ITER_KIND_CASES)
+def test_iterations_dependencies_and_memory(kind, p, m, M, costs, c_opt, n):
+    _check_iteration_dependencies(S.simulate_iterations(p, m, M, costs, n, c_opt, kind=kind))
+
+
+@pytest.mark.parametrize("kind,p,m,M,costs,c_opt,n", ITER_KIND_CASES)
+def test_one_iteration_is_the_single_iteration_schedule(kind, p, m, M, costs, c_opt, n):
+    r = S.simulate_iterations(p, m, M, costs, 1, c_opt, kind=kind)
+    single = S.simulate(kind, p, m, M, costs)
     for i in range(p):
         got = [(o.type, o.mb, o.start, o.end) for o in r.ops[i]]
         last_w = single.ops[i][-1].end
         assert got == [(o.type, o.mb, o.start, o.end) for o in single.ops[i]] + [("O", 0, last_w, last_w + c_opt)]
 
 
-@pytest.mark.parametrize("p,m,M,costs,c_opt,n", ITER_CASES)
-def test_iterations_repeat_with_stage0_period(p, m, M, costs, c_opt, n):
+@pytest.mark.parametrize("kind,p,m,M,costs,c_opt,n", ITER_KIND_CASES)
+def test_iterations_repeat_with_stage0_period(kind, p, m, M, costs, c_opt, n):
     """Every stage's iteration k is its iteration 0 shifted by k * T, with
     T = stage 0's single-iteration end + c_opt (stage 0 starts iteration k+1
     right after its optimizer step, and nothing else gates it), so the
     makespan is (n-1) T + makespan(1) + c_opt."""
-    r = S.simulate_iterations(p, m, M, costs, n, c_opt)
-    single = S.simulate("zb", p, m, M, costs)
+    r = S.simulate_iterations(p, m, M, costs, n, c_opt, kind=kind)
+    single = S.simulate(kind, p, m, M, costs)
     T = single.stats[0].last_end + c_opt
     for i in range(p):
         base = [(o.type, o.mb, o.start, o.end) for o in single.ops[i]]
@@ -270,3 +276,16 @@ def test_iterations_reject_bad_arguments():
         kw.update(bad)
         with pytest.raises(ValueError):
             S.simulate_iterations(**kw)
+
+
+@pytest.mark.parametrize("p,m,n", [(8, 16, 2), (4, 8, 3)])
+def test_1f1b_iterations_keep_a_bubble_where_zero_bubble_has_none(p, m, n):
+    """Equal costs, m >= 2p: over several iterations every 1F1B stage but the
+    first and the last idles inside its window (its ramp-up and ramp-down
+    gaps sit between iterations), while ZB(2p) tiles without idle."""
+    r1 = S.simulate_iterations(p, m, 0, (1, 1, 1), n, 1, kind="1f1b")
+    rz = S.simulate_iterations(p, m, 2 * p, (1, 1, 1), n, 1, kind="zb")
+    for i in range(p):
+        assert rz.stats[i].busy == rz.stats[i].last_end - rz.stats[i].first_start
+        if 0 < i < p - 1:
+            assert r1.stats[i].busy < r1.stats[i].last_end - r1.stats[i].first_start
