@@ -131,15 +131,25 @@ W_KERNEL_SOURCES = ("split_backward_amd/csrc/gemm_v2.hip", "split_backward_amd/c
 TRAFFIC_SUMMARY = "profiles/gemm_w_kernel_hbm_traffic_llama7b_stage4.md"
 
 
+COMMON_H_END = "// ------------------------------------------------- elementwise / norms ----"
+
+
 def kernel_source_hash() -> str:
     """sha256 prefix of the W kernel's sources with comments and whitespace
-    removed (a comment edit does not invalidate the measured traffic)."""
+    removed (a comment edit does not invalidate the measured traffic): all of
+    gemm_v2.hip, and common.h up to its elementwise / norms section (the
+    types and GEMM declarations the kernel is built from)."""
     import hashlib
     import re
     h = hashlib.sha256()
     for f in W_KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
             src = fh.read()
+        if f.endswith("common.h"):
+            cut = src.find(COMMON_H_END)
+            if cut < 0:
+                raise RuntimeError(f"{f}: section marker missing")
+            src = src[:cut]
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
         h.update("".join(src.split()).encode())

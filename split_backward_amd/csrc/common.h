@@ -84,10 +84,25 @@ int32_t gemm_bf16_group_segmented(const GemmDesc* ds, int n, hipStream_t s, bool
 
 // ------------------------------------------------- elementwise / norms ----
 int32_t fill_f32(float* p, size_t n, float v, hipStream_t s);
-// w (bf16 or fp32, dtype ZB_BF16 / ZB_F32) -= lr * dw (fp32), elementwise:
-// fp32 product and difference each rounded once, then rounded once to the
-// weight's type (round to nearest even).
-int32_t sgd_step(void* w, int dtype, const float* dw, size_t n, float lr, hipStream_t s);
+// fp32 w -= lr * dw, elementwise, the product and the difference each
+// rounded once.
+int32_t sgd_step_f32(float* w, const float* dw, size_t n, float lr, hipStream_t s);
+// bf16 w -= lr * dw for up to SGD_GROUP_MAX weights in one launch: fp32
+// product and difference each rounded once, then rounded once to bf16
+// (round to nearest even); each dW is cleared as it is consumed.
+// n4 = elements / 4 (bf16 stages have widths divisible by 8).
+constexpr int SGD_GROUP_MAX = 64;
+struct SgdSeg {
+    void* w;
+    float* dw;
+    size_t n4;
+};
+struct SgdGroup {
+    SgdSeg seg[SGD_GROUP_MAX];
+    int n;
+    float lr;
+};
+int32_t sgd_step_group_bf16(const SgdGroup& g, hipStream_t s);
 int32_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
 // n = RMS(x) * g, r = 1/sqrt(mean(x^2)+eps) per row; x, n bf16 [T, H]; r f32 [T].
 int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps,

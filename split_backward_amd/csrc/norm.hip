@@ -184,27 +184,34 @@ __global__ void fill_f32_kernel(float* p, size_t n, float v) {
 // Optimizer step w -= lr * dW, in fp32 with the product and the difference
 // each rounded once (no fused multiply-add: contraction is switched off in
 // these kernels; the __fmul_rn / __fsub_rn helpers are fused regardless,
-// because they are inlined from headers that allow it), then w
-// rounded once to bf16 (round to nearest even).  Four consecutive elements
-// per thread.
-__global__ void sgd_bf16_kernel(bf16_t* __restrict__ w, const float* __restrict__ dw, size_t n4, float lr) {
-#pragma clang fp contract(off)  // the product and the difference are rounded separately
+// because they are inlined from headers that allow it), then w rounded once
+// to the weight's type (bf16: round to nearest even).
+// All bf16 weights of a stage in one launch: segment blockIdx.y, grid-stride
+// over its groups of four; dW is cleared as it is consumed (the step ends
+// an iteration), so no separate fill pass follows.
+__global__ void sgd_bf16_group_kernel(SgdGroup g) {
+#pragma clang fp contract(off)
+    const SgdSeg sg = g.seg[blockIdx.y];
+    bf16_t* __restrict__ w = static_cast<bf16_t*>(sg.w);
+    float* __restrict__ dw = sg.dw;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < sg.n4; i += stride) {
         const floatx4 d = reinterpret_cast<const floatx4*>(dw)[i];
         u32x2 v = reinterpret_cast<const u32x2*>(w)[i];
         float x[4] = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
                       __uint_as_float(v[1] & 0xffff0000u)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float t = lr * d[e];
+            const float t = g.lr * d[e];
             x[e] = x[e] - t;
         }
         v[0] = uint32_t(f2bf(x[0])) | (uint32_t(f2bf(x[1])) << 16);
         v[1] = uint32_t(f2bf(x[2])) | (uint32_t(f2bf(x[3])) << 16);
         reinterpret_cast<u32x2*>(w)[i] = v;
+        reinterpret_cast<floatx4*>(dw)[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 }
+
 __global__ void sgd_f32_kernel(float* __restrict__ w, const float* __restrict__ dw, size_t n, float lr) {
 #pragma clang fp contract(off)
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -289,21 +296,26 @@ int32_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
     return ZB_OK;
 }
 
-int32_t sgd_step(void* w, int dtype, const float* dw, size_t n, float lr, hipStream_t s) {
+int32_t sgd_step_f32(float* w, const float* dw, size_t n, float lr, hipStream_t s) {
     if (n == 0) return ZB_OK;
-    if (dtype == ZB_F32) {
-        size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
-        hipLaunchKernelGGL(sgd_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<float*>(w), dw, n, lr);
-        ZB_HIP(hipGetLastError());
-        return ZB_OK;
+    size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
+    hipLaunchKernelGGL(sgd_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, dw, n, lr);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+int32_t sgd_step_group_bf16(const SgdGroup& g, hipStream_t s) {
+    if (g.n < 1 || g.n > SGD_GROUP_MAX) return fail(ZB_EINVAL, "sgd_step_group_bf16: bad segment count");
+    size_t most = 0;
+    for (int i = 0; i < g.n; ++i) {
+        const SgdSeg& sg = g.seg[i];
+        if ((reinterpret_cast<uintptr_t>(sg.w) & 7) || (reinterpret_cast<uintptr_t>(sg.dw) & 15))
+            return fail(ZB_EINVAL, "sgd_step_group_bf16: weights need 8-byte and dW 16-byte alignment");
+        most = std::max<size_t>(most, sg.n4);
     }
-    // bf16 stages have widths divisible by 8, so every bf16 weight is a
-    // whole number of four-element groups.
-    if ((reinterpret_cast<uintptr_t>(w) & 7) || (reinterpret_cast<uintptr_t>(dw) & 15) || n % 4)
-        return fail(ZB_EINVAL, "sgd_step: bf16 weights need 8-byte alignment, dW 16-byte, a size divisible by 4");
-    const size_t n4 = n / 4;
-    size_t blocks = std::min<size_t>((n4 + 255) / 256, 8192);
-    hipLaunchKernelGGL(sgd_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<bf16_t*>(w), dw, n4, lr);
+    if (most == 0) return ZB_OK;
+    const size_t bx = std::min<size_t>((most + 255) / 256, 2048);
+    hipLaunchKernelGGL(sgd_bf16_group_kernel, dim3((unsigned)bx, (unsigned)g.n), dim3(256), 0, s, g);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }

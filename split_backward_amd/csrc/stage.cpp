@@ -314,11 +314,32 @@ extern "C" int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream) {
     if (st->chain_valid[PASS_W]) ZB_HIP(hipStreamWaitEvent(s, st->chain[PASS_W], 0));
     const zb_stage_desc& d = st->desc;
     const int nw = zb_stage_num_weights(&d);
-    for (int i = 0; i < nw; ++i) {
-        const int32_t rc = sgd_step(st->w[i], d.dtype, st->dw[i], weight_elems(d, i), lr, s);
+    if (d.dtype != ZB_BF16) {  // the fp32 linear stage: per weight, then the clearing fill
+        for (int i = 0; i < nw; ++i) {
+            const int32_t rc = sgd_step_f32(static_cast<float*>(st->w[i]), st->dw[i], weight_elems(d, i), lr, s);
+            if (rc) return rc;
+        }
+        return zb_stage_zero_grad(st, stream);
+    }
+    // bf16: every weight in grouped launches that also clear dW
+    for (int i0 = 0; i0 < nw; i0 += SGD_GROUP_MAX) {
+        SgdGroup g{};
+        g.lr = lr;
+        g.n = std::min(SGD_GROUP_MAX, nw - i0);
+        for (int k = 0; k < g.n; ++k) {
+            const size_t n = weight_elems(d, i0 + k);
+            if (n % 4) return fail(ZB_EINVAL, "zb_stage_sgd_step: weight size not divisible by 4");
+            g.seg[k] = SgdSeg{st->w[i0 + k], st->dw[i0 + k], n / 4};
+        }
+        const int32_t rc = sgd_step_group_bf16(g, s);
         if (rc) return rc;
     }
-    return zb_stage_zero_grad(st, stream);
+    // the same reset as zb_stage_zero_grad, without its fill
+    ZB_HIP(hipEventRecord(st->chain[PASS_W], s));
+    st->chain_valid[PASS_W] = true;
+    for (auto& sl : st->slots) sl.mb = -1;
+    st->next_f = st->next_w = 0;
+    return ZB_OK;
 }
 
 extern "C" int32_t zb_stage_set_lr(zb_stage* st, float lr) {
