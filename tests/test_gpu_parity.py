@@ -206,6 +206,20 @@ def test_llama_small_parity(shape):
     assert max(r.values()) <= BF16_TOL, r
 
 
+def test_one_slot_ring_reused_by_every_microbatch():
+    """Ring of one slot (memory limit 1): F B W of each microbatch in turn,
+    every F reusing the slot the previous W released.  Equal to the oracle,
+    and bit for bit to the same order with a slot per microbatch."""
+    shape = synth.StageShape("llama", 256, 256, 344, n_layers=2, n_heads=2, n_kv_heads=1, head_dim=128)
+    g1, orc, _ = run_both(shape, 3, ring=1, order="immediate")
+    g3, _, _ = run_both(shape, 3, ring=3, order="immediate")
+    r = max_rel(g1, orc)
+    assert max(r.values()) <= BF16_TOL, r
+    for k in ("y", "dx", "dw"):
+        for a, b in zip(g1[k], g3[k]):
+            assert np.array_equal(a, b), k
+
+
 # ------------------------------------------------------------ state errors --
 
 def test_stage_state_machine_errors():

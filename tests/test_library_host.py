@@ -167,7 +167,8 @@ def test_compute_calls_reject_null_stage():
 @pytest.mark.parametrize("kind", ["zb", "1f1b"])
 @pytest.mark.parametrize("p,m,M,costs,c_opt,n", [(8, 16, 16, (1, 1, 1), 1, 3), (4, 8, 8, (2, 3, 2), 2, 2),
                                                 (8, 16, 8, (63, 84, 63), 1, 2), (4, 6, 5, (1, 2, 1), 3, 3),
-                                                (2, 1, 1, (1, 1, 1), 1, 2)])
+                                                (2, 1, 1, (1, 1, 1), 1, 2), (1, 4, 1, (2, 3, 1), 1, 3),
+                                                (4, 1, 1, (1, 2, 3), 2, 2)])
 def test_iteration_generator_matches_oracle_bit_exact(kind, p, m, M, costs, c_opt, n):
     from oracle.schedule import simulate_iterations
     M = M if kind == "zb" else 0

@@ -289,3 +289,32 @@ def test_1f1b_iterations_keep_a_bubble_where_zero_bubble_has_none(p, m, n):
         assert rz.stats[i].busy == rz.stats[i].last_end - rz.stats[i].first_start
         if 0 < i < p - 1:
             assert r1.stats[i].busy < r1.stats[i].last_end - r1.stats[i].first_start
+
+
+# ------------------------------------------------------ degenerate cases ---
+
+@pytest.mark.parametrize("costs", [(1, 1, 1), (2, 3, 1), (3, 1, 2)])
+@pytest.mark.parametrize("kind,M", [("gpipe", 0), ("1f1b", 0), ("zb", 1), ("zb", 3)])
+def test_single_stage_has_no_bubble(kind, M, costs):
+    """p = 1: nothing to wait for, so every order runs back to back."""
+    m = 5
+    r = simulate(kind, 1, m, M, costs)
+    assert r.stats[0].busy == r.makespan == m * sum(costs)
+    assert r.stats[0].first_start == 0
+
+
+def test_single_stage_zero_bubble_with_limit_one_is_f_b_w_per_microbatch():
+    r = simulate("zb", 1, 4, 1, (2, 3, 1))
+    assert r.order(0) == [(t, j) for j in range(4) for t in "FBW"]
+
+
+@pytest.mark.parametrize("p", [2, 4, 8])
+@pytest.mark.parametrize("costs", [(1, 1, 1), (2, 3, 1), (1, 2, 3)])
+def test_single_microbatch_runs_the_critical_path(p, costs):
+    """m = 1: F through every stage, B back through every stage, then the
+    first stage's W (zero bubble: W off the path except the last one); the
+    atomic backward orders carry W on the path at every stage."""
+    cF, cB, cW = costs
+    assert simulate("zb", p, 1, 1, costs).makespan == p * cF + p * cB + cW
+    for kind in ("gpipe", "1f1b"):
+        assert simulate(kind, p, 1, 0, costs).makespan == p * cF + p * (cB + cW)
