@@ -375,6 +375,13 @@ def multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o, p=8, stage_i
                 row[mode_name] = {"in_window_idle": round(r["in_window_idle"], 5),
                                   "stage_end_ms": round(r["t_last_end_ms"], 2),
                                   "gap_ms": round(om[o_idx[0] + 1][0] - om[o_idx[0]][1], 3)}
+                if mode == zb.EXEC_ORDERED:
+                    # waits besides the iteration gap: an op starting > 0.3 ms after the
+                    # previous op ended (ordered mode runs the list strictly in turn)
+                    waits = [(t_, j_, round(om[k][0] - om[k - 1][1], 2)) for k, (t_, j_) in enumerate(ops)
+                             if k > 0 and k != o_idx[0] + 1 and om[k][0] - om[k - 1][1] > 0.3]
+                    row[mode_name]["other_waits_ms"] = round(sum(w for _, _, w in waits), 2)
+                    row[mode_name]["other_waits"] = waits[:8]
             out[f"{kind}_{name}"] = row
     stage.set_lr(0.0)
     return out
@@ -444,18 +451,23 @@ def main():
     flops = linear_flops_per_mb(shape) * m
     tflops = flops / dt / 1e12
 
-    # per-pass unit time (for the executor's arrival unit u = mean of F, B, W)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    stage.zero_grad()
-    ev[0].record()
-    stage.fwd(0, xs[0], ys[0])
-    ev[1].record()
-    stage.bwd_input(0, dys[0], dxs[0])
-    ev[2].record()
-    stage.bwd_weight(0)
-    ev[3].record()
-    torch.cuda.synchronize()
-    t_f, t_b, t_w = (ev[i].elapsed_time(ev[i + 1]) for i in range(3))
+    # per-pass times (the executor's arrival unit u = mean of F, B, W, and its
+    # measured-cost runs): the median of five F, B, W passes, since a single
+    # pass right after the timed steps can run slower than the replay does
+    samples = []
+    for _ in range(5):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        stage.zero_grad()
+        ev[0].record()
+        stage.fwd(0, xs[0], ys[0])
+        ev[1].record()
+        stage.bwd_input(0, dys[0], dxs[0])
+        ev[2].record()
+        stage.bwd_weight(0)
+        ev[3].record()
+        torch.cuda.synchronize()
+        samples.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
+    t_f, t_b, t_w = (sorted(col)[len(col) // 2] for col in zip(*samples))
 
     roof = time_w_kernel(shape, args.workload, device)
     extra = {}

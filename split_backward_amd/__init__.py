@@ -248,7 +248,10 @@ class Stage:
                 self.torch.cuda.synchronize(self.device)
             except Exception:
                 pass
-            lib().zb_stage_destroy(h)
+            try:
+                lib().zb_stage_destroy(h)
+            except Exception:  # interpreter shutdown: module globals may already be gone
+                pass
             self.handle = None
 
     def slot_bytes(self) -> int:
