@@ -469,7 +469,10 @@ def main():
         samples.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
     t_f, t_b, t_w = (sorted(col)[len(col) // 2] for col in zip(*samples))
 
-    roof = time_w_kernel(shape, args.workload, device)
+    # The fp32 linear workload runs the fp32 GEMM (a few microseconds per
+    # product, launch-bound): no roofline figure for it.
+    roof = time_w_kernel(shape, args.workload, device) if shape.dtype == "bf16" else {
+        "bound": None, "note": "fp32 linear workload: launch-bound fp32 GEMM, no roofline figure"}
     extra = {}
     if shape.kind == "llama" and not args.no_executor:
         extra["executor_p8_stage3"] = executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w)
