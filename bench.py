@@ -348,9 +348,10 @@ def multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o, p=8, stage_i
     import torch
     import split_backward_amd as zb
     u = (t_f + t_b + t_w) / 3.0
-    ys2 = [torch.empty_like(y) for y in ys]
-    dxs2 = [torch.empty_like(d) for d in dxs]
-    X, Y, DY, DX = xs * n_iter, (ys + ys2)[:m * n_iter], dys * n_iter, (dxs + dxs2)[:m * n_iter]
+    # inputs repeat every iteration; each iteration writes outputs of its own
+    X, DY = xs * n_iter, dys * n_iter
+    Y = list(ys) + [torch.empty_like(y) for _ in range(n_iter - 1) for y in ys]
+    DX = list(dxs) + [torch.empty_like(d) for _ in range(n_iter - 1) for d in dxs]
     q = 0.1
     cases = [("costs_1:1:1", (10, 10, 10), max(1, int(round(10 * t_o / u))), u / 10),
              ("measured_costs", tuple(max(1, int(round(t / q))) for t in (t_f, t_b, t_w)), max(1, int(round(t_o / q))), q)]
