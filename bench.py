@@ -402,7 +402,7 @@ def main():
                     help="only run the copy + W-kernel workload that the --pmc passes count")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs one pipeline stage on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
