@@ -94,10 +94,9 @@ def issue_plan(order, pair_w=True):
 
 def make_inputs(shape, m, device):
     import torch
-    from tests.gpu_helpers import to_dev
     import synth
-    xs = [to_dev(synth.make_x(shape, j), device) for j in range(m)]
-    dys = [to_dev(synth.make_dy(shape, j), device) for j in range(m)]
+    xs = [synth.to_device(synth.make_x(shape, j), device) for j in range(m)]
+    dys = [synth.to_device(synth.make_dy(shape, j), device) for j in range(m)]
     dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
     out_w = shape.ffn if shape.kind == "linear" else shape.hidden
     ys = [torch.empty((shape.tokens, out_w), dtype=dt, device=device) for _ in range(m)]
@@ -408,7 +407,6 @@ def main():
     import torch
     import split_backward_amd as zb
     import synth
-    from tests.gpu_helpers import to_dev
 
     wl = synth.WORKLOADS[args.workload]
     shape, m = wl["shape"], wl["m"]
@@ -418,7 +416,7 @@ def main():
     if args.traffic_probe:
         traffic_probe(shape, device)
         return
-    weights = [to_dev(w, device) for w in synth.make_weights(shape)]
+    weights = [synth.to_device(w, device) for w in synth.make_weights(shape)]
     stage = zb.Stage(shape.kind, shape.tokens, shape.hidden, shape.ffn, weights, dtype=shape.dtype,
                      n_layers=shape.n_layers, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
                      head_dim=shape.head_dim if shape.kind == "llama" else 128, ring_slots=ring)

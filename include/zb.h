@@ -60,6 +60,8 @@ enum { ZB_F32 = 0, ZB_BF16 = 1 };
  *  ZB_MLP_GELU fc1 -> GeLU(tanh) -> fc2, no bias.  Weights {W1[ffn,hidden], W2[hidden,ffn]}.
  *  ZB_LLAMA    n_layers pre-norm decoder layers: RMSNorm, causal GQA
  *              attention (no RoPE), residual, RMSNorm, SwiGLU MLP, residual.
+ *              tokens must be a multiple of 128 (the attention kernels'
+ *              query and key blocks), head_dim 128, hidden <= 8192.
  *              Weights per layer l, in this order:
  *                Wqkv[(n_heads+2*n_kv_heads)*head_dim, hidden] (rows: q | k | v),
  *                Wo[hidden, n_heads*head_dim], Wgu[2*ffn, hidden] (rows: gate | up),
@@ -162,7 +164,8 @@ int32_t zb_stage_stash_tensor(zb_stage* st, int32_t mb, int32_t layer, int32_t w
  * (fp32 product and difference, each rounded once, then rounded once to the
  * weight's type, round to nearest even), after every issued W has completed
  * on the device; then dW is cleared and the stage is reset for a new
- * iteration as by zb_stage_zero_grad.  A plain SGD step: the pages name an
+ * iteration as by zb_stage_zero_grad.  The next F, on whatever stream it is
+ * issued, waits for the step on the device.  A plain SGD step: the pages name an
  * optimizer step per iteration but no optimizer.  lr must be finite.
  * Errors: ZB_EINVAL, ZB_ESTATE if a microbatch is in flight (its W not
  * issued). */
@@ -268,9 +271,16 @@ typedef struct {
  * zb_stage_sgd_step with the rate of zb_stage_set_lr on the high stream,
  * after every W issued before it, and the next F restarts the stage's own
  * numbering at 0.
+ * Each op's start stamp is taken after its dependency waits (its pass's
+ * previous op, its microbatch's previous op, the W that frees a reused ring
+ * slot) and its arrival wait, so op intervals and the idle figure count only
+ * time in which the op could run.
  * Errors: as the compute calls, plus ZB_EINVAL for a malformed op list (an
  * op type outside F, B, W, O, a negative index, or an op of an iteration an
- * optimizer step has already closed), detected before any work is issued. */
+ * optimizer step has already closed), a unit_ms that is not finite or < 0,
+ * or an arrival more than 30 s (the wait kernel's cap) after the start, all
+ * detected before any work is issued (the op list and the times are checked
+ * before the stage pointer). */
 int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t n,
                               const double* arrive_f, const double* arrive_b, double unit_ms,
                               const void* const* x, void* const* y,

@@ -13,8 +13,10 @@
 //            for the W that frees it), so W soaks up whatever gaps remain.
 // Optimizer-step ops (several iterations back to back) run on the high
 // stream after every W issued before them.  Each op is bracketed by two
-// clock-stamp kernels; idle time is the part of the stage's window
-// [first op start, last op end] that no op interval covers.
+// clock-stamp kernels, the first issued after the op's dependency and
+// arrival waits, so an interval covers only the time the op could run; idle
+// time is the part of the stage's window [first op start, last op end] that
+// no op interval covers.
 #include <algorithm>
 #include <cmath>
 #include <vector>
@@ -47,9 +49,13 @@ extern "C" int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t
                                          const double* arrive_b, double unit_ms, const void* const* x, void* const* y,
                                          const void* const* dy, void* const* dx, void* hi_stream, void* lo_stream,
                                          int32_t mode, zb_run_stats* stats, double* op_ms) {
-    if (!st || !ops || n < 1 || n > MAX_RUN_OPS || !arrive_f || !arrive_b || !(unit_ms >= 0.0) || !x || !y || !dy ||
-        !dx)
-        return fail(ZB_EINVAL, "zb_stage_run_schedule: bad argument");
+    // The op list and the times are checked first (host only, before the
+    // stage is looked at): every wait the run would issue must end within
+    // the wait kernel's 30 s cap.
+    if (!ops || n < 1 || n > MAX_RUN_OPS || !arrive_f || !arrive_b)
+        return fail(ZB_EINVAL, "zb_stage_run_schedule: bad op list or arrival arrays");
+    if (!std::isfinite(unit_ms) || unit_ms < 0.0)
+        return fail(ZB_EINVAL, "zb_stage_run_schedule: unit_ms must be finite and >= 0");
     if (mode != ZB_EXEC_ORDERED && mode != ZB_EXEC_FILLER) return fail(ZB_EINVAL, "zb_stage_run_schedule: bad mode");
     // F, B and W ops carry a microbatch index into x, y, dy, dx and the
     // arrivals; an optimizer-step op (ZB_OP_O, from
@@ -80,9 +86,14 @@ extern "C" int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t
             nmb = std::max(nmb, ops[k].mb + 1);
         }
     }
-    for (int j = 0; j < nmb; ++j)
+    constexpr double MAX_ARRIVAL_MS = 30000.0;  // the wait kernel's cap
+    for (int j = 0; j < nmb; ++j) {
         if (!(arrive_f[j] >= 0.0) || !(arrive_b[j] >= 0.0) || arrive_f[j] > 1e6 || arrive_b[j] > 1e6)
             return fail(ZB_EINVAL, "zb_stage_run_schedule: arrival times must be in [0, 1e6] units");
+        if (arrive_f[j] * unit_ms > MAX_ARRIVAL_MS || arrive_b[j] * unit_ms > MAX_ARRIVAL_MS)
+            return fail(ZB_EINVAL, "zb_stage_run_schedule: an arrival lies more than 30 s after the run's start");
+    }
+    if (!st || !x || !y || !dy || !dx) return fail(ZB_EINVAL, "zb_stage_run_schedule: bad argument");
 
     StreamGuard hi, lo;
     hi.s = static_cast<hipStream_t>(hi_stream);
@@ -120,6 +131,9 @@ extern "C" int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t
             hipError_t e = hipStreamWaitEvent(s, pool.ev[prev], 0);
             if (e != hipSuccess) { rc = fail(ZB_EHIP, "hipStreamWaitEvent failed"); break; }
         }
+        // the op's own dependencies (on the other stream too) before its start stamp
+        rc = st->wait_deps(op.type, local[k], s);
+        if (rc) break;
         if (op.type == ZB_OP_F || op.type == ZB_OP_B) {
             const double a = op.type == ZB_OP_F ? arrive_f[op.mb] : arrive_b[op.mb];
             const uint64_t delta = (uint64_t)std::llround(a * unit_ms * ticks_per_ms);

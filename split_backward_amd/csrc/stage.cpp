@@ -44,6 +44,7 @@ bool valid_desc(const zb_stage_desc* d, std::string& why) {
     if (d->head_dim != 128) { why = "head_dim must be 128"; return false; }
     if (d->hidden > 8192) { why = "hidden must be <= 8192"; return false; }
     if (!(d->rms_eps > 0.f)) { why = "rms_eps must be > 0"; return false; }
+    if (d->tokens % 128) { why = "the Llama stage's attention needs tokens to be a multiple of 128"; return false; }
     return true;
 }
 
@@ -137,6 +138,26 @@ int32_t zb_stage::order_after(int k, hipEvent_t dep, bool dep_valid, hipStream_t
     if (chain_valid[k]) ZB_HIP(hipStreamWaitEvent(s, chain[k], 0));
     if (dep_valid) ZB_HIP(hipStreamWaitEvent(s, dep, 0));
     return ZB_OK;
+}
+
+int32_t zb_stage::wait_deps(int type, int mb, hipStream_t s) {
+    if (mb < 0) return ZB_OK;
+    const Slot& sl = slots[mb % desc.ring_slots];
+    switch (type) {
+        case ZB_OP_F:
+            if (sl.mb >= 0 && !sl.w_issued) return ZB_OK;  // zb_fwd reports the full ring
+            return order_after(PASS_F, sl.evW, sl.w_event_valid, s);
+        case ZB_OP_B:
+            if (sl.mb != mb || sl.b_issued) return ZB_OK;
+            return order_after(PASS_B, sl.evF, true, s);
+        case ZB_OP_W:
+            if (sl.mb != mb || !sl.b_issued || sl.w_issued) return ZB_OK;
+            return order_after(PASS_W, sl.evB, true, s);
+        case ZB_OP_O:
+            return order_after(PASS_W, nullptr, false, s);
+        default:
+            return ZB_OK;
+    }
 }
 
 int32_t zb_stage::finish(int k, hipEvent_t ev, hipStream_t s) {
@@ -319,7 +340,13 @@ extern "C" int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream) {
             const int32_t rc = sgd_step_f32(static_cast<float*>(st->w[i]), st->dw[i], weight_elems(d, i), lr, s);
             if (rc) return rc;
         }
-        return zb_stage_zero_grad(st, stream);
+        const int32_t rc = zb_stage_zero_grad(st, stream);
+        if (rc) return rc;
+        for (int k : {PASS_F, PASS_B}) {  // the next F reads the updated weights
+            ZB_HIP(hipEventRecord(st->chain[k], s));
+            st->chain_valid[k] = true;
+        }
+        return ZB_OK;
     }
     // bf16: every weight in grouped launches that also clear dW
     for (int i0 = 0; i0 < nw; i0 += SGD_GROUP_MAX) {
@@ -334,9 +361,13 @@ extern "C" int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream) {
         const int32_t rc = sgd_step_group_bf16(g, s);
         if (rc) return rc;
     }
-    // the same reset as zb_stage_zero_grad, without its fill
-    ZB_HIP(hipEventRecord(st->chain[PASS_W], s));
-    st->chain_valid[PASS_W] = true;
+    // the same reset as zb_stage_zero_grad, without its fill; the step's
+    // completion also becomes the last op of F and B, so the next
+    // iteration's first F (on any stream) reads the updated weights
+    for (int k : {PASS_F, PASS_B, PASS_W}) {
+        ZB_HIP(hipEventRecord(st->chain[k], s));
+        st->chain_valid[k] = true;
+    }
     for (auto& sl : st->slots) sl.mb = -1;
     st->next_f = st->next_w = 0;
     return ZB_OK;

@@ -61,6 +61,12 @@ struct zb_stage {
     void* slot_tensor(int mb, int layer, int which) const;
     int32_t order_after(int pass, hipEvent_t dep, bool dep_valid, hipStream_t s);
     int32_t finish(int pass, hipEvent_t ev, hipStream_t s);
+    // Make `s` wait for every event the op (type, mb) waits for when it is
+    // issued (its pass's previous op, the microbatch's previous op, and for F
+    // the W that frees its ring slot); issues nothing for an op that its own
+    // call would reject.  The executor calls this before an op's start stamp,
+    // so the stamp marks the moment the op can actually run.
+    int32_t wait_deps(int type, int mb, hipStream_t s);
 };
 
 namespace zb {

@@ -181,6 +181,16 @@ def make_dy(s: StageShape, mb: int, std: float = None) -> Tensor:
     return make_tensor(f"dy{mb}", DY_SEED_BASE + mb, (s.tokens, out_width(s)), std, s.dtype)
 
 
+def to_device(t: Tensor, device="cuda"):
+    """The tensor's storage bytes as a torch tensor on `device` (float32, or
+    bfloat16 from the bit patterns): a copy of the very values the oracle
+    reads, nothing computed."""
+    import torch
+    if t.dtype == "f32":
+        return torch.from_numpy(t.storage.copy()).to(device)
+    return torch.from_numpy(t.storage.view(np.int16).copy()).view(torch.bfloat16).to(device)
+
+
 # Named workloads (the pages' stage shapes; sizes only, no arithmetic).
 WORKLOADS = {
     # fp32 single linear layer, X[128x256] W[256x256], 2 microbatches

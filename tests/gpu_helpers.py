@@ -11,10 +11,7 @@ import synth
 from oracle import dense as od
 
 
-def to_dev(t: synth.Tensor, device="cuda"):
-    if t.dtype == "f32":
-        return torch.from_numpy(t.storage.copy()).to(device)
-    return torch.from_numpy(t.storage.view(np.int16).copy()).view(torch.bfloat16).to(device)
+to_dev = synth.to_device
 
 
 def to_f64(x: torch.Tensor) -> np.ndarray:

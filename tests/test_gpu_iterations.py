@@ -58,6 +58,34 @@ def test_sgd_step_matches_oracle_bitwise(shape):
     torch.cuda.synchronize()
 
 
+def test_sgd_step_orders_the_next_forward_on_another_stream():
+    """The optimizer step and the next iteration's first F issued on two
+    different streams compute bit for bit what issuing both on one stream
+    computes: the next F waits for the step on the device, whatever stream
+    it is issued on."""
+    outs = []
+    for two_streams in (False, True):
+        st, _ = make_stage(SHAPE, 2)
+        st.zero_grad()
+        xs = [to_dev(synth.make_x(SHAPE, j)) for j in range(2)]
+        for j in range(2):
+            st.fwd(j, xs[j])
+        for j in range(2):
+            st.bwd_input(j, to_dev(synth.make_dy(SHAPE, j)))
+        for j in range(2):
+            st.bwd_weight(j)
+        torch.cuda.synchronize()
+        s1 = torch.cuda.Stream()
+        s2 = torch.cuda.Stream() if two_streams else s1
+        st.sgd_step(LR, stream=s1)
+        y = st.fwd(0, xs[0], stream=s2)
+        torch.cuda.synchronize()
+        outs.append((to_f64(y), [to_f64(w) for w in st.weights]))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    for a, b in zip(outs[0][1], outs[1][1]):
+        assert np.array_equal(a, b)
+
+
 def _inputs(m):
     xs = [to_dev(synth.make_x(SHAPE, j)) for j in range(m)]
     dys = [to_dev(synth.make_dy(SHAPE, j)) for j in range(m)]

@@ -133,7 +133,8 @@ def test_workspace_grows_by_one_slot_per_ring_slot():
 
 
 @pytest.mark.parametrize("bad", [dict(head_dim=64), dict(n_kv_heads=5), dict(ring_slots=0), dict(hidden=4100),
-                                 dict(dtype=zb.F32), dict(tokens=0), dict(kind=7)])
+                                 dict(dtype=zb.F32), dict(tokens=0), dict(kind=7), dict(tokens=4000),
+                                 dict(tokens=200)])
 def test_invalid_descs_rejected(bad):
     L = zb.lib()
     d = _desc(**bad)
@@ -191,3 +192,36 @@ def test_iteration_generator_rejects_bad_arguments():
         kw.update(bad)
         with pytest.raises(zb.ZbError):
             zb.schedule_generate_iters(**kw)
+
+
+def _run_args(n=2, af=(0.0, 0.0), ab=(0.0, 0.0), unit_ms=0.1):
+    ops = (zb.Op * n)(*([zb.Op(zb.OP_F, 0), zb.Op(zb.OP_B, 0)][:n]))
+    dbl = lambda v: (ctypes.c_double * len(v))(*v)
+    return ops, n, dbl(af), dbl(ab), unit_ms
+
+
+@pytest.mark.parametrize("unit_ms,af,msg", [(float("inf"), (0.0, 0.0), "unit_ms"), (float("nan"), (0.0, 0.0), "unit_ms"),
+                                            (-1.0, (0.0, 0.0), "unit_ms"), (1e12, (1.0, 0.0), "30 s"),
+                                            (100.0, (301.0, 0.0), "30 s"), (float("inf"), (0.0, 0.0), "unit_ms")])
+def test_executor_rejects_unbounded_waits_before_any_work(unit_ms, af, msg):
+    """Every arrival wait must end within the wait kernel's 30 s cap: a unit
+    that is not finite, or an arrival x unit beyond 30 s, is rejected while
+    checking the arguments, before the stage is looked at (so no GPU is
+    needed to see it)."""
+    L = zb.lib()
+    ops, n, a_f, a_b, u = _run_args(af=af, unit_ms=unit_ms)
+    rc = L.zb_stage_run_schedule(None, ops, n, a_f, a_b, u, None, None, None, None, None, None, zb.EXEC_ORDERED,
+                                 None, None)
+    assert rc == zb.EINVAL
+    assert msg in zb.last_error()
+
+
+def test_executor_bounded_waits_pass_argument_checks():
+    """A finite unit with every arrival within 30 s gets past the time checks
+    (and then fails on the NULL stage)."""
+    L = zb.lib()
+    ops, n, a_f, a_b, u = _run_args(af=(299.0, 0.0), unit_ms=100.0)
+    rc = L.zb_stage_run_schedule(None, ops, n, a_f, a_b, u, None, None, None, None, None, None, zb.EXEC_ORDERED,
+                                 None, None)
+    assert rc == zb.EINVAL
+    assert "bad argument" in zb.last_error()
