@@ -130,6 +130,23 @@ int32_t zb_bwd_input(zb_stage* st, int32_t mb, const void* dy, void* dx, void* s
  * the next W in ascending order. */
 int32_t zb_bwd_weight_accum(zb_stage* st, int32_t mb, void* stream);
 
+/* zb_bwd_weight_accum for callers that cannot allocate memory (code under
+ * HIP graph capture, tight loops, harnesses that forbid allocation): the
+ * same work, state rules, errors and bit-identical results, with the W pass's
+ * only scratch (the fp32 RMSNorm dgamma partials: ceil(tokens / 64) * hidden
+ * floats, Llama stages only) in a fixed device array of
+ * ZB_NOALLOC_SCRATCH_BYTES inside the library instead of the stage's
+ * workspace.  Each GPU holds its own copy of that array until the process
+ * ends; it is looked up on the first call on a device.  Calls no allocating
+ * routine.  All calls on one GPU share the array: calls that may overlap in
+ * time on one GPU (other stages, other streams without ordering between
+ * them) race and must be serialized by the caller.
+ * Errors: as zb_bwd_weight_accum, plus ZB_EINVAL when the stage needs more
+ * scratch than ZB_NOALLOC_SCRATCH_BYTES or the stage's device is not the
+ * current one. */
+#define ZB_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int32_t zb_bwd_weight_accum_noalloc(zb_stage* st, int32_t mb, void* stream);
+
 /* W for microbatches mb and mb + 1 in one pass.  The weight-gradient pass is
  * deferrable and needs only the stashed activations and output gradients
  * (Guide, "Core Innovation 1": the weight gradient does not feed any other

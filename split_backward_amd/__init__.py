@@ -73,6 +73,7 @@ _PROTOS = {
     "zb_bwd_input": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "zb_bwd_weight_accum": (_i32, [_vp, _i32, _vp]),
     "zb_bwd_weight_accum_pair": (_i32, [_vp, _i32, _vp]),
+    "zb_bwd_weight_accum_noalloc": (_i32, [_vp, _i32, _vp]),
     "zb_stage_zero_grad": (_i32, [_vp, _vp]),
     "zb_stage_sgd_step": (_i32, [_vp, ctypes.c_float, _vp]),
     "zb_stage_set_lr": (_i32, [_vp, ctypes.c_float]),
@@ -284,6 +285,11 @@ class Stage:
 
     def bwd_weight(self, mb: int, stream=None):
         check(lib().zb_bwd_weight_accum(self.handle, mb, _stream_ptr(stream)))
+
+    def bwd_weight_noalloc(self, mb: int, stream=None):
+        """W for microbatch mb with its scratch in the library's fixed device
+        array (zb_bwd_weight_accum_noalloc)."""
+        check(lib().zb_bwd_weight_accum_noalloc(self.handle, mb, _stream_ptr(stream)))
 
     def bwd_weight_pair(self, mb: int, stream=None):
         """W for microbatches mb and mb + 1 in one pass (zb_bwd_weight_accum_pair)."""

@@ -172,7 +172,11 @@ int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipSt
     return ZB_OK;
 }
 
-int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s) {
+size_t dgamma_scratch_bytes(const zb_stage_desc& d) {
+    return d.kind == ZB_LLAMA ? rmsnorm_dgamma_scratch_floats(d.tokens, d.hidden) * sizeof(float) : 0;
+}
+
+int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s, float* dg_part) {
     const zb_stage_desc& d = st.desc;
     const int T = d.tokens, H = d.hidden, F = d.ffn;
     if (d.kind == ZB_LINEAR)
@@ -188,7 +192,7 @@ int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s) {
         return gemm_bf16_group(g, 2, s);
     }
     const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
-    float* part = reinterpret_cast<float*>(st.scratch_w);
+    float* part = dg_part ? dg_part : reinterpret_cast<float*>(st.scratch_w);
     std::vector<GemmDesc> g;
     g.reserve(4 * d.n_layers);
     for (int l = 0; l < d.n_layers; ++l) {

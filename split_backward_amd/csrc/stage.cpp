@@ -201,6 +201,7 @@ extern "C" int32_t zb_stage_create(const zb_stage_desc* d, void* const* weights,
         if (!weights[i] || !dw[i]) return fail(ZB_EINVAL, "NULL weight or dW pointer " + std::to_string(i));
     auto st = new zb_stage();
     st->desc = *d;
+    if (hipGetDevice(&st->device) != hipSuccess) st->device = 0;
     st->lay.build(*d);
     if (ws_bytes < st->lay.total) {
         const size_t need = st->lay.total;
@@ -266,13 +267,16 @@ extern "C" int32_t zb_bwd_input(zb_stage* st, int32_t mb, const void* dy, void* 
 
 extern "C" int32_t zb_bwd_weight_accum(zb_stage* st, int32_t mb, void* stream) {
     if (!st || mb < 0) return fail(ZB_EINVAL, "zb_bwd_weight_accum: bad argument");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return bwd_weight_accum(st, mb, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int32_t zb::bwd_weight_accum(zb_stage* st, int mb, hipStream_t s, float* dg_part) {
     Slot& sl = st->slots[mb % st->desc.ring_slots];
     if (sl.mb != mb || !sl.b_issued || sl.w_issued) return fail(ZB_ESTATE, "zb_bwd_weight_accum: needs B(mb) issued and W(mb) not yet issued");
     if (mb != st->next_w) return fail(ZB_ESTATE, "zb_bwd_weight_accum: W must be issued in ascending microbatch order; expected mb " + std::to_string(st->next_w));
     int32_t rc = st->order_after(PASS_W, sl.evB, true, s);
     if (rc) return rc;
-    rc = run_backward_weight(*st, mb, s);
+    rc = run_backward_weight(*st, mb, s, dg_part);
     if (rc) return rc;
     sl.w_issued = true;
     sl.w_event_valid = true;

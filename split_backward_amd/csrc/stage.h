@@ -56,6 +56,7 @@ struct zb_stage {
     std::array<bool, 3> chain_valid{};
     int next_f = 0, next_w = 0;
     float lr = 0.f;  // learning rate of the executor's optimizer-step ops
+    int device = 0;  // the HIP device current when the stage was created
 
     ~zb_stage();
     void* slot_tensor(int mb, int layer, int which) const;
@@ -72,6 +73,12 @@ struct zb_stage {
 namespace zb {
 int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s);
 int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipStream_t s);
-int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s);
+// dg_part: fp32 scratch of the RMSNorm dgamma partials
+// (dgamma_scratch_bytes); nullptr = the stage's workspace scratch.
+int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s, float* dg_part = nullptr);
+size_t dgamma_scratch_bytes(const zb_stage_desc& d);
+// zb_bwd_weight_accum with the dgamma partials in dg_part (nullptr: the
+// stage's workspace scratch).
+int32_t bwd_weight_accum(zb_stage* st, int mb, hipStream_t s, float* dg_part);
 int32_t run_backward_weight_pair(zb_stage& st, int mb, hipStream_t s);
 }  // namespace zb
