@@ -22,7 +22,8 @@ Extra fields on the JSON line:
   (one decoder layer, one microbatch, 256 tokens, full widths).
 * executor_p8_stage3: the stage replayed with emulated arrivals (device-clock
   waits) for the 1F1B and zero-bubble orders; in-window idle of each, beside
-  the simulator's prediction (see executor_idle).
+  the simulator's prediction (see executor_idle); and interleaved 1F1B with
+  the stage split into two chunks (interleaved_idle).
 * memory_limit_sweep_p8_stage3: ZB(M) for M = 8 .. 16 replayed the same way,
   with the stash each order keeps resident at its peak (memory_limit_sweep).
 * two_iterations_p8_stage3: two iterations back to back with a per-stage
@@ -40,6 +41,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+
+
+def calibrate(stage, xs, ys, dys, dxs, n=5):
+    """Median over n passes of the F, B and W pass times of microbatch 0 (ms)."""
+    import torch
+    samples = []
+    for _ in range(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        stage.zero_grad()
+        ev[0].record()
+        stage.fwd(0, xs[0], ys[0])
+        ev[1].record()
+        stage.bwd_input(0, dys[0], dxs[0])
+        ev[2].record()
+        stage.bwd_weight(0)
+        ev[3].record()
+        torch.cuda.synchronize()
+        samples.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
+    return tuple(sorted(col)[len(col) // 2] for col in zip(*samples))
 
 
 def linear_flops_per_mb(s) -> float:
@@ -224,7 +244,7 @@ def traffic_probe(shape, device):
                       "shapes_MNK": gem, "kernel_source_sha256": kernel_source_hash()}), flush=True)
 
 
-def cpu_baseline(shape):
+def cpu_baseline(shape, m):
     """fp64 oracle on a bounded sample: one decoder layer (or the whole
     stage for the small kinds), one microbatch, F + B + W."""
     import numpy as np
@@ -260,8 +280,21 @@ def cpu_baseline(shape):
         t_total += time.perf_counter() - t0
         reps += 1
     flops = reps * linear_flops_per_mb(sample)
+    # the whole step's work over the sample's work, at the sample's flop rate
+    # (linear work grows with the tokens, attention with their square)
+    per_rep = t_total / reps
+    sample_work = linear_flops_per_mb(sample) + attention_flops_per_mb(sample)
+    full_work = (linear_flops_per_mb(shape) + attention_flops_per_mb(shape)) * m
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = None
     return {"value": round(flops / t_total / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{desc}; fp64 numpy; {reps} repetitions in {t_total:.1f} s"}
+            "sample": f"{desc}; fp64 numpy (products through its BLAS); {reps} repetitions in {t_total:.1f} s",
+            "nproc": os.cpu_count(), "affinity_cpus": affinity, "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "extrapolated_step_s": round(per_rep * full_work / sample_work, 1),
+            "extrapolated_note": "EXTRAPOLATED, not measured: the full step's linear and attention flops at the "
+                                 "sample's measured rate"}
 
 
 def executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w):
@@ -299,6 +332,68 @@ def executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w):
                      "busy_ms": round(r["busy_ms"], 2), "stage_end_ms": round(r["t_last_end_ms"], 2),
                      "predicted_in_window_idle": round(1 - g["busy"] / win, 5),
                      "predicted_stage_end_ms": round(g["last_end"] * u, 2)}
+    return out
+
+
+def interleaved_idle(weights, shape, m, xs, dys, p=8, stage_idx=3, v=2):
+    """Interleaved 1F1B (v = 2) on the GPU: the stage's layers split into
+    two chunks of n_layers / 2 layers (two stage objects sharing the
+    stage's weight tensors), replayed in the interleaved order of stage 3
+    of an emulated 8-stage pipeline with arrivals at chunk costs 1:1:1 in
+    units of the mean measured chunk pass time.  Reports measured in-window
+    idle and stage end beside the simulator's ([Guide] "Quantitative
+    Comparison": 17.9% bubble for v = 2 at p = 8, m = 16)."""
+    import torch
+    import split_backward_amd as zb
+    L = shape.n_layers
+    if L % v or m % p:
+        return None
+    lc = L // v
+    g = zb.schedule_generate_interleaved(p, m, v, (1, 1, 1), stage_idx)
+    peaks = []
+    for c in range(v):
+        live = peak = 0
+        for t, cc, _ in g["ops"]:
+            if cc == c and t in "FW":
+                live += 1 if t == "F" else -1
+                peak = max(peak, live)
+        peaks.append(peak)
+    chunks = [zb.Stage("llama", shape.tokens, shape.hidden, shape.ffn, weights[6 * lc * c:6 * lc * (c + 1)],
+                       n_layers=lc, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim,
+                       ring_slots=peaks[c]) for c in range(v)]
+    ys = [[torch.empty_like(x) for x in xs] for _ in range(v)]
+    dxs = [[torch.empty_like(x) for x in xs] for _ in range(v)]
+    # chunk pass times: the median of five F, B, W passes of chunk 0
+    samples = []
+    for _ in range(5):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        chunks[0].zero_grad()
+        ev[0].record()
+        chunks[0].fwd(0, xs[0], ys[0][0])
+        ev[1].record()
+        chunks[0].bwd_input(0, dys[0], dxs[0][0])
+        ev[2].record()
+        chunks[0].bwd_weight(0)
+        ev[3].record()
+        torch.cuda.synchronize()
+        samples.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
+    tc = [sorted(col)[len(col) // 2] for col in zip(*samples)]
+    unit = sum(tc) / 3.0
+    for c in chunks:
+        c.zero_grad()
+    torch.cuda.synchronize()
+    r = zb.run_schedule_chunks(chunks, g["ops"], g["arrive_f"], g["arrive_b"], unit, [xs] * v, ys, [dys] * v, dxs)
+    win = g["last_end"] - g["first_start"]
+    out = {"v": v, "layers_per_chunk": lc, "chunk_unit_ms": round(unit, 3),
+           "chunk_pass_ms": {"F": round(tc[0], 3), "B": round(tc[1], 3), "W": round(tc[2], 3)},
+           "ring_slots_per_chunk": peaks,
+           "in_window_idle": round(r["in_window_idle"], 5), "window_ms": round(r["window_ms"], 2),
+           "busy_ms": round(r["busy_ms"], 2), "stage_end_ms": round(r["t_last_end_ms"], 2),
+           "predicted_in_window_idle": round(1 - g["busy"] / win, 5),
+           "predicted_stage_end_ms": round(g["last_end"] * unit, 2),
+           "predicted_bubble_over_makespan": round((g["makespan"] - g["busy"]) / g["makespan"], 5)}
+    del chunks
+    torch.cuda.synchronize()
     return out
 
 
@@ -387,6 +482,73 @@ def multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o, p=8, stage_i
     return out
 
 
+REPLAY_RUNS = (("zb_M16_ordered", "zb", 16, 0), ("zb_M16_filler", "zb", 16, 1), ("1f1b_ordered", "1f1b", 0, 0))
+
+
+def replay_only(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3):
+    """The replays whose idle a rocprofv3 kernel trace measures
+    independently (--replay-only under rocprofv3 --kernel-trace, then
+    --trace-idle): zero bubble (M = 16) in ordered and filler mode and 1F1B,
+    arrivals at costs 1:1:1 in units of the mean pass time, one after the
+    other with the GPU idle in between."""
+    import torch
+    import split_backward_amd as zb
+    out = []
+    for name, kind, M, mode in REPLAY_RUNS:
+        g = zb.schedule_generate(kind, p, m, M, (1, 1, 1), stage_idx)
+        stage.zero_grad()
+        torch.cuda.synchronize()
+        r = stage.run_schedule(g["ops"], g["arrive_f"], g["arrive_b"], unit, xs, ys, dys, dxs, mode=mode)
+        torch.cuda.synchronize()
+        win = g["last_end"] - g["first_start"]
+        out.append({"name": name, "n_ops": len(g["ops"]), "unit_ms": round(unit, 4),
+                    "stamp_in_window_idle": round(r["in_window_idle"], 5), "stamp_window_ms": round(r["window_ms"], 3),
+                    "stamp_busy_ms": round(r["busy_ms"], 3),
+                    "predicted_in_window_idle": round(1 - g["busy"] / win, 5)})
+    return out
+
+
+def trace_idle(csv_path, replays_path):
+    """In-window idle of each replay from a rocprofv3 kernel trace: the
+    replays' clock-stamp kernels (1 + 2 per op, in time order) delimit them;
+    inside each, busy = the union of the intervals of every kernel except the
+    stamp and arrival-wait kernels, window = [first such kernel's start, last
+    one's end].  Prints one JSON line per replay beside the stamp figure."""
+    import csv
+    with open(replays_path) as fh:
+        replays = [json.loads(ln) for ln in fh if ln.strip().startswith("{")][-1]["replays"]
+    kernels = []
+    with open(csv_path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            kernels.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]), row["Kernel_Name"]))
+    kernels.sort()
+    stamps = [k for k in kernels if "stamp_kernel" in k[2]]
+    need = sum(1 + 2 * r["n_ops"] for r in replays)
+    if len(stamps) != need:
+        raise SystemExit(f"trace has {len(stamps)} stamp kernels, the replays need {need}")
+    i = 0
+    for r in replays:
+        grp = stamps[i:i + 1 + 2 * r["n_ops"]]
+        i += len(grp)
+        lo_t, hi_t = grp[0][0], grp[-1][1]
+        work = [(a, b) for a, b, nm in kernels
+                if lo_t <= a and b <= hi_t and "stamp_kernel" not in nm and "wait_kernel" not in nm]
+        w0, w1 = min(a for a, _ in work), max(b for _, b in work)
+        busy, cs, ce = 0, work[0][0], work[0][1]
+        for a, b in work[1:]:
+            if a > ce:
+                busy += ce - cs
+                cs, ce = a, b
+            else:
+                ce = max(ce, b)
+        busy += ce - cs
+        print(json.dumps({"name": r["name"], "kernels": len(work), "trace_window_ms": round((w1 - w0) / 1e6, 3),
+                          "trace_busy_ms": round(busy / 1e6, 3),
+                          "trace_in_window_idle": round((w1 - w0 - busy) / (w1 - w0), 5),
+                          "stamp_in_window_idle": r["stamp_in_window_idle"],
+                          "predicted_in_window_idle": r["predicted_in_window_idle"]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -399,7 +561,14 @@ def main():
                     help="issue every W on its own instead of pairing adjacent W(j), W(j+1)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the copy + W-kernel workload that the --pmc passes count")
+    ap.add_argument("--replay-only", action="store_true",
+                    help="only calibrate and run the replays a kernel trace measures (see trace_idle)")
+    ap.add_argument("--trace-idle", nargs=2, metavar=("KERNEL_TRACE_CSV", "REPLAY_JSON"),
+                    help="in-window idle of the --replay-only replays from a rocprofv3 kernel trace (no GPU)")
     args = ap.parse_args()
+    if args.trace_idle:
+        trace_idle(*args.trace_idle)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs one pipeline stage on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -439,6 +608,13 @@ def main():
             else:
                 stage.bwd_weight(j)
 
+    if args.replay_only:
+        step()  # warm-up
+        t_f, t_b, t_w = calibrate(stage, xs, ys, dys, dxs)
+        print(json.dumps({"replays": replay_only(stage, m, xs, ys, dys, dxs, (t_f + t_b + t_w) / 3.0),
+                          "pass_ms": [t_f, t_b, t_w]}), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -453,20 +629,7 @@ def main():
     # per-pass times (the executor's arrival unit u = mean of F, B, W, and its
     # measured-cost runs): the median of five F, B, W passes, since a single
     # pass right after the timed steps can run slower than the replay does
-    samples = []
-    for _ in range(5):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        stage.zero_grad()
-        ev[0].record()
-        stage.fwd(0, xs[0], ys[0])
-        ev[1].record()
-        stage.bwd_input(0, dys[0], dxs[0])
-        ev[2].record()
-        stage.bwd_weight(0)
-        ev[3].record()
-        torch.cuda.synchronize()
-        samples.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
-    t_f, t_b, t_w = (sorted(col)[len(col) // 2] for col in zip(*samples))
+    t_f, t_b, t_w = calibrate(stage, xs, ys, dys, dxs)
 
     # The fp32 linear workload runs the fp32 GEMM (a few microseconds per
     # product, launch-bound): no roofline figure for it.
@@ -475,6 +638,7 @@ def main():
     extra = {}
     if shape.kind == "llama" and not args.no_executor:
         extra["executor_p8_stage3"] = executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w)
+        extra["executor_p8_stage3"]["interleaved_1f1b_v2"] = interleaved_idle(weights, shape, m, xs, dys)
         extra["memory_limit_sweep_p8_stage3"] = memory_limit_sweep(stage, m, xs, ys, dys, dxs, (t_f + t_b + t_w) / 3.0)
         # the optimizer step's own time (SGD over every weight, then dW cleared)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -485,7 +649,7 @@ def main():
         torch.cuda.synchronize()
         t_o = e0.elapsed_time(e1)
         extra["two_iterations_p8_stage3"] = multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(shape)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(shape, m)
 
     line = {
         "metric": "stage F+B+W TFLOP/s (bf16) and % MFMA peak; stage idle fraction vs 1F1B",

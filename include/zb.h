@@ -254,6 +254,33 @@ int32_t zb_schedule_generate_iters(int32_t kind, int32_t p, int32_t m, int32_t m
                                    zb_op* ops, int64_t* start, int64_t* end, int32_t cap,
                                    int64_t* arrive_f, int64_t* arrive_b, zb_sched_stats* stats);
 
+/* Op of a schedule over several model chunks per stage (interleaved 1F1B):
+ * the op type, the chunk of this stage it runs on, the microbatch. */
+typedef struct { int32_t type; int32_t chunk; int32_t mb; } zb_chunk_op;
+
+/* Interleaved 1F1B, the virtual-stage variant of 1F1B that the Guide's
+ * "2. The 1F1B Schedule" and its "Quantitative Comparison" table (v = 2)
+ * compare against: each of the p stages holds v model chunks, chunk c of
+ * stage i being virtual stage c*p + i of a v*p-stage pipeline, so a
+ * microbatch's forward visits every stage v times.  The pages give no
+ * algorithm; this is the published interleaved schedule (microbatches in
+ * groups of p, chunk-major within a group), with (p-1-stage) + (v-1)p
+ * warm-up forwards, the fewest that cannot deadlock, then (forward, whole
+ * backward) pairs, then the remaining backwards; backwards stay whole (B then
+ * W at once), as in 1F1B.  Costs are per chunk.  With v = 1 it is
+ * ZB_SCHED_1F1B.  Its bubble over the makespan is (p-1)/(v m + p-1).
+ * Outputs as for zb_schedule_generate, with 3 v m ops of type F, B, W
+ * (ops, start, end: capacity cap >= 3 v m) and arrivals of v m entries
+ * indexed [chunk * m + mb]: arrive_f = end of the forward of the previous
+ * virtual stage (0 for virtual stage 0), arrive_b = end of the whole
+ * backward of the next virtual stage (0 for the last).  stats->peak_active
+ * counts chunk-microbatches stashed at once.  Host only.
+ * Returns the number of ops or ZB_EINVAL (p, m, v < 1; v > 1 with m not a
+ * multiple of p; bad costs or stage; cap too small). */
+int32_t zb_schedule_generate_interleaved(int32_t p, int32_t m, int32_t v, int32_t cF, int32_t cB, int32_t cW,
+                                         int32_t stage, zb_chunk_op* ops, int64_t* start, int64_t* end,
+                                         int32_t cap, int64_t* arrive_f, int64_t* arrive_b, zb_sched_stats* stats);
+
 /* ------------------------------------------------------------- executor -- */
 
 enum {
@@ -304,6 +331,21 @@ int32_t zb_stage_run_schedule(zb_stage* st, const zb_op* ops, int32_t n,
                               const void* const* dy, void* const* dx,
                               void* hi_stream, void* lo_stream, int32_t mode,
                               zb_run_stats* stats, double* op_ms);
+
+/* zb_stage_run_schedule for a stage made of v model chunks (interleaved
+ * 1F1B, zb_schedule_generate_interleaved): chunks[c] is the zb_stage object
+ * of chunk c (distinct objects, each with its own weights and stash ring),
+ * ops[k].chunk selects the object an op runs on, and x, y, dy, dx and the
+ * arrivals hold v * m entries indexed [chunk * m + mb] (the input of chunk
+ * c comes from the previous virtual stage, emulated like any arrival).  An
+ * optimizer-step op steps every chunk.  Timing, streams, modes, stamps,
+ * stats and errors as for zb_stage_run_schedule, plus ZB_EINVAL for an op
+ * whose chunk is outside [0, v) or whose microbatch is >= m, or a stage
+ * object given twice. */
+int32_t zb_run_schedule_chunks(zb_stage* const* chunks, int32_t v, const zb_chunk_op* ops, int32_t n, int32_t m,
+                               const double* arrive_f, const double* arrive_b, double unit_ms,
+                               const void* const* x, void* const* y, const void* const* dy, void* const* dx,
+                               void* hi_stream, void* lo_stream, int32_t mode, zb_run_stats* stats, double* op_ms);
 
 /* ------------------------------------------------------------- kernels --- */
 

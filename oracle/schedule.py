@@ -433,3 +433,134 @@ def simulate_iterations(p: int, m: int, M: int, costs=(1, 1, 1), n_iter: int = 2
     arrive_b = [[done[("B", i + 1, g)] if i < p - 1 else 0 for g in range(G)] for i in range(p)]
     makespan = max(s.last_end for s in stats)
     return IterResult(p, m, M, n_iter, (cF, cB, cW), c_opt, ops, stats, makespan, arrive_f, arrive_b)
+
+
+# ---------------------------------------------------------------------------
+# Interleaved 1F1B (virtual stages), the comparison schedule of [Guide] "2.
+# The 1F1B Schedule" (virtual stages lower the bubble) and of the "Quantitative
+# Comparison: LLaMA-3-70B on 8 Pipeline Stages" table (v = 2).  The pages
+# give no algorithm; this is the published interleaved schedule of Megatron-LM
+# (Narayanan et al., 2021), restated:
+#
+# * each of the p devices holds v model chunks; chunk c of device i is the
+#   virtual stage s = c*p + i of a pipeline of v*p virtual stages, so
+#   microbatch j's forward runs s = 0, 1, ..., v*p - 1 across the devices and
+#   its backward runs back down.  Op costs (cF, cB, cW) are per chunk.
+# * Dependencies: F(s, j) after F(s-1, j); the backward BW(s, j) (atomic,
+#   cost cB + cW, as in 1F1B) after F(s, j) and BW(s+1, j).
+# * The microbatches go p at a time (m must be a multiple of p): the k-th
+#   forward of a device is chunk (k mod vp) div p of microbatch
+#   (k div vp)*p + k mod p; the k-th backward the same microbatch of chunk
+#   v - 1 - (k mod vp) div p.
+# * Device i runs w_i = min((p-1-i) + (v-1)p, vm) warm-up forwards, then
+#   pairs (next forward, next backward), then the remaining backwards; each
+#   op starts at max(device free, inputs done).  w_i is the fewest warm-up
+#   forwards that never deadlock: the first backward that reaches device i
+#   needs the forwards of all v chunks of the first microbatch group.
+#   Megatron-LM adds another p-1-i warm-up forwards, which pair its sends and
+#   receives; the pages' model has no communication, and there they change
+#   no op time but keep more microbatch-chunks stashed.  With v = 1 the
+#   sequence is the plain 1F1B one.
+#
+# The idle time over the makespan is (p-1)/(vm + p-1), the bubble the [Guide]
+# table prints for v = 2 (17.9% at p = 8, m = 16).
+# ---------------------------------------------------------------------------
+
+INTERLEAVED = "interleaved"
+
+
+@dataclass
+class ChunkOp:
+    type: str      # "F", "B", "W" (the atomic backward's B, then its W)
+    chunk: int
+    mb: int
+    start: int
+    end: int
+
+
+@dataclass
+class InterleavedResult:
+    p: int
+    m: int
+    v: int
+    costs: Tuple[int, int, int]
+    ops: List[List[ChunkOp]]            # per device, in execution order
+    stats: List[StageStats]             # peak_active counts chunk-microbatches
+    makespan: int
+    arrive_f: List[List[List[int]]]     # [device][chunk][mb]: end of F(s-1, j), 0 for s = 0
+    arrive_b: List[List[List[int]]]     # [device][chunk][mb]: end of BW(s+1, j), 0 for the last s
+
+    def order(self, i: int) -> List[Tuple[str, int, int]]:
+        return [(o.type, o.chunk, o.mb) for o in self.ops[i]]
+
+    def idle_over_makespan(self, i: int) -> Fraction:
+        return Fraction(self.makespan - self.stats[i].busy, self.makespan)
+
+
+def interleaved_sequence(p: int, m: int, v: int, i: int) -> List[Tuple[str, int, int]]:
+    """Device i's op sequence: ("F" | "BW", chunk, microbatch)."""
+    n = v * m
+
+    def mb_of(k):
+        return (k // (p * v)) * p + k % p
+
+    def fwd(k):
+        return ("F", (k % (p * v)) // p, mb_of(k))
+
+    def bwd(k):
+        return ("BW", v - 1 - (k % (p * v)) // p, mb_of(k))
+
+    warm = min((p - 1 - i) + (v - 1) * p, n)
+    seq = [fwd(k) for k in range(warm)]
+    for k in range(n - warm):
+        seq += [fwd(warm + k), bwd(k)]
+    seq += [bwd(k) for k in range(n - warm, n)]
+    return seq
+
+
+def simulate_interleaved(p: int, m: int, v: int, costs=(1, 1, 1)) -> InterleavedResult:
+    cF, cB, cW = (int(c) for c in costs)
+    if p < 1 or m < 1 or v < 1 or (v > 1 and m % p) or cF < 1 or cB < 1 or cW < 0:
+        raise ValueError("bad arguments (v >= 1; with v > 1, m must be a multiple of p)")
+    seqs = [interleaved_sequence(p, m, v, i) for i in range(p)]
+    last = v * p - 1
+    end: Dict[Tuple[str, int, int], int] = {}
+    free = [0] * p
+    pos = [0] * p
+    ops: List[List[ChunkOp]] = [[] for _ in range(p)]
+    active, peak = [0] * p, [0] * p
+    remaining = sum(len(q) for q in seqs)
+    while remaining:
+        progressed = False
+        for i in range(p):
+            while pos[i] < len(seqs[i]):
+                t, c, j = seqs[i][pos[i]]
+                s = c * p + i
+                if t == "F":
+                    deps, cost = ([("F", s - 1, j)] if s > 0 else []), cF
+                else:
+                    deps, cost = [("F", s, j)] + ([("BW", s + 1, j)] if s < last else []), cB + cW
+                if any(d not in end for d in deps):
+                    break
+                st = max([free[i]] + [end[d] for d in deps])
+                end[(t, s, j)] = st + cost
+                free[i] = st + cost
+                if t == "F":
+                    ops[i].append(ChunkOp("F", c, j, st, st + cF))
+                    active[i] += 1
+                    peak[i] = max(peak[i], active[i])
+                else:
+                    ops[i].append(ChunkOp("B", c, j, st, st + cB))
+                    ops[i].append(ChunkOp("W", c, j, st + cB, st + cB + cW))
+                    active[i] -= 1
+                pos[i] += 1
+                remaining -= 1
+                progressed = True
+        if not progressed:
+            raise RuntimeError("interleaved order deadlocked")
+    stats = [StageStats(v * m * (cF + cB + cW), ops[i][0].start, ops[i][-1].end, peak[i]) for i in range(p)]
+    arrive_f = [[[end[("F", c * p + i - 1, j)] if c * p + i > 0 else 0 for j in range(m)] for c in range(v)]
+                for i in range(p)]
+    arrive_b = [[[end[("BW", c * p + i + 1, j)] if c * p + i < last else 0 for j in range(m)] for c in range(v)]
+                for i in range(p)]
+    return InterleavedResult(p, m, v, (cF, cB, cW), ops, stats, max(s.last_end for s in stats), arrive_f, arrive_b)

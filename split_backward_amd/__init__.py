@@ -51,6 +51,10 @@ class Op(ctypes.Structure):
     _fields_ = [("type", ctypes.c_int32), ("mb", ctypes.c_int32)]
 
 
+class ChunkOp(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int32), ("chunk", ctypes.c_int32), ("mb", ctypes.c_int32)]
+
+
 class SchedStats(ctypes.Structure):
     _fields_ = [("makespan", ctypes.c_int64), ("busy", ctypes.c_int64), ("first_start", ctypes.c_int64),
                 ("last_end", ctypes.c_int64), ("peak_active", ctypes.c_int32), ("n_ops", ctypes.c_int32)]
@@ -89,6 +93,14 @@ _PROTOS = {
                                      ctypes.POINTER(ctypes.c_double), ctypes.c_double, ctypes.POINTER(_vp),
                                      ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _vp, _i32,
                                      ctypes.POINTER(RunStats), ctypes.POINTER(ctypes.c_double)]),
+    "zb_schedule_generate_interleaved": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ChunkOp),
+                                                ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, ctypes.POINTER(_i64),
+                                                ctypes.POINTER(_i64), ctypes.POINTER(SchedStats)]),
+    "zb_run_schedule_chunks": (_i32, [ctypes.POINTER(_vp), _i32, ctypes.POINTER(ChunkOp), _i32, _i32,
+                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), ctypes.c_double,
+                                      ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                      ctypes.POINTER(_vp), _vp, _vp, _i32, ctypes.POINTER(RunStats),
+                                      ctypes.POINTER(ctypes.c_double)]),
     "zb_gemm": (_i32, [_i32, _i32, _i32, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _vp]),
     "zb_gemm_wgrad_group": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp]),
     "zb_last_error": (ctypes.c_char_p, []),
@@ -172,6 +184,61 @@ def schedule_generate_iters(p: int, m: int, mem_limit: int, costs=(1, 1, 1), c_o
         "makespan": stats.makespan, "busy": stats.busy, "first_start": stats.first_start,
         "last_end": stats.last_end, "peak_active": stats.peak_active,
     }
+
+
+def schedule_generate_interleaved(p: int, m: int, v: int, costs=(1, 1, 1), stage: int = 0) -> dict:
+    """Interleaved 1F1B order of one stage holding v model chunks (no GPU
+    needed): ops are (type, chunk, microbatch); arrivals are lists of v
+    lists of m entries ([chunk][mb])."""
+    n = 3 * v * m
+    ops = (ChunkOp * n)()
+    st = (ctypes.c_int64 * n)()
+    en = (ctypes.c_int64 * n)()
+    af = (ctypes.c_int64 * (v * m))()
+    ab = (ctypes.c_int64 * (v * m))()
+    stats = SchedStats()
+    cnt = lib().zb_schedule_generate_interleaved(p, m, v, costs[0], costs[1], costs[2], stage, ops, st, en, n, af, ab,
+                                                 ctypes.byref(stats))
+    check(cnt)
+    return {
+        "ops": [(OPNAME[ops[i].type], ops[i].chunk, ops[i].mb) for i in range(cnt)],
+        "start": list(st[:cnt]), "end": list(en[:cnt]),
+        "arrive_f": [list(af[c * m:(c + 1) * m]) for c in range(v)],
+        "arrive_b": [list(ab[c * m:(c + 1) * m]) for c in range(v)],
+        "makespan": stats.makespan, "busy": stats.busy, "first_start": stats.first_start,
+        "last_end": stats.last_end, "peak_active": stats.peak_active,
+    }
+
+
+def run_schedule_chunks(stages: Sequence["Stage"], ops, arrive_f, arrive_b, unit_ms: float, xs, ys, dys, dxs,
+                        mode: int = EXEC_ORDERED, hi_stream=None, lo_stream=None) -> dict:
+    """Replay an op list over a stage made of several model chunks
+    (zb_run_schedule_chunks).  ops: (type, chunk, mb); arrive_f / arrive_b:
+    [chunk][mb]; xs, ys, dys, dxs: [chunk][mb] device tensors."""
+    v = len(stages)
+    m = len(xs[0])
+    if not all(len(a) == v for a in (arrive_f, arrive_b, xs, ys, dys, dxs)):
+        raise ValueError("arrivals and tensors need one list per chunk")
+    if not all(len(q) == m for q in list(arrive_f) + list(arrive_b) + list(xs) + list(ys) + list(dys) + list(dxs)):
+        raise ValueError("every per-chunk list needs m entries")
+    n = len(ops)
+    code = {"F": OP_F, "B": OP_B, "W": OP_W, "O": OP_O}
+    opa = (ChunkOp * n)(*[ChunkOp(code[t], c, j) for t, c, j in ops])
+    flat = lambda L: [q for row in L for q in row]
+    af = (ctypes.c_double * (v * m))(*[float(a) for a in flat(arrive_f)])
+    ab = (ctypes.c_double * (v * m))(*[float(a) for a in flat(arrive_b)])
+    P = lambda ts: (ctypes.c_void_p * (v * m))(*[_ptr(t) for t in flat(ts)])
+    hs = (ctypes.c_void_p * v)(*[s_.handle.value for s_ in stages])
+    stats = RunStats()
+    op_ms = (ctypes.c_double * (2 * n))()
+    hi = hi_stream.cuda_stream if hi_stream is not None else None
+    lo = lo_stream.cuda_stream if lo_stream is not None else None
+    check(lib().zb_run_schedule_chunks(hs, v, opa, n, m, af, ab, unit_ms, P(xs), P(ys), P(dys), P(dxs), hi, lo, mode,
+                                       ctypes.byref(stats), op_ms))
+    return {"window_ms": stats.window_ms, "busy_ms": stats.busy_ms, "in_window_idle": stats.in_window_idle,
+            "t_first_start_ms": stats.t_first_start_ms, "t_last_end_ms": stats.t_last_end_ms,
+            "wait_late_ms": stats.wait_late_ms,
+            "op_ms": [(op_ms[2 * i], op_ms[2 * i + 1]) for i in range(n)]}
 
 
 # ---- device side (needs torch + a GPU) -------------------------------------

@@ -434,3 +434,111 @@ extern "C" int32_t zb_schedule_generate_iters(int32_t kind, int32_t p, int32_t m
     }
     return (int32_t)mine.size();
 }
+
+// ---------------------------------------------------------------------------
+// Interleaved 1F1B (virtual stages): the comparison schedule of the Guide's
+// "2. The 1F1B Schedule" and of its "Quantitative Comparison" table (v = 2).
+// Each device holds v model chunks; chunk c of device i is virtual stage
+// s = c*p + i of a v*p-stage pipeline.  Microbatches go p at a time (m a
+// multiple of p when v > 1): the k-th forward of a device is chunk
+// (k mod vp) div p of microbatch (k div vp)*p + k mod p, the k-th backward
+// the same microbatch of chunk v-1 - (k mod vp) div p.  Device i runs
+// (p-1-i) + (v-1)p warm-up forwards (the fewest that cannot deadlock: the
+// first backward to reach it needs all v chunks of the first microbatch
+// group), then pairs (forward, backward), then the rest of the backwards;
+// backwards stay whole (B then W), as in 1F1B, and each op starts when its
+// device is free and its inputs exist.  With v = 1 this is 1F1B.
+namespace {
+struct ChunkPlaced {
+    int type, chunk, mb;
+    int64_t start, end;
+};
+}  // namespace
+
+extern "C" int32_t zb_schedule_generate_interleaved(int32_t p, int32_t m, int32_t v, int32_t cF, int32_t cB,
+                                                    int32_t cW, int32_t stage, zb_chunk_op* ops, int64_t* start,
+                                                    int64_t* end, int32_t cap, int64_t* arrive_f, int64_t* arrive_b,
+                                                    zb_sched_stats* stats) {
+    if (p < 1 || m < 1 || v < 1 || (v > 1 && m % p) || stage < 0 || stage >= p || cF < 1 || cB < 1 || cW < 0)
+        return ZB_EINVAL;
+    if ((int64_t)p * m * v > 1 << 22) return ZB_EINVAL;
+    const int n = v * m;  // forwards (and backwards) per device
+    if ((ops || start || end) && cap < 3 * n) return ZB_EINVAL;
+    const int S = v * p;  // virtual stages
+    auto mb_of = [&](int k) { return (k / (p * v)) * p + k % p; };
+    // per device: (is_backward, chunk, mb)
+    struct Step { int bwd, chunk, mb; };
+    std::vector<std::vector<Step>> seq(p);
+    for (int i = 0; i < p; ++i) {
+        const int warm = std::min((p - 1 - i) + (v - 1) * p, n);
+        auto fwd = [&](int k) { return Step{0, (k % (p * v)) / p, mb_of(k)}; };
+        auto bwd = [&](int k) { return Step{1, v - 1 - (k % (p * v)) / p, mb_of(k)}; };
+        for (int k = 0; k < warm; ++k) seq[i].push_back(fwd(k));
+        for (int k = 0; k < n - warm; ++k) {
+            seq[i].push_back(fwd(warm + k));
+            seq[i].push_back(bwd(k));
+        }
+        for (int k = n - warm; k < n; ++k) seq[i].push_back(bwd(k));
+    }
+    std::vector<int64_t> Fe((size_t)S * m, NOT_DONE), BWe((size_t)S * m, NOT_DONE);
+    auto at = [m](int s, int j) { return (size_t)s * m + j; };
+    std::vector<std::vector<ChunkPlaced>> placed(p);
+    std::vector<size_t> next(p, 0);
+    std::vector<int64_t> free_at(p, 0);
+    std::vector<int> active(p, 0), peak(p, 0);
+    size_t left = (size_t)2 * n * p;
+    while (left > 0) {
+        bool moved = false;
+        for (int i = 0; i < p; ++i) {
+            while (next[i] < seq[i].size()) {
+                const Step q = seq[i][next[i]];
+                const int s = q.chunk * p + i;
+                int64_t ready;
+                if (!q.bwd) ready = s == 0 ? 0 : Fe[at(s - 1, q.mb)];
+                else ready = std::max(Fe[at(s, q.mb)], s == S - 1 ? int64_t(0) : BWe[at(s + 1, q.mb)]);
+                if (ready == NOT_DONE) break;
+                const int64_t st = std::max(ready, free_at[i]);
+                if (!q.bwd) {
+                    Fe[at(s, q.mb)] = st + cF;
+                    free_at[i] = st + cF;
+                    placed[i].push_back({ZB_OP_F, q.chunk, q.mb, st, st + cF});
+                    peak[i] = std::max(peak[i], ++active[i]);
+                } else {
+                    BWe[at(s, q.mb)] = st + cB + cW;
+                    free_at[i] = st + cB + cW;
+                    placed[i].push_back({ZB_OP_B, q.chunk, q.mb, st, st + cB});
+                    placed[i].push_back({ZB_OP_W, q.chunk, q.mb, st + cB, st + cB + cW});
+                    --active[i];
+                }
+                ++next[i];
+                --left;
+                moved = true;
+            }
+        }
+        if (!moved) return ZB_EINVAL;
+    }
+    const auto& mine = placed[stage];
+    for (size_t k = 0; k < mine.size(); ++k) {
+        if (ops) ops[k] = zb_chunk_op{mine[k].type, mine[k].chunk, mine[k].mb};
+        if (start) start[k] = mine[k].start;
+        if (end) end[k] = mine[k].end;
+    }
+    for (int c = 0; c < v; ++c) {
+        const int s = c * p + stage;
+        for (int j = 0; j < m; ++j) {
+            if (arrive_f) arrive_f[(size_t)c * m + j] = s == 0 ? 0 : Fe[at(s - 1, j)];
+            if (arrive_b) arrive_b[(size_t)c * m + j] = s == S - 1 ? 0 : BWe[at(s + 1, j)];
+        }
+    }
+    if (stats) {
+        int64_t mk = 0;
+        for (int i = 0; i < p; ++i) mk = std::max(mk, placed[i].back().end);
+        stats->makespan = mk;
+        stats->busy = (int64_t)n * (cF + cB + cW);
+        stats->first_start = mine.front().start;
+        stats->last_end = mine.back().end;
+        stats->peak_active = peak[stage];
+        stats->n_ops = (int32_t)mine.size();
+    }
+    return (int32_t)mine.size();
+}

@@ -159,3 +159,78 @@ def test_malformed_schedule_rejected():
                                         P(dxs), None, None, zb.EXEC_ORDERED, None, None)
     assert rc == zb.EINVAL
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", [zb.EXEC_ORDERED, zb.EXEC_FILLER], ids=["ordered", "filler"])
+def test_interleaved_replay_over_two_chunks_matches_oracle(mode):
+    """Interleaved 1F1B (zb_schedule_generate_interleaved, v = 2 chunks of
+    one decoder layer each, stage 1 of p = 4, m = 8) replayed over two stage
+    objects with zb_run_schedule_chunks: every chunk's y, dx and dW against
+    the fp64 oracle of that chunk (whole tensors, 2e-2 and the element
+    bound), arrivals honoured, and in ordered mode the list order kept."""
+    from tests.gpu_helpers import oracle_stage
+    from tests.stage_checks import Sampler
+    p, stage, m, v = 4, 1, 8, 2
+    chunk = synth.StageShape("llama", 256, 256, 344, n_layers=1, n_heads=2, n_kv_heads=1, head_dim=128)
+    g = zb.schedule_generate_interleaved(p, m, v, (1, 1, 1), stage)
+    peaks = []
+    for c in range(v):  # stashed microbatches of each chunk at once, from the op list
+        live = peak = 0
+        for t, cc, _ in g["ops"]:
+            if cc == c and t in "FW":
+                live += 1 if t == "F" else -1
+                peak = max(peak, live)
+        peaks.append(peak)
+    stages, weights = [], []
+    for c in range(v):
+        w = synth.make_weights(chunk, seed=c)
+        st, _ = make_stage(chunk, peaks[c], weights=w)
+        stages.append(st)
+        weights.append(w)
+    xin = [[synth.make_x(chunk, 100 * c + j) for j in range(m)] for c in range(v)]
+    dyin = [[synth.make_dy(chunk, 100 * c + j) for j in range(m)] for c in range(v)]
+    xs = [[to_dev(t) for t in row] for row in xin]
+    dys = [[to_dev(t) for t in row] for row in dyin]
+    ys = [[torch.empty((chunk.tokens, chunk.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(m)]
+          for _ in range(v)]
+    dxs = [[torch.empty_like(t) for t in row] for row in ys]
+    for st in stages:
+        st.zero_grad()
+    torch.cuda.synchronize()
+    unit_ms = 0.3
+    r = zb.run_schedule_chunks(stages, g["ops"], g["arrive_f"], g["arrive_b"], unit_ms, xs, ys, dys, dxs, mode=mode)
+    torch.cuda.synchronize()
+    S = Sampler(0)
+    for c in range(v):
+        ref = oracle_stage(chunk, weights[c])
+        oy = [ref.fwd(j, xin[c][j].f64) for j in range(m)]
+        odx = [ref.bwd_input(j, dyin[c][j].f64) for j in range(m)]
+        for j in range(m):
+            ref.bwd_weight(j)
+            S.record("y", to_f64(ys[c][j]), oy[j], 2e-2)
+            S.record("dx", to_f64(dxs[c][j]), odx[j], 2e-2)
+        for i, (d, o) in enumerate(zip(stages[c].dw, ref.grad)):
+            S.record(f"dw{i}", to_f64(d), o, 2e-2)
+    iv = r["op_ms"]
+    for (t, c, j), (s, e) in zip(g["ops"], iv):
+        if t == "F":
+            assert s >= g["arrive_f"][c][j] * unit_ms - 0.02
+        if t == "B":
+            assert s >= g["arrive_b"][c][j] * unit_ms - 0.02
+    if mode == zb.EXEC_ORDERED:
+        for (s0, e0), (s1, e1) in zip(iv, iv[1:]):
+            assert s1 >= e0 - 1e-6
+    assert 0.0 <= r["in_window_idle"] < 1.0
+
+
+def test_chunk_executor_rejects_chunk_out_of_range():
+    st, _ = make_stage(SHAPE, 2)
+    xs, ys, dys, dxs = _inputs(1)
+    with pytest.raises(zb.ZbError) as e:
+        zb.run_schedule_chunks([st], [("F", 1, 0)], [[0.0]], [[0.0]], 0.1, [xs], [ys], [dys], [dxs])
+    assert e.value.code == zb.EINVAL
+    with pytest.raises(zb.ZbError) as e:
+        zb.run_schedule_chunks([st, st], [("F", 0, 0)], [[0.0]] * 2, [[0.0]] * 2, 0.1, [xs] * 2, [ys] * 2, [dys] * 2,
+                               [dxs] * 2)
+    assert e.value.code == zb.EINVAL
+    torch.cuda.synchronize()

@@ -225,3 +225,45 @@ def test_executor_bounded_waits_pass_argument_checks():
                                  None, None)
     assert rc == zb.EINVAL
     assert "bad argument" in zb.last_error()
+
+
+@pytest.mark.parametrize("costs", [(1, 1, 1), (2, 3, 1), (1, 2, 0)])
+def test_interleaved_generator_matches_oracle_bit_exact(costs):
+    from oracle.schedule import simulate_interleaved
+    n = 0
+    for p in (1, 2, 3, 4, 8):
+        for v in (1, 2, 3):
+            for m in sorted({p, 2 * p, 3 * p, 16 if 16 % p == 0 else p}):
+                ref = simulate_interleaved(p, m, v, costs)
+                for stage in sorted({0, p // 2, p - 1}):
+                    got = zb.schedule_generate_interleaved(p, m, v, costs, stage)
+                    assert got["ops"] == ref.order(stage), (p, m, v, stage)
+                    assert got["start"] == [o.start for o in ref.ops[stage]]
+                    assert got["end"] == [o.end for o in ref.ops[stage]]
+                    assert got["arrive_f"] == ref.arrive_f[stage]
+                    assert got["arrive_b"] == ref.arrive_b[stage]
+                    assert got["makespan"] == ref.makespan
+                    assert got["busy"] == ref.stats[stage].busy
+                    assert got["peak_active"] == ref.stats[stage].peak_active
+                    n += 1
+    assert n > 60
+
+
+def test_interleaved_generator_rejects_bad_arguments():
+    L = zb.lib()
+    for args in ((8, 12, 2, 1, 1, 1, 0), (8, 16, 0, 1, 1, 1, 0), (8, 16, 2, 0, 1, 1, 0), (8, 16, 2, 1, 1, 1, 8)):
+        assert L.zb_schedule_generate_interleaved(*args, None, None, None, 0, None, None, None) == zb.EINVAL
+    ops = (zb.ChunkOp * 10)()
+    assert L.zb_schedule_generate_interleaved(2, 2, 2, 1, 1, 1, 0, ops, None, None, 10, None, None, None) == zb.EINVAL
+
+
+def test_chunk_executor_rejects_bad_op_lists_before_any_work():
+    L = zb.lib()
+    ops = (zb.ChunkOp * 2)(zb.ChunkOp(zb.OP_F, 0, 0), zb.ChunkOp(zb.OP_B, 0, 0))
+    d = lambda v: (ctypes.c_double * len(v))(*v)
+    rc = L.zb_run_schedule_chunks(None, 2, ops, 2, 1, d([0.0, 0.0]), d([0.0, 0.0]), float("inf"), None, None, None,
+                                  None, None, None, zb.EXEC_ORDERED, None, None)
+    assert rc == zb.EINVAL and "unit_ms" in zb.last_error()
+    rc = L.zb_run_schedule_chunks(None, 0, ops, 2, 1, d([0.0, 0.0]), d([0.0, 0.0]), 1.0, None, None, None,
+                                  None, None, None, zb.EXEC_ORDERED, None, None)
+    assert rc == zb.EINVAL

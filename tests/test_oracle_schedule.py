@@ -318,3 +318,182 @@ def test_single_microbatch_runs_the_critical_path(p, costs):
     assert simulate("zb", p, 1, 1, costs).makespan == p * cF + p * cB + cW
     for kind in ("gpipe", "1f1b"):
         assert simulate(kind, p, 1, 0, costs).makespan == p * cF + p * (cB + cW)
+
+
+# ------------------------------------------------- survey-derived regressions
+# Stage 3 of p = 8, m = 16 at costs 1:1:1, derived from the rules by an
+# independent simulation before this one was written; they pin the greedy's
+# behaviour below the memory limit 2p, which the closed forms do not cover.
+
+def _ops(s):
+    return [(t[0], int(t[1:])) for t in s.split()]
+
+
+def test_zb_p_limit_regression_values():
+    r = simulate("zb", 8, 16, M=8)
+    assert r.makespan == 57
+    for i in range(8):
+        assert r.idle_over_busy(i) == Fraction(3, 16)
+    assert r.order(3) == _ops("F0 F1 F2 F3 F4 F5 F6 F7 B0 W0 B1 W1 B2 W2 B3 W3 B4 F8 B5 W4 B6 F9 B7 W5 W6 F10 "
+                              "B8 W7 W8 F11 B9 F12 W9 B10 F13 W10 F14 B11 F15 B12 W11 W12 B13 W13 B14 W14 B15 W15")
+    assert (r.stats[3].first_start, r.stats[3].last_end) == (3, 54)
+    assert r.stats[3].in_window_idle == Fraction(3, 51)
+    assert r.arrive_f[3] == list(range(3, 11)) + [21, 25, 29, 33, 35, 39, 41, 43]
+    assert r.arrive_b[3] == list(range(12, 27, 2)) + [30, 34, 38, 42, 44, 48, 50, 52]
+
+
+def test_zb_2p_and_1f1b_stage3_regression_values():
+    z = simulate("zb", 8, 16, M=16)
+    assert z.order(3) == (_ops("F0 F1 F2 F3 F4 F5 F6 F7 F8") +
+                          [x for k in range(7) for x in (("B", k), ("F", 9 + k))] +
+                          [("B", 7)] + [x for k in range(7) for x in (("W", k), ("B", 8 + k))] +
+                          [("W", 7), ("B", 15)] + [("W", k) for k in range(8, 16)])
+    assert z.arrive_f[3] == list(range(3, 14)) + [15, 17, 19, 21, 23]
+    assert z.arrive_b[3] == list(range(12, 43, 2))
+    assert (z.stats[3].first_start, z.stats[3].last_end) == (3, 51)
+    o = simulate("1f1b", 8, 16)
+    assert o.arrive_f[3] == [3, 4, 5, 6, 7, 8] + list(range(21, 49, 3))
+    assert o.arrive_b[3] == list(range(16, 62, 3))
+    assert (o.stats[3].first_start, o.stats[3].last_end) == (3, 63)
+    assert o.stats[3].in_window_idle == Fraction(12, 60)
+
+
+# ------------------------------------------------------- interleaved 1F1B
+
+INTERLEAVED_COSTS = COSTS + [(1, 1, 0), (5, 1, 1)]
+
+
+def test_interleaved_bubble_closed_form():
+    """Virtual stages: the bubble over the makespan is (p-1)/(vm + p-1) on
+    every device ([Guide] "2. The 1F1B Schedule": virtual stages lower the
+    1F1B bubble, which is (p-1)/(m+p-1); with v chunks per device each
+    warm-up and cool-down step is 1/v of a stage)."""
+    n = 0
+    for costs in INTERLEAVED_COSTS:
+        for p in range(2, 10):
+            for v in (2, 3, 4):
+                for m in range(p, 6 * p + 1, p):
+                    r = S.simulate_interleaved(p, m, v, costs)
+                    for i in range(p):
+                        assert r.idle_over_makespan(i) == Fraction(p - 1, v * m + p - 1), (costs, p, m, v, i)
+                    n += 1
+    assert n > 500
+
+
+def test_interleaved_printed_table():
+    """The Quantitative Comparison table: 1F1B 30.4% and interleaved (v = 2)
+    17.9% at p = 8, m = 16, both with a memory limit of p microbatches
+    (a chunk holds 1/v of a stage's stash, so the peak of chunk-microbatches
+    divided by v)."""
+    for kind, v, p, m, pct, mem in _rows("guide_schedule_comparison_table.txt"):
+        v, p, m, mem = int(v), int(p), int(m), int(mem)
+        if kind == "interleaved":
+            r = S.simulate_interleaved(p, m, v)
+            peak = max(s.peak_active for s in r.stats)
+            assert Fraction(peak, v) == mem
+        else:
+            r = simulate(kind, p, m)
+            assert max(s.peak_active for s in r.stats) == mem
+        assert round(float(r.idle_over_makespan(0)) * 100, 1) == float(pct)
+
+
+def test_interleaved_one_chunk_is_1f1b():
+    """With one chunk per device the interleaved simulator is the plain 1F1B
+    one: the same ops at the same times and the same arrivals."""
+    for costs in COSTS:
+        for p in range(1, 9):
+            for m in range(1, 25):
+                a = S.simulate_interleaved(p, m, 1, costs)
+                b = simulate("1f1b", p, m, costs=costs)
+                assert a.makespan == b.makespan
+                for i in range(p):
+                    assert [(o.type, o.mb, o.start, o.end) for o in a.ops[i]] == \
+                           [(o.type, o.mb, o.start, o.end) for o in b.ops[i]]
+                    assert a.arrive_f[i][0] == b.arrive_f[i]
+                    assert a.arrive_b[i][0] == b.arrive_b[i]
+
+
+def _check_interleaved(r):
+    """Independent of the simulator's loop: every (chunk, mb) forward and
+    backward of every device exactly once; no overlap on a device; every op
+    after its inputs; every op as early as possible (it starts when its
+    device's previous op ended or when its last input arrived); arrivals
+    are the upstream / downstream op ends; peak stash as counted from the
+    list."""
+    p, m, v = r.p, r.m, r.v
+    cF, cB, cW = r.costs
+    fend, bend = {}, {}
+    for i in range(p):
+        for o in r.ops[i]:
+            s = o.chunk * p + i
+            if o.type == "F":
+                fend[(s, o.mb)] = o.end
+            elif o.type == "W":
+                bend[(s, o.mb)] = o.end
+    assert len(fend) == len(bend) == v * p * m
+    for i in range(p):
+        prev_end, active, peak = 0, 0, 0
+        ops = r.ops[i]
+        k = 0
+        while k < len(ops):
+            o = ops[k]
+            s = o.chunk * p + i
+            if o.type == "F":
+                deps = [fend[(s - 1, o.mb)]] if s > 0 else []
+                assert o.end - o.start == cF
+                active += 1
+                peak = max(peak, active)
+                k += 1
+            else:
+                w = ops[k + 1]
+                assert o.type == "B" and w.type == "W" and (w.chunk, w.mb) == (o.chunk, o.mb)
+                assert o.end - o.start == cB and w.start == o.end and w.end - w.start == cW
+                deps = [fend[(s, o.mb)]] + ([bend[(s + 1, o.mb)]] if s < v * p - 1 else [])
+                active -= 1
+                k += 2
+            assert o.start >= prev_end and all(o.start >= d for d in deps)
+            assert o.start == max([prev_end] + deps)
+            prev_end = ops[k - 1].end
+        assert peak == r.stats[i].peak_active
+        for c in range(v):
+            s = c * p + i
+            for j in range(m):
+                assert r.arrive_f[i][c][j] == (fend[(s - 1, j)] if s > 0 else 0)
+                assert r.arrive_b[i][c][j] == (bend[(s + 1, j)] if s < v * p - 1 else 0)
+
+
+def test_interleaved_valid_and_as_soon_as_possible():
+    for costs in INTERLEAVED_COSTS:
+        for p, m, v in ((2, 2, 2), (4, 8, 2), (8, 16, 2), (3, 9, 3), (5, 10, 4), (8, 8, 2), (1, 4, 3)):
+            _check_interleaved(S.simulate_interleaved(p, m, v, costs))
+
+
+def test_interleaved_peak_stash():
+    """Device i holds at most (p-1-i) + (v-1)p + 1 chunk-microbatches: its
+    warm-up forwards and one more; the first device holds v*p chunks, p whole
+    microbatches, the 1F1B bound."""
+    for p in range(2, 9):
+        for v in (2, 3):
+            for m in (p, 2 * p, 4 * p):
+                r = S.simulate_interleaved(p, m, v)
+                for i in range(p):
+                    assert r.stats[i].peak_active == min((p - 1 - i) + (v - 1) * p + 1, v * m)
+                assert r.stats[0].peak_active == min(v * p, v * m)
+
+
+def test_interleaved_stage3_of_8():
+    """Stage 3 of p = 8, m = 16, v = 2 (chunk costs 1:1:1): window and
+    in-window idle, beside 1F1B's 20% and zero bubble's 0."""
+    r = S.simulate_interleaved(8, 16, 2)
+    st = r.stats[3]
+    assert (st.first_start, st.last_end, st.busy) == (3, 111, 96)
+    assert st.in_window_idle == Fraction(12, 108)
+    assert r.makespan == 117
+
+
+def test_interleaved_rejects_bad_arguments():
+    for bad in ((8, 12, 2), (8, 16, 0), (0, 16, 2)):
+        with pytest.raises(ValueError):
+            S.simulate_interleaved(*bad)
+    with pytest.raises(ValueError):
+        S.simulate_interleaved(4, 8, 2, (0, 1, 1))
