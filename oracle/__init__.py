@@ -18,8 +18,12 @@ Modules:
 * ``dense``    -- F / B / W of a linear layer, the GPT MLP block and the
                   Llama decoder layer; a fused backward for the B+W
                   invariant; the stash-and-pop stage object.
-* ``schedule`` -- integer-time pipeline simulator for GPipe, 1F1B and the
-                  memory-limited zero-bubble greedy schedule.
+* ``schedule`` -- integer-time pipeline simulator for GPipe, 1F1B, the
+                  memory-limited zero-bubble greedy schedule (one iteration
+                  and several) and interleaved 1F1B.
+* ``fp8``      -- E4M3 decoding, rounding and per-tensor power-of-two
+                  scaling, the fp8 product, and the Llama stage with every
+                  linear product on fp8 operands.
 
 Pins (what ties each function to something other than itself) live in
 ``tests/test_oracle_*.py``: finite differences, textbook/library special
