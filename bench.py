@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA (256 CU x 8192 flop/clk x 2.4 GHz)
 
 
 def calibrate(stage, xs, ys, dys, dxs, n=5):
@@ -226,6 +227,42 @@ def time_w_kernel(shape, workload, device, reps=5):
             "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
 
 
+def time_w_kernel_fp8(shape, device, reps=5):
+    """The fp8 stage's W-pass launch (16 products on E4M3 codes, fp32 dW
+    accumulated in place) at the step's shapes, replayed on the current
+    stream and timed with HIP events, against the fp8 dense peak."""
+    import torch
+    import split_backward_amd as zb
+    gem = w_pass_gemms(shape)
+    As, Bs, Cs = [], [], []
+    for (M, N, K) in gem:
+        As.append(torch.randint(0, 0x7E, (M, K), dtype=torch.uint8, device=device))
+        Bs.append(torch.randint(0, 0x7E, (N, K), dtype=torch.uint8, device=device))
+        Cs.append(torch.zeros((M, N), dtype=torch.float32, device=device))
+    e = torch.full((1,), -12, dtype=torch.int32, device=device)
+    once = lambda: zb.gemm_fp8_wgrad_group(As, [e] * len(As), Bs, [e] * len(Bs), Cs)
+    once()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        once()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    launches = reps * ((len(gem) + 15) // 16)
+    flops = reps * sum(2.0 * M * N * K for M, N, K in gem)
+    achieved = flops / (ms_total * 1e-3) / 1e12
+    algo_bytes = sum(K * (M + N) + 2 * 4 * M * N for M, N, K in gem) / ((len(gem) + 15) // 16)
+    avg_ms = ms_total / launches
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": algo_bytes,
+            "stash_and_dw_GBps": round(algo_bytes / (avg_ms * 1e-3) / 1e9, 1),
+            "kernel": "gemm_f8_group_kernel<EPI_ACCUM_F32> (fp8 W pass: dW += dY^T X on E4M3 codes, fp32 in place)",
+            "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
+
+
 def traffic_probe(shape, device):
     """Workload for the rocprofv3 --pmc passes: a copy of known size (1 GiB
     read, 1 GiB written, elementwise negation) three times, then the W-pass
@@ -244,12 +281,14 @@ def traffic_probe(shape, device):
                       "shapes_MNK": gem, "kernel_source_sha256": kernel_source_hash()}), flush=True)
 
 
-def cpu_baseline(shape, m):
+def cpu_baseline(shape, m, fp8=False):
     """fp64 oracle on a bounded sample: one decoder layer (or the whole
-    stage for the small kinds), one microbatch, F + B + W."""
+    stage for the small kinds), one microbatch, F + B + W (the fp8 oracle
+    stage for the fp8 workload)."""
     import numpy as np
     import synth
     from oracle import dense as od
+    from oracle import fp8 as o8
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -272,7 +311,8 @@ def cpu_baseline(shape, m):
     dy = synth.make_dy(sample, 0).f64
     reps, t_total = 0, 0.0
     while t_total < 8.0 and reps < 50:
-        st = od.Stage(sample.kind, [t.f64 for t in w], dims, sample.n_layers)
+        st = (o8.Fp8LlamaStage([t.f64 for t in w], dims, sample.n_layers) if fp8 else
+              od.Stage(sample.kind, [t.f64 for t in w], dims, sample.n_layers))
         t0 = time.perf_counter()
         st.fwd(0, x)
         st.bwd_input(0, dy)
@@ -579,6 +619,8 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     shape, m = wl["shape"], wl["m"]
+    stage_dtype = wl.get("stage_dtype", shape.dtype)
+    fp8 = stage_dtype == "fp8"
     ring = wl.get("ring", m)
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
@@ -586,7 +628,7 @@ def main():
         traffic_probe(shape, device)
         return
     weights = [synth.to_device(w, device) for w in synth.make_weights(shape)]
-    stage = zb.Stage(shape.kind, shape.tokens, shape.hidden, shape.ffn, weights, dtype=shape.dtype,
+    stage = zb.Stage(shape.kind, shape.tokens, shape.hidden, shape.ffn, weights, dtype=stage_dtype,
                      n_layers=shape.n_layers, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
                      head_dim=shape.head_dim if shape.kind == "llama" else 128, ring_slots=ring)
     xs, ys, dys, dxs = make_inputs(shape, m, device)
@@ -633,10 +675,14 @@ def main():
 
     # The fp32 linear workload runs the fp32 GEMM (a few microseconds per
     # product, launch-bound): no roofline figure for it.
-    roof = time_w_kernel(shape, args.workload, device) if shape.dtype == "bf16" else {
-        "bound": None, "note": "fp32 linear workload: launch-bound fp32 GEMM, no roofline figure"}
+    if fp8:
+        roof = time_w_kernel_fp8(shape, device)
+    elif shape.dtype == "bf16":
+        roof = time_w_kernel(shape, args.workload, device)
+    else:
+        roof = {"bound": None, "note": "fp32 linear workload: launch-bound fp32 GEMM, no roofline figure"}
     extra = {}
-    if shape.kind == "llama" and not args.no_executor:
+    if shape.kind == "llama" and not args.no_executor and not fp8:
         extra["executor_p8_stage3"] = executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w)
         extra["executor_p8_stage3"]["interleaved_1f1b_v2"] = interleaved_idle(weights, shape, m, xs, dys)
         extra["memory_limit_sweep_p8_stage3"] = memory_limit_sweep(stage, m, xs, ys, dys, dxs, (t_f + t_b + t_w) / 3.0)
@@ -649,18 +695,20 @@ def main():
         torch.cuda.synchronize()
         t_o = e0.elapsed_time(e1)
         extra["two_iterations_p8_stage3"] = multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(shape, m)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(shape, m, fp8=fp8)
 
     line = {
         "metric": "stage F+B+W TFLOP/s (bf16) and % MFMA peak; stage idle fraction vs 1F1B",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": shape.dtype, "data": "synthetic",
+        "dtype": "fp8-e4m3 products (fp32 accumulation), bf16 elsewhere" if fp8 else shape.dtype,
+        "data": "synthetic",
         "config": {"workload": args.workload, "tokens": shape.tokens, "hidden": shape.hidden, "ffn": shape.ffn,
                    "n_layers": shape.n_layers, "n_heads": shape.n_heads, "n_kv_heads": shape.n_kv_heads,
                    "microbatches": m, "ring_slots": ring, "order": "zero-bubble greedy, M=min(16, ring), stage 3 of p=8",
                    "w_pairs": w_pairs},
-        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "pct_of_peak": round(100 * tflops / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS), 2),
+        "peak_tflops": PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS,
         "tflops_incl_attention": round((flops + attention_flops_per_mb(shape) * m) / dt / 1e12, 2),
         "pass_ms": {"F": round(t_f, 3), "B": round(t_b, 3), "W": round(t_w, 3)},
         "roofline": roof, "cpu_baseline": cpu,

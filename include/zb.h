@@ -53,7 +53,19 @@ enum {
     ZB_ENOMEM = -5         /* workspace smaller than zb_stage_workspace_bytes */
 };
 
-enum { ZB_F32 = 0, ZB_BF16 = 1 };
+/* Element types.  A stage's dtype is ZB_F32, ZB_BF16 or ZB_FP8; ZB_E4M3 and
+ * ZB_I32 only describe stashed tensors (zb_stage_stash_tensor).
+ *  ZB_FP8  (ZB_LLAMA only) bf16 weights, activations and gradients at the
+ *          boundary, fp32 dW; every linear product of F, B and W runs on
+ *          E4M3 operands (OCP 8-bit float, 3 mantissa bits) with one
+ *          power-of-two scale per tensor, 2^e with e the smallest integer such
+ *          that max|x| <= 448 * 2^e, values rounded to nearest even, fp32
+ *          accumulation ("The Ghost in the Machine ...", "Memory Pressure":
+ *          FP8 halves buffers and makes room for the deferred-W stash).  The
+ *          stash keeps the W-only operands as E4M3 codes, transposed so
+ *          that every product has a K-contiguous operand pair.  hidden and
+ *          ffn must be multiples of 128. */
+enum { ZB_F32 = 0, ZB_BF16 = 1, ZB_FP8 = 2, ZB_E4M3 = 3, ZB_I32 = 4 };
 
 /* Stage kinds.
  *  ZB_LINEAR   one layer Y = X W^T; in = hidden, out = ffn.  Weight list: {W[ffn,hidden]}.
@@ -70,7 +82,7 @@ enum { ZB_LINEAR = 0, ZB_MLP_GELU = 1, ZB_LLAMA = 2 };
 
 typedef struct {
     int32_t kind;        /* ZB_LINEAR / ZB_MLP_GELU / ZB_LLAMA                    */
-    int32_t dtype;       /* ZB_F32 (ZB_LINEAR only) or ZB_BF16                     */
+    int32_t dtype;       /* ZB_F32 (ZB_LINEAR only), ZB_BF16, ZB_FP8 (ZB_LLAMA only) */
     int32_t n_layers;    /* ZB_LLAMA: decoder layers; otherwise 1                  */
     int32_t tokens;      /* T = batch * sequence length of one microbatch          */
     int32_t hidden;      /* model width h                                         */
@@ -175,6 +187,13 @@ int32_t zb_stage_zero_grad(zb_stage* st, void* stream);
  * Valid between F(mb) (or B(mb) for gradients) and W(mb). */
 int32_t zb_stage_stash_tensor(zb_stage* st, int32_t mb, int32_t layer, int32_t which,
                               void** ptr, int32_t* rows, int32_t* cols, int32_t* dtype);
+
+/* Device pointers of the E4M3 copies of linear weight i of a ZB_FP8 stage
+ * (for inspection by tests): q [out][in] (used by F), qt [in][out] (used by
+ * B), and e, the int32 exponent of their common scale.  They are refreshed
+ * by the first F after zb_stage_create or zb_stage_sgd_step.  ZB_EINVAL for
+ * another dtype or an index that is not a linear weight. */
+int32_t zb_stage_fp8_weight(zb_stage* st, int32_t i, void** q, void** qt, void** e);
 
 /* Optimizer step of the stage, closing an iteration (the op ZB_OP_O of
  * zb_schedule_generate_iters): for every weight, w -= lr * dW elementwise
@@ -362,6 +381,35 @@ int32_t zb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K,
                 const void* A, int64_t lda, int32_t a_kmajor,
                 const void* B, int64_t ldb, int32_t b_kmajor,
                 void* C, int64_t ldc, int32_t out_f32, int32_t accumulate, void* stream);
+
+/* Per-tensor E4M3 quantization of a bf16 matrix x [rows, cols] (leading
+ * dimension ld, elements) as the ZB_FP8 stage quantizes its operands:
+ * *e_out (device int32) = the smallest e with max|x| <= 448 * 2^e (0 for an
+ * all-zero x); the codes of x * 2^-e, rounded to nearest even, row-major
+ * into q ([rows][ldq] bytes) and/or transposed into qt ([cols][ldqt]); q or
+ * qt may be NULL.  part: device scratch of 512 floats.  rows, cols, ldq,
+ * ldqt multiples of 16, ld of 8, pointers 16-byte aligned.  Errors:
+ * ZB_EINVAL. */
+int32_t zb_quantize_e4m3(const void* x, int32_t rows, int32_t cols, int64_t ld, void* q, int64_t ldq, void* qt,
+                         int64_t ldqt, void* e_out, void* part, void* stream);
+
+/* One fp8 product through the ZB_FP8 stage's kernel, for kernel tests:
+ * C[M,N] (op)= (A . B^T) * 2^(*ea + *eb), A [M][lda], B [N][ldb] E4M3
+ * codes (K contiguous in both), ea / eb device int32.  out_f32 = 0: C bf16
+ * (C = result); out_f32 = 1: C fp32 and C += result.  K a multiple of 128,
+ * lda, ldb multiples of 16.  Errors: ZB_EINVAL. */
+int32_t zb_gemm_fp8(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* ea, const void* B,
+                    int64_t ldb, const void* eb, void* C, int64_t ldc, int32_t out_f32, void* stream);
+
+/* The ZB_FP8 stage's W-pass launch for kernel timing and tests: for
+ * i < count, C_i[M_i, N_i] (fp32) += (A_i . B_i^T) * 2^(*ea_i + *eb_i) with
+ * E4M3 codes A_i [M_i][lda_i], B_i [N_i][ldb_i] (K contiguous), up to 16
+ * products per launch; each product obeys zb_gemm_fp8's rules.  Errors:
+ * ZB_EINVAL. */
+int32_t zb_gemm_fp8_wgrad_group(int32_t count, const int32_t* M, const int32_t* N, const int32_t* K,
+                                const void* const* A, const int64_t* lda, const void* const* ea,
+                                const void* const* B, const int64_t* ldb, const void* const* eb,
+                                void* const* C, const int64_t* ldc, void* stream);
 
 /* A group of weight-gradient products in one launch ([Guide] "Core
  * Innovation 1": W is each layer's weight gradient, and the products of one

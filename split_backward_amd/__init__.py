@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libzb.so")
 
 # ---- constants mirrored from include/zb.h ---------------------------------
 OK, EINVAL, ESTATE, ERING_FULL, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5
-F32, BF16 = 0, 1
+F32, BF16, FP8, E4M3, I32 = 0, 1, 2, 3, 4
+DTYPE = {"f32": F32, "bf16": BF16, "fp8": FP8}
 LINEAR, MLP_GELU, LLAMA = 0, 1, 2
 OP_F, OP_B, OP_W, OP_O = 0, 1, 2, 3
 SCHED_GPIPE, SCHED_1F1B, SCHED_ZB = 0, 1, 2
@@ -31,7 +32,8 @@ OPNAME = {OP_F: "F", OP_B: "B", OP_W: "W", OP_O: "O"}
 LIN_X, LIN_DY = 0, 1
 MLP_X, MLP_A, MLP_H, MLP_DY, MLP_DA = 0, 1, 2, 3, 4
 (L_X, L_R1, L_N1, L_QKV, L_A, L_LSE, L_H1, L_R2, L_N2, L_GU, L_S,
- L_DOUT, L_DGU, L_DN2, L_DH1, L_DQKV, L_DN1) = range(17)
+ L_DOUT, L_DGU, L_DN2, L_DH1, L_DQKV, L_DN1,
+ L_N1T, L_AT, L_N2T, L_ST, L_DOUTT, L_DGUT, L_DH1T, L_DQKVT, L_QEXP) = range(26)
 
 
 class ZbError(RuntimeError):
@@ -101,6 +103,10 @@ _PROTOS = {
                                       ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                       ctypes.POINTER(_vp), _vp, _vp, _i32, ctypes.POINTER(RunStats),
                                       ctypes.POINTER(ctypes.c_double)]),
+    "zb_stage_fp8_weight": (_i32, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
+    "zb_quantize_e4m3": (_i32, [_vp, _i32, _i32, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "zb_gemm_fp8": (_i32, [_i32, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _vp]),
+    "zb_gemm_fp8_wgrad_group": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "zb_gemm": (_i32, [_i32, _i32, _i32, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _vp]),
     "zb_gemm_wgrad_group": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp]),
     "zb_last_error": (ctypes.c_char_p, []),
@@ -280,7 +286,7 @@ class Stage:
                  rms_eps: float = 1e-5, ring_slots: int = 2, device=None):
         import torch
         self.torch = torch
-        self.desc = StageDesc(KIND[kind], BF16 if dtype == "bf16" else F32, n_layers, tokens, hidden, ffn,
+        self.desc = StageDesc(KIND[kind], DTYPE[dtype], n_layers, tokens, hidden, ffn,
                               n_heads, n_kv_heads, head_dim, rms_eps, ring_slots)
         self.kind = kind
         self.dtype = dtype
@@ -290,7 +296,7 @@ class Stage:
             raise ValueError(f"expected {nw} weights, got {len(weights)}")
         device = device or weights[0].device
         self.device = device
-        want = torch.bfloat16 if dtype == "bf16" else torch.float32
+        want = torch.float32 if dtype == "f32" else torch.bfloat16  # fp8 stages keep bf16 weights
         for w in weights:
             if w.dtype != want or not w.is_contiguous() or w.device != device:
                 raise ValueError("weights must be contiguous device tensors of the stage dtype")
@@ -332,7 +338,7 @@ class Stage:
 
     @property
     def act_dtype(self):
-        return self.torch.bfloat16 if self.dtype == "bf16" else self.torch.float32
+        return self.torch.float32 if self.dtype == "f32" else self.torch.bfloat16
 
     @property
     def out_width(self) -> int:
@@ -380,9 +386,21 @@ class Stage:
                                           ctypes.byref(c), ctypes.byref(dt)))
         torch = self.torch
         off = p.value - self.ws.data_ptr()
-        tdt = torch.float32 if dt.value == F32 else torch.bfloat16
-        nbytes = r.value * c.value * (4 if dt.value == F32 else 2)
+        tdt, esz = {F32: (torch.float32, 4), BF16: (torch.bfloat16, 2), E4M3: (torch.uint8, 1),
+                    I32: (torch.int32, 4)}[dt.value]
+        nbytes = r.value * c.value * esz
         return self.ws[off:off + nbytes].view(tdt).view(r.value, c.value)
+
+    def fp8_weight(self, i: int):
+        """(codes [out][in], codes [in][out], exponent) of linear weight i of
+        an fp8 stage, as torch views (uint8, uint8, int32 of one element)."""
+        q, qt, e = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        check(lib().zb_stage_fp8_weight(self.handle, i, ctypes.byref(q), ctypes.byref(qt), ctypes.byref(e)))
+        out_, in_ = self.weights[i].shape
+        base = self.ws.data_ptr()
+        view = lambda p, n: self.ws[p - base:p - base + n]
+        return (view(q.value, out_ * in_).view(out_, in_), view(qt.value, out_ * in_).view(in_, out_),
+                view(e.value, 4).view(self.torch.int32))
 
     def run_schedule(self, ops, arrive_f, arrive_b, unit_ms: float, xs, ys, dys, dxs, mode: int = EXEC_ORDERED,
                      hi_stream=None, lo_stream=None):
@@ -420,6 +438,44 @@ def gemm(A, B, C, *, a_kmajor: bool, b_kmajor: bool, M: int, N: int, K: int, acc
     check(lib().zb_gemm(dt, M, N, K, _ptr(A), lda, int(a_kmajor), _ptr(B), ldb, int(b_kmajor), _ptr(C), ldc,
                         out_f32, int(accumulate), _stream_ptr(stream)))
     return C
+
+
+def quantize_e4m3(x, q=None, qt=None, stream=None):
+    """Per-tensor E4M3 quantization of a bf16 matrix through the library's
+    kernels: returns (q [rows][cols] uint8 or None, qt [cols][rows] or None,
+    exponent int32 tensor of one element)."""
+    import torch
+    rows, cols = x.shape
+    e = torch.zeros(1, dtype=torch.int32, device=x.device)
+    part = torch.empty(512, dtype=torch.float32, device=x.device)
+    check(lib().zb_quantize_e4m3(_ptr(x), rows, cols, x.stride(0), _ptr(q) if q is not None else None, cols,
+                                 _ptr(qt) if qt is not None else None, rows, _ptr(e), _ptr(part),
+                                 _stream_ptr(stream)))
+    return q, qt, e
+
+
+def gemm_fp8(A, ea, B, eb, C, stream=None):
+    """C (op)= (A . B^T) * 2^(ea + eb) over E4M3 codes A [M][K], B [N][K];
+    C bf16 (assigned) or fp32 (accumulated)."""
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+    out_f32 = 1 if C.dtype == torch.float32 else 0
+    check(lib().zb_gemm_fp8(M, N, K, _ptr(A), A.stride(0), _ptr(ea), _ptr(B), B.stride(0), _ptr(eb), _ptr(C),
+                            C.stride(0), out_f32, _stream_ptr(stream)))
+
+
+def gemm_fp8_wgrad_group(As, eas, Bs, ebs, Cs, stream=None):
+    """C_i += (A_i . B_i^T) * 2^(ea_i + eb_i) over E4M3 codes, fp32 C_i, in
+    grouped launches (zb_gemm_fp8_wgrad_group)."""
+    n = len(As)
+    i32 = lambda v: (ctypes.c_int32 * n)(*v)
+    i64 = lambda v: (ctypes.c_int64 * n)(*v)
+    P = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])
+    check(lib().zb_gemm_fp8_wgrad_group(n, i32([a.shape[0] for a in As]), i32([b.shape[0] for b in Bs]),
+                                        i32([a.shape[1] for a in As]), P(As), i64([a.stride(0) for a in As]), P(eas),
+                                        P(Bs), i64([b.stride(0) for b in Bs]), P(ebs), P(Cs),
+                                        i64([c.stride(0) for c in Cs]), _stream_ptr(stream)))
 
 
 def gemm_wgrad_group(As, Bs, Cs, Ms, Ns, Ks, a_kmajor=False, b_kmajor=False, stream=None):

@@ -49,12 +49,9 @@ enum Epi : int {
 
 struct GemmDesc {
     int M, N, K;
-    const void* A; int64_t lda; int a_kmajor;   // opA[m][k] = a_kmajor ? A[m*lda+k] : A[k*lda+m]
-    const void* B; int64_t ldb; int b_kmajor;   // opB[k][n] = b_kmajor ? B[n*ldb+k] : B[k*ldb+n]
-    void* C; int64_t ldc;
+    int a_kmajor;                              // opA[m][k] = a_kmajor ? A[m*lda+k] : A[k*lda+m]
+    int b_kmajor;                              // opB[k][n] = b_kmajor ? B[n*ldb+k] : B[k*ldb+n]
     int epi;
-    const void* R; int64_t ldr;                // residual / stash operand of the epilogue
-    void* C2; int64_t ldc2;                    // second output of the epilogue
     int half_n;                                // EPI_SWIGLU_*: width of g (= ffn)
     // Second K segment (W over two microbatches): with K1 > 0, k < K1 reads
     // A and B and k >= K1 reads A2 and B2 at row k - K1 (same leading
@@ -62,8 +59,18 @@ struct GemmDesc {
     // both operands M/N-contiguous and EPI_ACCUM_F32 takes it
     // (gemm_bf16_group_segmented); every other path rejects K1 != 0.
     int K1;
+    const void* A; int64_t lda;
+    const void* B; int64_t ldb;
+    void* C; int64_t ldc;
+    const void* R; int64_t ldr;                // residual / stash operand of the epilogue
+    void* C2; int64_t ldc2;                    // second output of the epilogue
     const void* A2;
     const void* B2;
+    // fp8 products (gemm_fp8 / gemm_fp8_group): A and B hold E4M3 codes
+    // (K-contiguous both) with per-tensor power-of-two scales 2^*ea, 2^*eb
+    // read on the device; the epilogue sees acc * 2^(*ea + *eb).
+    const int32_t* ea;
+    const int32_t* eb;
 };
 
 int32_t gemm_bf16(const GemmDesc& d, hipStream_t s);
@@ -81,6 +88,22 @@ int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s);
 // K = 2 * K1, K1 a multiple of 32); the caller then issues the segments as
 // separate products.
 int32_t gemm_bf16_group_segmented(const GemmDesc* ds, int n, hipStream_t s, bool* handled);
+// C (epi)= (A . B^T) * 2^(ea + eb) with A [M, K], B [N, K] E4M3 codes, both
+// K-contiguous (a_kmajor = b_kmajor = 1), K a multiple of 128, leading
+// dimensions multiples of 16 bytes; any epilogue of the bf16 kernel.
+int32_t gemm_fp8(const GemmDesc& d, hipStream_t s);
+// Up to 16 such products of one epilogue in one launch.
+int32_t gemm_fp8_group(const GemmDesc* ds, int n, hipStream_t s);
+
+// ------------------------------------------------------- fp8 operands ----
+// Per-tensor E4M3 quantization of a bf16 [rows, cols] matrix (leading
+// dimension ld): *e_out = the smallest e with max|x| <= 448 * 2^e, codes of
+// x * 2^-e (round to nearest even) row-major into q (ldq) and/or transposed
+// ([cols][rows]) into qt (ldqt); either may be null.  rows and cols are
+// multiples of 16.  part: AMAX_PARTS floats of scratch.
+constexpr int AMAX_PARTS = 512;
+int32_t quantize_e4m3(const bf16_t* x, int rows, int cols, int64_t ld, uint8_t* q, int64_t ldq, uint8_t* qt,
+                      int64_t ldqt, int32_t* e_out, float* part, hipStream_t s);
 
 // ------------------------------------------------- elementwise / norms ----
 int32_t fill_f32(float* p, size_t n, float v, hipStream_t s);

@@ -824,6 +824,167 @@ __device__ __forceinline__ void gemm_64_tile(const GemmDesc& d, int tm, int tn, 
     gemm_epilogue<A_KMAJ, B_KMAJ, EPI, TBM>(d, sp, acc, m0, n0, smem);
 }
 
+// ---- fp8 (E4M3) products: both operands K-contiguous, 128-k parts ------
+// v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands: each lane holds 32 codes of
+// one row (A) or column (B), the 32 consecutive k of its lane group (lane
+// l: row l % 32, k 32 (l / 32) .. + 31 of a 64-k step); A and B use the same
+// lane-to-k assignment, so every product pairs A[i][k] with B[k][j].  A
+// 128-k part row is 128 bytes, the same LDS geometry as the bf16 kernel's
+// 64-k parts: the five-slot ring, its DMA schedule and its swizzle carry
+// over; a k-tile is two 64-k MFMA steps.
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+constexpr int BK8 = 128;  // k per fp8 k-tile (bytes per part row)
+
+template <bool PAIRED, int NI>
+__device__ __forceinline__ void dma_offsets_f8(uint32_t (&off)[NI], int64_t ld, int row0, int rows_total,
+                                               int half_n, int k_lim, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int b = i * 4 + wave;
+        const int r = b * 8 + (lane >> 3);
+        const int kc = (lane & 7) ^ key8(r);  // 16-byte chunk = 16 codes
+        int grow;
+        bool ok;
+        if (PAIRED) {
+            const int rr = row0 + (r & 127);
+            ok = rr < half_n;
+            grow = (r < 128) ? rr : half_n + rr;
+        } else {
+            grow = row0 + r;
+            ok = grow < rows_total;
+        }
+        off[i] = (ok && kc * 16 < k_lim) ? (uint32_t)((int64_t)grow * ld + kc * 16) : OOB;
+    }
+}
+
+// Fragment of 32 codes: row `row`, 64-k step kk, lane group g (chunks
+// 4kk + 2g and 4kk + 2g + 1 of the 128-byte row).
+__device__ __forceinline__ v8i32 frag_f8(const lds_void* tile, int row, int kk, int g) {
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    const __attribute__((address_space(3))) char* base =
+        (const __attribute__((address_space(3))) char*)tile + row * 128;
+    const int c0 = (kk * 4 + g * 2) ^ key8(row), c1 = (kk * 4 + g * 2 + 1) ^ key8(row);
+    const u32x4 lo = *(const lds_u32x4*)(base + c0 * 16);
+    const u32x4 hi = *(const lds_u32x4*)(base + c1 * 16);
+    return v8i32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+__device__ __forceinline__ floatx16 mfma_f8(const v8i32& a, const v8i32& b, const floatx16& c) {
+    // formats 0 / 0: both operands E4M3; block scales 127 = 2^0 (unscaled)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int EPI, int TBM>
+__device__ __forceinline__ void gemm_f8_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
+    constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
+    constexpr int MI = TBM / 64;
+    constexpr int NA = TBM / 32, NB = 8;  // DMA instructions per wave per part
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int g = lane >> 5, lrow = lane & 31;
+    const int m0 = tm * TBM;
+    const int n0 = PAIRED ? tn * (BN / 2) : tn * BN;
+    const int nk = d.K / BK8;  // K is a multiple of 128 (checked on the host)
+
+    uint32_t offa[NA], offb[NB];
+    dma_offsets_f8<false, NA>(offa, d.lda, m0, d.M, 0, BK8, lane, wave);
+    dma_offsets_f8<PAIRED, NB>(offb, d.ldb, n0, d.N, d.half_n, BK8, lane, wave);
+    auto dma_part = [&](int p) {
+        const int kt = p >> 1;
+        char* dst = smem + (p % NSLOT) * PART_BYTES;
+        const bool live = kt < nk;
+        const uint32_t adv = live ? (uint32_t)(kt * BK8) : 0u;
+        if ((p & 1) == 0) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(d.A) + adv, live ? sp.a - adv : 0u);
+            dma_issue_n<NA>(rs, (lds_void*)dst, offa, wave);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(d.B) + adv, live ? sp.b - adv : 0u);
+            dma_issue_n<NB>(rs, (lds_void*)dst, offb, wave);
+        }
+    };
+
+    floatx16 acc[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    auto frag_a = [&](const lds_void* ta, int mi, int kk) { return frag_f8(ta, wm * (TBM / 2) + mi * 32 + lrow, kk, g); };
+    auto frag_b = [&](const lds_void* tb, int ni, int kk) {
+        const int row = PAIRED ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + lrow) : (wn * 128 + ni * 32 + lrow);
+        return frag_f8(tb, row, kk, g);
+    };
+    constexpr int RD = 2 * (MI + 4);  // LDS reads per 64-k step
+    constexpr int NM = MI * 4;        // MFMAs per 64-k step
+
+    // Iteration kt multiplies the two 64-k steps of k-tile kt, each while
+    // the next step's fragments are read.  During step 0 the A part of
+    // k-tile kt+2 goes into the slot k-tile kt-1's B part left; then every
+    // read of kt has completed and k-tile kt+1 has landed, a barrier, and
+    // during step 1 the first fragments of kt+1 are read and the B part of
+    // kt+2 goes into the slot kt's A part left.
+#pragma unroll
+    for (int p = 0; p < NSLOT - 1; ++p) dma_part(p);
+    wait_vm<NA + NB>();  // parts 0 and 1 (k-tile 0) landed
+    workgroup_barrier();
+    v8i32 fa0[MI], fb0[4], fa1[MI], fb1[4];
+    {
+        const lds_void* ta = (const lds_void*)smem;
+        const lds_void* tb = (const lds_void*)(smem + PART_BYTES);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < MI) fa0[i] = frag_a(ta, i, 0);
+            fb0[i] = frag_b(tb, i, 0);
+        }
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const lds_void* ta = (const lds_void*)(smem + ((2 * kt) % NSLOT) * PART_BYTES);
+        const lds_void* tb = (const lds_void*)(smem + ((2 * kt + 1) % NSLOT) * PART_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < MI) fa1[i] = frag_a(ta, i, 1);
+            fb1[i] = frag_b(tb, i, 1);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_f8(fa0[mi], fb0[ni], acc[mi][ni]);
+        dma_part(2 * kt + 4);  // the A part of k-tile kt+2, into the slot kt-1's B part left
+        interleave_reads_dma_mfma<RD, NA, NM, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every read of k-tile kt has completed
+        wait_vm<NA>();                                      // k-tile kt+1 landed
+        workgroup_barrier();
+        {
+            const lds_void* na = (const lds_void*)(smem + ((2 * kt + 2) % NSLOT) * PART_BYTES);
+            const lds_void* nb = (const lds_void*)(smem + ((2 * kt + 3) % NSLOT) * PART_BYTES);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i < MI) fa0[i] = frag_a(na, i, 0);
+                fb0[i] = frag_b(nb, i, 0);
+            }
+        }
+        dma_part(2 * kt + 5);  // the B part of k-tile kt+2, into the slot kt's A part left
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_f8(fa1[mi], fb1[ni], acc[mi][ni]);
+        interleave_reads_dma_mfma<RD, NB, NM, 0>();
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the unused reads of k-tile nk
+    // dequantization: both scales are powers of two, so this multiply is exact
+    const float sc = __builtin_ldexpf(1.f, *d.ea + *d.eb);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][ni][e] *= sc;
+    gemm_epilogue<true, true, EPI, TBM>(d, sp, acc, m0, n0, smem);
+}
+
 // LDS of one workgroup: five 32 KB slots for products with a K-contiguous A
 // (64-k parts), four 32 KB stages otherwise (the epilogue reuses the first
 // 68 KB).
@@ -878,6 +1039,33 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_group_kernel(GemmGroup grp) {
     const GemmDesc d = grp.d[g];  // a value copy: its fields stay in scalar registers
     const BufSpans sp = grp.sp[g];
     gemm_tile<A_KMAJ, B_KMAJ, EPI, BM>(d, tm, tn, sp, smem);
+}
+
+// fp8 products (both operands K-contiguous E4M3): single and grouped.
+template <int EPI, int TBM>
+__global__ __launch_bounds__(NTHR) void gemm_f8_kernel(GemmDesc d, int tiles_m, int tiles_n, int tn_base,
+                                                       BufSpans sp) {
+    __shared__ __attribute__((aligned(1024))) char smem[NSLOT * PART_BYTES];
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    gemm_f8_tile<EPI, TBM>(d, tm, tn_base + tn, sp, smem);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NTHR) void gemm_f8_group_kernel(GemmGroup grp) {
+    __shared__ __attribute__((aligned(1024))) char smem[NSLOT * PART_BYTES];
+    const int bid = blockIdx.x;
+    int g = 0;
+    while (g + 1 < grp.n && bid >= grp.off[g + 1]) ++g;
+    const int local = bid - grp.off[g];
+    const int nwg = grp.tiles_m[g] * grp.tiles_n[g];
+    const int q = nwg >> 3, r = nwg & 7, xcd = local & 7;
+    if ((local >> 3) >= (xcd < r ? q + 1 : q)) return;  // padding workgroup
+    int tm, tn;
+    tile_of(local, grp.tiles_m[g], grp.tiles_n[g], tm, tn);
+    const GemmDesc d = grp.d[g];
+    const BufSpans sp = grp.sp[g];
+    gemm_f8_tile<EPI, BM>(d, tm, tn, sp, smem);
 }
 
 template <bool AK, bool BKM, int TBM>
@@ -1053,6 +1241,100 @@ int32_t gemm_bf16_group_segmented(const GemmDesc* ds, int n, hipStream_t s, bool
     }
     *handled = true;
     return launch_group<false, false>(g, EPI_ACCUM_F32, s);
+}
+
+namespace {
+// Whether an fp8 product fits the kernel: spans (bytes) below 2^31, K and
+// the leading dimensions multiples of 16 codes, 16-byte aligned operands,
+// vector-friendly epilogue outputs (as for the bf16 kernel).
+V2Plan plan_f8(const GemmDesc& d) {
+    V2Plan p{};
+    if (!d.a_kmajor || !d.b_kmajor || d.K1 != 0 || !d.ea || !d.eb) return p;
+    if (d.K % 128 || d.lda % 16 || d.ldb % 16) return p;
+    if ((reinterpret_cast<uintptr_t>(d.A) | reinterpret_cast<uintptr_t>(d.B)) & 15) return p;
+    GemmDesc b = d;  // the epilogue spans and checks of the bf16 plan, operand spans replaced below
+    b.K = 1;
+    b.lda = 1;
+    b.ldb = 1;
+    V2Plan q = plan_v2(b);
+    if (!q.ok) return p;
+    const uint64_t ab = (uint64_t)((int64_t)(d.M - 1) * d.lda + d.K);
+    const uint64_t bb = (uint64_t)((int64_t)((d.epi == EPI_SWIGLU_FWD ? 2 * d.half_n : d.N) - 1) * d.ldb + d.K);
+    if (ab >= OOB || bb >= OOB) return p;
+    q.sp.a = (uint32_t)ab;
+    q.sp.b = (uint32_t)bb;
+    return q;
+}
+
+template <int TBM>
+int32_t launch_f8(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, int tn_base, const BufSpans& sp) {
+    dim3 grid(tiles_m * tiles_n), block(NTHR);
+    switch (d.epi) {
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_f8_kernel<E, TBM>), grid, block, 0, s, d, tiles_m, tiles_n, tn_base, sp); break;
+        ZB_CASE(EPI_STORE)
+        ZB_CASE(EPI_RESID)
+        ZB_CASE(EPI_ACCUM_F32)
+        ZB_CASE(EPI_GELU_FWD)
+        ZB_CASE(EPI_GELU_BWD)
+        ZB_CASE(EPI_SWIGLU_FWD)
+        ZB_CASE(EPI_SWIGLU_BWD)
+#undef ZB_CASE
+        default: return fail(ZB_EINVAL, "gemm_fp8: unknown epilogue");
+    }
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+}  // namespace
+
+int32_t gemm_fp8(const GemmDesc& d, hipStream_t s) {
+    if (d.M <= 0 || d.N <= 0 || d.K <= 0) return fail(ZB_EINVAL, "gemm_fp8: empty shape");
+    if (d.epi == EPI_SWIGLU_FWD && d.half_n <= 0) return fail(ZB_EINVAL, "gemm_fp8: bad SwiGLU pairing");
+    const V2Plan p = plan_f8(d);
+    if (!p.ok)
+        return fail(ZB_EINVAL, "gemm_fp8: needs K-contiguous operands, K a multiple of 128, leading dimensions multiples of 16, "
+                               "16-byte aligned operands, exponent pointers, and spans below 2 GiB");
+    const int tiles_m_half = (d.M + BM / 2 - 1) / (BM / 2);
+    const TileSplit t = getenv("ZB_GEMM_FULL_TILES") ? TileSplit{p.tiles_n}
+                                                     : split_columns(p.tiles_m, p.tiles_n, tiles_m_half, cu_count());
+    if (t.n_full > 0) {
+        const int32_t rc = launch_f8<BM>(d, s, p.tiles_m, t.n_full, 0, p.sp);
+        if (rc != ZB_OK) return rc;
+    }
+    if (t.n_full < p.tiles_n) return launch_f8<BM / 2>(d, s, tiles_m_half, p.tiles_n - t.n_full, t.n_full, p.sp);
+    return ZB_OK;
+}
+
+int32_t gemm_fp8_group(const GemmDesc* ds, int n, hipStream_t s) {
+    if (n <= 0) return ZB_OK;
+    if (n > GROUP_MAX) return fail(ZB_EINVAL, "gemm_fp8_group: at most 16 products");
+    GemmGroup g{};
+    g.n = n;
+    g.off[0] = 0;
+    for (int i = 0; i < n; ++i) {
+        const V2Plan p = plan_f8(ds[i]);
+        if (!p.ok || ds[i].epi != ds[0].epi || ds[i].M <= 0 || ds[i].N <= 0 || ds[i].K <= 0 ||
+            ds[i].epi == EPI_SWIGLU_FWD)
+            return fail(ZB_EINVAL, "gemm_fp8_group: a product does not fit the grouped fp8 kernel");
+        g.d[i] = ds[i];
+        g.tiles_m[i] = p.tiles_m;
+        g.tiles_n[i] = p.tiles_n;
+        g.sp[i] = p.sp;
+        g.off[i + 1] = g.off[i] + ((p.tiles_m * p.tiles_n + 7) & ~7);
+    }
+    dim3 grid(g.off[n]), block(NTHR);
+    switch (ds[0].epi) {
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_f8_group_kernel<E>), grid, block, 0, s, g); break;
+        ZB_CASE(EPI_STORE)
+        ZB_CASE(EPI_RESID)
+        ZB_CASE(EPI_ACCUM_F32)
+        ZB_CASE(EPI_GELU_FWD)
+        ZB_CASE(EPI_GELU_BWD)
+        ZB_CASE(EPI_SWIGLU_BWD)
+#undef ZB_CASE
+        default: return fail(ZB_EINVAL, "gemm_fp8_group: unknown epilogue");
+    }
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
 }
 
 int32_t gemm_bf16_group(const GemmDesc* ds, int n, hipStream_t s) {

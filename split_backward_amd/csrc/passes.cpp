@@ -57,6 +57,7 @@ bf16_t* bf(void* p) { return static_cast<bf16_t*>(p); }
 
 int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s) {
     const zb_stage_desc& d = st.desc;
+    if (d.dtype == ZB_FP8) return run_forward_fp8(st, mb, x, y, s);
     const int T = d.tokens, H = d.hidden, F = d.ffn;
     if (d.kind == ZB_LINEAR) {
         void* xs = st.slot_tensor(mb, 0, LIN_X);
@@ -114,6 +115,7 @@ int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s)
 
 int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipStream_t s) {
     const zb_stage_desc& d = st.desc;
+    if (d.dtype == ZB_FP8) return run_backward_input_fp8(st, mb, dy, dx, s);
     const int T = d.tokens, H = d.hidden, F = d.ffn;
     if (d.kind == ZB_LINEAR) {
         void* dys = st.slot_tensor(mb, 0, LIN_DY);
@@ -178,6 +180,7 @@ size_t dgamma_scratch_bytes(const zb_stage_desc& d) {
 
 int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s, float* dg_part) {
     const zb_stage_desc& d = st.desc;
+    if (d.dtype == ZB_FP8) return run_backward_weight_fp8(st, mb, s, dg_part);
     const int T = d.tokens, H = d.hidden, F = d.ffn;
     if (d.kind == ZB_LINEAR)
         return linear_gemm(st, tn(F, H, T, st.slot_tensor(mb, 0, LIN_DY), F, st.slot_tensor(mb, 0, LIN_X), H, st.dw[0]), s);
@@ -222,6 +225,10 @@ int32_t run_backward_weight(zb_stage& st, int mb, hipStream_t s, float* dg_part)
 // the same order as two W passes.
 int32_t run_backward_weight_pair(zb_stage& st, int mb, hipStream_t s) {
     const zb_stage_desc& d = st.desc;
+    if (d.dtype == ZB_FP8) {  // no two-segment fp8 kernel: two single passes
+        ZB_TRY(run_backward_weight(st, mb, s));
+        return run_backward_weight(st, mb + 1, s);
+    }
     const int T = d.tokens, H = d.hidden, F = d.ffn;
     std::vector<GemmDesc> g;
     auto two = [&](GemmDesc a, const void* dy1, const void* x1) {

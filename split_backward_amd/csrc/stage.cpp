@@ -26,17 +26,19 @@ namespace {
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
-size_t elem_bytes(int dtype) { return dtype == ZB_F32 ? 4 : 2; }
+size_t elem_bytes(int dtype) { return dtype == ZB_F32 || dtype == ZB_I32 ? 4 : dtype == ZB_E4M3 ? 1 : 2; }
 
 bool valid_desc(const zb_stage_desc* d, std::string& why) {
     if (!d) { why = "desc is NULL"; return false; }
     if (d->tokens < 1 || d->hidden < 1 || d->ffn < 1 || d->ring_slots < 1) { why = "tokens, hidden, ffn, ring_slots must be >= 1"; return false; }
-    if (d->dtype != ZB_F32 && d->dtype != ZB_BF16) { why = "dtype must be ZB_F32 or ZB_BF16"; return false; }
+    if (d->dtype != ZB_F32 && d->dtype != ZB_BF16 && d->dtype != ZB_FP8) { why = "dtype must be ZB_F32, ZB_BF16 or ZB_FP8"; return false; }
+    if (d->dtype == ZB_FP8 && d->kind != ZB_LLAMA) { why = "ZB_FP8 is a Llama stage dtype"; return false; }
+    if (d->dtype == ZB_FP8 && (d->hidden % 128 || d->ffn % 128)) { why = "ZB_FP8 needs hidden and ffn multiples of 128"; return false; }
     if (d->kind == ZB_LINEAR) {
         if (d->dtype == ZB_BF16 && (d->hidden % 8 || d->ffn % 8)) { why = "bf16 linear needs hidden, ffn multiples of 8"; return false; }
         return true;
     }
-    if (d->dtype != ZB_BF16) { why = "only the linear kind supports fp32"; return false; }
+    if (d->dtype == ZB_F32) { why = "only the linear kind supports fp32"; return false; }
     if (d->hidden % 8 || d->ffn % 8) { why = "hidden and ffn must be multiples of 8"; return false; }
     if (d->kind == ZB_MLP_GELU) return true;
     if (d->kind != ZB_LLAMA) { why = "unknown kind"; return false; }
@@ -72,6 +74,29 @@ void Layout::build(const zb_stage_desc& d) {
         add(0, MLP_H, T, F, ZB_BF16);
         add(0, MLP_DY, T, H, ZB_BF16);
         add(0, MLP_DA, T, F, ZB_BF16);
+    } else if (d.dtype == ZB_FP8) {
+        const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
+        for (int l = 0; l < d.n_layers; ++l) {
+            add(l, L_X, T, H, ZB_BF16);
+            add(l, L_R1, T, 1, ZB_F32);
+            add(l, L_QKV, T, QKV, ZB_BF16);
+            add(l, L_A, T, QD, ZB_BF16);
+            add(l, L_LSE, d.n_heads, T, ZB_F32);
+            add(l, L_H1, T, H, ZB_BF16);
+            add(l, L_R2, T, 1, ZB_F32);
+            add(l, L_GU, T, 2 * F, ZB_BF16);
+            add(l, L_DN2, T, H, ZB_BF16);
+            add(l, L_DN1, T, H, ZB_BF16);
+            add(l, L_N1T, H, T, ZB_E4M3);
+            add(l, L_AT, QD, T, ZB_E4M3);
+            add(l, L_N2T, H, T, ZB_E4M3);
+            add(l, L_ST, F, T, ZB_E4M3);
+            add(l, L_DOUTT, H, T, ZB_E4M3);
+            add(l, L_DGUT, 2 * F, T, ZB_E4M3);
+            add(l, L_DH1T, H, T, ZB_E4M3);
+            add(l, L_DQKVT, QKV, T, ZB_E4M3);
+            add(l, L_QEXP, 1, NQ8, ZB_I32);
+        }
     } else {
         const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim;
         for (int l = 0; l < d.n_layers; ++l) {
@@ -104,9 +129,45 @@ void Layout::build(const zb_stage_desc& d) {
                     align_up(attn_bwd_scratch_bytes(d.tokens, d.n_heads, d.n_kv_heads));
         scratch_w = align_up(rmsnorm_dgamma_scratch_floats(d.tokens, d.hidden) * 4);
     }
+    scratch_f = 0;
+    w8_bytes = 0;
+    w8_q.clear();
+    w8_qt.clear();
+    w8_e.clear();
+    if (d.kind == ZB_LLAMA && d.dtype == ZB_FP8) {
+        const size_t QD = (size_t)d.n_heads * d.head_dim, QKV = QD + 2 * (size_t)d.n_kv_heads * d.head_dim;
+        // F: one bf16 activation (n1, n2 or s), its row-major codes, amax partials
+        f_act = 0;
+        f_q = align_up(T * std::max(H, F) * 2);
+        f_part = f_q + align_up(T * std::max({H, QD, F}));
+        scratch_f = f_part + align_up(AMAX_PARTS * 4);
+        // B: after the bf16 stage's scratch, dg|du, dh1, dq|dk|dv, two
+        // ping-pong output gradients, row-major codes, amax partials
+        b_dgu = scratch_b;
+        b_dh1 = b_dgu + align_up(T * 2 * F * 2);
+        b_dqkv = b_dh1 + align_up(T * H * 2);
+        b_dout[0] = b_dqkv + align_up(T * QKV * 2);
+        b_dout[1] = b_dout[0] + align_up(T * H * 2);
+        b_q = b_dout[1] + align_up(T * H * 2);
+        b_part = b_q + align_up(T * std::max({2 * F, QKV, H}));
+        scratch_b = b_part + align_up(AMAX_PARTS * 4);
+        // E4M3 copies [out][in] and [in][out] of every linear weight, one exponent each
+        const int nw = 6 * d.n_layers;
+        w8_q.assign(nw, 0);
+        w8_qt.assign(nw, 0);
+        w8_e.assign(nw, 0);
+        for (int i = 0; i < nw; ++i) {
+            if (i % 6 >= 4) continue;  // RMSNorm gains stay bf16
+            const size_t n = weight_elems(d, i);
+            w8_q[i] = w8_bytes;
+            w8_qt[i] = w8_bytes + align_up(n);
+            w8_e[i] = w8_qt[i] + align_up(n);
+            w8_bytes = w8_e[i] + ALIGN;
+        }
+    }
     stamps_bytes = align_up(sizeof(uint64_t) * (3 * (size_t)MAX_RUN_OPS + 8));
     ring_bytes = slot_bytes * d.ring_slots;
-    total = ring_bytes + scratch_b + scratch_w + stamps_bytes;
+    total = ring_bytes + scratch_b + scratch_w + scratch_f + w8_bytes + stamps_bytes;
 }
 
 const Layout::Tensor* Layout::find(int layer, int which) const {
@@ -213,7 +274,9 @@ extern "C" int32_t zb_stage_create(const zb_stage_desc* d, void* const* weights,
     st->ws = static_cast<char*>(workspace);
     st->scratch_b = st->ws + st->lay.ring_bytes;
     st->scratch_w = st->scratch_b + st->lay.scratch_b;
-    st->stamps = reinterpret_cast<uint64_t*>(st->scratch_w + st->lay.scratch_w);
+    st->scratch_f = st->scratch_w + st->lay.scratch_w;
+    st->w8 = st->scratch_f + st->lay.scratch_f;
+    st->stamps = reinterpret_cast<uint64_t*>(st->w8 + st->lay.w8_bytes);
     st->slots.resize(d->ring_slots);
     auto mk = [&](hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming); };
     for (auto& s : st->slots) {
@@ -339,7 +402,7 @@ extern "C" int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream) {
     if (st->chain_valid[PASS_W]) ZB_HIP(hipStreamWaitEvent(s, st->chain[PASS_W], 0));
     const zb_stage_desc& d = st->desc;
     const int nw = zb_stage_num_weights(&d);
-    if (d.dtype != ZB_BF16) {  // the fp32 linear stage: per weight, then the clearing fill
+    if (d.dtype == ZB_F32) {  // the fp32 linear stage: per weight, then the clearing fill
         for (int i = 0; i < nw; ++i) {
             const int32_t rc = sgd_step_f32(static_cast<float*>(st->w[i]), st->dw[i], weight_elems(d, i), lr, s);
             if (rc) return rc;
@@ -365,6 +428,7 @@ extern "C" int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream) {
         const int32_t rc = sgd_step_group_bf16(g, s);
         if (rc) return rc;
     }
+    st->w8_dirty = true;  // ZB_FP8: the next F re-quantizes the updated weights
     // the same reset as zb_stage_zero_grad, without its fill; the step's
     // completion also becomes the last op of F and B, so the next
     // iteration's first F (on any stream) reads the updated weights
@@ -393,6 +457,67 @@ extern "C" int32_t zb_stage_stash_tensor(zb_stage* st, int32_t mb, int32_t layer
     if (rows) *rows = t->rows;
     if (cols) *cols = t->cols;
     if (dtype) *dtype = t->dtype;
+    return ZB_OK;
+}
+
+extern "C" int32_t zb_stage_fp8_weight(zb_stage* st, int32_t i, void** q, void** qt, void** e) {
+    if (!st || st->desc.dtype != ZB_FP8 || i < 0 || i >= (int)st->lay.w8_e.size() || i % 6 >= 4)
+        return fail(ZB_EINVAL, "zb_stage_fp8_weight: not a linear weight of a ZB_FP8 stage");
+    if (q) *q = st->w8 + st->lay.w8_q[i];
+    if (qt) *qt = st->w8 + st->lay.w8_qt[i];
+    if (e) *e = st->w8 + st->lay.w8_e[i];
+    return ZB_OK;
+}
+
+extern "C" int32_t zb_quantize_e4m3(const void* x, int32_t rows, int32_t cols, int64_t ld, void* q, int64_t ldq,
+                                    void* qt, int64_t ldqt, void* e_out, void* part, void* stream) {
+    return quantize_e4m3(static_cast<const bf16_t*>(x), rows, cols, ld, static_cast<uint8_t*>(q), ldq,
+                         static_cast<uint8_t*>(qt), ldqt, static_cast<int32_t*>(e_out), static_cast<float*>(part),
+                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t zb_gemm_fp8(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, const void* ea,
+                               const void* B, int64_t ldb, const void* eb, void* C, int64_t ldc, int32_t out_f32,
+                               void* stream) {
+    if (!A || !B || !C || !ea || !eb || M < 1 || N < 1 || K < 1 || lda < K || ldb < K || ldc < N)
+        return fail(ZB_EINVAL, "zb_gemm_fp8: bad argument");
+    GemmDesc g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.a_kmajor = 1;
+    g.B = B; g.ldb = ldb; g.b_kmajor = 1;
+    g.C = C; g.ldc = ldc;
+    g.ea = static_cast<const int32_t*>(ea);
+    g.eb = static_cast<const int32_t*>(eb);
+    g.epi = out_f32 ? EPI_ACCUM_F32 : EPI_STORE;
+    return gemm_fp8(g, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t zb_gemm_fp8_wgrad_group(int32_t count, const int32_t* M, const int32_t* N, const int32_t* K,
+                                           const void* const* A, const int64_t* lda, const void* const* ea,
+                                           const void* const* B, const int64_t* ldb, const void* const* eb,
+                                           void* const* C, const int64_t* ldc, void* stream) {
+    if (count < 1 || count > 256 || !M || !N || !K || !A || !lda || !ea || !B || !ldb || !eb || !C || !ldc)
+        return fail(ZB_EINVAL, "zb_gemm_fp8_wgrad_group: bad argument");
+    std::vector<GemmDesc> g(count);
+    for (int i = 0; i < count; ++i) {
+        if (!A[i] || !B[i] || !C[i] || !ea[i] || !eb[i] || M[i] < 1 || N[i] < 1 || K[i] < 1 || lda[i] < K[i] ||
+            ldb[i] < K[i] || ldc[i] < N[i])
+            return fail(ZB_EINVAL, "zb_gemm_fp8_wgrad_group: bad product");
+        GemmDesc& d = g[i];
+        d = GemmDesc{};
+        d.M = M[i]; d.N = N[i]; d.K = K[i];
+        d.A = A[i]; d.lda = lda[i]; d.a_kmajor = 1;
+        d.B = B[i]; d.ldb = ldb[i]; d.b_kmajor = 1;
+        d.C = C[i]; d.ldc = ldc[i];
+        d.ea = static_cast<const int32_t*>(ea[i]);
+        d.eb = static_cast<const int32_t*>(eb[i]);
+        d.epi = EPI_ACCUM_F32;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < count; i += 16) {
+        const int32_t rc = gemm_fp8_group(&g[i], std::min(16, count - i), s);
+        if (rc != ZB_OK) return rc;
+    }
     return ZB_OK;
 }
 

@@ -16,8 +16,13 @@ enum { LIN_X = 0, LIN_DY = 1 };
 enum { MLP_X = 0, MLP_A = 1, MLP_H = 2, MLP_DY = 3, MLP_DA = 4 };
 enum {
     L_X = 0, L_R1, L_N1, L_QKV, L_A, L_LSE, L_H1, L_R2, L_N2, L_GU, L_S,  // kept by F
-    L_DOUT, L_DGU, L_DN2, L_DH1, L_DQKV, L_DN1                            // kept by B
+    L_DOUT, L_DGU, L_DN2, L_DH1, L_DQKV, L_DN1,                           // kept by B
+    // ZB_FP8 stages: the W-only operands as transposed E4M3 codes
+    // ([features][tokens]) and their exponents (int32, in this order);
+    // those stages keep no bf16 n1, n2, s, dout, dgu, dh1, dqkv.
+    L_N1T, L_AT, L_N2T, L_ST, L_DOUTT, L_DGUT, L_DH1T, L_DQKVT, L_QEXP
 };
+constexpr int NQ8 = 8;  // quantized stash tensors per layer (L_N1T .. L_DQKVT)
 enum { PASS_F = 0, PASS_B = 1, PASS_W = 2 };
 
 struct Layout {
@@ -27,6 +32,12 @@ struct Layout {
     };
     std::vector<Tensor> off;
     size_t slot_bytes = 0, ring_bytes = 0, scratch_b = 0, scratch_w = 0, stamps_bytes = 0, total = 0;
+    // ZB_FP8 stages: F-pass scratch, the E4M3 weight copies, and offsets
+    // inside the pass scratch (bytes from its start).
+    size_t scratch_f = 0, w8_bytes = 0;
+    size_t f_act = 0, f_q = 0, f_part = 0;                                  // F scratch
+    size_t b_dgu = 0, b_dh1 = 0, b_dqkv = 0, b_dout[2] = {0, 0}, b_q = 0, b_part = 0;  // B scratch
+    std::vector<size_t> w8_q, w8_qt, w8_e;                                  // per weight index (0 if none)
     void build(const zb_stage_desc& d);
     const Tensor* find(int layer, int which) const;
 };
@@ -50,6 +61,9 @@ struct zb_stage {
     char* ws = nullptr;
     char* scratch_b = nullptr;
     char* scratch_w = nullptr;
+    char* scratch_f = nullptr;  // ZB_FP8: F-pass scratch
+    char* w8 = nullptr;         // ZB_FP8: E4M3 weight copies
+    bool w8_dirty = true;       // ZB_FP8: refresh the copies at the next F
     uint64_t* stamps = nullptr;
     std::vector<zb::Slot> slots;
     std::array<hipEvent_t, 3> chain{};     // last op of each pass (scratch reuse order)
@@ -81,4 +95,8 @@ size_t dgamma_scratch_bytes(const zb_stage_desc& d);
 // stage's workspace scratch).
 int32_t bwd_weight_accum(zb_stage* st, int mb, hipStream_t s, float* dg_part);
 int32_t run_backward_weight_pair(zb_stage& st, int mb, hipStream_t s);
+// ZB_FP8 Llama stages (passes_fp8.cpp)
+int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_t s);
+int32_t run_backward_input_fp8(zb_stage& st, int mb, const void* dy, void* dx, hipStream_t s);
+int32_t run_backward_weight_fp8(zb_stage& st, int mb, hipStream_t s, float* dg_part);
 }  // namespace zb

@@ -200,6 +200,9 @@ WORKLOADS = {
     # Llama-7B-shape stage: 4 decoder layers, h=4096, 32 heads, ffn 11008, s=4096, 16 microbatches
     "llama7b_stage4": dict(shape=StageShape("llama", 4096, 4096, 11008, n_layers=4,
                                             n_heads=32, n_kv_heads=32, head_dim=128), m=16),
+    # the same stage with every linear product on E4M3 operands (stage dtype fp8)
+    "llama7b_stage4_fp8": dict(shape=StageShape("llama", 4096, 4096, 11008, n_layers=4,
+                                                n_heads=32, n_kv_heads=32, head_dim=128), m=16, stage_dtype="fp8"),
     # Llama-70B-shape slice: 2 layers, h=8192, 64/8 heads, ffn 28672, s=4096, 24 microbatches, 8-slot ring
     "llama70b_slice2": dict(shape=StageShape("llama", 4096, 8192, 28672, n_layers=2,
                                              n_heads=64, n_kv_heads=8, head_dim=128), m=24, ring=8),
