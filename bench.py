@@ -437,14 +437,21 @@ def interleaved_idle(weights, shape, m, xs, dys, p=8, stage_idx=3, v=2):
     return out
 
 
-def memory_limit_sweep(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3):
+def memory_limit_sweep(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3, weights=None, shape=None):
     """ZB(M) for M = p .. 2p on the GPU (arrivals at costs 1:1:1 in units of
     the mean pass time), replayed in ordered mode and in filler mode (W on
     the second stream): measured in-window idle and stage end beside the
     simulator's, and the stash the order keeps resident at its peak (peak
-    in-flight microbatches x bytes per ring slot)."""
+    in-flight microbatches x bytes per ring slot).  When the benchmark
+    stage's ring is smaller than 2p (the Llama-70B slice keeps 8 slots), a
+    second stage with a 2p-slot ring, sharing the weight tensors, runs the
+    sweep."""
     import torch
     import split_backward_amd as zb
+    if stage.desc.ring_slots < 2 * p and weights is not None:
+        stage = zb.Stage(shape.kind, shape.tokens, shape.hidden, shape.ffn, weights, dtype=shape.dtype,
+                         n_layers=shape.n_layers, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
+                         head_dim=shape.head_dim, ring_slots=2 * p)
     slot = stage.slot_bytes()
     rows = []
     for M in range(p, 2 * p + 1):
@@ -490,9 +497,10 @@ def multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o, p=8, stage_i
     cases = [("costs_1:1:1", (10, 10, 10), max(1, int(round(10 * t_o / u))), u / 10),
              ("measured_costs", tuple(max(1, int(round(t / q))) for t in (t_f, t_b, t_w)), max(1, int(round(t_o / q))), q)]
     stage.set_lr(lr)
-    out = {"optimizer_step_ms": round(t_o, 3), "n_iter": n_iter, "M": 2 * p}
+    out = {"optimizer_step_ms": round(t_o, 3), "n_iter": n_iter, "M": min(2 * p, stage.desc.ring_slots)}
     for name, costs, c_opt, unit in cases:
-        for kind, M, modes in (("zb", 2 * p, (("ordered", zb.EXEC_ORDERED), ("filler", zb.EXEC_FILLER))),
+        for kind, M, modes in (("zb", min(2 * p, stage.desc.ring_slots),
+                                (("ordered", zb.EXEC_ORDERED), ("filler", zb.EXEC_FILLER))),
                                ("1f1b", 0, (("ordered", zb.EXEC_ORDERED),))):
             g = zb.schedule_generate_iters(p, m, M, costs, c_opt, n_iter, stage_idx, kind=kind)
             ops = g["ops"]
@@ -685,7 +693,8 @@ def main():
     if shape.kind == "llama" and not args.no_executor and not fp8:
         extra["executor_p8_stage3"] = executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w)
         extra["executor_p8_stage3"]["interleaved_1f1b_v2"] = interleaved_idle(weights, shape, m, xs, dys)
-        extra["memory_limit_sweep_p8_stage3"] = memory_limit_sweep(stage, m, xs, ys, dys, dxs, (t_f + t_b + t_w) / 3.0)
+        extra["memory_limit_sweep_p8_stage3"] = memory_limit_sweep(stage, m, xs, ys, dys, dxs, (t_f + t_b + t_w) / 3.0,
+                                                                   weights=weights, shape=shape)
         # the optimizer step's own time (SGD over every weight, then dW cleared)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         stage.sgd_step(0.0)

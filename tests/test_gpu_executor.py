@@ -234,3 +234,43 @@ def test_chunk_executor_rejects_chunk_out_of_range():
                                [dxs] * 2)
     assert e.value.code == zb.EINVAL
     torch.cuda.synchronize()
+
+
+def test_memory_limit_sweep_stash_matches_simulator():
+    """ZB(M) for M = p .. 2p ([Guide] "Core Innovation 2": the memory limit
+    between p and 2p in-flight microbatches): the simulator's peak of
+    stashed microbatches equals the peak counted from its op list, a ring of
+    exactly that many slots replays the order (result bit for bit that of
+    sequential issue, which here is the oracle-checked path), and one slot
+    fewer refuses it with ZB_ERING_FULL before any work of the refused op."""
+    p, stage, m = 4, 1, 10
+    for M in range(p, 2 * p + 1):
+        g = zb.schedule_generate("zb", p, m, M, (1, 1, 1), stage)
+        live = peak = 0
+        for t, _ in g["ops"]:
+            live += {"F": 1, "W": -1}.get(t, 0)
+            peak = max(peak, live)
+        assert peak == g["peak_active"] <= M
+        st, _ = make_stage(SHAPE, peak)
+        xs, ys, dys, dxs = _inputs(m)
+        st.zero_grad()
+        torch.cuda.synchronize()
+        st.run_schedule(g["ops"], g["arrive_f"], g["arrive_b"], 0.05, xs, ys, dys, dxs)
+        torch.cuda.synchronize()
+        y_ref, dx_ref, dw_ref = _sequential(g["ops"], peak, m)
+        for a, b in zip([to_f64(y) for y in ys] + [to_f64(d) for d in dxs] + [to_f64(w) for w in st.dw],
+                        y_ref + dx_ref + dw_ref):
+            assert np.array_equal(a, b)
+        if peak > 1:
+            small, _ = make_stage(SHAPE, peak - 1)
+            small.zero_grad()
+            with pytest.raises(zb.ZbError) as e:
+                for t, j in g["ops"]:
+                    if t == "F":
+                        small.fwd(j, xs[j], ys[j])
+                    elif t == "B":
+                        small.bwd_input(j, dys[j], dxs[j])
+                    else:
+                        small.bwd_weight(j)
+            assert e.value.code == zb.ERING_FULL
+            torch.cuda.synchronize()
