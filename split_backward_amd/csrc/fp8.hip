@@ -10,13 +10,15 @@
 // to even (the hardware conversion v_cvt_pk_fp8_f32).  x * 2^-e is exact in
 // fp32, so the E4M3 rounding is the only rounding.
 //
-// Three kernels, all HBM-bound:
-//   amax_partial_kernel   max|x| of row groups -> AMAX_PARTS partials
-//   amax_final_kernel     max of the partials -> the exponent e (int32)
-//   quantize_kernel       64 x 64 tiles: codes row-major [rows][cols] and/or
+// Two kernels, both HBM-bound:
+//   amax_partial_kernel   max|x| of grid-strided 16-byte chunks -> up to
+//                         AMAX_PARTS partial maxima
+//   quantize_kernel       the exponent from the partials (every block), then
+//                         64 x 64 tiles: codes row-major [rows][cols] and/or
 //                         transposed [cols][rows] (through LDS), so that a
 //                         product's K index is contiguous whichever operand
 //                         the tensor becomes.
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -32,23 +34,34 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Rows blockIdx.x, blockIdx.x + gridDim.x, ...; 8 columns per thread.
+// max|x| over the matrix in 16-byte chunks (8 values), chunk c of a grid
+// stride loop at row c / (cols / 8); four loads in flight per thread.
 __global__ __launch_bounds__(256) void amax_partial_kernel(const bf16_t* __restrict__ x, int rows, int cols,
                                                            int64_t ld, float* __restrict__ part) {
     __shared__ float red[4];
     float m = 0.f;
-    const int per_row = cols / 8;
-    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
-        const bf16_t* row = x + (int64_t)r * ld;
-        for (int c = threadIdx.x; c < per_row; c += 256) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(row + c * 8);
+    const uint32_t per_row = (uint32_t)cols / 8, total = (uint32_t)rows * per_row;
+    const uint32_t stride = gridDim.x * 256u;
+    auto at = [&](uint32_t c) {
+        const uint32_t r = c / per_row, k = c - r * per_row;
+        return *reinterpret_cast<const u32x4*>(x + (int64_t)r * ld + (int64_t)k * 8);
+    };
+    auto fold = [&](const u32x4& v) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                m = fmaxf(m, fabsf(__uint_as_float(v[i] << 16)));
-                m = fmaxf(m, fabsf(__uint_as_float(v[i] & 0xffff0000u)));
-            }
+        for (int i = 0; i < 4; ++i) {
+            m = fmaxf(m, fabsf(__uint_as_float(v[i] << 16)));
+            m = fmaxf(m, fabsf(__uint_as_float(v[i] & 0xffff0000u)));
         }
+    };
+    uint32_t c = blockIdx.x * 256u + threadIdx.x;
+    for (; c + 3 * stride < total; c += 4 * stride) {
+        const u32x4 v0 = at(c), v1 = at(c + stride), v2 = at(c + 2 * stride), v3 = at(c + 3 * stride);
+        fold(v0);
+        fold(v1);
+        fold(v2);
+        fold(v3);
     }
+    for (; c < total; c += stride) fold(at(c));
     m = wave_max(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
@@ -65,27 +78,27 @@ __device__ __forceinline__ int scale_exponent(float amax) {
     return f <= 0.875f ? x - 9 : x - 8;
 }
 
-__global__ __launch_bounds__(256) void amax_final_kernel(const float* __restrict__ part, int nparts,
-                                                         int32_t* __restrict__ e_out) {
-    __shared__ float red[4];
-    float m = 0.f;
-    for (int i = threadIdx.x; i < nparts; i += 256) m = fmaxf(m, part[i]);
-    m = wave_max(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) *e_out = scale_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-}
-
 // One 64 x 64 tile per block (blockIdx.x: column tile, blockIdx.y: row
 // tile); thread t converts 16 consecutive columns of row t / 4.  rows and
 // cols are multiples of 16.  Codes of four values go into one dword with two
 // packed conversions.
 __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict__ x, int rows, int cols, int64_t ld,
-                                                       const int32_t* __restrict__ e_in, uint8_t* __restrict__ q,
+                                                       const float* __restrict__ part, int nparts,
+                                                       int32_t* __restrict__ e_out, uint8_t* __restrict__ q,
                                                        int64_t ldq, uint8_t* __restrict__ qt, int64_t ldqt) {
     __shared__ uint32_t tile[QT][QT / 4 + 1];  // codes, 4 per word, padded row
+    __shared__ float red[4];
     const int tid = threadIdx.x;
-    const int ne = -*e_in;  // x * 2^-e with v_ldexp_f32: exact, whatever the range of 2^-e
+    // every block reduces the partial maxima itself (the same values in the
+    // same order, so the same exponent); block (0, 0) publishes it
+    float am = 0.f;
+    for (int i = tid; i < nparts; i += 256) am = fmaxf(am, part[i]);
+    am = wave_max(am);
+    if ((tid & 63) == 0) red[tid >> 6] = am;
+    __syncthreads();
+    const int e = scale_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) *e_out = e;
+    const int ne = -e;  // x * 2^-e with v_ldexp_f32: exact, whatever the range of 2^-e
     const int r0 = blockIdx.y * QT, c0 = blockIdx.x * QT;
     const int rr = tid >> 2, cc = (tid & 3) * 16;
     const int r = r0 + rr, c = c0 + cc;
@@ -142,13 +155,13 @@ int32_t quantize_e4m3(const bf16_t* x, int rows, int cols, int64_t ld, uint8_t* 
         return fail(ZB_EINVAL, "quantize_e4m3: rows and cols must be multiples of 16, leading dimensions aligned");
     if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(qt)) & 15)
         return fail(ZB_EINVAL, "quantize_e4m3: pointers must be 16-byte aligned");
-    const int nparts = rows < AMAX_PARTS ? rows : AMAX_PARTS;
+    const int64_t chunks = (int64_t)rows * (cols / 8);
+    if (chunks >= (int64_t)1 << 31) return fail(ZB_EINVAL, "quantize_e4m3: tensor too large");
+    const int nparts = (int)std::min<int64_t>(AMAX_PARTS, (chunks + 1023) / 1024);
     hipLaunchKernelGGL(amax_partial_kernel, dim3(nparts), dim3(256), 0, s, x, rows, cols, ld, part);
     ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(256), 0, s, part, nparts, e_out);
-    ZB_HIP(hipGetLastError());
     hipLaunchKernelGGL(quantize_kernel, dim3((cols + QT - 1) / QT, (rows + QT - 1) / QT), dim3(256), 0, s, x, rows,
-                       cols, ld, e_out, q, ldq, qt, ldqt);
+                       cols, ld, part, nparts, e_out, q, ldq, qt, ldqt);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
