@@ -148,7 +148,9 @@ def w_kernel_launches(shape, device):
 
 W_KERNEL = "gemm_v2_group_kernel<false,false,EPI_ACCUM_F32>"
 W_KERNEL_SOURCES = ("split_backward_amd/csrc/gemm_v2.hip", "split_backward_amd/csrc/common.h")
-TRAFFIC_SUMMARY = "profiles/gemm_w_kernel_hbm_traffic_llama7b_stage4.md"
+# Counter summaries of the W kernel's HBM traffic, by workload.
+TRAFFIC_SUMMARIES = {"llama7b_stage4": "profiles/gemm_w_kernel_hbm_traffic_llama7b_stage4.md",
+                     "llama7b_stage4_fp8": "profiles/gemm_w_fp8_kernel_hbm_traffic_llama7b_stage4_fp8.md"}
 
 
 COMMON_H_END = "// ------------------------------------------------- elementwise / norms ----"
@@ -182,8 +184,10 @@ def measured_traffic(workload):
     for a copy kernel of known size), or None when the summary is missing,
     covers another workload or was taken on other kernel sources."""
     import re
+    if workload not in TRAFFIC_SUMMARIES:
+        return None
     try:
-        with open(os.path.join(ROOT, TRAFFIC_SUMMARY)) as fh:
+        with open(os.path.join(ROOT, TRAFFIC_SUMMARIES[workload])) as fh:
             txt = fh.read()
     except OSError:
         return None
@@ -227,20 +231,37 @@ def time_w_kernel(shape, workload, device, reps=5):
             "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
 
 
-def time_w_kernel_fp8(shape, device, reps=5):
+def w_kernel_launches_fp8(shape, device):
+    """The fp8 stage's W-pass products (E4M3 codes of dY^T and X^T, both
+    K-contiguous, fp32 dW in place) at the step's shapes, and a closure
+    issuing them as one grouped launch per 16 products.  The codes are the
+    library's own quantization of normal bf16 [K, M] and [K, N] tensors into
+    their transposed layout, as the stage stashes its activations and
+    gradients (uniformly random codes would not have the value distribution
+    of the stage's operands)."""
+    import torch
+    import split_backward_amd as zb
+    gem = w_pass_gemms(shape)
+    As, eas, Bs, ebs, Cs = [], [], [], [], []
+    for (M, N, K) in gem:
+        for rows_out, codes, exps in ((M, As, eas), (N, Bs, ebs)):
+            src = torch.randn((K, rows_out), device=device).to(torch.bfloat16)
+            qt = torch.empty((rows_out, K), dtype=torch.uint8, device=device)
+            _, _, e = zb.quantize_e4m3(src, qt=qt)
+            codes.append(qt)
+            exps.append(e)
+            del src
+        Cs.append(torch.zeros((M, N), dtype=torch.float32, device=device))
+    torch.cuda.synchronize()
+    return gem, lambda: zb.gemm_fp8_wgrad_group(As, eas, Bs, ebs, Cs)
+
+
+def time_w_kernel_fp8(shape, workload, device, reps=5):
     """The fp8 stage's W-pass launch (16 products on E4M3 codes, fp32 dW
     accumulated in place) at the step's shapes, replayed on the current
     stream and timed with HIP events, against the fp8 dense peak."""
     import torch
-    import split_backward_amd as zb
-    gem = w_pass_gemms(shape)
-    As, Bs, Cs = [], [], []
-    for (M, N, K) in gem:
-        As.append(torch.randint(0, 0x7E, (M, K), dtype=torch.uint8, device=device))
-        Bs.append(torch.randint(0, 0x7E, (N, K), dtype=torch.uint8, device=device))
-        Cs.append(torch.zeros((M, N), dtype=torch.float32, device=device))
-    e = torch.full((1,), -12, dtype=torch.int32, device=device)
-    once = lambda: zb.gemm_fp8_wgrad_group(As, [e] * len(As), Bs, [e] * len(Bs), Cs)
+    gem, once = w_kernel_launches_fp8(shape, device)
     once()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -255,25 +276,29 @@ def time_w_kernel_fp8(shape, device, reps=5):
     achieved = flops / (ms_total * 1e-3) / 1e12
     algo_bytes = sum(K * (M + N) + 2 * 4 * M * N for M, N, K in gem) / ((len(gem) + 15) // 16)
     avg_ms = ms_total / launches
+    traffic = measured_traffic(workload)
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": algo_bytes,
             "stash_and_dw_GBps": round(algo_bytes / (avg_ms * 1e-3) / 1e9, 1),
+            "hbm_GBps": round(traffic / (avg_ms * 1e-3) / 1e9, 1) if traffic else None,
             "kernel": "gemm_f8_group_kernel<EPI_ACCUM_F32> (fp8 W pass: dW += dY^T X on E4M3 codes, fp32 in place)",
             "avg_launch_us": round(avg_ms * 1e3, 1), "launches_timed": launches}
 
 
-def traffic_probe(shape, device):
+def traffic_probe(shape, device, fp8=False):
     """Workload for the rocprofv3 --pmc passes: a copy of known size (1 GiB
     read, 1 GiB written, elementwise negation) three times, then the W-pass
-    launches twice.  Prints the kernel-source hash the counters belong to."""
+    launches (bf16, or fp8 for the fp8 stage) twice.  Prints the
+    kernel-source hash the counters belong to."""
     import torch
     n = 1 << 28  # fp32 elements = 1 GiB
     src = torch.ones(n, device=device)
     dst = torch.empty_like(src)
     for _ in range(3):
         torch.neg(src, out=dst)
-    gem, once = w_kernel_launches(shape, device)
+    gem, once = (w_kernel_launches_fp8 if fp8 else w_kernel_launches)(shape, device)
     for _ in range(2):
         once()
     torch.cuda.synchronize()
@@ -530,26 +555,36 @@ def multi_iteration(stage, m, xs, ys, dys, dxs, t_f, t_b, t_w, t_o, p=8, stage_i
     return out
 
 
-REPLAY_RUNS = (("zb_M16_ordered", "zb", 16, 0), ("zb_M16_filler", "zb", 16, 1), ("1f1b_ordered", "1f1b", 0, 0))
+# (name, order, M, mode, costs): costs None = 1:1:1 in units of the mean
+# pass time, "measured" = the calibrated F, B, W times in 0.1 ms units.
+REPLAY_RUNS = (("zb_M16_ordered", "zb", 16, 0, None), ("zb_M16_filler", "zb", 16, 1, None),
+               ("1f1b_ordered", "1f1b", 0, 0, None),
+               ("zb_M16_ordered_measured_costs", "zb", 16, 0, "measured"),
+               ("zb_M16_filler_measured_costs", "zb", 16, 1, "measured"))
 
 
-def replay_only(stage, m, xs, ys, dys, dxs, unit, p=8, stage_idx=3):
+def replay_only(stage, m, xs, ys, dys, dxs, pass_ms, p=8, stage_idx=3):
     """The replays whose idle a rocprofv3 kernel trace measures
     independently (--replay-only under rocprofv3 --kernel-trace, then
-    --trace-idle): zero bubble (M = 16) in ordered and filler mode and 1F1B,
-    arrivals at costs 1:1:1 in units of the mean pass time, one after the
+    --trace-idle): zero bubble (M = 16) in ordered and filler mode and 1F1B
+    with arrivals at costs 1:1:1 in units of the mean pass time, then zero
+    bubble again with arrivals at the measured F, B, W costs, one after the
     other with the GPU idle in between."""
     import torch
     import split_backward_amd as zb
     out = []
-    for name, kind, M, mode in REPLAY_RUNS:
-        g = zb.schedule_generate(kind, p, m, M, (1, 1, 1), stage_idx)
+    for name, kind, M, mode, costs in REPLAY_RUNS:
+        if costs is None:
+            c, unit = (1, 1, 1), sum(pass_ms) / 3.0
+        else:
+            c, unit = tuple(max(1, int(round(t * 10))) for t in pass_ms), 0.1
+        g = zb.schedule_generate(kind, p, m, M, c, stage_idx)
         stage.zero_grad()
         torch.cuda.synchronize()
         r = stage.run_schedule(g["ops"], g["arrive_f"], g["arrive_b"], unit, xs, ys, dys, dxs, mode=mode)
         torch.cuda.synchronize()
         win = g["last_end"] - g["first_start"]
-        out.append({"name": name, "n_ops": len(g["ops"]), "unit_ms": round(unit, 4),
+        out.append({"name": name, "n_ops": len(g["ops"]), "costs": list(c), "unit_ms": round(unit, 4),
                     "stamp_in_window_idle": round(r["in_window_idle"], 5), "stamp_window_ms": round(r["window_ms"], 3),
                     "stamp_busy_ms": round(r["busy_ms"], 3),
                     "predicted_in_window_idle": round(1 - g["busy"] / win, 5)})
@@ -633,7 +668,7 @@ def main():
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     if args.traffic_probe:
-        traffic_probe(shape, device)
+        traffic_probe(shape, device, fp8)
         return
     weights = [synth.to_device(w, device) for w in synth.make_weights(shape)]
     stage = zb.Stage(shape.kind, shape.tokens, shape.hidden, shape.ffn, weights, dtype=stage_dtype,
@@ -661,7 +696,7 @@ def main():
     if args.replay_only:
         step()  # warm-up
         t_f, t_b, t_w = calibrate(stage, xs, ys, dys, dxs)
-        print(json.dumps({"replays": replay_only(stage, m, xs, ys, dys, dxs, (t_f + t_b + t_w) / 3.0),
+        print(json.dumps({"replays": replay_only(stage, m, xs, ys, dys, dxs, (t_f, t_b, t_w)),
                           "pass_ms": [t_f, t_b, t_w]}), flush=True)
         return
 
@@ -684,7 +719,7 @@ def main():
     # The fp32 linear workload runs the fp32 GEMM (a few microseconds per
     # product, launch-bound): no roofline figure for it.
     if fp8:
-        roof = time_w_kernel_fp8(shape, device)
+        roof = time_w_kernel_fp8(shape, args.workload, device)
     elif shape.dtype == "bf16":
         roof = time_w_kernel(shape, args.workload, device)
     else:

@@ -10,8 +10,8 @@ import bench
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _summary(tmp_path, workload, sha):
-    p = tmp_path / "traffic.md"
+def _summary(tmp_path, workload, sha, name="traffic.md"):
+    p = tmp_path / name
     p.write_text("# summary\n\nhbm_bytes_per_launch: 1.250000e+10\n"
                  f"workload: {workload}\nkernel_source_sha256: {sha}\n")
     return p
@@ -22,10 +22,18 @@ def test_traffic_needs_matching_workload_and_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     # kernel_source_hash reads the sources under ROOT: keep the repository's hash
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: sha)
-    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", "traffic.md")
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARIES", {"llama7b_stage4": "traffic.md",
+                                                      "llama7b_stage4_fp8": "traffic_fp8.md"})
     _summary(tmp_path, "llama7b_stage4", sha)
     assert bench.measured_traffic("llama7b_stage4") == 1.25e10
     assert bench.measured_traffic("llama70b_slice2") is None
+    # the fp8 workload reads its own summary only
+    assert bench.measured_traffic("llama7b_stage4_fp8") is None
+    (tmp_path / "traffic.md").rename(tmp_path / "traffic_fp8.md")
+    assert bench.measured_traffic("llama7b_stage4_fp8") is None  # summary names another workload
+    _summary(tmp_path, "llama7b_stage4", sha)
+    _summary(tmp_path, "llama7b_stage4_fp8", sha, name="traffic_fp8.md")
+    assert bench.measured_traffic("llama7b_stage4_fp8") == 1.25e10
     _summary(tmp_path, "llama7b_stage4", "0" * 16)
     assert bench.measured_traffic("llama7b_stage4") is None
     (tmp_path / "traffic.md").unlink()
