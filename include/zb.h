@@ -212,6 +212,39 @@ int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream);
  * is not finite. */
 int32_t zb_stage_set_lr(zb_stage* st, float lr);
 
+/* Debug aids.  The pages define none; they check the ring discipline the
+ * split relies on (the Guide's "Memory Management & Activation Rollback": a
+ * microbatch's stash is freed only once its W has run, so a slot is reused
+ * only after that W).  The host already enforces that order when calls are
+ * issued (ZB_ESTATE, ZB_ERING_FULL); these check it where the work runs.
+ *  ZB_DEBUG_SLOT_TAGS  every pass checks, on the device and in stream order
+ *                      with its kernels, the tag of its microbatch's ring
+ *                      slot, then updates it: tag = 4 mb + 1 after F(mb),
+ *                      + 2 after B(mb), + 3 after W(mb), -1 unused.  F needs
+ *                      an unused slot or one whose W is done, B(mb) needs
+ *                      4 mb + 1, W(mb) needs 4 mb + 2.  A mismatch is
+ *                      counted and recorded (zb_stage_debug_report); nothing
+ *                      traps.  Enabling the flag resets every tag to unused
+ *                      (after the stage's issued work), so microbatches in
+ *                      flight at that moment report at their next pass.
+ *  ZB_DEBUG_SERIALIZE  every op (F, B, W, W pair, optimizer step) ends with
+ *                      hipDeviceSynchronize; a device fault is then reported
+ *                      (ZB_EHIP) by the op that caused it.  Timing figures of
+ *                      zb_stage_run_schedule are meaningless in this mode.
+ * w_delay_us (0 .. 1000000): each W pass (single or pair) first waits that
+ * long on its stream (a device-clock wait kernel), to test that nothing
+ * overwrites a slot before a slow W has read it.  ZB_EINVAL for an unknown
+ * flag or a delay out of range. */
+enum { ZB_DEBUG_SLOT_TAGS = 1, ZB_DEBUG_SERIALIZE = 2 };
+int32_t zb_stage_set_debug(zb_stage* st, int32_t flags, int32_t w_delay_us, void* stream);
+
+/* Waits for the device, then returns the number of slot-tag mismatches
+ * since the tags were enabled (>= 0) and, if info is non-NULL, writes the
+ * last one: info[0..4] = {op type (ZB_OP_F/B/W), mb, slot, tag found, tag
+ * expected (-2: unused or W done)}.  ZB_ESTATE if slot tags are not
+ * enabled. */
+int32_t zb_stage_debug_report(zb_stage* st, int32_t* info);
+
 /* ------------------------------------------------------------ schedules -- */
 
 /* Op of a per-stage schedule (the Guide scheduler listing's task types). */

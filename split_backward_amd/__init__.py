@@ -21,6 +21,7 @@ F32, BF16, FP8, E4M3, I32 = 0, 1, 2, 3, 4
 DTYPE = {"f32": F32, "bf16": BF16, "fp8": FP8}
 LINEAR, MLP_GELU, LLAMA = 0, 1, 2
 OP_F, OP_B, OP_W, OP_O = 0, 1, 2, 3
+DEBUG_SLOT_TAGS, DEBUG_SERIALIZE = 1, 2
 SCHED_GPIPE, SCHED_1F1B, SCHED_ZB = 0, 1, 2
 EXEC_ORDERED, EXEC_FILLER = 0, 1
 
@@ -83,6 +84,8 @@ _PROTOS = {
     "zb_stage_zero_grad": (_i32, [_vp, _vp]),
     "zb_stage_sgd_step": (_i32, [_vp, ctypes.c_float, _vp]),
     "zb_stage_set_lr": (_i32, [_vp, ctypes.c_float]),
+    "zb_stage_set_debug": (_i32, [_vp, _i32, _i32, _vp]),
+    "zb_stage_debug_report": (_i32, [_vp, ctypes.POINTER(_i32)]),
     "zb_stage_stash_tensor": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
                                      ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "zb_schedule_generate": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Op),
@@ -378,6 +381,25 @@ class Stage:
 
     def zero_grad(self, stream=None):
         check(lib().zb_stage_zero_grad(self.handle, _stream_ptr(stream)))
+
+    def set_debug(self, slot_tags: bool = False, serialize: bool = False, w_delay_us: int = 0, stream=None):
+        """Debug aids (zb_stage_set_debug): device-side ring-slot tags,
+        a device synchronization after every op, a delay before every W."""
+        flags = (DEBUG_SLOT_TAGS if slot_tags else 0) | (DEBUG_SERIALIZE if serialize else 0)
+        check(lib().zb_stage_set_debug(self.handle, flags, int(w_delay_us), _stream_ptr(stream)))
+
+    def debug_report(self):
+        """(mismatch count, last mismatch as a dict or None) of the slot
+        tags (zb_stage_debug_report; waits for the device)."""
+        info = (_i32 * 5)()
+        n = lib().zb_stage_debug_report(self.handle, info)
+        if n < 0:
+            check(n)
+        last = None
+        if n:
+            last = {"op": "FBW"[info[0]] if 0 <= info[0] < 3 else info[0], "mb": info[1], "slot": info[2],
+                    "found": info[3], "expected": info[4]}
+        return n, last
 
     def stash(self, mb: int, layer: int, which: int):
         """Torch view of a stashed tensor (valid until W(mb) completes)."""

@@ -19,7 +19,7 @@ BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libzb.so")
 
 SOURCES = ["errors.cpp", "gemm.hip", "gemm_v2.hip", "norm.hip", "attention.hip", "stage.cpp", "passes.cpp",
-           "schedule.cpp", "executor.cpp", "noalloc.cpp", "fp8.hip", "passes_fp8.cpp"]
+           "schedule.cpp", "executor.cpp", "noalloc.cpp", "fp8.hip", "passes_fp8.cpp", "debug.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -149,6 +149,18 @@ size_t attn_bwd_scratch_bytes(int T, int nq, int nkv);
 int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout,
                  bf16_t* dqkv, float* delta, float* part, int T, int nq, int nkv, hipStream_t s);
 
+// ---------------------------------------------------------------- debug ---
+// Ring-slot tags (debug.hip): tags[slot] = 4 * mb + phase (1 F, 2 B, 3 W
+// done), -1 = unused.  slot_tag checks tags[slot] against `expect` (a tag,
+// TAG_FREE = unused or phase 3, TAG_ANY = no check), records a mismatch in
+// rec[0..5] = {count, op, mb, slot, found, expected}, then stores `set`
+// unless it is TAG_KEEP.
+constexpr int TAG_FREE = -2, TAG_ANY = -3, TAG_KEEP = -4;
+constexpr int DEBUG_REC = 8;  // int32 words of the mismatch record
+int32_t slot_tag(int32_t* tags, int32_t* rec, int slot, int op, int mb, int expect, int set, hipStream_t s);
+// tags[0..n) = -1, rec[0..DEBUG_REC) = 0.
+int32_t tag_reset(int32_t* tags, int n, int32_t* rec, hipStream_t s);
+
 // --------------------------------------------------------------- timing ---
 int32_t stamp_now(uint64_t* dst, hipStream_t s);
 int32_t wait_until(const uint64_t* t0, uint64_t delta_ticks, uint64_t* wait_end, hipStream_t s);

@@ -166,8 +166,10 @@ void Layout::build(const zb_stage_desc& d) {
         }
     }
     stamps_bytes = align_up(sizeof(uint64_t) * (3 * (size_t)MAX_RUN_OPS + 8));
+    // debug area: the delay stamp (8 bytes), the mismatch record, one tag per slot
+    debug_bytes = align_up(8 + 4 * (size_t)DEBUG_REC + 4 * (size_t)d.ring_slots);
     ring_bytes = slot_bytes * d.ring_slots;
-    total = ring_bytes + scratch_b + scratch_w + scratch_f + w8_bytes + stamps_bytes;
+    total = ring_bytes + scratch_b + scratch_w + scratch_f + w8_bytes + stamps_bytes + debug_bytes;
 }
 
 const Layout::Tensor* Layout::find(int layer, int which) const {
@@ -219,6 +221,25 @@ int32_t zb_stage::wait_deps(int type, int mb, hipStream_t s) {
         default:
             return ZB_OK;
     }
+}
+
+int32_t zb_stage::tag(int op, int mb, int expect, int set, hipStream_t s) {
+    if (!(debug_flags & ZB_DEBUG_SLOT_TAGS)) return ZB_OK;
+    return slot_tag(tags, dbg_rec, mb % desc.ring_slots, op, mb, expect, set, s);
+}
+
+int32_t zb_stage::delay_w(hipStream_t s) {
+    if (w_delay_us <= 0) return ZB_OK;
+    int32_t rc = stamp_now(dbg_t0, s);
+    if (rc) return rc;
+    return wait_until(dbg_t0, wall_clock_hz() / 1000000ull * (uint64_t)w_delay_us, nullptr, s);
+}
+
+int32_t zb_stage::serialize() {
+    if (!(debug_flags & ZB_DEBUG_SERIALIZE)) return ZB_OK;
+    ZB_HIP(hipDeviceSynchronize());
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
 }
 
 int32_t zb_stage::finish(int k, hipEvent_t ev, hipStream_t s) {
@@ -277,6 +298,10 @@ extern "C" int32_t zb_stage_create(const zb_stage_desc* d, void* const* weights,
     st->scratch_f = st->scratch_w + st->lay.scratch_w;
     st->w8 = st->scratch_f + st->lay.scratch_f;
     st->stamps = reinterpret_cast<uint64_t*>(st->w8 + st->lay.w8_bytes);
+    char* dbg = reinterpret_cast<char*>(st->stamps) + st->lay.stamps_bytes;
+    st->dbg_t0 = reinterpret_cast<uint64_t*>(dbg);
+    st->dbg_rec = reinterpret_cast<int32_t*>(dbg + 8);
+    st->tags = st->dbg_rec + DEBUG_REC;
     st->slots.resize(d->ring_slots);
     auto mk = [&](hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming); };
     for (auto& s : st->slots) {
@@ -305,14 +330,16 @@ extern "C" int32_t zb_fwd(zb_stage* st, int32_t mb, const void* x, void* y, void
         return fail(ZB_ERING_FULL, "zb_fwd: ring slot still holds microbatch " + std::to_string(sl.mb) + " (its W has not been issued)");
     int32_t rc = st->order_after(PASS_F, sl.evW, sl.w_event_valid, s);
     if (rc) return rc;
+    if ((rc = st->tag(ZB_OP_F, mb, TAG_FREE, TAG_KEEP, s))) return rc;
     rc = run_forward(*st, mb, x, y, s);
     if (rc) return rc;
+    if ((rc = st->tag(ZB_OP_F, mb, TAG_ANY, 4 * mb + 1, s))) return rc;
     sl.mb = mb;
     sl.b_issued = sl.w_issued = false;
     rc = st->finish(PASS_F, sl.evF, s);
     if (rc) return rc;
     ++st->next_f;
-    return ZB_OK;
+    return st->serialize();
 }
 
 extern "C" int32_t zb_bwd_input(zb_stage* st, int32_t mb, const void* dy, void* dx, void* stream) {
@@ -322,10 +349,13 @@ extern "C" int32_t zb_bwd_input(zb_stage* st, int32_t mb, const void* dy, void* 
     if (sl.mb != mb || sl.b_issued) return fail(ZB_ESTATE, "zb_bwd_input: needs F(mb) issued and B(mb) not yet issued");
     int32_t rc = st->order_after(PASS_B, sl.evF, true, s);
     if (rc) return rc;
+    if ((rc = st->tag(ZB_OP_B, mb, 4 * mb + 1, TAG_KEEP, s))) return rc;
     rc = run_backward_input(*st, mb, dy, dx, s);
     if (rc) return rc;
+    if ((rc = st->tag(ZB_OP_B, mb, TAG_ANY, 4 * mb + 2, s))) return rc;
     sl.b_issued = true;
-    return st->finish(PASS_B, sl.evB, s);
+    if ((rc = st->finish(PASS_B, sl.evB, s))) return rc;
+    return st->serialize();
 }
 
 extern "C" int32_t zb_bwd_weight_accum(zb_stage* st, int32_t mb, void* stream) {
@@ -339,12 +369,16 @@ int32_t zb::bwd_weight_accum(zb_stage* st, int mb, hipStream_t s, float* dg_part
     if (mb != st->next_w) return fail(ZB_ESTATE, "zb_bwd_weight_accum: W must be issued in ascending microbatch order; expected mb " + std::to_string(st->next_w));
     int32_t rc = st->order_after(PASS_W, sl.evB, true, s);
     if (rc) return rc;
+    if ((rc = st->delay_w(s))) return rc;
+    if ((rc = st->tag(ZB_OP_W, mb, 4 * mb + 2, TAG_KEEP, s))) return rc;
     rc = run_backward_weight(*st, mb, s, dg_part);
     if (rc) return rc;
+    if ((rc = st->tag(ZB_OP_W, mb, TAG_ANY, 4 * mb + 3, s))) return rc;
     sl.w_issued = true;
     sl.w_event_valid = true;
     ++st->next_w;
-    return st->finish(PASS_W, sl.evW, s);
+    if ((rc = st->finish(PASS_W, sl.evW, s))) return rc;
+    return st->serialize();
 }
 
 extern "C" int32_t zb_bwd_weight_accum_pair(zb_stage* st, int32_t mb, void* stream) {
@@ -363,15 +397,21 @@ extern "C" int32_t zb_bwd_weight_accum_pair(zb_stage* st, int32_t mb, void* stre
     int32_t rc = st->order_after(PASS_W, s0.evB, true, s);
     if (rc) return rc;
     ZB_HIP(hipStreamWaitEvent(s, s1.evB, 0));
+    if ((rc = st->delay_w(s))) return rc;
+    for (int j : {mb, mb + 1})
+        if ((rc = st->tag(ZB_OP_W, j, 4 * j + 2, TAG_KEEP, s))) return rc;
     rc = run_backward_weight_pair(*st, mb, s);
     if (rc) return rc;
+    for (int j : {mb, mb + 1})
+        if ((rc = st->tag(ZB_OP_W, j, TAG_ANY, 4 * j + 3, s))) return rc;
     for (Slot* sl : {&s0, &s1}) {
         sl->w_issued = true;
         sl->w_event_valid = true;
     }
     st->next_w += 2;
     ZB_HIP(hipEventRecord(s1.evW, s));
-    return st->finish(PASS_W, s0.evW, s);
+    if ((rc = st->finish(PASS_W, s0.evW, s))) return rc;
+    return st->serialize();
 }
 
 extern "C" int32_t zb_stage_zero_grad(zb_stage* st, void* stream) {
@@ -438,7 +478,39 @@ extern "C" int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream) {
     }
     for (auto& sl : st->slots) sl.mb = -1;
     st->next_f = st->next_w = 0;
+    return st->serialize();
+}
+
+extern "C" int32_t zb_stage_set_debug(zb_stage* st, int32_t flags, int32_t w_delay_us, void* stream) {
+    if (!st || (flags & ~(ZB_DEBUG_SLOT_TAGS | ZB_DEBUG_SERIALIZE)) || w_delay_us < 0 || w_delay_us > 1000000)
+        return fail(ZB_EINVAL, "zb_stage_set_debug: bad argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((flags & ZB_DEBUG_SLOT_TAGS) && !(st->debug_flags & ZB_DEBUG_SLOT_TAGS)) {
+        // tags start at "unused"; they must not be reset under a pass that
+        // is still running, so the reset follows the last op of every pass
+        for (int k : {PASS_F, PASS_B, PASS_W})
+            if (st->chain_valid[k]) ZB_HIP(hipStreamWaitEvent(s, st->chain[k], 0));
+        const int32_t rc = tag_reset(st->tags, st->desc.ring_slots, st->dbg_rec, s);
+        if (rc) return rc;
+        for (int k : {PASS_F, PASS_B, PASS_W}) {  // and every later pass follows the reset
+            ZB_HIP(hipEventRecord(st->chain[k], s));
+            st->chain_valid[k] = true;
+        }
+    }
+    st->debug_flags = flags;
+    st->w_delay_us = w_delay_us;
     return ZB_OK;
+}
+
+extern "C" int32_t zb_stage_debug_report(zb_stage* st, int32_t* info) {
+    if (!st) return fail(ZB_EINVAL, "zb_stage_debug_report: NULL stage");
+    if (!(st->debug_flags & ZB_DEBUG_SLOT_TAGS)) return fail(ZB_ESTATE, "zb_stage_debug_report: slot tags are not enabled");
+    int32_t rec[DEBUG_REC];
+    ZB_HIP(hipDeviceSynchronize());
+    ZB_HIP(hipMemcpy(rec, st->dbg_rec, sizeof(rec), hipMemcpyDeviceToHost));
+    if (info)
+        for (int i = 0; i < 5; ++i) info[i] = rec[i + 1];
+    return rec[0];
 }
 
 extern "C" int32_t zb_stage_set_lr(zb_stage* st, float lr) {

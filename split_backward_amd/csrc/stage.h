@@ -31,7 +31,7 @@ struct Layout {
         size_t offset;  // within a slot
     };
     std::vector<Tensor> off;
-    size_t slot_bytes = 0, ring_bytes = 0, scratch_b = 0, scratch_w = 0, stamps_bytes = 0, total = 0;
+    size_t slot_bytes = 0, ring_bytes = 0, scratch_b = 0, scratch_w = 0, stamps_bytes = 0, debug_bytes = 0, total = 0;
     // ZB_FP8 stages: F-pass scratch, the E4M3 weight copies, and offsets
     // inside the pass scratch (bytes from its start).
     size_t scratch_f = 0, w8_bytes = 0;
@@ -71,6 +71,14 @@ struct zb_stage {
     int next_f = 0, next_w = 0;
     float lr = 0.f;  // learning rate of the executor's optimizer-step ops
     int device = 0;  // the HIP device current when the stage was created
+    // Debug aids (zb_stage_set_debug): flags, the injected delay before each
+    // W pass, and the workspace's debug area (ring-slot tags, the mismatch
+    // record, the delay's clock stamp).
+    int debug_flags = 0;
+    int w_delay_us = 0;
+    int32_t* tags = nullptr;
+    int32_t* dbg_rec = nullptr;
+    uint64_t* dbg_t0 = nullptr;
 
     ~zb_stage();
     void* slot_tensor(int mb, int layer, int which) const;
@@ -82,6 +90,13 @@ struct zb_stage {
     // call would reject.  The executor calls this before an op's start stamp,
     // so the stamp marks the moment the op can actually run.
     int32_t wait_deps(int type, int mb, hipStream_t s);
+    // Debug hooks of the passes; each does nothing unless its flag is set.
+    // tag: check-and-set of the slot tag of microbatch mb (slot_tag).
+    int32_t tag(int op, int mb, int expect, int set, hipStream_t s);
+    // Before a W pass: wait w_delay_us on the device.
+    int32_t delay_w(hipStream_t s);
+    // After every op: wait for the whole device and report its errors.
+    int32_t serialize();
 };
 
 namespace zb {
