@@ -306,6 +306,61 @@ def traffic_probe(shape, device, fp8=False):
                       "shapes_MNK": gem, "kernel_source_sha256": kernel_source_hash()}), flush=True)
 
 
+def blas_comparison(shape, device, reps=20):
+    """The stage's bf16 linear products, each timed through the library's
+    kernels and through torch.mm (hipBLASLt) at the same shape and operand
+    layout, with HIP events: F (Y = X W^T), B (dX = dY W) and W
+    (dW = dY^T X).  torch.mm writes a bf16 product; the library's W product
+    accumulates into fp32 dW in place (its extra read-modify-write is in its
+    time).  Context for the kernels' rates, not part of the step."""
+    import torch
+    import split_backward_amd as zb
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    T = shape.tokens
+    seen, rows = set(), []
+    for (M, N, K) in w_pass_gemms(shape):  # W: dW[M, N] += dY[K, M]^T X[K, N]
+        if (M, N, K) in seen:
+            continue
+        seen.add((M, N, K))
+        fl = 2.0 * M * N * K
+        A = torch.randn(K, M, device=device).to(torch.bfloat16)
+        B = torch.randn(K, N, device=device).to(torch.bfloat16)
+        C = torch.zeros(M, N, device=device, dtype=torch.float32)
+        Cb = torch.empty(M, N, device=device, dtype=torch.bfloat16)
+        t_lib = timeit(lambda: zb.gemm(A, B, C, a_kmajor=False, b_kmajor=False, M=M, N=N, K=K, accumulate=True))
+        t_mm = timeit(lambda: torch.mm(A.t(), B, out=Cb))
+        rows.append({"pass": "W", "MNK": [M, N, K], "lib_tflops": round(fl / t_lib / 1e9, 1),
+                     "torch_mm_tflops": round(fl / t_mm / 1e9, 1)})
+        # the F product with this weight (Y[T, M] = X[T, N] W[M, N]^T) and its B (dX[T, N] = dY[T, M] W[M, N])
+        X = torch.randn(T, N, device=device).to(torch.bfloat16)
+        Wt = torch.randn(M, N, device=device).to(torch.bfloat16)
+        Y = torch.empty(T, M, device=device, dtype=torch.bfloat16)
+        t_lib = timeit(lambda: zb.gemm(X, Wt, Y, a_kmajor=True, b_kmajor=True, M=T, N=M, K=N))
+        t_mm = timeit(lambda: torch.mm(X, Wt.t(), out=Y))
+        rows.append({"pass": "F", "MNK": [T, M, N], "lib_tflops": round(fl / t_lib / 1e9, 1),
+                     "torch_mm_tflops": round(fl / t_mm / 1e9, 1)})
+        dY = torch.randn(T, M, device=device).to(torch.bfloat16)
+        dX = torch.empty(T, N, device=device, dtype=torch.bfloat16)
+        t_lib = timeit(lambda: zb.gemm(dY, Wt, dX, a_kmajor=True, b_kmajor=False, M=T, N=N, K=M))
+        t_mm = timeit(lambda: torch.mm(dY, Wt, out=dX))
+        rows.append({"pass": "B", "MNK": [T, N, M], "lib_tflops": round(fl / t_lib / 1e9, 1),
+                     "torch_mm_tflops": round(fl / t_mm / 1e9, 1)})
+        del A, B, C, Cb, X, Wt, Y, dY, dX
+    return rows
+
+
 def cpu_baseline(shape, m, fp8=False):
     """fp64 oracle on a bounded sample: one decoder layer (or the whole
     stage for the small kinds), one microbatch, F + B + W (the fp8 oracle
@@ -644,6 +699,8 @@ def main():
                     help="issue every W on its own instead of pairing adjacent W(j), W(j+1)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the copy + W-kernel workload that the --pmc passes count")
+    ap.add_argument("--compare-blas", action="store_true",
+                    help="only time the stage's bf16 products through the library and through torch.mm (hipBLASLt)")
     ap.add_argument("--replay-only", action="store_true",
                     help="only calibrate and run the replays a kernel trace measures (see trace_idle)")
     ap.add_argument("--trace-idle", nargs=2, metavar=("KERNEL_TRACE_CSV", "REPLAY_JSON"),
@@ -669,6 +726,10 @@ def main():
     torch.cuda.set_device(device)
     if args.traffic_probe:
         traffic_probe(shape, device, fp8)
+        return
+    if args.compare_blas:
+        for row in blas_comparison(shape, device):
+            print(json.dumps(row), flush=True)
         return
     weights = [synth.to_device(w, device) for w in synth.make_weights(shape)]
     stage = zb.Stage(shape.kind, shape.tokens, shape.hidden, shape.ffn, weights, dtype=stage_dtype,
