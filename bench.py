@@ -362,59 +362,105 @@ def blas_comparison(shape, device, reps=20):
 
 
 def cpu_baseline(shape, m, fp8=False):
-    """fp64 oracle on a bounded sample: one decoder layer (or the whole
-    stage for the small kinds), one microbatch, F + B + W (the fp8 oracle
-    stage for the fp8 workload)."""
+    """The oracle timed on this host on a bounded sample.
+
+    value: the fp64 loop-nest oracle (oracle/loopnest.c, OpenMP over output
+    rows) running F, B and W of every linear product of one decoder layer
+    (the whole block for the small kinds) at a reduced token count, in
+    linear-layer TFLOP/s like the metric; `extrapolated_step_s` is the whole
+    step's linear work at that rate.  `oracle_stage_numpy`: the numpy
+    oracle's whole stage step (attention and norms included, products
+    through numpy's BLAS) on one layer at 256 tokens, for context.  The fp8
+    line times the fp8 oracle stage instead of the loop nests."""
     import numpy as np
     import synth
     from oracle import dense as od
     from oracle import fp8 as o8
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    if shape.kind == "llama":
-        sample = synth.StageShape("llama", 256, shape.hidden, shape.ffn, n_layers=1, n_heads=shape.n_heads,
-                                  n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim)
-        desc = f"one decoder layer, one microbatch, 256 tokens, h={shape.hidden}, ffn={shape.ffn}"
-    elif shape.kind == "mlp":
-        sample = synth.StageShape("mlp", 512, shape.hidden, shape.ffn)
-        desc = f"one microbatch, 512 tokens, h={shape.hidden}, ffn={shape.ffn}"
-    else:
-        sample = shape
-        desc = "one microbatch of the full shape"
-    w = synth.make_weights(sample)
-    dims = od.LlamaDims(sample.hidden, sample.ffn, sample.n_heads, sample.n_kv_heads, sample.head_dim) \
-        if sample.kind == "llama" else None
-    x = synth.make_x(sample, 0).f64
-    dy = synth.make_dy(sample, 0).f64
-    reps, t_total = 0, 0.0
-    while t_total < 8.0 and reps < 50:
-        st = (o8.Fp8LlamaStage([t.f64 for t in w], dims, sample.n_layers) if fp8 else
-              od.Stage(sample.kind, [t.f64 for t in w], dims, sample.n_layers))
-        t0 = time.perf_counter()
-        st.fwd(0, x)
-        st.bwd_input(0, dy)
-        st.bwd_weight(0)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    flops = reps * linear_flops_per_mb(sample)
-    # the whole step's work over the sample's work, at the sample's flop rate
-    # (linear work grows with the tokens, attention with their square)
-    per_rep = t_total / reps
-    sample_work = linear_flops_per_mb(sample) + attention_flops_per_mb(sample)
-    full_work = (linear_flops_per_mb(shape) + attention_flops_per_mb(shape)) * m
+    from oracle import loopnest as ln
     try:
         affinity = len(os.sched_getaffinity(0))
     except Exception:
         affinity = None
-    return {"value": round(flops / t_total / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{desc}; fp64 numpy (products through its BLAS); {reps} repetitions in {t_total:.1f} s",
-            "nproc": os.cpu_count(), "affinity_cpus": affinity, "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
-            "extrapolated_step_s": round(per_rep * full_work / sample_work, 1),
-            "extrapolated_note": "EXTRAPOLATED, not measured: the full step's linear and attention flops at the "
-                                 "sample's measured rate"}
+    env = {"nproc": os.cpu_count(), "affinity_cpus": affinity, "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+    full_linear = linear_flops_per_mb(shape) * m
+
+    def numpy_stage():
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        if shape.kind == "llama":
+            sample = synth.StageShape("llama", 256, shape.hidden, shape.ffn, n_layers=1, n_heads=shape.n_heads,
+                                      n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim)
+            desc = f"one decoder layer, one microbatch, 256 tokens, h={shape.hidden}, ffn={shape.ffn}"
+        elif shape.kind == "mlp":
+            sample = synth.StageShape("mlp", 512, shape.hidden, shape.ffn)
+            desc = f"one microbatch, 512 tokens, h={shape.hidden}, ffn={shape.ffn}"
+        else:
+            sample = shape
+            desc = "one microbatch of the full shape"
+        w = synth.make_weights(sample)
+        dims = od.LlamaDims(sample.hidden, sample.ffn, sample.n_heads, sample.n_kv_heads, sample.head_dim) \
+            if sample.kind == "llama" else None
+        x = synth.make_x(sample, 0).f64
+        dy = synth.make_dy(sample, 0).f64
+        reps, t_total = 0, 0.0
+        while t_total < 8.0 and reps < 50:
+            st = (o8.Fp8LlamaStage([t.f64 for t in w], dims, sample.n_layers) if fp8 else
+                  od.Stage(sample.kind, [t.f64 for t in w], dims, sample.n_layers))
+            t0 = time.perf_counter()
+            st.fwd(0, x)
+            st.bwd_input(0, dy)
+            st.bwd_weight(0)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        per_rep = t_total / reps
+        sample_work = linear_flops_per_mb(sample) + attention_flops_per_mb(sample)
+        full_work = (linear_flops_per_mb(shape) + attention_flops_per_mb(shape)) * m
+        kind = "fp8 oracle stage (E4M3 rounding in numpy, products through its BLAS)" if fp8 else \
+            "fp64 numpy oracle stage (products through its BLAS)"
+        return {"value": round(reps * linear_flops_per_mb(sample) / t_total / 1e12, 4), "unit": "TFLOP/s",
+                "cores": cores, "kind": "oracle",
+                "sample": f"{desc}; {kind}; {reps} repetitions in {t_total:.1f} s",
+                "extrapolated_step_s": round(per_rep * full_work / sample_work, 1),
+                "extrapolated_note": "EXTRAPOLATED, not measured: the full step's linear and attention flops at "
+                                     "the sample's measured rate"}
+
+    if fp8:
+        return {**numpy_stage(), **env}
+
+    # products of one layer (the whole block for the small kinds): (out, in)
+    # per weight, at a token count that keeps the sample near 0.15 TFLOP
+    prods = [(M, N) for (M, N, _) in w_pass_gemms(shape)]
+    if shape.kind == "llama":
+        prods = prods[:4]
+    per_token = 6.0 * sum(M * N for M, N in prods)  # F + B + W flops per token
+    tokens = shape.tokens
+    while tokens > 16 and tokens * per_token > 1.6e11:
+        tokens //= 2
+    r = np.random.default_rng(0)
+    data = [(r.standard_normal((tokens, N)), r.standard_normal((M, N)), r.standard_normal((tokens, M)),
+             np.zeros((M, N))) for M, N in prods]
+    reps, t_total = 0, 0.0
+    while t_total < 8.0 and reps < 50:
+        t0 = time.perf_counter()
+        for X, W, dY, dW in data:
+            ln.linear_fwd(X, W)
+            ln.linear_bwd_input(dY, W)
+            ln.linear_bwd_weight(dY, X, dW)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    rate = reps * tokens * per_token / t_total
+    what = "one decoder layer's" if shape.kind == "llama" else "the block's"
+    return {"value": round(rate / 1e12, 4), "unit": "TFLOP/s", "cores": ln.threads(), "kind": "oracle",
+            "sample": f"fp64 loop-nest oracle (C, OpenMP over output rows): F, B and W of {what} {len(prods)} "
+                      f"linear products at {tokens} tokens, one microbatch; {reps} repetitions in {t_total:.1f} s",
+            **env,
+            "extrapolated_step_s": round(full_linear / rate, 1),
+            "extrapolated_note": "EXTRAPOLATED, not measured: the full step's linear flops at the sample's "
+                                 "measured rate",
+            "oracle_stage_numpy": numpy_stage()}
 
 
 def executor_idle(stage, shape, m, xs, ys, dys, dxs, t_f, t_b, t_w):

@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY.  Nothing in the product package may import, call,
 link or run anything here; only the tests, the smoke check and the benchmark's
 CPU-baseline leg do.  The oracle shares no code with the HIP path: it is plain
-numpy in float64 with no intermediate rounding.
+numpy in float64 with no intermediate rounding, plus the C loop nests of
+``loopnest.c`` (fp64, sums in index order).
 
 Sources ("the pages"):
 
@@ -21,6 +22,9 @@ Modules:
 * ``schedule`` -- integer-time pipeline simulator for GPipe, 1F1B, the
                   memory-limited zero-bubble greedy schedule (one iteration
                   and several) and interleaved 1F1B.
+* ``loopnest`` -- F, B and W of a linear layer as plain fp64 C loop nests
+                  (``loopnest.c``, OpenMP over output rows): the products'
+                  defining sums, timed as the benchmark's CPU baseline.
 * ``fp8``      -- E4M3 decoding, rounding and per-tensor power-of-two
                   scaling, the fp8 product, and the Llama stage with every
                   linear product on fp8 operands.
