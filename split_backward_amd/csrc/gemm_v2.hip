@@ -262,14 +262,39 @@ struct BufSpans {
 // k-tile stages are free by then) and out with the fused operation EPI.
 // Called once every DMA into LDS has been issued: the waits below count the
 // loads still in flight.
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
-__device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans& sp, floatx16 (&acc)[TBM / 64][4],
-                                              int m0, int n0, char* smem) {
+// Staging of the 32-row block mi of a wave's accumulators into `stage`
+// (32 rows of P floats, 128 columns), from either MFMA layout.
+// 32x32 blocks: slot r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
+// column l % 32.
+template <int MI, int P>
+__device__ __forceinline__ void stage_block(floatx16 (&acc)[MI][4], int mi, float* stage, int lane) {
+    const int g = lane >> 5, lrow = lane & 31;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) stage[((r >> 2) * 8 + g * 4 + (r & 3)) * P + ni * 32 + lrow] = acc[mi][ni][r];
+}
+// 16x16 blocks (two per 32 rows): slot i of lane l is row 4 (l / 16) + i,
+// column l % 16.
+template <int MB, int P>
+__device__ __forceinline__ void stage_block(floatx4 (&acc)[MB][8], int mi, float* stage, int lane) {
+    const int kg = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) stage[(h * 16 + kg * 4 + i) * P + ni * 16 + r16] = acc[2 * mi + h][ni][i];
+}
+
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM, class ACC>
+__device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans& sp, ACC& acc, int m0, int n0,
+                                              char* smem) {
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
-    constexpr int MI = TBM / 64;
+    constexpr int MI = TBM / 64;                              // 32-row blocks per wave
+    constexpr int MI_ACC = sizeof(ACC) / sizeof(acc[0]);     // first extent of the accumulator array
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int g = lane >> 5, lrow = lane & 31;
     __builtin_amdgcn_sched_barrier(0);
     const int c4 = (lane & 31) * 4;
     const int gcol = n0 + wn * 128 + c4;
@@ -343,11 +368,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans&
         for (int mi = 0; mi < MI; ++mi) {
             if (mi + 1 < MI) load_block(mi + 1, cin[(mi + 1) & 1]);
             const int rbase = m0 + wm * (TBM / 2) + mi * 32;
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    stage[((r >> 2) * 8 + g * 4 + (r & 3)) * P + ni * 32 + lrow] = acc[mi][ni][r];
+            stage_block<MI_ACC, P>(acc, mi, stage, lane);
 #pragma unroll
             for (int it = 0; it < 16; ++it) {
                 const int lr = 2 * it + (lane >> 5);
@@ -366,11 +387,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans&
         const int rbase = m0 + wm * (TBM / 2) + mi * 32;
         if (!PAIRED) {
             if (HAS_R && mi + 1 < MI) load_r(mi + 1, (mi + 1) & 1);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    stage[((r >> 2) * 8 + g * 4 + (r & 3)) * P + ni * 32 + lrow] = acc[mi][ni][r];
+            stage_block<MI_ACC, P>(acc, mi, stage, lane);
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 const int lr = 2 * it + (lane >> 5);
@@ -410,11 +427,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans&
             const int c4 = (lane & 15) * 4;
             const int gcol = n0 + wn * 64 + c4;
             const bool col_ok = gcol < d.half_n;
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    stage[((r >> 2) * 8 + g * 4 + (r & 3)) * P + ni * 32 + lrow] = acc[mi][ni][r];
+            stage_block<MI_ACC, P>(acc, mi, stage, lane);
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
                 const int lr = 4 * it + (lane >> 4);
@@ -656,6 +669,7 @@ __device__ __forceinline__ void dma_issue_n(__amdgpu_buffer_rsrc_t rs, lds_void*
     for (int i = 0; i < NI; ++i) dma_issue_one(rs, tile, off[i], i * 4 + wave);
 }
 
+
 __device__ __forceinline__ bf16x8 frag_k64(const lds_void* tile, int row, int kk, int g) {
     const int chunk = (kk * 2 + g) ^ key8(row);
     return *(const lds_bf16x8*)((const __attribute__((address_space(3))) char*)tile + row * 128 + chunk * 16);
@@ -821,6 +835,138 @@ __device__ __forceinline__ void gemm_64_tile(const GemmDesc& d, int tm, int tn, 
         if constexpr (KK) interleave_reads_dma_mfma<RD, NB, NM, 0>();
     }
     lds_wait(fa0, fb0);  // the unused reads of k-tile nk (see the 32-k loop)
+    gemm_epilogue<A_KMAJ, B_KMAJ, EPI, TBM>(d, sp, acc, m0, n0, smem);
+}
+
+
+// 16x16x32 fragments of a 64-k part.  K-contiguous part (128-byte rows):
+// lane l holds row `row`, k = 8 (l / 16) .. + 7 of 32-k step kk.
+__device__ __forceinline__ bf16x8 frag16_k64(const lds_void* tile, int row, int kk, int kg) {
+    const int chunk = (kk * 4 + kg) ^ key8(row);
+    return *(const lds_bf16x8*)((const __attribute__((address_space(3))) char*)tile + row * 128 + chunk * 16);
+}
+// One TBM x 256 tile with both operands K-contiguous (the F pass) on 64-k
+// parts, every product a v_mfma_f32_16x16x32_bf16: each wave computes
+// (TBM / 2) x 128 as (TBM / 32) x 8 blocks of 16 x 16 (256 or 128
+// accumulators).  Same parts, ring, DMA schedule and epilogues as the 32x32
+// loop above; per 32-k step a wave reads TBM / 32 + 8 fragments (16 bytes
+// per lane each) and issues (TBM / 32) x 8 MFMAs.  On the F products this
+// keeps the matrix units busier than the 32x32x16 loop (+5-7% on one box);
+// on the B pass (transpose reads of B) it was slower and is not used.  K
+// must be a multiple of 64 (every k-tile full); other K take the 32x32 loop,
+// whose last k-tile masks k >= K.
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
+__device__ __forceinline__ void gemm_64_tile16(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
+    static_assert(A_KMAJ && B_KMAJ, "16x16x32 loop: both operands K-contiguous");
+    constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
+    constexpr int MB = TBM / 32;          // 16-row blocks per wave
+    constexpr int NA = TBM / 32, NB = 8;  // DMA instructions per wave per part
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int kg = lane >> 4, r16 = lane & 15;
+    const int m0 = tm * TBM;
+    const int n0 = PAIRED ? tn * (BN / 2) : tn * BN;
+    const int nk = (d.K + BK64 - 1) / BK64;  // K is a multiple of 64 here (no partial k-tile)
+
+    uint32_t offa[NA], offb[NB];
+    dma_offsets_k64<false, NA>(offa, d.lda, m0, d.M, 0, BK64, lane, wave);
+    dma_offsets_k64<PAIRED, NB>(offb, d.ldb, n0, d.N, d.half_n, BK64, lane, wave);
+    const int64_t step_a = BK64 * 2, step_b = BK64 * 2;
+    // Part p of the sequence; parts past the last k-tile get an empty range
+    // (zeros, nothing fetched) so every iteration issues the same loads.
+    auto dma_part = [&](int p) {
+        const int kt = p >> 1;
+        char* dst = smem + (p % NSLOT) * PART_BYTES;
+        const bool live = kt < nk;
+        if ((p & 1) == 0) {
+            const uint32_t adv = live ? (uint32_t)(kt * step_a) : 0u;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(d.A) + adv, live ? sp.a - adv : 0u);
+            dma_issue_n<NA>(rs, (lds_void*)dst, offa, wave);
+        } else {
+            const uint32_t adv = live ? (uint32_t)(kt * step_b) : 0u;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(d.B) + adv, live ? sp.b - adv : 0u);
+            dma_issue_n<NB>(rs, (lds_void*)dst, offb, wave);
+        }
+    };
+
+    floatx4 acc[MB][8];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    auto frag_a = [&](const lds_void* ta, int mi, int kk) -> bf16x8 {
+        return frag16_k64(ta, wm * (TBM / 2) + mi * 16 + r16, kk, kg);
+    };
+    // B columns of block ni: with the SwiGLU pairing, blocks 0..3 are the
+    // wave's 64 gate columns and 4..7 the matching up columns (staged as
+    // columns 0..63 and 64..127, which the epilogue expects).
+    auto frag_b = [&](const lds_void* tb, int ni, int kk) -> bf16x8 {
+        const int row = PAIRED ? ((ni >> 2) * 128 + wn * 64 + (ni & 3) * 16 + r16) : (wn * 128 + ni * 16 + r16);
+        return frag16_k64(tb, row, kk, kg);
+    };
+    constexpr int RD = MB + 8;  // LDS read instructions per 32-k step
+    constexpr int NM = MB * 8;  // MFMAs per 32-k step
+
+    // Iteration kt multiplies the two 32-k steps of k-tile kt, each while the
+    // next step's fragments are read.  During step 0 the A part of k-tile
+    // kt+2 goes into the slot k-tile kt-1's B part left.  Before step 1 every
+    // read of kt has completed and k-tile kt+1 has landed (the A part of kt+2
+    // may still be in flight), then a barrier; during step 1 the first
+    // fragments of kt+1 are read and the B part of kt+2 goes into the slot
+    // kt's A part left.
+#pragma unroll
+    for (int p = 0; p < NSLOT - 1; ++p) dma_part(p);
+    wait_vm<NA + NB>();  // parts 0 and 1 (k-tile 0) landed
+    workgroup_barrier();
+    bf16x8 fa0[MB], fb0[8], fa1[MB], fb1[8];
+    {
+        const lds_void* ta = (const lds_void*)smem;
+        const lds_void* tb = (const lds_void*)(smem + PART_BYTES);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < MB) fa0[i] = frag_a(ta, i, 0);
+            fb0[i] = frag_b(tb, i, 0);
+        }
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const lds_void* ta = (const lds_void*)(smem + ((2 * kt) % NSLOT) * PART_BYTES);
+        const lds_void* tb = (const lds_void*)(smem + ((2 * kt + 1) % NSLOT) * PART_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < MB) fa1[i] = frag_a(ta, i, 1);
+            fb1[i] = frag_b(tb, i, 1);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 8; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0[mi], fb0[ni], acc[mi][ni], 0, 0, 0);
+        dma_part(2 * kt + 4);  // the A part of k-tile kt+2, into the slot kt-1's B part left
+        interleave_reads_dma_mfma<RD, NA, NM, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every read of k-tile kt has completed
+        wait_vm<NA>();                                        // k-tile kt+1 landed
+        workgroup_barrier();
+        {
+            const lds_void* na = (const lds_void*)(smem + ((2 * kt + 2) % NSLOT) * PART_BYTES);
+            const lds_void* nb = (const lds_void*)(smem + ((2 * kt + 3) % NSLOT) * PART_BYTES);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i < MB) fa0[i] = frag_a(na, i, 0);
+                fb0[i] = frag_b(nb, i, 0);
+            }
+        }
+        dma_part(2 * kt + 5);  // the B part of k-tile kt+2, into the slot kt's A part left
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 8; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1[mi], fb1[ni], acc[mi][ni], 0, 0, 0);
+        interleave_reads_dma_mfma<RD, NB, NM, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the unused reads of k-tile nk
     gemm_epilogue<A_KMAJ, B_KMAJ, EPI, TBM>(d, sp, acc, m0, n0, smem);
 }
 
@@ -993,20 +1139,24 @@ constexpr int gemm_lds_bytes() { return A_KMAJ ? NSLOT * PART_BYTES : STAGES * S
 
 // Products with a K-contiguous A (the F and B passes) run on 64-k parts;
 // those with an M/N-contiguous A (the W pass) measured faster on 32-k tiles.
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
+// K16: both operands K-contiguous and K a multiple of 64, the 16x16x32 loop
+// (a kernel of its own: sharing one function with the 32x32 loop costs the
+// register allocator its room).
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM, bool K16 = false>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tm, int tn, const BufSpans& sp, char* smem) {
-    if constexpr (A_KMAJ) gemm_64_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn, sp, smem);
+    if constexpr (K16) gemm_64_tile16<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn, sp, smem);
+    else if constexpr (A_KMAJ) gemm_64_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn, sp, smem);
     else gemm_v2_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn, sp, smem);
 }
 
 // Tiles (tm, tn_base + tn) for tm < tiles_m, tn < tiles_n, of height TBM.
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM>
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM, bool K16 = false>
 __global__ __launch_bounds__(NTHR) void gemm_v2_kernel(GemmDesc d, int tiles_m, int tiles_n, int tn_base,
                                                        BufSpans sp) {
     __shared__ __attribute__((aligned(1024))) char smem[gemm_lds_bytes<A_KMAJ, B_KMAJ>()];
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    gemm_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn_base + tn, sp, smem);
+    gemm_tile<A_KMAJ, B_KMAJ, EPI, TBM, K16>(d, tm, tn_base + tn, sp, smem);
 }
 
 // Up to GROUP_MAX independent products of one layout and epilogue in one
@@ -1068,8 +1218,32 @@ __global__ __launch_bounds__(NTHR) void gemm_f8_group_kernel(GemmGroup grp) {
     gemm_f8_tile<EPI, BM>(d, tm, tn, sp, smem);
 }
 
+// The 16x16x32 loop runs full-height tiles of both-K-contiguous products
+// with K a multiple of 64 and the F pass's epilogues.  The other cases keep
+// the 32x32 loop: for them (half-height tiles, the fp32-accumulate and
+// GeLU-backward epilogues) the register allocator moves accumulators between
+// registers on every iteration of the 16x16 loop (checked in the generated
+// code: the 256-row F-epilogue loops copy at most 16 registers per
+// iteration, those cases 128-350).
 template <bool AK, bool BKM, int TBM>
 int32_t launch_v2(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, int tn_base, const BufSpans& sp) {
+    if constexpr (AK && BKM && TBM == BM) {
+        if (d.K % BK64 == 0 && d.epi != EPI_ACCUM_F32 && d.epi != EPI_GELU_BWD) {
+            dim3 grid(tiles_m * tiles_n), block(NTHR);
+            switch (d.epi) {
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E, TBM, true>), grid, block, 0, s, d, tiles_m, tiles_n, tn_base, sp); break;
+                ZB_CASE(EPI_STORE)
+                ZB_CASE(EPI_RESID)
+                ZB_CASE(EPI_GELU_FWD)
+                ZB_CASE(EPI_SWIGLU_FWD)
+                ZB_CASE(EPI_SWIGLU_BWD)
+#undef ZB_CASE
+                default: return fail(ZB_EINVAL, "gemm: unknown epilogue");
+            }
+            ZB_HIP(hipGetLastError());
+            return ZB_OK;
+        }
+    }
     dim3 grid(tiles_m * tiles_n), block(NTHR);
     switch (d.epi) {
 #define ZB_CASE(E) case E: hipLaunchKernelGGL((gemm_v2_kernel<AK, BKM, E, TBM>), grid, block, 0, s, d, tiles_m, tiles_n, tn_base, sp); break;
