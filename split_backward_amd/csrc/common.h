@@ -128,11 +128,13 @@ struct SgdGroup {
 int32_t sgd_step_group_bf16(const SgdGroup& g, hipStream_t s);
 int32_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
 // n = RMS(x) * g, r = 1/sqrt(mean(x^2)+eps) per row; x, n bf16 [T, H]; r f32 [T].
+// xcopy (optional): receives a copy of x.
 int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps,
-                    hipStream_t s);
+                    hipStream_t s, bf16_t* xcopy = nullptr);
 // dx = dres + r * (dn*g - xhat * mean(dn*g*xhat)), xhat = x*r.
+// rescopy (optional): receives a copy of dres.
 int32_t rmsnorm_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn,
-                    const bf16_t* dres, bf16_t* dx, int T, int H, hipStream_t s);
+                    const bf16_t* dres, bf16_t* dx, int T, int H, hipStream_t s, bf16_t* rescopy = nullptr);
 // dgamma[h] += sum_t dn[t,h] * x[t,h] * r[t]   (partials in scratch, fixed order)
 int32_t rmsnorm_dgamma(const bf16_t* x, const float* r, const bf16_t* dn, float* dgamma,
                        float* scratch, int T, int H, hipStream_t s);

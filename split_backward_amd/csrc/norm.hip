@@ -41,9 +41,12 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
 }
 
 // One workgroup per row; H is a multiple of 8 and at most 8 * RT * 4.
+// xcopy (optional): a copy of x written as it is read (the stage stashes
+// its input this way instead of with a separate copy).
 template <int CH>
 __global__ __launch_bounds__(RT) void rms_fwd_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ g,
-                                                     bf16_t* __restrict__ n, float* __restrict__ r, int H, float eps) {
+                                                     bf16_t* __restrict__ n, float* __restrict__ r,
+                                                     bf16_t* __restrict__ xcopy, int H, float eps) {
     __shared__ float red[RT / 64];
     const int64_t row = blockIdx.x;
     const bf16_t* xr = x + row * H;
@@ -53,7 +56,9 @@ __global__ __launch_bounds__(RT) void rms_fwd_kernel(const bf16_t* __restrict__ 
     for (int c = 0; c < CH; ++c) {
         const int col = (threadIdx.x + c * RT) * 8;
         if (col < H) {
-            unpack8(*reinterpret_cast<const u32x4*>(xr + col), v[c]);
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + col);
+            if (xcopy) *reinterpret_cast<u32x4*>(xcopy + row * H + col) = raw;
+            unpack8(raw, v[c]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss += v[c][i] * v[c][i];
         }
@@ -74,10 +79,12 @@ __global__ __launch_bounds__(RT) void rms_fwd_kernel(const bf16_t* __restrict__ 
     }
 }
 
+// rescopy (optional): a copy of dres written as it is read.
 template <int CH>
 __global__ __launch_bounds__(RT) void rms_bwd_kernel(const bf16_t* __restrict__ x, const float* __restrict__ r,
                                                      const bf16_t* __restrict__ g, const bf16_t* __restrict__ dn,
-                                                     const bf16_t* __restrict__ dres, bf16_t* __restrict__ dx, int H) {
+                                                     const bf16_t* __restrict__ dres, bf16_t* __restrict__ dx,
+                                                     bf16_t* __restrict__ rescopy, int H) {
     __shared__ float red[RT / 64];
     const int64_t row = blockIdx.x;
     const float rr = r[row];
@@ -105,7 +112,9 @@ __global__ __launch_bounds__(RT) void rms_bwd_kernel(const bf16_t* __restrict__ 
         const int col = (threadIdx.x + c * RT) * 8;
         if (col < H) {
             float res[8], o[8];
-            unpack8(*reinterpret_cast<const u32x4*>(dres + row * H + col), res);
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(dres + row * H + col);
+            if (rescopy) *reinterpret_cast<u32x4*>(rescopy + row * H + col) = raw;
+            unpack8(raw, res);
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = res[i] + rr * (dg[c][i] - xh[c][i] * mean);
             *reinterpret_cast<u32x4*>(dx + row * H + col) = pack8(o);
@@ -242,36 +251,38 @@ __global__ void wait_kernel(const uint64_t* t0, uint64_t delta, uint64_t cap, ui
 }
 
 template <int CH>
-int32_t launch_rms_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps, hipStream_t s) {
-    hipLaunchKernelGGL(rms_fwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, g, n, r, H, eps);
+int32_t launch_rms_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, bf16_t* xcopy, int T, int H, float eps,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(rms_fwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, g, n, r, xcopy, H, eps);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
 template <int CH>
 int32_t launch_rms_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn, const bf16_t* dres,
-                       bf16_t* dx, int T, int H, hipStream_t s) {
-    hipLaunchKernelGGL(rms_bwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, r, g, dn, dres, dx, H);
+                       bf16_t* dx, bf16_t* rescopy, int T, int H, hipStream_t s) {
+    hipLaunchKernelGGL(rms_bwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, r, g, dn, dres, dx, rescopy, H);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
 
 }  // namespace
 
-int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps, hipStream_t s) {
+int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps, hipStream_t s,
+                    bf16_t* xcopy) {
     if (H % 8 || H > 8 * RT * 4 || T <= 0) return fail(ZB_EINVAL, "rmsnorm: hidden must be a multiple of 8 and <= 8192");
     const int ch = (H / 8 + RT - 1) / RT;
-    if (ch <= 1) return launch_rms_fwd<1>(x, g, n, r, T, H, eps, s);
-    if (ch <= 2) return launch_rms_fwd<2>(x, g, n, r, T, H, eps, s);
-    return launch_rms_fwd<4>(x, g, n, r, T, H, eps, s);
+    if (ch <= 1) return launch_rms_fwd<1>(x, g, n, r, xcopy, T, H, eps, s);
+    if (ch <= 2) return launch_rms_fwd<2>(x, g, n, r, xcopy, T, H, eps, s);
+    return launch_rms_fwd<4>(x, g, n, r, xcopy, T, H, eps, s);
 }
 
 int32_t rmsnorm_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn, const bf16_t* dres,
-                    bf16_t* dx, int T, int H, hipStream_t s) {
+                    bf16_t* dx, int T, int H, hipStream_t s, bf16_t* rescopy) {
     if (H % 8 || H > 8 * RT * 4 || T <= 0) return fail(ZB_EINVAL, "rmsnorm: hidden must be a multiple of 8 and <= 8192");
     const int ch = (H / 8 + RT - 1) / RT;
-    if (ch <= 1) return launch_rms_bwd<1>(x, r, g, dn, dres, dx, T, H, s);
-    if (ch <= 2) return launch_rms_bwd<2>(x, r, g, dn, dres, dx, T, H, s);
-    return launch_rms_bwd<4>(x, r, g, dn, dres, dx, T, H, s);
+    if (ch <= 1) return launch_rms_bwd<1>(x, r, g, dn, dres, dx, rescopy, T, H, s);
+    if (ch <= 2) return launch_rms_bwd<2>(x, r, g, dn, dres, dx, rescopy, T, H, s);
+    return launch_rms_bwd<4>(x, r, g, dn, dres, dx, rescopy, T, H, s);
 }
 
 size_t rmsnorm_dgamma_scratch_floats(int T, int H) { return (size_t)((T + DG_ROWS - 1) / DG_ROWS) * H; }

@@ -79,7 +79,6 @@ int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s)
     for (int l = 0; l < d.n_layers; ++l) {
         void* const* w = &st.w[6 * l];
         bf16_t* xl = bf(st.slot_tensor(mb, l, L_X));
-        if (l == 0) ZB_TRY(copy_bytes(xl, x, (size_t)T * H * 2, s));
         float* r1 = static_cast<float*>(st.slot_tensor(mb, l, L_R1));
         bf16_t* n1 = bf(st.slot_tensor(mb, l, L_N1));
         bf16_t* qkv = bf(st.slot_tensor(mb, l, L_QKV));
@@ -92,7 +91,9 @@ int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s)
         bf16_t* sw = bf(st.slot_tensor(mb, l, L_S));
         void* out = (l == d.n_layers - 1) ? y : st.slot_tensor(mb, l + 1, L_X);
 
-        ZB_TRY(rmsnorm_fwd(xl, cbf(w[4]), n1, r1, T, H, d.rms_eps, s));
+        // layer 0 stashes the stage input as its norm reads it
+        if (l == 0) ZB_TRY(rmsnorm_fwd(cbf(x), cbf(w[4]), n1, r1, T, H, d.rms_eps, s, xl));
+        else ZB_TRY(rmsnorm_fwd(xl, cbf(w[4]), n1, r1, T, H, d.rms_eps, s));
         ZB_TRY(gemm_bf16(nt(T, QKV, H, n1, H, w[0], H, qkv, QKV), s));
         ZB_TRY(attn_fwd(qkv, a, lse, T, d.n_heads, d.n_kv_heads, s));
         GemmDesc go = nt(T, H, QD, a, QD, w[1], QD, h1, H, EPI_RESID);
@@ -157,15 +158,18 @@ int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipSt
         bf16_t* dqkv = bf(st.slot_tensor(mb, l, L_DQKV));
         bf16_t* dn1 = bf(st.slot_tensor(mb, l, L_DN1));
         void* dest = (l == 0) ? dx : st.slot_tensor(mb, l - 1, L_DOUT);
-        if (l == d.n_layers - 1) ZB_TRY(copy_bytes(dout, dy, (size_t)T * H * 2, s));
+        // the last layer reads the incoming gradient itself and stashes it
+        // (for W) in its second norm's backward, which reads it whole
+        const bool last = l == d.n_layers - 1;
+        const bf16_t* gin = last ? cbf(dy) : dout;
 
-        GemmDesc gd = nn(T, F, H, dout, H, w[3], F, dgu, 2 * F, EPI_SWIGLU_BWD);
+        GemmDesc gd = nn(T, F, H, gin, H, w[3], F, dgu, 2 * F, EPI_SWIGLU_BWD);
         gd.R = gu;
         gd.ldr = 2 * F;
         gd.half_n = F;
         ZB_TRY(gemm_bf16(gd, s));
         ZB_TRY(gemm_bf16(nn(T, H, 2 * F, dgu, 2 * F, w[2], H, dn2, H), s));
-        ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, dout, dh1, T, H, s));
+        ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, gin, dh1, T, H, s, last ? dout : nullptr));
         ZB_TRY(gemm_bf16(nn(T, QD, H, dh1, H, w[1], QD, da, QD), s));
         ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, part, T, d.n_heads, d.n_kv_heads, s));
         ZB_TRY(gemm_bf16(nn(T, H, QKV, dqkv, QKV, w[0], H, dn1, H), s));

@@ -122,7 +122,6 @@ int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_
         void* const* w = &st.w[6 * l];
         const W8 wqkv = w8(st, 6 * l), wo = w8(st, 6 * l + 1), wgu = w8(st, 6 * l + 2), wd = w8(st, 6 * l + 3);
         bf16_t* xl = bf(st.slot_tensor(mb, l, L_X));
-        if (l == 0) ZB_TRY(copy_bytes(xl, x, (size_t)T * H * 2, s));
         float* r1 = static_cast<float*>(st.slot_tensor(mb, l, L_R1));
         bf16_t* qkv = bf(st.slot_tensor(mb, l, L_QKV));
         bf16_t* a = bf(st.slot_tensor(mb, l, L_A));
@@ -133,7 +132,9 @@ int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_
         int32_t* ex = i32(st.slot_tensor(mb, l, L_QEXP));
         void* out = (l == d.n_layers - 1) ? y : st.slot_tensor(mb, l + 1, L_X);
 
-        ZB_TRY(rmsnorm_fwd(xl, cbf(w[4]), act, r1, T, H, d.rms_eps, s));
+        // layer 0 stashes the stage input as its norm reads it
+        if (l == 0) ZB_TRY(rmsnorm_fwd(cbf(x), cbf(w[4]), act, r1, T, H, d.rms_eps, s, xl));
+        else ZB_TRY(rmsnorm_fwd(xl, cbf(w[4]), act, r1, T, H, d.rms_eps, s));
         ZB_TRY(quantize_e4m3(act, T, H, H, qrow, H, u8(st.slot_tensor(mb, l, L_N1T)), T, ex + Q_N1, part, s));
         ZB_TRY(gemm_fp8(q8(T, D.QKV, H, qrow, ex + Q_N1, wqkv.q, wqkv.e, qkv, D.QKV), s));
         ZB_TRY(attn_fwd(qkv, a, lse, T, d.n_heads, d.n_kv_heads, s));
