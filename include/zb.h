@@ -207,6 +207,15 @@ int32_t zb_stage_fp8_weight(zb_stage* st, int32_t i, void** q, void** qt, void**
  * issued). */
 int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream);
 
+/* The stage keeps copies of its linear weights that its passes read instead
+ * of the caller's: E4M3 codes in a ZB_FP8 stage (refreshed by its first F),
+ * transposed bf16 copies [in][out] in a bf16 ZB_LLAMA stage (refreshed by its
+ * first B; the B pass multiplies by them so that its products have both
+ * operands K-contiguous).  They are refreshed after zb_stage_create and
+ * zb_stage_sgd_step; a caller that writes the weights itself calls this
+ * before the next F and B.  ZB_EINVAL for a NULL stage. */
+int32_t zb_stage_weights_changed(zb_stage* st);
+
 /* Learning rate of the optimizer steps zb_stage_run_schedule issues for
  * ZB_OP_O ops (default 0: the weights are left unchanged).  ZB_EINVAL if lr
  * is not finite. */

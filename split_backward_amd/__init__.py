@@ -84,6 +84,7 @@ _PROTOS = {
     "zb_stage_zero_grad": (_i32, [_vp, _vp]),
     "zb_stage_sgd_step": (_i32, [_vp, ctypes.c_float, _vp]),
     "zb_stage_set_lr": (_i32, [_vp, ctypes.c_float]),
+    "zb_stage_weights_changed": (_i32, [_vp]),
     "zb_stage_set_debug": (_i32, [_vp, _i32, _i32, _vp]),
     "zb_stage_debug_report": (_i32, [_vp, ctypes.POINTER(_i32)]),
     "zb_stage_stash_tensor": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
@@ -374,6 +375,11 @@ class Stage:
     def sgd_step(self, lr: float, stream=None):
         """w -= lr * dW for every weight, then zero_grad (zb_stage_sgd_step)."""
         check(lib().zb_stage_sgd_step(self.handle, lr, _stream_ptr(stream)))
+
+    def weights_changed(self):
+        """The caller wrote the weights: refresh the stage's copies of them
+        (zb_stage_weights_changed)."""
+        check(lib().zb_stage_weights_changed(self.handle))
 
     def set_lr(self, lr: float):
         """Rate of the optimizer steps the executor runs for "O" ops."""

@@ -127,6 +127,8 @@ struct SgdGroup {
 };
 int32_t sgd_step_group_bf16(const SgdGroup& g, hipStream_t s);
 int32_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
+// dst [cols, rows] = transpose of the bf16 matrix src [rows, cols].
+int32_t transpose_bf16(const bf16_t* src, bf16_t* dst, int rows, int cols, hipStream_t s);
 // n = RMS(x) * g, r = 1/sqrt(mean(x^2)+eps) per row; x, n bf16 [T, H]; r f32 [T].
 // xcopy (optional): receives a copy of x.
 int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps,

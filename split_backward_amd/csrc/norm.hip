@@ -250,6 +250,27 @@ __global__ void wait_kernel(const uint64_t* t0, uint64_t delta, uint64_t cap, ui
     if (wait_end) *wait_end = now;
 }
 
+// dst[c][r] = src[r][c] for a bf16 [rows, cols] matrix, through a 64 x 64
+// LDS tile per workgroup: each thread reads 16 consecutive columns of one
+// row and writes 16 consecutive rows of one output row.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
+                                                             int rows, int cols) {
+    __shared__ bf16_t tile[64][64 + 2];
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int r = r0 + tr, c = c0 + tc + j;
+        tile[tr][tc + j] = (r < rows && c < cols) ? src[(int64_t)r * cols + c] : (bf16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int orow = c0 + tr, ocol = r0 + tc + j;  // dst[orow][ocol] = src[ocol][orow]
+        if (orow < cols && ocol < rows) dst[(int64_t)orow * rows + ocol] = tile[tc + j][tr];
+    }
+}
+
 template <int CH>
 int32_t launch_rms_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, bf16_t* xcopy, int T, int H, float eps,
                        hipStream_t s) {
@@ -283,6 +304,14 @@ int32_t rmsnorm_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16
     if (ch <= 1) return launch_rms_bwd<1>(x, r, g, dn, dres, dx, rescopy, T, H, s);
     if (ch <= 2) return launch_rms_bwd<2>(x, r, g, dn, dres, dx, rescopy, T, H, s);
     return launch_rms_bwd<4>(x, r, g, dn, dres, dx, rescopy, T, H, s);
+}
+
+int32_t transpose_bf16(const bf16_t* src, bf16_t* dst, int rows, int cols, hipStream_t s) {
+    if (!src || !dst || rows < 1 || cols < 1) return fail(ZB_EINVAL, "transpose_bf16: bad argument");
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((cols + 63) / 64, (rows + 63) / 64), dim3(256), 0, s, src, dst, rows,
+                       cols);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
 }
 
 size_t rmsnorm_dgamma_scratch_floats(int T, int H) { return (size_t)((T + DG_ROWS - 1) / DG_ROWS) * H; }

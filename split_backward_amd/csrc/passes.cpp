@@ -135,6 +135,7 @@ int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipSt
         return gemm_bf16(nn(T, H, F, da, F, st.w[0], H, dx, H), s);
     }
     const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
+    if (st.wt_dirty) ZB_TRY(transpose_weights(st, s));
     bf16_t* da = bf(st.scratch_b);
     float* delta = reinterpret_cast<float*>(st.scratch_b + ((size_t)T * QD * 2 + 255) / 256 * 256);
     float* part = attn_bwd_scratch_bytes(T, d.n_heads, d.n_kv_heads) == 0
@@ -163,18 +164,42 @@ int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipSt
         const bool last = l == d.n_layers - 1;
         const bf16_t* gin = last ? cbf(dy) : dout;
 
-        GemmDesc gd = nn(T, F, H, gin, H, w[3], F, dgu, 2 * F, EPI_SWIGLU_BWD);
+        // transposed weights [in][out]: every product below is A . B^T
+        const void* wqkv_t = st.wt + st.lay.wt_off[6 * l];      // [H][QKV]
+        const void* wo_t = st.wt + st.lay.wt_off[6 * l + 1];    // [QD][H]
+        const void* wgu_t = st.wt + st.lay.wt_off[6 * l + 2];   // [H][2F]
+        const void* wd_t = st.wt + st.lay.wt_off[6 * l + 3];    // [F][H]
+        GemmDesc gd = nt(T, F, H, gin, H, wd_t, H, dgu, 2 * F, EPI_SWIGLU_BWD);
         gd.R = gu;
         gd.ldr = 2 * F;
         gd.half_n = F;
         ZB_TRY(gemm_bf16(gd, s));
-        ZB_TRY(gemm_bf16(nn(T, H, 2 * F, dgu, 2 * F, w[2], H, dn2, H), s));
+        ZB_TRY(gemm_bf16(nt(T, H, 2 * F, dgu, 2 * F, wgu_t, 2 * F, dn2, H), s));
         ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, gin, dh1, T, H, s, last ? dout : nullptr));
-        ZB_TRY(gemm_bf16(nn(T, QD, H, dh1, H, w[1], QD, da, QD), s));
+        ZB_TRY(gemm_bf16(nt(T, QD, H, dh1, H, wo_t, H, da, QD), s));
         ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, part, T, d.n_heads, d.n_kv_heads, s));
-        ZB_TRY(gemm_bf16(nn(T, H, QKV, dqkv, QKV, w[0], H, dn1, H), s));
+        ZB_TRY(gemm_bf16(nt(T, H, QKV, dqkv, QKV, wqkv_t, QKV, dn1, H), s));
         ZB_TRY(rmsnorm_bwd(xl, r1, cbf(w[4]), dn1, dh1, bf(dest), T, H, s));
     }
+    return ZB_OK;
+}
+
+// The B pass of a bf16 Llama stage multiplies by each linear weight with its
+// output index as the reduction index; from a transposed copy [in][out] that
+// product has both operands K-contiguous (the F-layout GEMM).  Refreshed after
+// the weights change (zb_stage_create, zb_stage_sgd_step,
+// zb_stage_weights_changed), on the B stream, before the B that reads them.
+int32_t transpose_weights(zb_stage& st, hipStream_t s) {
+    const zb_stage_desc& d = st.desc;
+    const int H = d.hidden, F = d.ffn;
+    const int QD = d.n_heads * d.head_dim, QKV = QD + 2 * d.n_kv_heads * d.head_dim;
+    const int rows[4] = {QKV, H, 2 * F, H}, cols[4] = {H, QD, H, F};  // Wqkv, Wo, Wgu, Wd as stored [out][in]
+    for (int l = 0; l < d.n_layers; ++l)
+        for (int k = 0; k < 4; ++k) {
+            const int i = 6 * l + k;
+            ZB_TRY(transpose_bf16(cbf(st.w[i]), bf(st.wt + st.lay.wt_off[i]), rows[k], cols[k], s));
+        }
+    st.wt_dirty = false;
     return ZB_OK;
 }
 

@@ -165,11 +165,22 @@ void Layout::build(const zb_stage_desc& d) {
             w8_bytes = w8_e[i] + ALIGN;
         }
     }
+    wt_bytes = 0;
+    wt_off.clear();
+    if (d.kind == ZB_LLAMA && d.dtype == ZB_BF16) {
+        const int nw = 6 * d.n_layers;
+        wt_off.assign(nw, 0);
+        for (int i = 0; i < nw; ++i) {
+            if (i % 6 >= 4) continue;  // RMSNorm gains
+            wt_off[i] = wt_bytes;
+            wt_bytes += align_up(weight_elems(d, i) * 2);
+        }
+    }
     stamps_bytes = align_up(sizeof(uint64_t) * (3 * (size_t)MAX_RUN_OPS + 8));
     // debug area: the delay stamp (8 bytes), the mismatch record, one tag per slot
     debug_bytes = align_up(8 + 4 * (size_t)DEBUG_REC + 4 * (size_t)d.ring_slots);
     ring_bytes = slot_bytes * d.ring_slots;
-    total = ring_bytes + scratch_b + scratch_w + scratch_f + w8_bytes + stamps_bytes + debug_bytes;
+    total = ring_bytes + scratch_b + scratch_w + scratch_f + w8_bytes + wt_bytes + stamps_bytes + debug_bytes;
 }
 
 const Layout::Tensor* Layout::find(int layer, int which) const {
@@ -297,7 +308,8 @@ extern "C" int32_t zb_stage_create(const zb_stage_desc* d, void* const* weights,
     st->scratch_w = st->scratch_b + st->lay.scratch_b;
     st->scratch_f = st->scratch_w + st->lay.scratch_w;
     st->w8 = st->scratch_f + st->lay.scratch_f;
-    st->stamps = reinterpret_cast<uint64_t*>(st->w8 + st->lay.w8_bytes);
+    st->wt = st->w8 + st->lay.w8_bytes;
+    st->stamps = reinterpret_cast<uint64_t*>(st->wt + st->lay.wt_bytes);
     char* dbg = reinterpret_cast<char*>(st->stamps) + st->lay.stamps_bytes;
     st->dbg_t0 = reinterpret_cast<uint64_t*>(dbg);
     st->dbg_rec = reinterpret_cast<int32_t*>(dbg + 8);
@@ -469,6 +481,7 @@ extern "C" int32_t zb_stage_sgd_step(zb_stage* st, float lr, void* stream) {
         if (rc) return rc;
     }
     st->w8_dirty = true;  // ZB_FP8: the next F re-quantizes the updated weights
+    st->wt_dirty = true;  // bf16 Llama: the next B re-transposes them
     // the same reset as zb_stage_zero_grad, without its fill; the step's
     // completion also becomes the last op of F and B, so the next
     // iteration's first F (on any stream) reads the updated weights
@@ -511,6 +524,13 @@ extern "C" int32_t zb_stage_debug_report(zb_stage* st, int32_t* info) {
     if (info)
         for (int i = 0; i < 5; ++i) info[i] = rec[i + 1];
     return rec[0];
+}
+
+extern "C" int32_t zb_stage_weights_changed(zb_stage* st) {
+    if (!st) return fail(ZB_EINVAL, "zb_stage_weights_changed: NULL stage");
+    st->w8_dirty = true;
+    st->wt_dirty = true;
+    return ZB_OK;
 }
 
 extern "C" int32_t zb_stage_set_lr(zb_stage* st, float lr) {

@@ -38,6 +38,11 @@ struct Layout {
     size_t f_act = 0, f_q = 0, f_part = 0;                                  // F scratch
     size_t b_dgu = 0, b_dh1 = 0, b_dqkv = 0, b_dout[2] = {0, 0}, b_q = 0, b_part = 0;  // B scratch
     std::vector<size_t> w8_q, w8_qt, w8_e;                                  // per weight index (0 if none)
+    // bf16 Llama stages: transposed copies [in][out] of the linear weights,
+    // which the B pass reads so that its products have both operands
+    // K-contiguous (offset per weight index, 0 for the norm gains).
+    size_t wt_bytes = 0;
+    std::vector<size_t> wt_off;
     void build(const zb_stage_desc& d);
     const Tensor* find(int layer, int which) const;
 };
@@ -64,6 +69,8 @@ struct zb_stage {
     char* scratch_f = nullptr;  // ZB_FP8: F-pass scratch
     char* w8 = nullptr;         // ZB_FP8: E4M3 weight copies
     bool w8_dirty = true;       // ZB_FP8: refresh the copies at the next F
+    char* wt = nullptr;         // bf16 ZB_LLAMA: transposed weight copies
+    bool wt_dirty = true;       // bf16 ZB_LLAMA: refresh them at the next B
     uint64_t* stamps = nullptr;
     std::vector<zb::Slot> slots;
     std::array<hipEvent_t, 3> chain{};     // last op of each pass (scratch reuse order)
@@ -114,4 +121,6 @@ int32_t run_backward_weight_pair(zb_stage& st, int mb, hipStream_t s);
 int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_t s);
 int32_t run_backward_input_fp8(zb_stage& st, int mb, const void* dy, void* dx, hipStream_t s);
 int32_t run_backward_weight_fp8(zb_stage& st, int mb, hipStream_t s, float* dg_part);
+// bf16 Llama stages: write the transposed weight copies (passes.cpp).
+int32_t transpose_weights(zb_stage& st, hipStream_t s);
 }  // namespace zb
