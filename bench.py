@@ -308,11 +308,12 @@ def traffic_probe(shape, device, fp8=False):
 
 def blas_comparison(shape, device, reps=20):
     """The stage's bf16 linear products, each timed through the library's
-    kernels and through torch.mm (hipBLASLt) at the same shape and operand
-    layout, with HIP events: F (Y = X W^T), B (dX = dY W) and W
-    (dW = dY^T X).  torch.mm writes a bf16 product; the library's W product
-    accumulates into fp32 dW in place (its extra read-modify-write is in its
-    time).  Context for the kernels' rates, not part of the step."""
+    kernels as the stage runs them and through torch.mm (hipBLASLt), with HIP
+    events: F (Y = X W^T), B (dX = dY W; the library multiplies by the
+    stage's transposed weight copy, torch.mm by W) and W (dW = dY^T X).
+    torch.mm writes a bf16 product; the library's W product accumulates into
+    fp32 dW in place (its extra read-modify-write is in its time).  Context
+    for the kernels' rates, not part of the step."""
     import torch
     import split_backward_amd as zb
 
@@ -351,13 +352,15 @@ def blas_comparison(shape, device, reps=20):
         t_mm = timeit(lambda: torch.mm(X, Wt.t(), out=Y))
         rows.append({"pass": "F", "MNK": [T, M, N], "lib_tflops": round(fl / t_lib / 1e9, 1),
                      "torch_mm_tflops": round(fl / t_mm / 1e9, 1)})
+        # the stage's B pass multiplies by its transposed weight copy [in][out]
         dY = torch.randn(T, M, device=device).to(torch.bfloat16)
         dX = torch.empty(T, N, device=device, dtype=torch.bfloat16)
-        t_lib = timeit(lambda: zb.gemm(dY, Wt, dX, a_kmajor=True, b_kmajor=False, M=T, N=N, K=M))
+        WtT = Wt.t().contiguous()
+        t_lib = timeit(lambda: zb.gemm(dY, WtT, dX, a_kmajor=True, b_kmajor=True, M=T, N=N, K=M))
         t_mm = timeit(lambda: torch.mm(dY, Wt, out=dX))
         rows.append({"pass": "B", "MNK": [T, N, M], "lib_tflops": round(fl / t_lib / 1e9, 1),
                      "torch_mm_tflops": round(fl / t_mm / 1e9, 1)})
-        del A, B, C, Cb, X, Wt, Y, dY, dX
+        del A, B, C, Cb, X, Wt, Y, dY, dX, WtT
     return rows
 
 

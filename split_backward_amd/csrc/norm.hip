@@ -252,22 +252,48 @@ __global__ void wait_kernel(const uint64_t* t0, uint64_t delta, uint64_t cap, ui
 
 // dst[c][r] = src[r][c] for a bf16 [rows, cols] matrix, through a 64 x 64
 // LDS tile per workgroup: each thread reads 16 consecutive columns of one
-// row and writes 16 consecutive rows of one output row.
+// row (two 16-byte loads when they lie inside the matrix and its rows are
+// 16-byte aligned, else element by element) and writes 16 consecutive
+// columns of one output row the same way.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
                                                              int rows, int cols) {
     __shared__ bf16_t tile[64][64 + 2];
     const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
     const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+    {
+        const int r = r0 + tr, c = c0 + tc;
+        if (r < rows && c + 16 <= cols && (cols & 7) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(src + (int64_t)r * cols + c);
+            const u32x4 v0 = p[0], v1 = p[1];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int r = r0 + tr, c = c0 + tc + j;
-        tile[tr][tc + j] = (r < rows && c < cols) ? src[(int64_t)r * cols + c] : (bf16_t)0;
+            for (int j = 0; j < 4; ++j) {
+                tile[tr][tc + 2 * j] = (bf16_t)(v0[j] & 0xffffu);
+                tile[tr][tc + 2 * j + 1] = (bf16_t)(v0[j] >> 16);
+                tile[tr][tc + 8 + 2 * j] = (bf16_t)(v1[j] & 0xffffu);
+                tile[tr][tc + 8 + 2 * j + 1] = (bf16_t)(v1[j] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                tile[tr][tc + j] = (r < rows && c + j < cols) ? src[(int64_t)r * cols + c + j] : (bf16_t)0;
+        }
     }
     __syncthreads();
+    const int orow = c0 + tr, ocol = r0 + tc;  // dst[orow][ocol + j] = src[ocol + j][orow]
+    if (orow < cols && ocol + 16 <= rows && (rows & 7) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        u32x4 v0, v1;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int orow = c0 + tr, ocol = r0 + tc + j;  // dst[orow][ocol] = src[ocol][orow]
-        if (orow < cols && ocol < rows) dst[(int64_t)orow * rows + ocol] = tile[tc + j][tr];
+        for (int j = 0; j < 4; ++j) {
+            v0[j] = uint32_t(tile[tc + 2 * j][tr]) | (uint32_t(tile[tc + 2 * j + 1][tr]) << 16);
+            v1[j] = uint32_t(tile[tc + 8 + 2 * j][tr]) | (uint32_t(tile[tc + 8 + 2 * j + 1][tr]) << 16);
+        }
+        u32x4* q = reinterpret_cast<u32x4*>(dst + (int64_t)orow * rows + ocol);
+        q[0] = v0;
+        q[1] = v1;
+    } else if (orow < cols) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (ocol + j < rows) dst[(int64_t)orow * rows + ocol + j] = tile[tc + j][tr];
     }
 }
 
