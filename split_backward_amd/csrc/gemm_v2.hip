@@ -1,10 +1,16 @@
 // bf16 GEMM, second generation: direct-to-LDS operand staging.
 //
-// Workgroup tile 256 x 256 (k-tiles of 32), 256 threads = 4 waves in a 2 x 2
-// grid, each wave owning a 128 x 128 sub-tile = 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, held in AGPRs).
+// Workgroup tile 256 x 256, 256 threads = 4 waves in a 2 x 2 grid, each wave
+// owning a 128 x 128 sub-tile (256 fp32 accumulators per lane, held in
+// AGPRs): 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, or, for products with
+// both operands K-contiguous (the F pass, and the B pass on transposed
+// weights), 8 x 8 blocks of v_mfma_f32_16x16x32_bf16 (gemm_64_tile16).
 // For a K-contiguous A the tile may instead be 128 x 256 (each wave 64 x 128),
 // used where a launch's last round of tiles would leave most CUs idle.
+//
+// The description below is that of the 32-k loop of the W pass; the loops
+// of products with a K-contiguous A (64-k parts in a ring of five LDS slots)
+// are described where they are defined.
 //
 // Operands go HBM -> LDS with buffer_load ... lds (16 bytes per lane): no
 // VGPR staging, no ds_write, and out-of-range rows / columns / k read as zero
