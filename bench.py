@@ -150,7 +150,8 @@ W_KERNEL = "gemm_v2_group_kernel<false,false,EPI_ACCUM_F32>"
 W_KERNEL_SOURCES = ("split_backward_amd/csrc/gemm_v2.hip", "split_backward_amd/csrc/common.h")
 # Counter summaries of the W kernel's HBM traffic, by workload.
 TRAFFIC_SUMMARIES = {"llama7b_stage4": "profiles/gemm_w_kernel_hbm_traffic_llama7b_stage4.md",
-                     "llama7b_stage4_fp8": "profiles/gemm_w_fp8_kernel_hbm_traffic_llama7b_stage4_fp8.md"}
+                     "llama7b_stage4_fp8": "profiles/gemm_w_fp8_kernel_hbm_traffic_llama7b_stage4_fp8.md",
+                     "llama70b_slice2": "profiles/gemm_w_kernel_hbm_traffic_llama70b_slice2.md"}
 
 
 COMMON_H_END = "// ------------------------------------------------- elementwise / norms ----"
