@@ -8,23 +8,29 @@
 // CDNA4 design.  Every product is a v_mfma_f32_32x32x16_bf16.  The wave
 // index is read into a scalar register so that LDS DMA destinations (M0) are
 // computed by scalar instructions.
-// * Tiles of K, V (forward, dq) and of Q, dO (dk/dv) are DMA'd HBM -> LDS
-//   with buffer_load ... lds in their natural [rows][128 d] layout (256-byte
-//   rows, 16-byte chunks XOR-swizzled by the row), double buffered.
+// * Tiles of K, V (forward, dq), of Q, dO (dk/dv) and of dS^T (dq) are DMA'd
+//   HBM -> LDS with buffer_load ... lds in their natural [rows][128] layout
+//   (256-byte rows, 16-byte chunks XOR-swizzled by the row), double buffered.
 // * Operands whose reduction index is the row of such a tile (V^T in o,
-//   K^T in dq, dO^T and Q^T in dv / dk) are read with the gfx950 transpose
-//   read ds_read_b64_tr_b16; the row addresses are chosen so the lane receives
-//   the keys (or queries) in exactly the order the score accumulator holds
-//   them (8(s/4) + 4g + s%4 within a 16-row step), so probabilities go from
-//   the accumulator into the next MFMA without any shuffle.
-// * The forward and dq kernels compute the transposed score block S^T = K Q^T:
-//   each lane owns one query column, so softmax statistics are per-lane
-//   scalars combined with the partner lane 32 away.  The forward rescales its
-//   running output only when a row maximum grows by more than 2^8 (exact:
-//   output and normaliser always share one reference maximum), and skips the
-//   rescale entirely when no lane of the wave needs it.
-// * The dk/dv kernel owns a key block per workgroup and sweeps query blocks,
-//   accumulating dK^T and dV^T in registers: no atomics, deterministic.
+//   K^T and dS^T in dq, dO^T and Q^T in dv / dk) are read with the gfx950
+//   transpose read ds_read_b64_tr_b16; the row addresses are chosen so the
+//   lane receives the keys (or queries) in exactly the order the score
+//   accumulator holds them (8(s/4) + 4g + s%4 within a 16-row step), so
+//   probabilities go from the accumulator into the next MFMA without any
+//   shuffle.
+// * The forward computes the transposed score block S^T = K Q^T: each lane
+//   owns one query column, so softmax statistics are per-lane scalars
+//   combined with the partner lane 32 away.  It rescales its running output
+//   only when a row maximum grows by more than 2^8 (exact: output and
+//   normaliser always share one reference maximum), and skips the rescale
+//   entirely when no lane of the wave needs it.
+// * The backward computes S and dP once.  The dk/dv kernel owns a key block
+//   per workgroup and sweeps query blocks, accumulating dK^T and dV^T in
+//   registers (no atomics, deterministic); it also writes dS^T in bf16 (the
+//   operand its own dK product uses) to a scratch [head][key][query].  The
+//   dq kernel then forms dQ = dS K from that scratch and K alone, summing
+//   over keys in a fixed order.  delta = rowsum(dO o) comes from a small
+//   kernel before both.
 // Softmax runs in fp32 in base 2; the stashed row statistic is
 // lse2 = max + log2(sum) of the scaled scores.
 #include "common.h"
@@ -118,28 +124,45 @@ __device__ __forceinline__ bf16x8 frag_row(const lds_void* tile, int row, int kk
 // column i of the row read by lane 4s + i/4.  The row's low 4 bits do not
 // depend on t, so the per-lane byte offsets of (dblk, lo/hi) are computed
 // once (tr_bases) and t enters as the instruction's immediate offset.
+struct TrCol {
+    uint32_t lo, hi;
+};
+// Offsets of the 32-column block cb (0..3) of the tile.
+__device__ __forceinline__ TrCol tr_col(int lane, int cb) {
+    const int G = lane >> 4, j = lane & 15;
+    const int s = j >> 2, q = j & 3;
+    const int row_lo = (G >> 1) * 4 + s, row_hi = row_lo + 8;
+    const int d = cb * 32 + (G & 1) * 16 + q * 4;
+    return TrCol{(uint32_t)(row_lo * 256 + (((d >> 3) ^ swz(row_lo)) << 4) + (d & 7) * 2),
+                 (uint32_t)(row_hi * 256 + (((d >> 3) ^ swz(row_hi)) << 4) + (d & 7) * 2)};
+}
 struct TrBases {
     uint32_t lo[4], hi[4];
 };
 __device__ __forceinline__ TrBases tr_bases(int lane) {
-    const int G = lane >> 4, j = lane & 15;
-    const int s = j >> 2, q = j & 3;
-    const int row_lo = (G >> 1) * 4 + s, row_hi = row_lo + 8;
     TrBases b;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + (G & 1) * 16 + q * 4;
-        b.lo[db] = row_lo * 256 + (((d >> 3) ^ swz(row_lo)) << 4) + (d & 7) * 2;
-        b.hi[db] = row_hi * 256 + (((d >> 3) ^ swz(row_hi)) << 4) + (d & 7) * 2;
+        const TrCol c = tr_col(lane, db);
+        b.lo[db] = c.lo;
+        b.hi[db] = c.hi;
     }
     return b;
 }
 template <int T16>
-__device__ __forceinline__ bf16x8 frag_tr(uint32_t tile, const TrBases& b, int db) {
+__device__ __forceinline__ bf16x8 frag_tr(uint32_t tile, uint32_t lo_off, uint32_t hi_off) {
     u32x2 lo, hi;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(tile + b.lo[db]), "i"(T16 * 4096));
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(tile + b.hi[db]), "i"(T16 * 4096));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(tile + lo_off), "i"(T16 * 4096));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(tile + hi_off), "i"(T16 * 4096));
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+template <int T16>
+__device__ __forceinline__ bf16x8 frag_tr(uint32_t tile, const TrBases& b, int db) {
+    return frag_tr<T16>(tile, b.lo[db], b.hi[db]);
+}
+template <int T16>
+__device__ __forceinline__ bf16x8 frag_tr(uint32_t tile, const TrCol& c) {
+    return frag_tr<T16>(tile, c.lo, c.hi);
 }
 
 // Wait for all LDS reads; `v` becomes an output so its uses stay below.
@@ -183,6 +206,8 @@ __device__ __forceinline__ void lds_wait_keep(F&... f) {
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
@@ -194,16 +219,25 @@ __device__ __forceinline__ void vm_wait() {
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Item of workgroup b in a 1-D grid of n: the hardware deals workgroups to
+// the 8 XCDs round-robin (XCD b % 8), and this gives each XCD a contiguous
+// range of items, so the workgroups sharing an XCD's L2 work on the same few
+// heads (items are numbered head-major).
+__device__ __forceinline__ int xcd_item(int b, int n) {
+    const int xcd = b & 7, local = b >> 3;
+    const int q = n >> 3, r = n & 7;
+    return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
 // ======================================================== forward ========
 constexpr int FQ = 128, FKV = 64, FTHR = 256;
 constexpr int KV_TILE = FKV * D * 2;  // 16 KB
 
-// One query block qb (128 queries) of head blockIdx.y.
-__device__ __forceinline__ void attn_fwd_block(int qb, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
+// One query block qb (128 queries) of head h.
+__device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
                                                bf16_t* __restrict__ o, float* __restrict__ lse, int T, int nq,
                                                int nkv) {
     const int ld = (nq + 2 * nkv) * D;
-    const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
@@ -341,125 +375,138 @@ __device__ __forceinline__ void attn_fwd_block(int qb, char (*sm)[2 * KV_TILE], 
 
 // Causal query blocks differ in length up to nb-fold: each workgroup runs
 // block nb-1-x and then its mirror x, so every workgroup does the same work
-// and the two resident per CU finish together.
+// and the two resident per CU finish together.  Grid: (nb + 1) / 2 pairs per
+// head, 1-D, items head-major (xcd_item).
 __global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ o,
                                                            float* __restrict__ lse, int T, int nq, int nkv) {
     __shared__ __attribute__((aligned(1024))) char sm[2][2 * KV_TILE];  // [stage][K | V]
-    const int nb = T / FQ;
-    const int a = nb - 1 - (int)blockIdx.x, b = (int)blockIdx.x;
+    const int nb = T / FQ, npair = (nb + 1) / 2;
+    const int item = xcd_item(blockIdx.x, gridDim.x);
+    const int h = item / npair, x = item % npair;
+    const int a = nb - 1 - x, b = x;
     for (int pass = 0; pass < (b < a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();  // every wave is done with the stages
-        attn_fwd_block(pass ? b : a, sm, qkv, o, lse, T, nq, nkv);
+        attn_fwd_block(pass ? b : a, h, sm, qkv, o, lse, T, nq, nkv);
     }
 }
 
+// =================================================== delta kernel ========
+// delta[h][q] = sum_d dO[q][h][d] o[q][h][d] in fp32, the row statistic of
+// dS = P (dP - delta).  16 lanes per (query, head): 8 products each, then a
+// sum across the 16 lanes.
+__global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+                                                         float* __restrict__ delta, int T, int nq) {
+    const int64_t pair = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (pair >= (int64_t)T * nq) return;  // whole 16-lane groups
+    const int q = (int)(pair / nq), h = (int)(pair % nq);
+    const int j = threadIdx.x & 15;
+    const int64_t e = (int64_t)q * nq * D + h * D + j * 8;
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + e);
+    const bf16x8 dv = *reinterpret_cast<const bf16x8*>(dout + e);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum = fmaf((float)ov[i], (float)dv[i], sum);
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 16);
+    if (j == 0) delta[(int64_t)h * T + q] = sum;
+}
+
 // ====================================================== dq kernel ========
-// Per (query block of 128, query head).  Mirrors the forward: S^T = K Q^T,
-// dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
-// Two workgroups per CU as in the dk/dv kernel (64 KB of LDS each).
-constexpr int DQ_STAGES = 2;
-__device__ __forceinline__ void attn_dq_block(int qb, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
-                                              const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
-                                              const float* __restrict__ lse, float* __restrict__ delta,
-                                              bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
+// dS^T scratch layout: 2 KB chunks [head][query block of 32][key block of 32],
+// each holding dS^T of 32 keys x 32 queries in the order the dk/dv kernel's
+// lanes hold it, so that kernel stores 1 KB contiguous per instruction: half
+// j (queries 16j .. 16j+15), then for key kk and lane half g the 16 bytes at
+// 32 kk + 16 g: queries 16j + 4g + 0..3, then 16j + 8 + 4g + 0..3.
+constexpr int DS_CHUNK = 2048;
+// Byte offset, in a wave's 4 KB of two consecutive chunks (64 keys, 32
+// queries), at which lane `lane` starts its transpose reads of dS^T: source
+// lane j = 4s + c of 16-lane group G reads key 4(G/2) + s of a 16-key step
+// at queries 16(G%2) + 4c .. +3, which lands output lane i of the group, slot
+// s, on query 16(G%2) + i and key 4(G/2) + s: the score-accumulator order of
+// the keys.  A group's 16 reads cover one contiguous 128-byte range.
+__device__ __forceinline__ uint32_t ds_gather_base(int lane) {
+    const int G = lane >> 4, j = lane & 15, s = j >> 2, c = j & 3;
+    return (uint32_t)((G & 1) * 1024 + (4 * (G >> 1) + s) * 32 + (c & 1) * 16 + (c >> 1) * 8);
+}
+// Fragment of 16-key step t (keys 16t .. 16t+15 of the 64): keys 16t + 4g + s
+// in slots 0..3 and 16t + 8 + 4g + s in slots 4..7.
+template <int T16>
+__device__ __forceinline__ bf16x8 frag_ds(uint32_t tile, uint32_t base) {
+    constexpr int off = (T16 >> 1) * DS_CHUNK + (T16 & 1) * 512;
+    u32x2 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(tile + base), "i"(off));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(tile + base), "i"(off + 256));
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Per (query block of 128, query head): dQ^T += K^T dS^T over the key
+// blocks of 64 at or before the block's queries, both operands from LDS by
+// transpose reads.  dS^T of the head was written by the dk/dv kernel (bf16,
+// zero where the key follows the query); each wave DMAs the two chunks of
+// its 32 queries per key block (4 KB) and reads nothing else of it, so the
+// kernel streams dS^T from HBM once while K comes mostly from L2.  dS^T
+// stages sit in a ring of three (two in flight while one is used), K tiles
+// in a ring of two: 80 KB of LDS, two workgroups per CU.
+constexpr int DQ_K_STAGES = 2, DQ_S_STAGES = 3;
+constexpr int DS_STAGE = 4 * 2 * DS_CHUNK;  // four waves x 64 keys x 32 queries: 16 KB
+struct DqSmem {
+    char k[DQ_K_STAGES][KV_TILE];
+    char s[DQ_S_STAGES][DS_STAGE];
+};
+__device__ __forceinline__ void attn_dq_block(int qb, int h, DqSmem& sm, const bf16_t* __restrict__ qkv,
+                                              const bf16_t* __restrict__ dst, bf16_t* __restrict__ dqkv, int T, int nq,
+                                              int nkv) {
     const int ld = (nq + 2 * nkv) * D;
-    const int h = blockIdx.y;
     const int grp = h / (nq / nkv);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int qw0 = qb * FQ + wave * 32;
     const int q = qw0 + col;
+    const int nq32 = T / 32;
     const bf16_t* kbase = qkv + nq * D + grp * D;
-    const bf16_t* vbase = qkv + (nq + nkv) * D + grp * D;
-    const int ldo = nq * D;
-
-    bf16x8 qf[8], dof[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        qf[kk] = *reinterpret_cast<const bf16x8*>(qkv + (int64_t)q * ld + h * D + kk * 16 + g * 8);
-        dof[kk] = *reinterpret_cast<const bf16x8*>(dout + (int64_t)q * ldo + h * D + kk * 16 + g * 8);
-    }
-    const float lq = lse[(int64_t)h * T + q];
-    // delta = rowsum(dO o) of the lane's query: half of the row's 128 products
-    // in each of the lanes q and q+32; stored for the dk/dv kernel.
-    float dsum = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + (int64_t)q * ldo + h * D + kk * 16 + g * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dsum = fmaf((float)ov[e], (float)dof[kk][e], dsum);
-    }
-    dsum += __shfl_xor(dsum, 32, 64);
-    const float dq_delta = dsum;
-    if (g == 0) delta[(int64_t)h * T + q] = dsum;
-    const float c = LOG2E / sqrtf((float)D);
+    // the wave's chunks: [h][query block qw0 / 32][key block 0 ..]
+    const bf16_t* dsw = dst + ((int64_t)h * nq32 + qw0 / 32) * nq32 * (DS_CHUNK / 2);
 
     floatx16 dacc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dacc[i] = zero16();
     const TrBases trb = tr_bases(lane);
+    const uint32_t sgat = ds_gather_base(lane);
 
     const int nkb = (qb * FQ + FQ) / FKV;
-    // Ring of DQ_STAGES K/V blocks: the DMA of blocks kb+1 .. kb+DQ_STAGES-1
-    // is issued while block kb is used (8 loads per wave per block; blocks
-    // past the last are empty).
-    auto dma = [&](int kb) {
-        char* st = sm[kb % DQ_STAGES];
-        const bool live = kb < nkb;
-        dma_rows<FKV, 4>(kbase, ld, kb * FKV, T, 0, (lds_void*)st, lane, wave, live);
-        dma_rows<FKV, 4>(vbase, ld, kb * FKV, T, 0, (lds_void*)(st + KV_TILE), lane, wave, live);
+    // 4 loads per wave for either tile; blocks past the last are empty.
+    auto dma_k = [&](int kb) {
+        dma_rows<FKV, 4>(kbase, ld, kb * FKV, T, 0, (lds_void*)sm.k[kb % DQ_K_STAGES], lane, wave, kb < nkb);
     };
+    auto dma_s = [&](int kb) {
+        const bool live = kb < nkb;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(dsw + (int64_t)(live ? kb : 0) * 2 * (DS_CHUNK / 2), live ? 2 * DS_CHUNK : 0);
+        lds_char* dstl = (lds_char*)sm.s[kb % DQ_S_STAGES] + wave * 2 * DS_CHUNK;
 #pragma unroll
-    for (int t = 0; t < DQ_STAGES - 1; ++t) dma(t);
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dstl + i * 1024), 16, i * 1024 + lane * 16, 0, 0, 0);
+    };
+    // Issue order K(0) S(0) S(1), then per iteration kb: K(kb+1) S(kb+2).  At
+    // the top of iteration kb only S(kb+1) (4 loads) may still be in flight.
+    dma_k(0);
+    dma_s(0);
+    dma_s(1);
     for (int kb = 0; kb < nkb; ++kb) {
-        vm_wait<8 * (DQ_STAGES - 2)>();  // block kb landed
-        wg_barrier();
-        dma(kb + DQ_STAGES - 1);  // into the stage block kb-1 used
+        vm_wait<4>();  // K(kb) and S(kb) landed
+        wg_barrier();  // and every wave is done with block kb-1's stages
+        dma_k(kb + 1);
+        dma_s(kb + 2);
         const int k0 = kb * FKV;
-        if (k0 > qw0 + 31) continue;
-        const lds_void* kt = (const lds_void*)sm[kb % DQ_STAGES];
-        const lds_void* vt = (const lds_void*)(sm[kb % DQ_STAGES] + KV_TILE);
-        floatx16 s[2], dp[2];
-        s[0] = s[1] = dp[0] = dp[1] = zero16();
-        {
-            // K and V row fragments of step (j, kk) + 1 are read while step (j, kk) multiplies
-            const uint32_t ka = (uint32_t)(uintptr_t)kt;
-            bf16x8 fk[2], fv[2];
-            auto rd = [&](int st, int slot) {
-                const uint32_t ro = tile_off((st >> 3) * 32 + col, (st & 7) * 2 + g);
-                asm volatile("ds_read_b128 %0, %1" : "=v"(fk[slot]) : "v"(ka + ro));
-                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fv[slot]) : "v"(ka + ro), "i"(KV_TILE));
-            };
-            rd(0, 0);
-#pragma unroll
-            for (int st = 0; st < 16; ++st) {
-                const int cur = st & 1, j = st >> 3, kk = st & 7;
-                if (st + 1 < 16) {
-                    rd(st + 1, cur ^ 1);
-                    lds_wait_keep<2>(fk[cur], fv[cur]);
-                } else {
-                    lds_wait_keep<0>(fk[cur], fv[cur]);
-                }
-                s[j] = mfma(fk[cur], qf[kk], s[j]);
-                dp[j] = mfma(fv[cur], dof[kk], dp[j]);
-            }
-        }
-        const bool diag = (k0 + FKV - 1 > qw0);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(s[j][r], c, -lq));
-                if (diag) {
-                    const int key = k0 + j * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    if (key > q) p = 0.f;
-                }
-                s[j][r] = p * (dp[j][r] - dq_delta);  // dS^T
-            }
+        if (k0 > qw0 + 31) continue;  // every key of the block follows every query of the wave
+        const uint32_t kaddr = (uint32_t)(uintptr_t)sm.k[kb % DQ_K_STAGES];
+        const uint32_t saddr = (uint32_t)(uintptr_t)sm.s[kb % DQ_S_STAGES] + wave * 2 * DS_CHUNK;
+        // dS^T fragments: the wave's queries, the block's keys in accumulator order
         bf16x8 sb[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) sb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
-        const uint32_t kaddr = (uint32_t)(uintptr_t)kt;
+        sb[0] = frag_ds<0>(saddr, sgat);
+        sb[1] = frag_ds<1>(saddr, sgat);
+        sb[2] = frag_ds<2>(saddr, sgat);
+        sb[3] = frag_ds<3>(saddr, sgat);
         {
             // K^T fragments of d block db, read one block ahead (8 reads each)
             bf16x8 kf[2][4];
@@ -475,9 +522,9 @@ __device__ __forceinline__ void attn_dq_block(int qb, char (*sm)[2 * KV_TILE], c
                 bf16x8(&cur)[4] = kf[db & 1];
                 if (db + 1 < 4) {
                     rd(db + 1);
-                    lds_wait_keep<8>(cur[0], cur[1], cur[2], cur[3]);
+                    lds_wait_keep<8>(cur[0], cur[1], cur[2], cur[3], sb[0], sb[1], sb[2], sb[3]);
                 } else {
-                    lds_wait_keep<0>(cur[0], cur[1], cur[2], cur[3]);
+                    lds_wait_keep<0>(cur[0], cur[1], cur[2], cur[3], sb[0], sb[1], sb[2], sb[3]);
                 }
 #pragma unroll
                 for (int t = 0; t < 4; ++t) dacc[db] = mfma(cur[t], sb[t], dacc[db]);
@@ -498,28 +545,27 @@ __device__ __forceinline__ void attn_dq_block(int qb, char (*sm)[2 * KV_TILE], c
         }
 }
 
-// Paired query blocks as in the forward kernel.
+// Paired query blocks as in the forward kernel; 1-D grid, items head-major.
 __global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
-                                                          const bf16_t* __restrict__ o,
-                                                          const bf16_t* __restrict__ dout,
-                                                          const float* __restrict__ lse,
-                                                          float* __restrict__ delta,
+                                                          const bf16_t* __restrict__ dst,
                                                           bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
-    __shared__ __attribute__((aligned(1024))) char sm[DQ_STAGES][2 * KV_TILE];
-    const int nb = T / FQ;
-    const int a = nb - 1 - (int)blockIdx.x, b = (int)blockIdx.x;
+    __shared__ __attribute__((aligned(1024))) DqSmem sm;
+    const int nb = T / FQ, npair = (nb + 1) / 2;
+    const int item = xcd_item(blockIdx.x, gridDim.x);
+    const int h = item / npair, x = item % npair;
+    const int a = nb - 1 - x, b = x;
     for (int pass = 0; pass < (b < a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();
-        attn_dq_block(pass ? b : a, sm, qkv, o, dout, lse, delta, dqkv, T, nq, nkv);
+        attn_dq_block(pass ? b : a, h, sm, qkv, dst, dqkv, T, nq, nkv);
     }
 }
 
 // ===================================================== dk / dv kernel ====
-// Per (key block of 128, KV head).  Each wave owns 32 keys (K and V rows in
-// registers as B operands).  Sweeps the query heads of the group and the
-// query blocks of 32 rows at or after the diagonal:
+// Per (key block of 128, KV head).  Each wave owns 32 keys (K rows in
+// registers, V rows in LDS, as B operands).  Sweeps the query heads of the
+// group and the query blocks of 32 rows at or after the diagonal:
 //   S = Q K^T, P = exp2(S c - lse2), dP = dO V^T, dS = P (dP - delta),
-//   dV^T += dO^T P,  dK^T += Q^T dS.
+//   dV^T += dO^T P,  dK^T += Q^T dS,  and stores dS^T (bf16) for dQ.
 constexpr int BKV = 128, BQB = 32;
 constexpr int Q_TILE = BQB * D * 2;  // 8 KB
 // Two workgroups per CU (two waves per SIMD, at most 256 registers per
@@ -531,16 +577,16 @@ constexpr int KV_STAGES = 2;
 __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], char* svt, float (*sl)[2][BQB],
                                                const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dout,
                                                const float* __restrict__ lse, const float* __restrict__ delta,
-                                               bf16_t* __restrict__ dqkv, float* __restrict__ part, int T, int nq,
-                                               int nkv) {
+                                               bf16_t* __restrict__ dqkv, float* __restrict__ part,
+                                               bf16_t* __restrict__ dst, int T, int nq, int nkv, int grp, int zi,
+                                               int nz) {
     const int ld = (nq + 2 * nkv) * D;
     const int ldo = nq * D;
-    const int grp = blockIdx.y;
-    // The group's query heads split over gridDim.z workgroups (head subset
-    // blockIdx.z); with more than one, each writes fp32 partial dK, dV to
-    // `part` and attn_dkv_reduce_kernel adds them in subset order.
-    const int rep = nq / nkv / (int)gridDim.z;
-    const int head0 = (grp * (int)gridDim.z + (int)blockIdx.z) * rep;
+    // The group's query heads split over nz workgroups (head subset zi);
+    // with more than one, each writes fp32 partial dK, dV to `part` and
+    // attn_dkv_reduce_kernel adds them in subset order.
+    const int rep = nq / nkv / nz;
+    const int head0 = (grp * nz + zi) * rep;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     const int kw0 = kb * BKV + wave * 32;
@@ -587,14 +633,32 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
         }
     };
 
-#pragma unroll
-    for (int t = 0; t < KV_STAGES - 1; ++t) fetch(t);
+    // dS^T of the wave's 32 keys x the block's 32 queries: one 2 KB chunk
+    // (layout above the dq kernel), two 1 KB stores.  Slots 0..7 of the
+    // lane's accumulator are queries 4g + 0..3 and 8 + 4g + 0..3, slots 8..15
+    // the same plus 16.
+    const int nq32 = T / 32;
+    auto ds_store = [&](int hh, int q0, const u32x4& w0, const u32x4& w1) {
+        const __amdgpu_buffer_rsrc_t rds =
+            make_rsrc(dst + ((int64_t)hh * nq32 + q0 / 32) * nq32 * (DS_CHUNK / 2), nq32 * DS_CHUNK);
+        const uint32_t off = (uint32_t)((kb * 4 + wave) * DS_CHUNK + (2 * col + g) * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(w0, rds, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w1, rds, off + 1024, 0, 0);
+    };
+    // Each iteration ends with its 2 dS^T stores, so the DMA of the next
+    // block is waited for with those 2 stores still in flight (vector memory
+    // operations complete in issue order).  A wave whose keys all follow the
+    // block's queries runs the block anyway: the causal mask makes its P and
+    // dS zero, which is what dS^T must hold there, and the iteration count
+    // of stores stays exact.
+    static_assert(KV_STAGES == 2, "the wait below counts one block of DMA and one of stores");
+    fetch(0);
     for (int it = 0; it < total; ++it) {
-        vm_wait<6 * (KV_STAGES - 2)>();  // block it landed
+        if (it == 0) vm_wait<0>();
+        else vm_wait<2>();  // block it landed (the previous block's 2 stores may be in flight)
         wg_barrier();
-        fetch(it + KV_STAGES - 1);  // into the stage block it-1 used
+        fetch(it + 1);  // into the stage block it-1 used
         const int q0 = (qb0 + it % per_head) * BQB;
-        if (q0 + BQB - 1 < kw0) continue;  // every query of the block precedes every key of the wave
         const int stg = it % KV_STAGES;
         const lds_void* qt = (const lds_void*)sm[stg];
         const lds_void* ot = (const lds_void*)(sm[stg] + Q_TILE);
@@ -674,10 +738,11 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
                 dk[db] = mfma(cur[3], s1, dk[db]);
             }
         }
+        ds_store(head0 + it / per_head, q0, __builtin_bit_cast(u32x4, s0), __builtin_bit_cast(u32x4, s1));
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the empty trailing blocks still write LDS
     if (part) {  // fp32 partials [subset][key][kv head][dK | dV][D], dK not yet scaled
-        float* pk = part + (((int64_t)blockIdx.z * T + key) * nkv + grp) * 2 * D;
+        float* pk = part + (((int64_t)zi * T + key) * nkv + grp) * 2 * D;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -713,15 +778,19 @@ __global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restr
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ delta,
                                                            bf16_t* __restrict__ dqkv, float* __restrict__ part,
-                                                           int T, int nq, int nkv) {
+                                                           bf16_t* __restrict__ dst, int T, int nq, int nkv,
+                                                           int nz) {
     __shared__ __attribute__((aligned(1024))) char sm[KV_STAGES][2 * Q_TILE];  // [stage][Q | dO]
     __shared__ __attribute__((aligned(1024))) char svt[BKV * D * 2];           // V rows of the block
     __shared__ float sl[KV_STAGES][2][BQB];                                     // [stage][lse | delta]
-    const int nb = T / BKV;
-    const int a = (int)blockIdx.x, b = nb - 1 - (int)blockIdx.x;  // a: the longer sweep
+    const int nb = T / BKV, npair = (nb + 1) / 2;
+    // 1-D grid of npair x nz x nkv items, KV-head-major (xcd_item)
+    const int item = xcd_item(blockIdx.x, gridDim.x);
+    const int x = item % npair, zi = (item / npair) % nz, grp = item / (npair * nz);
+    const int a = x, b = nb - 1 - x;  // a: the longer sweep
     for (int pass = 0; pass < (b > a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();
-        attn_dkv_block(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, part, T, nq, nkv);
+        attn_dkv_block(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, part, dst, T, nq, nkv, grp, zi, nz);
     }
 }
 
@@ -759,11 +828,13 @@ int dkv_split(int T, int nq, int nkv) {
     return rep;
 }
 
+size_t ds_bytes(int T, int nq) { return ((size_t)nq * T * T * 2 + 255) / 256 * 256; }
+
 }  // namespace
 
 int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s) {
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3((T / FQ + 1) / 2, nq), dim3(FTHR), 0, s, qkv, o, lse, T, nq, nkv);
+    hipLaunchKernelGGL(attn_fwd_kernel, dim3((T / FQ + 1) / 2 * nq), dim3(FTHR), 0, s, qkv, o, lse, T, nq, nkv);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
@@ -771,20 +842,23 @@ int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nk
 size_t attn_bwd_scratch_bytes(int T, int nq, int nkv) {
     if (!shapes_ok(T, nq, nkv)) return 0;
     const int z = dkv_split(T, nq, nkv);
-    return z > 1 ? (size_t)z * T * nkv * 2 * D * 4 : 0;
+    return ds_bytes(T, nq) + (z > 1 ? (size_t)z * T * nkv * 2 * D * 4 : 0);
 }
 
 int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout, bf16_t* dqkv, float* delta,
-                 float* part, int T, int nq, int nkv, hipStream_t s) {
+                 void* scratch, int T, int nq, int nkv, hipStream_t s) {
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
-    // the dq kernel also computes delta = rowsum(dO o), which the dk/dv kernel reads
-    hipLaunchKernelGGL(attn_dq_kernel, dim3((T / FQ + 1) / 2, nq), dim3(FTHR), 0, s, qkv, o, dout, lse, delta, dqkv, T,
-                       nq, nkv);
-    ZB_HIP(hipGetLastError());
+    if (scratch == nullptr) return fail(ZB_EINVAL, "attention: missing backward scratch");
+    bf16_t* dst = static_cast<bf16_t*>(scratch);
     const int z = dkv_split(T, nq, nkv);
-    if (z > 1 && part == nullptr) return fail(ZB_EINVAL, "attention: missing dk/dv partial scratch");
-    hipLaunchKernelGGL(attn_dkv_kernel, dim3((T / BKV + 1) / 2, nkv, z), dim3(FTHR), 0, s, qkv, dout, lse, delta, dqkv,
-                       z > 1 ? part : nullptr, T, nq, nkv);
+    float* part = z > 1 ? reinterpret_cast<float*>(static_cast<char*>(scratch) + ds_bytes(T, nq)) : nullptr;
+    // delta = rowsum(dO o), read by the dk/dv kernel
+    const int64_t pairs = (int64_t)T * nq;
+    hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, s, o, dout, delta, T, nq);
+    ZB_HIP(hipGetLastError());
+    // dK, dV (or their per-subset partials) and dS^T
+    hipLaunchKernelGGL(attn_dkv_kernel, dim3((T / BKV + 1) / 2 * nkv * z), dim3(FTHR), 0, s, qkv, dout, lse, delta,
+                       dqkv, part, dst, T, nq, nkv, z);
     ZB_HIP(hipGetLastError());
     if (z > 1) {
         const int64_t n4 = (int64_t)T * nkv * 2 * D / 4;
@@ -792,6 +866,9 @@ int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf1
                            nq, nkv, z);
         ZB_HIP(hipGetLastError());
     }
+    // dQ = dS K from the scratch
+    hipLaunchKernelGGL(attn_dq_kernel, dim3((T / FQ + 1) / 2 * nq), dim3(FTHR), 0, s, qkv, dst, dqkv, T, nq, nkv);
+    ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
 

@@ -45,6 +45,7 @@ enum Epi : int {
     EPI_GELU_BWD = 4,     // C(bf16) = acc * gelu_tanh'(R)              (R = stashed pre-activation)
     EPI_SWIGLU_FWD = 5,   // paired tiles: C = [g | u] (bf16), C2 = silu(g) * u (bf16)
     EPI_SWIGLU_BWD = 6,   // acc = ds; R = [g | u]; C = [dg | du] (bf16)
+    EPI_STORE_F32 = 7,    // C(f32) = acc                               (split-K partial sums)
 };
 
 struct GemmDesc {
@@ -74,6 +75,15 @@ struct GemmDesc {
 };
 
 int32_t gemm_bf16(const GemmDesc& d, hipStream_t s);
+// Split-K for products whose tiles would fill little of the chip (K-contiguous
+// A, epilogues STORE, RESID, GELU_FWD, GELU_BWD): gemm_splitk_factor(d) K
+// slices (1 = none; chosen for 256 workgroups of half-height tiles), each
+// storing its fp32 partial product in part[slice][M][N], then one pass that
+// adds the slices in slice order and applies d's epilogue.  part holds
+// gemm_splitk_scratch_bytes(d.M, d.N, split) bytes.
+int gemm_splitk_factor(const GemmDesc& d);
+size_t gemm_splitk_scratch_bytes(int M, int N, int split);
+int32_t gemm_bf16_splitk(const GemmDesc& d, int split, float* part, hipStream_t s);
 // Direct-to-LDS kernel; sets *handled = false (and does nothing) when an
 // operand is too large for one buffer range or the epilogue cannot use
 // vector accesses (the first-generation kernel then runs).
@@ -146,12 +156,13 @@ size_t rmsnorm_dgamma_scratch_floats(int T, int H);
 // Causal GQA attention, head_dim 128.  q/k/v are column blocks of the packed
 // qkv [T, (nq + 2 nkv) * 128] buffer; o [T, nq*128]; lse f32 [nq, T].
 int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s);
-// dqkv [T, (nq + 2 nkv)*128]; delta scratch f32 [nq, T]; part: scratch of
-// attn_bwd_scratch_bytes(T, nq, nkv) bytes (fp32 partial dK, dV when the
-// query heads of a KV head are split over workgroups; nullptr if 0).
+// dqkv [T, (nq + 2 nkv)*128]; delta scratch f32 [nq, T]; scratch: device
+// memory of attn_bwd_scratch_bytes(T, nq, nkv) bytes (dS^T in bf16
+// [nq][T][T], then fp32 partial dK, dV when the query heads of a KV head are
+// split over workgroups).
 size_t attn_bwd_scratch_bytes(int T, int nq, int nkv);
 int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout,
-                 bf16_t* dqkv, float* delta, float* part, int T, int nq, int nkv, hipStream_t s);
+                 bf16_t* dqkv, float* delta, void* scratch, int T, int nq, int nkv, hipStream_t s);
 
 // ---------------------------------------------------------------- debug ---
 // Ring-slot tags (debug.hip): tags[slot] = 4 * mb + phase (1 F, 2 B, 3 W

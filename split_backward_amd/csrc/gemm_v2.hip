@@ -367,12 +367,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans&
     // divisible by 4 are routed to the first-generation kernel instead.)
     constexpr int P = 132;  // floats per staged row: 128 + 4 padding
     float* stage = reinterpret_cast<float*>(smem) + wave * 32 * P;
-    if constexpr (EPI == EPI_ACCUM_F32) {
+    if constexpr (EPI == EPI_ACCUM_F32 || EPI == EPI_STORE_F32) {
         // dW += acc: the old values of block mi+1 are loaded while block mi
         // is added and stored, so at most one HBM round trip is exposed.
+        // (EPI_STORE_F32: the same stores, nothing loaded.)
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-            if (mi + 1 < MI) load_block(mi + 1, cin[(mi + 1) & 1]);
+            if (EPI == EPI_ACCUM_F32 && mi + 1 < MI) load_block(mi + 1, cin[(mi + 1) & 1]);
             const int rbase = m0 + wm * (TBM / 2) + mi * 32;
             stage_block<MI_ACC, P>(acc, mi, stage, lane);
 #pragma unroll
@@ -380,7 +381,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans&
                 const int lr = 2 * it + (lane >> 5);
                 const int row = rbase + lr;
                 const uint32_t off = (row < d.M && col_ok) ? (uint32_t)(((int64_t)row * d.ldc + gcol) * 4) : OOB;
-                const floatx4 v = *reinterpret_cast<const floatx4*>(stage + lr * P + c4) + cin[mi & 1][it];
+                floatx4 v = *reinterpret_cast<const floatx4*>(stage + lr * P + c4);
+                if constexpr (EPI == EPI_ACCUM_F32) v += cin[mi & 1][it];
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);  // dropped outside C
             }
         }
@@ -1180,7 +1182,7 @@ struct GemmGroup {
 };
 static_assert(sizeof(GemmGroup) <= 3072, "kernel argument block");
 
-template <bool A_KMAJ, bool B_KMAJ, int EPI>
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM = BM>
 __global__ __launch_bounds__(NTHR) void gemm_v2_group_kernel(GemmGroup grp) {
     __shared__ __attribute__((aligned(1024))) char smem[gemm_lds_bytes<A_KMAJ, B_KMAJ>()];
     const int bid = blockIdx.x;
@@ -1194,7 +1196,7 @@ __global__ __launch_bounds__(NTHR) void gemm_v2_group_kernel(GemmGroup grp) {
     tile_of(local, grp.tiles_m[g], grp.tiles_n[g], tm, tn);
     const GemmDesc d = grp.d[g];  // a value copy: its fields stay in scalar registers
     const BufSpans sp = grp.sp[g];
-    gemm_tile<A_KMAJ, B_KMAJ, EPI, BM>(d, tm, tn, sp, smem);
+    gemm_tile<A_KMAJ, B_KMAJ, EPI, TBM>(d, tm, tn, sp, smem);
 }
 
 // fp8 products (both operands K-contiguous E4M3): single and grouped.
@@ -1293,15 +1295,15 @@ V2Plan plan_v2(const GemmDesc& d) {
     const int64_t c_w = paired ? 2 * (int64_t)d.half_n : d.epi == EPI_SWIGLU_BWD ? (int64_t)d.half_n + d.N : d.N;
     const int64_t r_w = d.epi == EPI_SWIGLU_BWD ? (int64_t)d.half_n + d.N : d.N;
     const int64_t c2_w = paired ? d.half_n : d.N;
-    const uint64_t cb = d.epi == EPI_ACCUM_F32 ? (uint64_t)((int64_t)(d.M - 1) * d.ldc + d.N) * 4
-                                               : span_bytes(d.M, d.ldc, c_w);
+    const bool c_f32 = d.epi == EPI_ACCUM_F32 || d.epi == EPI_STORE_F32;
+    const uint64_t cb = c_f32 ? (uint64_t)((int64_t)(d.M - 1) * d.ldc + d.N) * 4 : span_bytes(d.M, d.ldc, c_w);
     const uint64_t rb = has_r ? span_bytes(d.M, d.ldr, r_w) : 0;
     const uint64_t c2b = has_c2 ? span_bytes(d.M, d.ldc2, c2_w) : 0;
     if (ab >= OOB || bb >= OOB || cb >= OOB || rb >= OOB || c2b >= OOB) return p;  // too large for one buffer range
     // 16-byte (fp32) / 8-byte (bf16) epilogue accesses need widths and leading
     // dimensions divisible by 4 and aligned base pointers.
     auto al = [](const void* q, int a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
-    bool vec = (d.N % 4 == 0) && (d.ldc % 4 == 0) && al(d.C, d.epi == EPI_ACCUM_F32 ? 16 : 8);
+    bool vec = (d.N % 4 == 0) && (d.ldc % 4 == 0) && al(d.C, c_f32 ? 16 : 8);
     if (has_r) vec = vec && (d.ldr % 4 == 0) && al(d.R, 8);
     if (has_c2) vec = vec && (d.ldc2 % 4 == 0) && al(d.C2, 8);
     if (d.epi == EPI_SWIGLU_BWD || paired) vec = vec && (d.half_n % 4 == 0);
@@ -1512,6 +1514,124 @@ int32_t gemm_fp8_group(const GemmDesc* ds, int n, hipStream_t s) {
         ZB_CASE(EPI_SWIGLU_BWD)
 #undef ZB_CASE
         default: return fail(ZB_EINVAL, "gemm_fp8_group: unknown epilogue");
+    }
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+namespace {
+// Sum of the split-K slices in slice order, then the product's epilogue (the
+// same operations as the GEMM epilogue on an unsplit product); one thread per
+// 4 consecutive columns of a row.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int split, int M, int N,
+                                                            bf16_t* __restrict__ C, int64_t ldc,
+                                                            const bf16_t* __restrict__ R, int64_t ldr,
+                                                            bf16_t* __restrict__ C2, int64_t ldc2) {
+    const int64_t n4 = N / 4;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)M * n4) return;
+    const int64_t row = i / n4;
+    const int col = (int)(i % n4) * 4;
+    const int64_t slice = (int64_t)M * N;
+    const float* p = part + row * N + col;
+    floatx4 acc = *reinterpret_cast<const floatx4*>(p);
+    for (int k = 1; k < split; ++k) acc += *reinterpret_cast<const floatx4*>(p + k * slice);
+    u32x2 rw{0u, 0u};
+    if constexpr (EPI == EPI_RESID || EPI == EPI_GELU_BWD) rw = *reinterpret_cast<const u32x2*>(R + row * ldr + col);
+    float o[4], o2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x = acc[e];
+        const uint32_t w = rw[e >> 1];
+        const float rv = (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+        if (EPI == EPI_STORE) o[e] = x;
+        else if (EPI == EPI_RESID) o[e] = x + rv;
+        else if (EPI == EPI_GELU_FWD) { o[e] = x; o2[e] = gelu_tanh_f(x); }
+        else if (EPI == EPI_GELU_BWD) o[e] = x * gelu_tanh_grad_f(rv);
+    }
+    *reinterpret_cast<u32x2*>(C + row * ldc + col) = pack_bf16x4(o);
+    if constexpr (EPI == EPI_GELU_FWD) *reinterpret_cast<u32x2*>(C2 + row * ldc2 + col) = pack_bf16x4(o2);
+}
+
+bool splitk_epilogue(int epi) {
+    return epi == EPI_STORE || epi == EPI_RESID || epi == EPI_GELU_FWD || epi == EPI_GELU_BWD;
+}
+}  // namespace
+
+// K slices for a product whose half-height tiles would fill little of a
+// 256-CU part: the largest power of two that keeps the slices' tiles within
+// one round of 256 workgroups, each slice at least 512 deep and a multiple of
+// the 64-k part.
+int gemm_splitk_factor(const GemmDesc& d) {
+    constexpr int64_t TARGET = 256;
+    if (!d.a_kmajor || d.K1 != 0 || d.M <= 0 || d.N <= 0 || d.K <= 0 || d.N % 4 != 0 || !splitk_epilogue(d.epi))
+        return 1;
+    const int64_t tiles = (int64_t)((d.M + BM / 2 - 1) / (BM / 2)) * ((d.N + BN - 1) / BN);
+    int split = 1;
+    while (tiles * split * 2 <= TARGET && split * 2 <= GROUP_MAX && d.K % (split * 2 * BK64) == 0 &&
+           d.K / (split * 2) >= 512)
+        split *= 2;
+    return split;
+}
+
+size_t gemm_splitk_scratch_bytes(int M, int N, int split) {
+    return split > 1 ? (size_t)split * (size_t)M * (size_t)N * 4 : 0;
+}
+
+int32_t gemm_bf16_splitk(const GemmDesc& d, int split, float* part, hipStream_t s) {
+    if (split <= 1) return gemm_bf16(d, s);
+    if (split > GROUP_MAX || part == nullptr || !d.a_kmajor || d.K1 != 0 || d.K % (split * BK64) != 0 ||
+        d.N % 4 != 0 || !splitk_epilogue(d.epi) || d.lda % 8 != 0 || d.ldb % 8 != 0 || (!d.b_kmajor && d.N % 8 != 0) ||
+        ((reinterpret_cast<uintptr_t>(d.A) | reinterpret_cast<uintptr_t>(d.B) | reinterpret_cast<uintptr_t>(part)) & 15))
+        return fail(ZB_EINVAL, "gemm: unsupported split-K product");
+    const V2Plan whole = plan_v2(d);  // the epilogue's outputs must suit the vector accesses
+    if (!whole.ok) return fail(ZB_EINVAL, "gemm: split-K product does not fit the kernel");
+    const int ks = d.K / split;
+    GemmGroup g{};
+    g.n = split;
+    g.off[0] = 0;
+    for (int i = 0; i < split; ++i) {
+        GemmDesc q = d;
+        q.K = ks;
+        q.A = static_cast<const char*>(d.A) + (size_t)i * ks * 2;
+        q.B = static_cast<const char*>(d.B) + (d.b_kmajor ? (size_t)i * ks * 2 : (size_t)i * ks * d.ldb * 2);
+        q.C = part + (size_t)i * d.M * d.N;
+        q.ldc = d.N;
+        q.epi = EPI_STORE_F32;
+        q.R = nullptr;
+        q.ldr = 0;
+        q.C2 = nullptr;
+        q.ldc2 = 0;
+        q.half_n = 0;
+        const V2Plan p = plan_v2(q);
+        if (!p.ok) return fail(ZB_EINVAL, "gemm: split-K slice does not fit the kernel");
+        const int tiles_m = (d.M + BM / 2 - 1) / (BM / 2);
+        g.d[i] = q;
+        g.tiles_m[i] = tiles_m;
+        g.tiles_n[i] = p.tiles_n;
+        g.sp[i] = p.sp;
+        g.off[i + 1] = g.off[i] + ((tiles_m * p.tiles_n + 7) & ~7);
+    }
+    if (d.b_kmajor)
+        hipLaunchKernelGGL((gemm_v2_group_kernel<true, true, EPI_STORE_F32, BM / 2>), dim3(g.off[g.n]), dim3(NTHR), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemm_v2_group_kernel<true, false, EPI_STORE_F32, BM / 2>), dim3(g.off[g.n]), dim3(NTHR), 0, s,
+                           g);
+    ZB_HIP(hipGetLastError());
+    const int64_t threads = (int64_t)d.M * (d.N / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    bf16_t* C = static_cast<bf16_t*>(d.C);
+    const bf16_t* R = static_cast<const bf16_t*>(d.R);
+    bf16_t* C2 = static_cast<bf16_t*>(d.C2);
+    switch (d.epi) {
+#define ZB_CASE(E) case E: hipLaunchKernelGGL((splitk_reduce_kernel<E>), grid, block, 0, s, part, split, d.M, d.N, C, d.ldc, R, d.ldr, C2, d.ldc2); break;
+        ZB_CASE(EPI_STORE)
+        ZB_CASE(EPI_RESID)
+        ZB_CASE(EPI_GELU_FWD)
+        ZB_CASE(EPI_GELU_BWD)
+#undef ZB_CASE
+        default: return fail(ZB_EINVAL, "gemm: unsupported split-K epilogue");
     }
     ZB_HIP(hipGetLastError());
     return ZB_OK;

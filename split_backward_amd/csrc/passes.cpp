@@ -50,6 +50,15 @@ int32_t linear_gemm(const zb_stage& st, const GemmDesc& g, hipStream_t s) {
     return gemm_bf16(g, s);
 }
 
+// A product whose tiles would fill little of the chip runs split along K
+// when the pass scratch holds the partial sums.
+int32_t gemm_split_if_small(const GemmDesc& g, char* scratch, size_t bytes, hipStream_t s) {
+    const int split = gemm_splitk_factor(g);
+    if (split > 1 && scratch != nullptr && gemm_splitk_scratch_bytes(g.M, g.N, split) <= bytes)
+        return gemm_bf16_splitk(g, split, reinterpret_cast<float*>(scratch), s);
+    return gemm_bf16(g, s);
+}
+
 const bf16_t* cbf(const void* p) { return static_cast<const bf16_t*>(p); }
 bf16_t* bf(void* p) { return static_cast<bf16_t*>(p); }
 
@@ -72,8 +81,8 @@ int32_t run_forward(zb_stage& st, int mb, const void* x, void* y, hipStream_t s)
         GemmDesc g1 = nt(T, F, H, xs, H, st.w[0], H, a, F, EPI_GELU_FWD);
         g1.C2 = h;
         g1.ldc2 = F;
-        ZB_TRY(gemm_bf16(g1, s));
-        return gemm_bf16(nt(T, H, F, h, F, st.w[1], F, y, H), s);
+        ZB_TRY(gemm_split_if_small(g1, st.scratch_f, st.lay.scratch_f, s));
+        return gemm_split_if_small(nt(T, H, F, h, F, st.w[1], F, y, H), st.scratch_f, st.lay.scratch_f, s);
     }
     const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
     for (int l = 0; l < d.n_layers; ++l) {
@@ -131,17 +140,14 @@ int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipSt
         GemmDesc g2 = nn(T, F, H, dys, H, st.w[1], F, da, F, EPI_GELU_BWD);
         g2.R = a;
         g2.ldr = F;
-        ZB_TRY(gemm_bf16(g2, s));
-        return gemm_bf16(nn(T, H, F, da, F, st.w[0], H, dx, H), s);
+        ZB_TRY(gemm_split_if_small(g2, st.scratch_b, st.lay.scratch_b, s));
+        return gemm_split_if_small(nn(T, H, F, da, F, st.w[0], H, dx, H), st.scratch_b, st.lay.scratch_b, s);
     }
     const int QD = d.n_heads * d.head_dim, KVD = d.n_kv_heads * d.head_dim, QKV = QD + 2 * KVD;
     if (st.wt_dirty) ZB_TRY(transpose_weights(st, s));
     bf16_t* da = bf(st.scratch_b);
     float* delta = reinterpret_cast<float*>(st.scratch_b + ((size_t)T * QD * 2 + 255) / 256 * 256);
-    float* part = attn_bwd_scratch_bytes(T, d.n_heads, d.n_kv_heads) == 0
-                      ? nullptr
-                      : reinterpret_cast<float*>(reinterpret_cast<char*>(delta) +
-                                                 ((size_t)d.n_heads * T * 4 + 255) / 256 * 256);
+    void* ascratch = reinterpret_cast<char*>(delta) + ((size_t)d.n_heads * T * 4 + 255) / 256 * 256;
     for (int l = d.n_layers - 1; l >= 0; --l) {
         void* const* w = &st.w[6 * l];
         bf16_t* xl = bf(st.slot_tensor(mb, l, L_X));
@@ -177,7 +183,7 @@ int32_t run_backward_input(zb_stage& st, int mb, const void* dy, void* dx, hipSt
         ZB_TRY(gemm_bf16(nt(T, H, 2 * F, dgu, 2 * F, wgu_t, 2 * F, dn2, H), s));
         ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, gin, dh1, T, H, s, last ? dout : nullptr));
         ZB_TRY(gemm_bf16(nt(T, QD, H, dh1, H, wo_t, H, da, QD), s));
-        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, part, T, d.n_heads, d.n_kv_heads, s));
+        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, ascratch, T, d.n_heads, d.n_kv_heads, s));
         ZB_TRY(gemm_bf16(nt(T, H, QKV, dqkv, QKV, wqkv_t, QKV, dn1, H), s));
         ZB_TRY(rmsnorm_bwd(xl, r1, cbf(w[4]), dn1, dh1, bf(dest), T, H, s));
     }

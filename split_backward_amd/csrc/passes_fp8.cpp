@@ -166,10 +166,7 @@ int32_t run_backward_input_fp8(zb_stage& st, int mb, const void* dy, void* dx, h
     char* sb = st.scratch_b;
     bf16_t* da = bf(sb);
     float* delta = reinterpret_cast<float*>(sb + ((size_t)T * D.QD * 2 + 255) / 256 * 256);
-    float* apart = attn_bwd_scratch_bytes(T, d.n_heads, d.n_kv_heads) == 0
-                       ? nullptr
-                       : reinterpret_cast<float*>(reinterpret_cast<char*>(delta) +
-                                                  ((size_t)d.n_heads * T * 4 + 255) / 256 * 256);
+    void* ascratch = reinterpret_cast<char*>(delta) + ((size_t)d.n_heads * T * 4 + 255) / 256 * 256;
     bf16_t* dgu = bf(sb + st.lay.b_dgu);
     bf16_t* dh1 = bf(sb + st.lay.b_dh1);
     bf16_t* dqkv = bf(sb + st.lay.b_dqkv);
@@ -206,7 +203,7 @@ int32_t run_backward_input_fp8(zb_stage& st, int mb, const void* dy, void* dx, h
         ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, dout, dh1, T, H, s));
         ZB_TRY(quantize_e4m3(dh1, T, H, H, qrow, H, u8(st.slot_tensor(mb, l, L_DH1T)), T, ex + Q_DH1, part, s));
         ZB_TRY(gemm_fp8(q8(T, D.QD, H, qrow, ex + Q_DH1, wo.qt, wo.e, da, D.QD), s));
-        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, apart, T, d.n_heads, d.n_kv_heads, s));
+        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, ascratch, T, d.n_heads, d.n_kv_heads, s));
         ZB_TRY(quantize_e4m3(dqkv, T, D.QKV, D.QKV, qrow, D.QKV, u8(st.slot_tensor(mb, l, L_DQKVT)), T, ex + Q_DQKV,
                              part, s));
         ZB_TRY(gemm_fp8(q8(T, H, D.QKV, qrow, ex + Q_DQKV, wqkv.qt, wqkv.e, dn1, H), s));

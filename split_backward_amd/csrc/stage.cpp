@@ -124,12 +124,30 @@ void Layout::build(const zb_stage_desc& d) {
     scratch_w = 0;
     if (d.kind == ZB_LLAMA) {
         const size_t QD = (size_t)d.n_heads * d.head_dim;
-        // da + delta + the dk/dv partials of split query-head groups
+        // da + delta + the attention backward's scratch (dS^T, and the dk/dv
+        // partials of split query-head groups)
         scratch_b = align_up(T * QD * 2) + align_up((size_t)d.n_heads * T * 4) +
                     align_up(attn_bwd_scratch_bytes(d.tokens, d.n_heads, d.n_kv_heads));
         scratch_w = align_up(rmsnorm_dgamma_scratch_floats(d.tokens, d.hidden) * 4);
     }
     scratch_f = 0;
+    if (d.kind == ZB_MLP_GELU && d.dtype == ZB_BF16) {
+        // split-K partial sums of the products whose tiles would fill little
+        // of the chip (the pass code asks gemm_splitk_factor the same), one
+        // set per pass: F's fc1 [T, ffn] (K = hidden) and fc2 [T, hidden]
+        // (K = ffn), B's products of the same shapes
+        auto need = [&](int N, int K, int epi) {
+            GemmDesc g{};
+            g.M = d.tokens;
+            g.N = N;
+            g.K = K;
+            g.a_kmajor = 1;
+            g.epi = epi;
+            return gemm_splitk_scratch_bytes(g.M, g.N, gemm_splitk_factor(g));
+        };
+        scratch_f = align_up(std::max(need(d.ffn, d.hidden, EPI_GELU_FWD), need(d.hidden, d.ffn, EPI_STORE)));
+        scratch_b = align_up(std::max(need(d.ffn, d.hidden, EPI_GELU_BWD), need(d.hidden, d.ffn, EPI_STORE)));
+    }
     w8_bytes = 0;
     w8_q.clear();
     w8_qt.clear();

@@ -187,8 +187,20 @@ def test_mlp_ragged_parity():
     assert max(r.values()) <= BF16_TOL, r
 
 
+def test_mlp_split_k_ragged_parity():
+    """264 tokens at h=1024, ffn=2048: every product's half-height tiles fill
+    few CUs, so all four run split along K (fc1 and its input gradient in 2
+    slices, fc2 and the stage's input gradient in 4), with a ragged last
+    tile row."""
+    shape = synth.StageShape("mlp", 264, 1024, 2048)
+    gpu, orc, _ = run_both(shape, 2)
+    r = max_rel(gpu, orc)
+    assert max(r.values()) <= BF16_TOL, r
+
+
 def test_mlp_full_width_parity():
-    """GPT MLP at its full shape (s=2048, h=1024, ffn=4096), 2 microbatches."""
+    """GPT MLP at its full shape (s=2048, h=1024, ffn=4096), 2 microbatches
+    (fc2 and the stage's input gradient run split along K)."""
     shape = synth.WORKLOADS["gpt_mlp_h1024"]["shape"]
     gpu, orc, _ = run_both(shape, 2)
     r = max_rel(gpu, orc)
