@@ -233,10 +233,12 @@ __device__ __forceinline__ int xcd_item(int b, int n) {
 constexpr int FQ = 128, FKV = 64, FTHR = 256;
 constexpr int KV_TILE = FKV * D * 2;  // 16 KB
 
-// One query block qb (128 queries) of head h.
+// One query block qb (32 NW queries, a wave's 32 each) of head h.
+template <int NW>
 __device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
                                                bf16_t* __restrict__ o, float* __restrict__ lse, int T, int nq,
                                                int nkv) {
+    constexpr int FQ = 32 * NW;
     const int ld = (nq + 2 * nkv) * D;
     const int grp = h / (nq / nkv);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -261,8 +263,8 @@ __device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_
     const int nkb = (qb * FQ + FQ) / FKV;
     auto dma = [&](int kb) {
         char* st = sm[kb & 1];
-        dma_rows<FKV, 4>(kbase, ld, kb * FKV, T, 0, (lds_void*)st, lane, wave);
-        dma_rows<FKV, 4>(vbase, ld, kb * FKV, T, 0, (lds_void*)(st + KV_TILE), lane, wave);
+        dma_rows<FKV, NW>(kbase, ld, kb * FKV, T, 0, (lds_void*)st, lane, wave);
+        dma_rows<FKV, NW>(vbase, ld, kb * FKV, T, 0, (lds_void*)(st + KV_TILE), lane, wave);
     };
     dma(0);
     for (int kb = 0; kb < nkb; ++kb) {
@@ -375,18 +377,23 @@ __device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_
 
 // Causal query blocks differ in length up to nb-fold: each workgroup runs
 // block nb-1-x and then its mirror x, so every workgroup does the same work
-// and the two resident per CU finish together.  Grid: (nb + 1) / 2 pairs per
-// head, 1-D, items head-major (xcd_item).
-__global__ __launch_bounds__(FTHR, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ o,
-                                                           float* __restrict__ lse, int T, int nq, int nkv) {
+// and the workgroups resident on a CU finish together.  Grid: (nb + 1) / 2
+// pairs per head, 1-D, items head-major (xcd_item).  NW = 8: one workgroup
+// of 256 queries per CU, whose eight waves share each K/V tile (half the
+// DMA per query of two 128-query workgroups); NW = 4 for token counts that
+// are not a multiple of 256.
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
+                                                                   bf16_t* __restrict__ o, float* __restrict__ lse,
+                                                                   int T, int nq, int nkv) {
     __shared__ __attribute__((aligned(1024))) char sm[2][2 * KV_TILE];  // [stage][K | V]
-    const int nb = T / FQ, npair = (nb + 1) / 2;
+    const int nb = T / (32 * NW), npair = (nb + 1) / 2;
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int h = item / npair, x = item % npair;
     const int a = nb - 1 - x, b = x;
     for (int pass = 0; pass < (b < a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();  // every wave is done with the stages
-        attn_fwd_block(pass ? b : a, h, sm, qkv, o, lse, T, nq, nkv);
+        attn_fwd_block<NW>(pass ? b : a, h, sm, qkv, o, lse, T, nq, nkv);
     }
 }
 
@@ -561,19 +568,22 @@ __global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restri
 }
 
 // ===================================================== dk / dv kernel ====
-// Per (key block of 128, KV head).  Each wave owns 32 keys (K rows in
-// registers, V rows in LDS, as B operands).  Sweeps the query heads of the
-// group and the query blocks of 32 rows at or after the diagonal:
+// Per (key block of 32 NW keys, KV head).  Each of the NW waves owns 32 keys
+// (K rows in registers, V rows in LDS, as B operands).  Sweeps the query
+// heads of the group and the query blocks of 32 rows at or after the
+// diagonal:
 //   S = Q K^T, P = exp2(S c - lse2), dP = dO V^T, dS = P (dP - delta),
 //   dV^T += dO^T P,  dK^T += Q^T dS,  and stores dS^T (bf16) for dQ.
-constexpr int BKV = 128, BQB = 32;
+// NW = 4: two workgroups per CU (two waves per SIMD, at most 256 registers
+// per lane, 64.5 KB of LDS each), so one workgroup's softmax, barrier and
+// LDS latency overlap the other's MFMAs.  NW = 8: one workgroup of 256 keys
+// per CU (97 KB of LDS), whose eight waves share each Q and dO block.
+// Double-buffered query blocks suffice with that overlap.
+constexpr int BQB = 32;
 constexpr int Q_TILE = BQB * D * 2;  // 8 KB
-// Two workgroups per CU (two waves per SIMD, at most 256 registers per
-// lane, 64.5 KB of LDS each): one workgroup's softmax, barrier and LDS
-// latency overlap the other's MFMAs.  Double-buffered query blocks suffice
-// with that overlap.
 constexpr int KV_STAGES = 2;
 
+template <int NW>
 __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], char* svt, float (*sl)[2][BQB],
                                                const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dout,
                                                const float* __restrict__ lse, const float* __restrict__ delta,
@@ -589,16 +599,17 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
     const int head0 = (grp * nz + zi) * rep;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
+    constexpr int BKV = 32 * NW;
     const int kw0 = kb * BKV + wave * 32;
     const int key = kw0 + col;
 
-    // K rows of the wave's keys stay in registers; V rows of the block's 128
-    // keys go to LDS once (8 loads per wave, waited for with the first block).
+    // K rows of the wave's keys stay in registers; V rows of the block's keys
+    // go to LDS once (8 loads per wave, waited for with the first block).
     bf16x8 kf[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
         kf[kk] = *reinterpret_cast<const bf16x8*>(qkv + (int64_t)key * ld + nq * D + grp * D + kk * 16 + g * 8);
-    dma_rows<BKV, 4>(qkv + (nq + nkv) * D + grp * D, ld, kb * BKV, T, 0, (lds_void*)svt, lane, wave);
+    dma_rows<BKV, NW>(qkv + (nq + nkv) * D + grp * D, ld, kb * BKV, T, 0, (lds_void*)svt, lane, wave);
     floatx16 dk[4], dv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -613,18 +624,18 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
     const int total = per_head * rep;
 
     // Ring of KV_STAGES query blocks: the DMA of blocks it+1 .. it+KV_STAGES-1
-    // is issued while block it is used.  Every wave issues 6 loads per block
-    // (2 + 2 DMA of Q and dO, and the 32 row statistics of lse and delta,
-    // written identically by each wave's lanes 0..31); blocks past the last
-    // are empty.
+    // is issued while block it is used.  Every wave issues 2 (8 / NW) + 2
+    // loads per block (DMA of Q and dO, and the 32 row statistics of lse and
+    // delta, written identically by each wave's lanes 0..31); blocks past the
+    // last are empty.
     auto fetch = [&](int it) {
         const bool live = it < total;
         const int itc = live ? it : 0;
         const int hh = head0 + itc / per_head;
         const int q0 = (qb0 + itc % per_head) * BQB;
         char* st = sm[it % KV_STAGES];
-        dma_rows<BQB, 4>(qkv + hh * D, ld, q0, T, 0, (lds_void*)st, lane, wave, live);
-        dma_rows<BQB, 4>(dout + hh * D, ldo, q0, T, 0, (lds_void*)(st + Q_TILE), lane, wave, live);
+        dma_rows<BQB, NW>(qkv + hh * D, ld, q0, T, 0, (lds_void*)st, lane, wave, live);
+        dma_rows<BQB, NW>(dout + hh * D, ldo, q0, T, 0, (lds_void*)(st + Q_TILE), lane, wave, live);
         if (lane < BQB) {
             const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (int64_t)hh * T + q0, live ? BQB * 4 : 0);
             const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (int64_t)hh * T + q0, live ? BQB * 4 : 0);
@@ -641,7 +652,7 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
     auto ds_store = [&](int hh, int q0, const u32x4& w0, const u32x4& w1) {
         const __amdgpu_buffer_rsrc_t rds =
             make_rsrc(dst + ((int64_t)hh * nq32 + q0 / 32) * nq32 * (DS_CHUNK / 2), nq32 * DS_CHUNK);
-        const uint32_t off = (uint32_t)((kb * 4 + wave) * DS_CHUNK + (2 * col + g) * 16);
+        const uint32_t off = (uint32_t)((kb * NW + wave) * DS_CHUNK + (2 * col + g) * 16);
         __builtin_amdgcn_raw_buffer_store_b128(w0, rds, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(w1, rds, off + 1024, 0, 0);
     };
@@ -773,24 +784,25 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
 
 // Key block kb sweeps the query blocks at or after it: pairs kb with its
 // mirror so every workgroup does the same work.
-__global__ __launch_bounds__(FTHR, 2) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
-                                                           const bf16_t* __restrict__ dout,
-                                                           const float* __restrict__ lse,
-                                                           const float* __restrict__ delta,
-                                                           bf16_t* __restrict__ dqkv, float* __restrict__ part,
-                                                           bf16_t* __restrict__ dst, int T, int nq, int nkv,
-                                                           int nz) {
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
+                                                                   const bf16_t* __restrict__ dout,
+                                                                   const float* __restrict__ lse,
+                                                                   const float* __restrict__ delta,
+                                                                   bf16_t* __restrict__ dqkv, float* __restrict__ part,
+                                                                   bf16_t* __restrict__ dst, int T, int nq, int nkv,
+                                                                   int nz) {
     __shared__ __attribute__((aligned(1024))) char sm[KV_STAGES][2 * Q_TILE];  // [stage][Q | dO]
-    __shared__ __attribute__((aligned(1024))) char svt[BKV * D * 2];           // V rows of the block
+    __shared__ __attribute__((aligned(1024))) char svt[32 * NW * D * 2];       // V rows of the block
     __shared__ float sl[KV_STAGES][2][BQB];                                     // [stage][lse | delta]
-    const int nb = T / BKV, npair = (nb + 1) / 2;
+    const int nb = T / (32 * NW), npair = (nb + 1) / 2;
     // 1-D grid of npair x nz x nkv items, KV-head-major (xcd_item)
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int x = item % npair, zi = (item / npair) % nz, grp = item / (npair * nz);
     const int a = x, b = nb - 1 - x;  // a: the longer sweep
     for (int pass = 0; pass < (b > a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();
-        attn_dkv_block(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, part, dst, T, nq, nkv, grp, zi, nz);
+        attn_dkv_block<NW>(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, part, dst, T, nq, nkv, grp, zi, nz);
     }
 }
 
@@ -817,14 +829,19 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(const float* __res
 
 bool shapes_ok(int T, int nq, int nkv) { return T > 0 && T % FQ == 0 && nq > 0 && nkv > 0 && nq % nkv == 0; }
 
+// Waves per dk/dv workgroup: 8 (256 keys) when the key blocks tile T.
+int dkv_waves(int T) { return T % 256 == 0 ? 8 : 4; }
+
 // Query-head subsets per KV head for the dk/dv kernel: the smallest divisor
-// of the group size that gives at least 512 workgroups (two per CU on a
-// 256-CU part).  A group of 8 query heads per KV head (Llama-70B: 8 KV heads,
-// 16 key-block pairs) would otherwise run 128 workgroups.
+// of the group size that fills a 256-CU part (512 workgroups of 128 keys,
+// two per CU, or 256 of 256 keys).  A group of 8 query heads per KV head
+// (Llama-70B: 8 KV heads, 8 key-block pairs of 256) would otherwise run 64
+// workgroups.
 int dkv_split(int T, int nq, int nkv) {
-    const int rep = nq / nkv, wgs = (T / BKV + 1) / 2 * nkv;
+    const int nw = dkv_waves(T);
+    const int rep = nq / nkv, wgs = (T / (32 * nw) + 1) / 2 * nkv;
     for (int z = 1; z < rep; ++z)
-        if (rep % z == 0 && wgs * z >= 512) return z;
+        if (rep % z == 0 && wgs * z >= 2048 / nw) return z;
     return rep;
 }
 
@@ -834,7 +851,10 @@ size_t ds_bytes(int T, int nq) { return ((size_t)nq * T * T * 2 + 255) / 256 * 2
 
 int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s) {
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3((T / FQ + 1) / 2 * nq), dim3(FTHR), 0, s, qkv, o, lse, T, nq, nkv);
+    if (T % 256 == 0)
+        hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3((T / 256 + 1) / 2 * nq), dim3(512), 0, s, qkv, o, lse, T, nq, nkv);
+    else
+        hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3((T / 128 + 1) / 2 * nq), dim3(256), 0, s, qkv, o, lse, T, nq, nkv);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
@@ -857,8 +877,12 @@ int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf1
     hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, s, o, dout, delta, T, nq);
     ZB_HIP(hipGetLastError());
     // dK, dV (or their per-subset partials) and dS^T
-    hipLaunchKernelGGL(attn_dkv_kernel, dim3((T / BKV + 1) / 2 * nkv * z), dim3(FTHR), 0, s, qkv, dout, lse, delta,
-                       dqkv, part, dst, T, nq, nkv, z);
+    if (dkv_waves(T) == 8)
+        hipLaunchKernelGGL(attn_dkv_kernel<8>, dim3((T / 256 + 1) / 2 * nkv * z), dim3(512), 0, s, qkv, dout, lse,
+                           delta, dqkv, part, dst, T, nq, nkv, z);
+    else
+        hipLaunchKernelGGL(attn_dkv_kernel<4>, dim3((T / 128 + 1) / 2 * nkv * z), dim3(256), 0, s, qkv, dout, lse,
+                           delta, dqkv, part, dst, T, nq, nkv, z);
     ZB_HIP(hipGetLastError());
     if (z > 1) {
         const int64_t n4 = (int64_t)T * nkv * 2 * D / 4;

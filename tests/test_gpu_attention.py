@@ -2,11 +2,12 @@
 
 S and dP are computed once, by the kernel that owns a key block; it forms
 dK and dV and stores dS^T, from which the dq kernel then forms dQ = dS K.
-Checked on one-layer stages whose token counts span several 128-key blocks,
-an odd number of them (the middle block pairs with itself in the mirrored
-launch) and an even one, with and without grouped-query heads (the grouped
-shapes split a KV head's query heads over workgroups and add their partial
-dK, dV in a fixed order):
+Checked on one-layer stages whose token counts span several key blocks: 640
+tokens (128-key and 128-query blocks, an odd number of them, so the middle
+block pairs with itself in the mirrored launch) and 256, 512 and 1024 (the
+256-key and 256-query workgroups), with and without grouped-query heads (the
+grouped shapes split a KV head's query heads over workgroups and add their
+partial dK, dV in a fixed order):
 
 * every head's dq and every KV head's dk and dv against the fp64 oracle
   ("Zero-Bubble Pipeline Parallelism Guide for LLMs", "Core Innovation 1":
@@ -34,7 +35,7 @@ pytestmark = pytest.mark.gpu
 D = 128
 
 
-@pytest.mark.parametrize("T,nq,nkv", [(640, 2, 2), (640, 2, 1), (1024, 4, 2)])
+@pytest.mark.parametrize("T,nq,nkv", [(640, 2, 2), (640, 2, 1), (1024, 4, 2), (512, 2, 2), (256, 2, 1)])
 def test_attention_backward_every_head_and_deterministic(T, nq, nkv):
     shape = synth.StageShape("llama", T, 256, 384, n_layers=1, n_heads=nq, n_kv_heads=nkv, head_dim=D)
     weights = synth.make_weights(shape)
