@@ -431,3 +431,49 @@ def test_sgd_step_special_cases():
     # a step against the gradient lowers a quadratic loss sum(w^2)/2 (dW = w)
     ww = od.bf16_round(rng.standard_normal(4096).astype(np.float32))
     assert np.sum(od.sgd_step(ww, ww.astype(np.float32), 0.1, "bf16") ** 2) < np.sum(ww ** 2)
+
+
+def test_sgd_step_rounds_the_product_to_float32_first():
+    """A case built by hand where the stage's reading (float32 product, then
+    float32 difference, then bf16) and an exact or fp64 formulation part:
+    lr = 1 + 2^-12 and dW = 2^-9 (1 - 2^-12 + 2^-24), both float32 values,
+    have the exact product 2^-9 + 2^-45, which float32 rounds to 2^-9.  Then
+    w - t = 1 - 2^-9 exactly, a bf16 tie between 1 - 2^-8 (odd) and 1.0
+    (even): 1.0.  Rounded once from the exact 1 - 2^-9 - 2^-45 it would be
+    1 - 2^-8."""
+    lr = 1.0 + 2.0 ** -12
+    dw = np.array([2.0 ** -9 * (1.0 - 2.0 ** -12 + 2.0 ** -24)])
+    assert float(np.float32(lr)) == lr and float(np.float32(dw[0])) == dw[0]
+    assert od.sgd_step(np.array([1.0]), dw, lr, "bf16")[0] == 1.0
+    exact = 1.0 - lr * dw[0]
+    assert exact == 1.0 - 2.0 ** -9 - 2.0 ** -45
+    # float32 cannot hold the exact difference (it rounds it to the tie), so
+    # the single-rounding formulation is checked in float64 against the bf16
+    # grid directly: the exact value lies below the midpoint 1 - 2^-9, so its
+    # nearest bf16 is 1 - 2^-8
+    lo, hi = 1.0 - 2.0 ** -8, 1.0
+    assert abs(exact - lo) < abs(exact - hi)
+    # the fp32 formulation's difference for the f32 dtype
+    assert od.sgd_step(np.array([1.0]), dw, lr, "f32")[0] == 1.0 - 2.0 ** -9
+
+
+def test_sgd_step_f32_rounds_the_product_exact_arithmetic():
+    """fp32 stage, w = 1: near cancellation the product's float32 rounding
+    error is far above the spacing of the difference, so the reading
+    (product rounded to float32, then an exact difference) and a formulation
+    that rounds only the difference give different float32 results.  The
+    expected value is worked out in exact rational arithmetic:
+    lr dW = 1 - 2^-12 + 2^-20 + 2^-21 - 2^-23 - 2^-31 + 2^-33 + 2^-41, whose
+    float32 (spacing 2^-24 in [1/2, 1)) drops the last three terms."""
+    from fractions import Fraction as Fr
+    lr = 1.0 + 2.0 ** -12 + 2.0 ** -20
+    dw = 1.0 - 2.0 ** -11 + 2.0 ** -21
+    exact = Fr(lr) * Fr(dw)
+    assert exact == 1 - Fr(2) ** -12 + Fr(2) ** -20 + Fr(2) ** -21 - Fr(2) ** -23 - Fr(2) ** -31 + Fr(2) ** -33 + Fr(2) ** -41
+    t32 = Fr(round(exact / Fr(2) ** -24)) * Fr(2) ** -24
+    assert t32 == 1 - Fr(2) ** -12 + Fr(2) ** -20 + Fr(2) ** -21 - Fr(2) ** -23
+    want = 1 - t32  # exactly representable: the difference of two nearby float32 values
+    got = od.sgd_step(np.array([1.0]), np.array([dw]), lr, "f32")[0]
+    assert Fr(got) == want
+    # rounding only the difference (from the exact product) lands elsewhere
+    assert Fr(float(np.float32(float(1 - exact)))) != want
