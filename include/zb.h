@@ -98,7 +98,10 @@ typedef struct {
 int32_t zb_stage_num_weights(const zb_stage_desc* desc);
 
 /* Bytes of device workspace zb_stage_create needs: the stash ring
- * (ring_slots slots) plus per-pass scratch.  Returns 0 for an invalid desc
+ * (ring_slots slots) plus per-pass scratch.  The B scratch of a Llama stage
+ * includes the attention backward's dS^T, n_heads * tokens^2 bf16 values
+ * (1.07 GB at 32 heads and 4096 tokens); GPT-MLP stages add fp32 split-K
+ * partial sums to the F and B scratch.  Returns 0 for an invalid desc
  * (zb_last_error says why). */
 size_t zb_stage_workspace_bytes(const zb_stage_desc* desc);
 
