@@ -238,12 +238,12 @@ template <int NW>
 __device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
                                                bf16_t* __restrict__ o, float* __restrict__ lse, int T, int nq,
                                                int nkv) {
-    constexpr int FQ = 32 * NW;
+    constexpr int QB = 32 * NW;  // queries per block
     const int ld = (nq + 2 * nkv) * D;
     const int grp = h / (nq / nkv);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
-    const int qw0 = qb * FQ + wave * 32;
+    const int qw0 = qb * QB + wave * 32;
     const int q = qw0 + col;
     const bf16_t* kbase = qkv + nq * D + grp * D;
     const bf16_t* vbase = qkv + (nq + nkv) * D + grp * D;
@@ -260,7 +260,7 @@ __device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_
     const TrBases trb = tr_bases(lane);
     const float c = LOG2E / sqrtf((float)D);
 
-    const int nkb = (qb * FQ + FQ) / FKV;
+    const int nkb = (qb * QB + QB) / FKV;
     auto dma = [&](int kb) {
         char* st = sm[kb & 1];
         dma_rows<FKV, NW>(kbase, ld, kb * FKV, T, 0, (lds_void*)st, lane, wave);
