@@ -77,6 +77,17 @@ __device__ __forceinline__ bf16x8 acc_half_to_bf16(const floatx16& c, int half) 
     return v;
 }
 
+// x as three bf16 terms hi + mid + lo whose sum is x to within fp32 rounding
+// (slots 0..2; the rest zero).
+__device__ __forceinline__ bf16x8 split3(float x) {
+    const __bf16 hi = (__bf16)x;
+    const float r1 = x - (float)hi;
+    const __bf16 mid = (__bf16)r1;
+    const __bf16 lo = (__bf16)(r1 - (float)mid);
+    const __bf16 z = (__bf16)0.f;
+    return bf16x8{hi, mid, lo, z, z, z, z, z};
+}
+
 // ---- [rows][128] tiles in LDS ---------------------------------------------
 // 256-byte rows of 16 chunks (16 B); chunk c of row r sits at c ^ swz(r).
 // With b_i the bits of r, swz = (b0^b1^b3, b0, b1, b2) is a bijection of the
@@ -617,7 +628,13 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
         dv[i] = zero16();
     }
     const float c = LOG2E / sqrtf((float)D);
+    const float inv_c = 1.f / c;
     const TrBases trb = tr_bases(lane);
+    // B operand that adds k = 0..2 of an A fragment into every column: ones
+    // at k 0..2 (lane group 0), zeros elsewhere.
+    bf16x8 ones3;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones3[i] = (__bf16)((g == 0 && i < 3) ? 1.f : 0.f);
     const int qb0 = (kb * BKV) / BQB;
     const int nqb = T / BQB;
     const int per_head = nqb - qb0;
@@ -675,7 +692,21 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
         const lds_void* ot = (const lds_void*)(sm[stg] + Q_TILE);
         // Fragment reads as asm (explicit waits): the compiler would otherwise
         // wait for the DMA of the next block, issued just above, before them.
-        floatx16 s = zero16(), dp = zero16();
+        // The row statistics enter as the accumulators' initial values: an MFMA
+        // of an A fragment holding query row l's value in k = 0..2 (lane l,
+        // split3) with ones3 writes -lse2/c into every key column of S's row
+        // l and -delta into dP's, in the accumulator's own row order, so no
+        // lane gathers its rows' statistics.
+        floatx16 s, dp;
+        {
+            const uint32_t la = (uint32_t)(uintptr_t)&sl[stg][0][0] + col * 4;
+            float ls, ds;
+            asm volatile("ds_read_b32 %0, %1" : "=v"(ls) : "v"(la));
+            asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(ds) : "v"(la), "i"(BQB * 4));
+            lds_wait_keep<0>(ls, ds);
+            s = mfma(split3(-ls * inv_c), ones3, zero16());
+            dp = mfma(split3(-ds), ones3, zero16());
+        }
         {
             const uint32_t qa = (uint32_t)(uintptr_t)qt, va = (uint32_t)(uintptr_t)svt + wave * 32 * 256;
             // Q, dO and V row fragments of k step kk + 1 are read while step kk multiplies
@@ -701,25 +732,14 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
             }
         }
         const bool diag = (q0 < kw0 + 31);
-        // row statistics of the accumulator rows (r/4)*8 + 4g + r%4, 16-byte
-        // reads issued as asm (see frag_tr), two row groups at a time
-        const uint32_t lb = (uint32_t)(uintptr_t)&sl[stg][0][0] + g * 16;
-        const uint32_t db = (uint32_t)(uintptr_t)&sl[stg][1][0] + g * 16;
+        // accumulator row of slot r: query (r/4)*8 + 4g + r%4 of the block
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            floatx4 lsv, dsv;
-            asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(lsv) : "v"(lb), "i"(rb * 32));
-            asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dsv) : "v"(db), "i"(rb * 32));
-            lds_wait_keep<0>(lsv, dsv);
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int r = rb * 4 + r4;
-                const int qr = rb * 8 + g * 4 + r4;
-                float p = fast_exp2(fmaf(s[r], c, -lsv[r4]));
-                if (diag && key > q0 + qr) p = 0.f;
-                s[r] = p;
-                dp[r] = p * (dp[r] - dsv[r4]);
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int qr = (r >> 2) * 8 + g * 4 + (r & 3);
+            float p = fast_exp2(s[r] * c);  // s = S - lse2/c
+            if (diag && key > q0 + qr) p = 0.f;
+            s[r] = p;
+            dp[r] = p * dp[r];  // dp = dP - delta
         }
         const bf16x8 p0 = acc_half_to_bf16(s, 0), p1 = acc_half_to_bf16(s, 1);
         const bf16x8 s0 = acc_half_to_bf16(dp, 0), s1 = acc_half_to_bf16(dp, 1);
