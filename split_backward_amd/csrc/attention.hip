@@ -46,6 +46,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 constexpr uint32_t OOB = 0x80000000u;
+constexpr int CPOL_NT = 2;  // cache-policy operand of buffer loads and stores: non-temporal
 
 __device__ __forceinline__ floatx16 zero16() {
     floatx16 z;
@@ -503,7 +504,8 @@ __device__ __forceinline__ void attn_dq_block(int qb, int h, DqSmem& sm, const b
         lds_char* dstl = (lds_char*)sm.s[kb % DQ_S_STAGES] + wave * 2 * DS_CHUNK;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dstl + i * 1024), 16, i * 1024 + lane * 16, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dstl + i * 1024), 16, i * 1024 + lane * 16, 0, 0,
+                                                     CPOL_NT);  // read once: non-temporal
     };
     // Issue order K(0) S(0) S(1), then per iteration kb: K(kb+1) S(kb+2).  At
     // the top of iteration kb only S(kb+1) (4 loads) may still be in flight.
@@ -670,8 +672,10 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
         const __amdgpu_buffer_rsrc_t rds =
             make_rsrc(dst + ((int64_t)hh * nq32 + q0 / 32) * nq32 * (DS_CHUNK / 2), nq32 * DS_CHUNK);
         const uint32_t off = (uint32_t)((kb * NW + wave) * DS_CHUNK + (2 * col + g) * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(w0, rds, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(w1, rds, off + 1024, 0, 0);
+        // non-temporal: left dirty in the caches, the 537 MB (Llama-7B shape)
+        // would still be written back while the dq kernel reads it
+        __builtin_amdgcn_raw_buffer_store_b128(w0, rds, off, 0, CPOL_NT);
+        __builtin_amdgcn_raw_buffer_store_b128(w1, rds, off + 1024, 0, CPOL_NT);
     };
     // Each iteration ends with its 2 dS^T stores, so the DMA of the next
     // block is waited for with those 2 stores still in flight (vector memory
