@@ -72,6 +72,11 @@ struct GemmDesc {
     // read on the device; the epilogue sees acc * 2^(*ea + *eb).
     const int32_t* ea;
     const int32_t* eb;
+    // fp8 stages, the SwiGLU epilogues only: per-wave max|output| (of the
+    // tensor the next product quantizes: C2 = silu(g) u for EPI_SWIGLU_FWD,
+    // C = [dg | du] for EPI_SWIGLU_BWD, as the bf16 values stored) to
+    // amax[4 * workgroup + wave] of each launch; null elsewhere.
+    float* amax;
 };
 
 int32_t gemm_bf16(const GemmDesc& d, hipStream_t s);
@@ -101,7 +106,9 @@ int32_t gemm_bf16_group_segmented(const GemmDesc* ds, int n, hipStream_t s, bool
 // C (epi)= (A . B^T) * 2^(ea + eb) with A [M, K], B [N, K] E4M3 codes, both
 // K-contiguous (a_kmajor = b_kmajor = 1), K a multiple of 128, leading
 // dimensions multiples of 16 bytes; any epilogue of the bf16 kernel.
-int32_t gemm_fp8(const GemmDesc& d, hipStream_t s);
+// With d.amax set, *amax_n = the number of partial maxima written there; a
+// product that would write more than amax_cap is rejected before any launch.
+int32_t gemm_fp8(const GemmDesc& d, hipStream_t s, int* amax_n = nullptr, int amax_cap = 0);
 // Up to 16 such products of one epilogue in one launch.
 int32_t gemm_fp8_group(const GemmDesc* ds, int n, hipStream_t s);
 
@@ -114,6 +121,13 @@ int32_t gemm_fp8_group(const GemmDesc* ds, int n, hipStream_t s);
 constexpr int AMAX_PARTS = 512;
 int32_t quantize_e4m3(const bf16_t* x, int rows, int cols, int64_t ld, uint8_t* q, int64_t ldq, uint8_t* qt,
                       int64_t ldqt, int32_t* e_out, float* part, hipStream_t s);
+// The same for a tensor whose producer already wrote partial maxima of
+// |x| (part[0..nparts), every element of x covered by one of them): one
+// small kernel reduces them into *amax, then the codes; no pass over x for
+// its maximum.
+int32_t quantize_e4m3_from_partials(const bf16_t* x, int rows, int cols, int64_t ld, uint8_t* q, int64_t ldq,
+                                    uint8_t* qt, int64_t ldqt, int32_t* e_out, const float* part, int nparts,
+                                    float* amax, hipStream_t s);
 
 // ------------------------------------------------- elementwise / norms ----
 int32_t fill_f32(float* p, size_t n, float v, hipStream_t s);
@@ -141,12 +155,15 @@ int32_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
 int32_t transpose_bf16(const bf16_t* src, bf16_t* dst, int rows, int cols, hipStream_t s);
 // n = RMS(x) * g, r = 1/sqrt(mean(x^2)+eps) per row; x, n bf16 [T, H]; r f32 [T].
 // xcopy (optional): receives a copy of x.
+// amax_rows (optional): max|n| of each row (the stored bf16 values), T floats.
 int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps,
-                    hipStream_t s, bf16_t* xcopy = nullptr);
+                    hipStream_t s, bf16_t* xcopy = nullptr, float* amax_rows = nullptr);
 // dx = dres + r * (dn*g - xhat * mean(dn*g*xhat)), xhat = x*r.
 // rescopy (optional): receives a copy of dres.
+// amax_rows (optional): max|dx| of each row (the stored bf16 values), T floats.
 int32_t rmsnorm_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn,
-                    const bf16_t* dres, bf16_t* dx, int T, int H, hipStream_t s, bf16_t* rescopy = nullptr);
+                    const bf16_t* dres, bf16_t* dx, int T, int H, hipStream_t s, bf16_t* rescopy = nullptr,
+                    float* amax_rows = nullptr);
 // dgamma[h] += sum_t dn[t,h] * x[t,h] * r[t]   (partials in scratch, fixed order)
 int32_t rmsnorm_dgamma(const bf16_t* x, const float* r, const bf16_t* dn, float* dgamma,
                        float* scratch, int T, int H, hipStream_t s);

@@ -18,6 +18,9 @@
 //                         transposed [cols][rows] (through LDS), so that a
 //                         product's K index is contiguous whichever operand
 //                         the tensor becomes.
+// Where the kernel that wrote x already produced partial maxima (the RMSNorm
+// kernels per row, the SwiGLU GEMM epilogues per wave), amax_reduce_kernel
+// folds them into one value instead of the pass over x.
 #include <algorithm>
 #include <cmath>
 
@@ -66,6 +69,23 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const bf16_t* __restr
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// max of n partial maxima into *out (one workgroup; max is exact, so the
+// order does not matter)
+__global__ __launch_bounds__(1024) void amax_reduce_kernel(const float* __restrict__ part, int n,
+                                                          float* __restrict__ out) {
+    __shared__ float red[16];
+    float m = 0.f;
+    for (int i = threadIdx.x; i < n; i += 1024) m = fmaxf(m, part[i]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = red[0];
+        for (int i = 1; i < 16; ++i) t = fmaxf(t, red[i]);
+        *out = t;
+    }
 }
 
 // Smallest e with amax <= 448 * 2^e: amax = f * 2^x with f in [0.5, 1), so
@@ -162,6 +182,24 @@ int32_t quantize_e4m3(const bf16_t* x, int rows, int cols, int64_t ld, uint8_t* 
     ZB_HIP(hipGetLastError());
     hipLaunchKernelGGL(quantize_kernel, dim3((cols + QT - 1) / QT, (rows + QT - 1) / QT), dim3(256), 0, s, x, rows,
                        cols, ld, part, nparts, e_out, q, ldq, qt, ldqt);
+    ZB_HIP(hipGetLastError());
+    return ZB_OK;
+}
+
+int32_t quantize_e4m3_from_partials(const bf16_t* x, int rows, int cols, int64_t ld, uint8_t* q, int64_t ldq,
+                                    uint8_t* qt, int64_t ldqt, int32_t* e_out, const float* part, int nparts,
+                                    float* amax, hipStream_t s) {
+    if (!x || !e_out || !part || !amax || nparts < 1 || rows < 1 || cols < 1 || (!q && !qt))
+        return fail(ZB_EINVAL, "quantize_e4m3_from_partials: bad argument");
+    if (rows % 16 || cols % 16 || ld % 8 || (q && ldq % 16) || (qt && ldqt % 16) || ld < cols || (q && ldq < cols) ||
+        (qt && ldqt < rows))
+        return fail(ZB_EINVAL, "quantize_e4m3: rows and cols must be multiples of 16, leading dimensions aligned");
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(qt)) & 15)
+        return fail(ZB_EINVAL, "quantize_e4m3: pointers must be 16-byte aligned");
+    hipLaunchKernelGGL(amax_reduce_kernel, dim3(1), dim3(1024), 0, s, part, nparts, amax);
+    ZB_HIP(hipGetLastError());
+    hipLaunchKernelGGL(quantize_kernel, dim3((cols + QT - 1) / QT, (rows + QT - 1) / QT), dim3(256), 0, s, x, rows,
+                       cols, ld, amax, 1, e_out, q, ldq, qt, ldqt);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }

@@ -230,6 +230,7 @@ __device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rc
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // Four floats -> four bf16 (round to nearest even), two per conversion instruction.
 __device__ __forceinline__ u32x2 pack_bf16x4(const float (&f)[4]) {
     return u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[0], f[1]}, bf16x2_t)),
@@ -293,7 +294,9 @@ __device__ __forceinline__ void stage_block(floatx4 (&acc)[MB][8], int mi, float
             for (int i = 0; i < 4; ++i) stage[(h * 16 + kg * 4 + i) * P + ni * 16 + r16] = acc[2 * mi + h][ni][i];
 }
 
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM, class ACC>
+// TRACK (the fp8 kernels): the SwiGLU epilogues also leave the per-wave
+// maxima of their quantized output at d.amax when it is set.
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TBM, bool TRACK = false, class ACC>
 __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans& sp, ACC& acc, int m0, int n0,
                                               char* smem) {
     constexpr bool PAIRED = (EPI == EPI_SWIGLU_FWD);
@@ -390,6 +393,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans&
     }
     constexpr bool HAS_C2 = EPI == EPI_GELU_FWD || PAIRED;
     const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(d.C2, HAS_C2 ? sp.c2 : 0u);
+    // SwiGLU epilogues: the largest |value| of the quantized output, as bf16
+    // magnitudes (sign bit cleared; for them integer order is value order)
+    // of the packed words stored, two per register; rows and columns outside
+    // the matrix hold zeros
+    u16x2 mxb = {0, 0};
+    auto track = [&](const u32x2& w) {
+        mxb = __builtin_elementwise_max(mxb, __builtin_bit_cast(u16x2, w[0] & 0x7fff7fffu));
+        mxb = __builtin_elementwise_max(mxb, __builtin_bit_cast(u16x2, w[1] & 0x7fff7fffu));
+    };
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
         const int rbase = m0 + wm * (TBM / 2) + mi * 32;
@@ -422,13 +434,19 @@ __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans&
                     }
                 }
                 const int64_t ec = (int64_t)row * d.ldc + gcol;
-                __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(o), rc, ok ? (uint32_t)(ec * 2) : OOB, 0, 0);
+                const u32x2 wo = pack_bf16x4(o);
+                __builtin_amdgcn_raw_buffer_store_b64(wo, rc, ok ? (uint32_t)(ec * 2) : OOB, 0, 0);
                 if (EPI == EPI_GELU_FWD)
                     __builtin_amdgcn_raw_buffer_store_b64(
                         pack_bf16x4(o2), rc2, ok ? (uint32_t)(((int64_t)row * d.ldc2 + gcol) * 2) : OOB, 0, 0);
-                if (EPI == EPI_SWIGLU_BWD)
-                    __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(o2), rc, ok ? (uint32_t)((ec + d.half_n) * 2) : OOB, 0,
-                                                          0);
+                if constexpr (EPI == EPI_SWIGLU_BWD) {
+                    const u32x2 wo2 = pack_bf16x4(o2);
+                    __builtin_amdgcn_raw_buffer_store_b64(wo2, rc, ok ? (uint32_t)((ec + d.half_n) * 2) : OOB, 0, 0);
+                    if constexpr (TRACK) {
+                        track(wo);
+                        track(wo2);
+                    }
+                }
             }
         } else {
             // paired SwiGLU forward: staged columns 0..63 are gate, 64..127 up
@@ -453,9 +471,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmDesc& d, const BufSpans&
                 const int64_t ec = (int64_t)row * d.ldc + gcol;
                 __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(og), rc, ok ? (uint32_t)(ec * 2) : OOB, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(ou), rc, ok ? (uint32_t)((ec + d.half_n) * 2) : OOB, 0, 0);
+                const u32x2 ws = pack_bf16x4(os);
                 __builtin_amdgcn_raw_buffer_store_b64(
-                    pack_bf16x4(os), rc2, ok ? (uint32_t)(((int64_t)row * d.ldc2 + gcol) * 2) : OOB, 0, 0);
+                    ws, rc2, ok ? (uint32_t)(((int64_t)row * d.ldc2 + gcol) * 2) : OOB, 0, 0);
+                if constexpr (TRACK && EPI == EPI_SWIGLU_FWD) track(ws);
             }
+        }
+    }
+    if constexpr (TRACK && (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD)) {
+        if (d.amax) {
+            uint32_t m = mxb[0] > mxb[1] ? mxb[0] : mxb[1];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const uint32_t t = (uint32_t)__shfl_xor((int)m, o, 64);
+                m = t > m ? t : m;
+            }
+            if (lane == 0) d.amax[blockIdx.x * (NTHR / 64) + wave] = __uint_as_float(m << 16);
         }
     }
 }
@@ -1136,7 +1167,7 @@ __device__ __forceinline__ void gemm_f8_tile(const GemmDesc& d, int tm, int tn, 
         for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[mi][ni][e] *= sc;
-    gemm_epilogue<true, true, EPI, TBM>(d, sp, acc, m0, n0, smem);
+    gemm_epilogue<true, true, EPI, TBM, true>(d, sp, acc, m0, n0, smem);
 }
 
 // LDS of one workgroup: five 32 KB slots for products with a K-contiguous A
@@ -1468,9 +1499,11 @@ int32_t launch_f8(const GemmDesc& d, hipStream_t s, int tiles_m, int tiles_n, in
 }
 }  // namespace
 
-int32_t gemm_fp8(const GemmDesc& d, hipStream_t s) {
+int32_t gemm_fp8(const GemmDesc& d, hipStream_t s, int* amax_n, int amax_cap) {
     if (d.M <= 0 || d.N <= 0 || d.K <= 0) return fail(ZB_EINVAL, "gemm_fp8: empty shape");
     if (d.epi == EPI_SWIGLU_FWD && d.half_n <= 0) return fail(ZB_EINVAL, "gemm_fp8: bad SwiGLU pairing");
+    if (d.amax && (d.epi != EPI_SWIGLU_FWD && d.epi != EPI_SWIGLU_BWD))
+        return fail(ZB_EINVAL, "gemm_fp8: output maxima only from the SwiGLU epilogues");
     const V2Plan p = plan_f8(d);
     if (!p.ok)
         return fail(ZB_EINVAL, "gemm_fp8: needs K-contiguous operands, K a multiple of 128, leading dimensions multiples of 16, "
@@ -1478,11 +1511,23 @@ int32_t gemm_fp8(const GemmDesc& d, hipStream_t s) {
     const int tiles_m_half = (d.M + BM / 2 - 1) / (BM / 2);
     const TileSplit t = getenv("ZB_GEMM_FULL_TILES") ? TileSplit{p.tiles_n}
                                                      : split_columns(p.tiles_m, p.tiles_n, tiles_m_half, cu_count());
+    constexpr int WAVES = NTHR / 64;  // partial maxima per workgroup
+    if (d.amax && (int64_t)(p.tiles_m * t.n_full + tiles_m_half * (p.tiles_n - t.n_full)) * WAVES > amax_cap)
+        return fail(ZB_EINVAL, "gemm_fp8: more partial maxima than amax_cap");
+    int n_parts = 0;
     if (t.n_full > 0) {
         const int32_t rc = launch_f8<BM>(d, s, p.tiles_m, t.n_full, 0, p.sp);
         if (rc != ZB_OK) return rc;
+        n_parts += p.tiles_m * t.n_full * WAVES;
     }
-    if (t.n_full < p.tiles_n) return launch_f8<BM / 2>(d, s, tiles_m_half, p.tiles_n - t.n_full, t.n_full, p.sp);
+    if (t.n_full < p.tiles_n) {
+        GemmDesc h = d;  // the half-height launch writes its maxima after the first launch's
+        if (h.amax) h.amax += n_parts;
+        const int32_t rc = launch_f8<BM / 2>(h, s, tiles_m_half, p.tiles_n - t.n_full, t.n_full, p.sp);
+        if (rc != ZB_OK) return rc;
+        n_parts += tiles_m_half * (p.tiles_n - t.n_full) * WAVES;
+    }
+    if (amax_n) *amax_n = d.amax ? n_parts : 0;
     return ZB_OK;
 }
 

@@ -26,6 +26,22 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return t;
 }
 
+// max over the workgroup, written by thread 0 to *out as the bf16 value it
+// rounds to (rounding is monotonic, so that is the largest stored |value|)
+__device__ __forceinline__ void block_max_to(float v, float* red, float* out) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = red[0];
+#pragma unroll
+        for (int i = 1; i < RT / 64; ++i) t = fmaxf(t, red[i]);
+        *out = __uint_as_float((uint32_t)f2bf(t) << 16);
+    }
+}
+
 __device__ __forceinline__ void unpack8(const u32x4 v, float (&f)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -42,11 +58,13 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
 
 // One workgroup per row; H is a multiple of 8 and at most 8 * RT * 4.
 // xcopy (optional): a copy of x written as it is read (the stage stashes
-// its input this way instead of with a separate copy).
+// its input this way instead of with a separate copy).  amax (optional):
+// max|n| of the row at amax[row].
 template <int CH>
 __global__ __launch_bounds__(RT) void rms_fwd_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ g,
                                                      bf16_t* __restrict__ n, float* __restrict__ r,
-                                                     bf16_t* __restrict__ xcopy, int H, float eps) {
+                                                     bf16_t* __restrict__ xcopy, float* __restrict__ amax, int H,
+                                                     float eps) {
     __shared__ float red[RT / 64];
     const int64_t row = blockIdx.x;
     const bf16_t* xr = x + row * H;
@@ -66,6 +84,7 @@ __global__ __launch_bounds__(RT) void rms_fwd_kernel(const bf16_t* __restrict__ 
     const float tot = block_sum(ss, red);
     const float rr = 1.f / sqrtf(tot / float(H) + eps);
     if (threadIdx.x == 0) r[row] = rr;
+    float mx = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int col = (threadIdx.x + c * RT) * 8;
@@ -73,18 +92,23 @@ __global__ __launch_bounds__(RT) void rms_fwd_kernel(const bf16_t* __restrict__ 
             float gg[8], o[8];
             unpack8(*reinterpret_cast<const u32x4*>(g + col), gg);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = v[c][i] * rr * gg[i];
+            for (int i = 0; i < 8; ++i) {
+                o[i] = v[c][i] * rr * gg[i];
+                mx = fmaxf(mx, fabsf(o[i]));
+            }
             *reinterpret_cast<u32x4*>(n + row * H + col) = pack8(o);
         }
     }
+    if (amax) block_max_to(mx, red, amax + row);
 }
 
-// rescopy (optional): a copy of dres written as it is read.
+// rescopy (optional): a copy of dres written as it is read.  amax
+// (optional): max|dx| of the row at amax[row].
 template <int CH>
 __global__ __launch_bounds__(RT) void rms_bwd_kernel(const bf16_t* __restrict__ x, const float* __restrict__ r,
                                                      const bf16_t* __restrict__ g, const bf16_t* __restrict__ dn,
                                                      const bf16_t* __restrict__ dres, bf16_t* __restrict__ dx,
-                                                     bf16_t* __restrict__ rescopy, int H) {
+                                                     bf16_t* __restrict__ rescopy, float* __restrict__ amax, int H) {
     __shared__ float red[RT / 64];
     const int64_t row = blockIdx.x;
     const float rr = r[row];
@@ -107,6 +131,7 @@ __global__ __launch_bounds__(RT) void rms_bwd_kernel(const bf16_t* __restrict__ 
         }
     }
     const float mean = block_sum(dot, red) / float(H);
+    float mx = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int col = (threadIdx.x + c * RT) * 8;
@@ -116,10 +141,14 @@ __global__ __launch_bounds__(RT) void rms_bwd_kernel(const bf16_t* __restrict__ 
             if (rescopy) *reinterpret_cast<u32x4*>(rescopy + row * H + col) = raw;
             unpack8(raw, res);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = res[i] + rr * (dg[c][i] - xh[c][i] * mean);
+            for (int i = 0; i < 8; ++i) {
+                o[i] = res[i] + rr * (dg[c][i] - xh[c][i] * mean);
+                mx = fmaxf(mx, fabsf(o[i]));
+            }
             *reinterpret_cast<u32x4*>(dx + row * H + col) = pack8(o);
         }
     }
+    if (amax) block_max_to(mx, red, amax + row);
 }
 
 // dgamma partials.  Block (column block of 512, row chunk of DG_ROWS rows):
@@ -298,16 +327,16 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __res
 }
 
 template <int CH>
-int32_t launch_rms_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, bf16_t* xcopy, int T, int H, float eps,
-                       hipStream_t s) {
-    hipLaunchKernelGGL(rms_fwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, g, n, r, xcopy, H, eps);
+int32_t launch_rms_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, bf16_t* xcopy, float* amax, int T, int H,
+                       float eps, hipStream_t s) {
+    hipLaunchKernelGGL(rms_fwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, g, n, r, xcopy, amax, H, eps);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
 template <int CH>
 int32_t launch_rms_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn, const bf16_t* dres,
-                       bf16_t* dx, bf16_t* rescopy, int T, int H, hipStream_t s) {
-    hipLaunchKernelGGL(rms_bwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, r, g, dn, dres, dx, rescopy, H);
+                       bf16_t* dx, bf16_t* rescopy, float* amax, int T, int H, hipStream_t s) {
+    hipLaunchKernelGGL(rms_bwd_kernel<CH>, dim3(T), dim3(RT), 0, s, x, r, g, dn, dres, dx, rescopy, amax, H);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
@@ -315,21 +344,21 @@ int32_t launch_rms_bwd(const bf16_t* x, const float* r, const bf16_t* g, const b
 }  // namespace
 
 int32_t rmsnorm_fwd(const bf16_t* x, const bf16_t* g, bf16_t* n, float* r, int T, int H, float eps, hipStream_t s,
-                    bf16_t* xcopy) {
+                    bf16_t* xcopy, float* amax_rows) {
     if (H % 8 || H > 8 * RT * 4 || T <= 0) return fail(ZB_EINVAL, "rmsnorm: hidden must be a multiple of 8 and <= 8192");
     const int ch = (H / 8 + RT - 1) / RT;
-    if (ch <= 1) return launch_rms_fwd<1>(x, g, n, r, xcopy, T, H, eps, s);
-    if (ch <= 2) return launch_rms_fwd<2>(x, g, n, r, xcopy, T, H, eps, s);
-    return launch_rms_fwd<4>(x, g, n, r, xcopy, T, H, eps, s);
+    if (ch <= 1) return launch_rms_fwd<1>(x, g, n, r, xcopy, amax_rows, T, H, eps, s);
+    if (ch <= 2) return launch_rms_fwd<2>(x, g, n, r, xcopy, amax_rows, T, H, eps, s);
+    return launch_rms_fwd<4>(x, g, n, r, xcopy, amax_rows, T, H, eps, s);
 }
 
 int32_t rmsnorm_bwd(const bf16_t* x, const float* r, const bf16_t* g, const bf16_t* dn, const bf16_t* dres,
-                    bf16_t* dx, int T, int H, hipStream_t s, bf16_t* rescopy) {
+                    bf16_t* dx, int T, int H, hipStream_t s, bf16_t* rescopy, float* amax_rows) {
     if (H % 8 || H > 8 * RT * 4 || T <= 0) return fail(ZB_EINVAL, "rmsnorm: hidden must be a multiple of 8 and <= 8192");
     const int ch = (H / 8 + RT - 1) / RT;
-    if (ch <= 1) return launch_rms_bwd<1>(x, r, g, dn, dres, dx, rescopy, T, H, s);
-    if (ch <= 2) return launch_rms_bwd<2>(x, r, g, dn, dres, dx, rescopy, T, H, s);
-    return launch_rms_bwd<4>(x, r, g, dn, dres, dx, rescopy, T, H, s);
+    if (ch <= 1) return launch_rms_bwd<1>(x, r, g, dn, dres, dx, rescopy, amax_rows, T, H, s);
+    if (ch <= 2) return launch_rms_bwd<2>(x, r, g, dn, dres, dx, rescopy, amax_rows, T, H, s);
+    return launch_rms_bwd<4>(x, r, g, dn, dres, dx, rescopy, amax_rows, T, H, s);
 }
 
 int32_t transpose_bf16(const bf16_t* src, bf16_t* dst, int rows, int cols, hipStream_t s) {

@@ -13,6 +13,11 @@
 //   (pass scratch, the K-contiguous A operand of F's or B's product) and
 //   transposed [features][T] (ring slot, the K-contiguous operand of W's
 //   product).  The same tensor, the same exponent, the same codes.
+// * Its maximum comes from the kernel that wrote it where that kernel can
+//   give it cheaply: the RMSNorm kernels (forward and backward) leave one
+//   per row, the SwiGLU GEMM epilogues one per wave, and a one-workgroup
+//   kernel reduces them.  The attention outputs (a, dq|dk|dv) and the
+//   stage's incoming gradient take a pass over the tensor instead.
 // * Weights are quantized once per iteration (first F after creation or an
 //   optimizer step) into [out][in] codes (F's B operand, K = in) and
 //   [in][out] codes (B's B operand, K = out).
@@ -110,6 +115,15 @@ int32_t quantize_weights(zb_stage& st, hipStream_t s) {
 
 }  // namespace
 
+// Codes (row-major into q, transposed into qt) and exponent of a [rows, cols]
+// tensor whose producer wrote n partial maxima to part (capacity
+// st.lay.amax_cap, the reduced value right after it).
+static int32_t quantize_from(zb_stage& st, const bf16_t* x, int rows, int cols, uint8_t* q, uint8_t* qt, int32_t* e,
+                      float* part, int n, hipStream_t s) {
+    if (n > (int)st.lay.amax_cap) return fail(ZB_EINVAL, "fp8 stage: more partial maxima than the scratch holds");
+    return quantize_e4m3_from_partials(x, rows, cols, cols, q, cols, qt, rows, e, part, n, part + st.lay.amax_cap, s);
+}
+
 int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_t s) {
     const zb_stage_desc& d = st.desc;
     const Dims D = dims_of(d);
@@ -132,10 +146,11 @@ int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_
         int32_t* ex = i32(st.slot_tensor(mb, l, L_QEXP));
         void* out = (l == d.n_layers - 1) ? y : st.slot_tensor(mb, l + 1, L_X);
 
-        // layer 0 stashes the stage input as its norm reads it
-        if (l == 0) ZB_TRY(rmsnorm_fwd(cbf(x), cbf(w[4]), act, r1, T, H, d.rms_eps, s, xl));
-        else ZB_TRY(rmsnorm_fwd(xl, cbf(w[4]), act, r1, T, H, d.rms_eps, s));
-        ZB_TRY(quantize_e4m3(act, T, H, H, qrow, H, u8(st.slot_tensor(mb, l, L_N1T)), T, ex + Q_N1, part, s));
+        // layer 0 stashes the stage input as its norm reads it; the norms,
+        // and the SwiGLU product, leave the partial maxima of their outputs
+        if (l == 0) ZB_TRY(rmsnorm_fwd(cbf(x), cbf(w[4]), act, r1, T, H, d.rms_eps, s, xl, part));
+        else ZB_TRY(rmsnorm_fwd(xl, cbf(w[4]), act, r1, T, H, d.rms_eps, s, nullptr, part));
+        ZB_TRY(quantize_from(st, act, T, H, qrow, u8(st.slot_tensor(mb, l, L_N1T)), ex + Q_N1, part, T, s));
         ZB_TRY(gemm_fp8(q8(T, D.QKV, H, qrow, ex + Q_N1, wqkv.q, wqkv.e, qkv, D.QKV), s));
         ZB_TRY(attn_fwd(qkv, a, lse, T, d.n_heads, d.n_kv_heads, s));
         ZB_TRY(quantize_e4m3(a, T, D.QD, D.QD, qrow, D.QD, u8(st.slot_tensor(mb, l, L_AT)), T, ex + Q_A, part, s));
@@ -143,14 +158,16 @@ int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_
         go.R = xl;
         go.ldr = H;
         ZB_TRY(gemm_fp8(go, s));
-        ZB_TRY(rmsnorm_fwd(h1, cbf(w[5]), act, r2, T, H, d.rms_eps, s));
-        ZB_TRY(quantize_e4m3(act, T, H, H, qrow, H, u8(st.slot_tensor(mb, l, L_N2T)), T, ex + Q_N2, part, s));
+        ZB_TRY(rmsnorm_fwd(h1, cbf(w[5]), act, r2, T, H, d.rms_eps, s, nullptr, part));
+        ZB_TRY(quantize_from(st, act, T, H, qrow, u8(st.slot_tensor(mb, l, L_N2T)), ex + Q_N2, part, T, s));
         GemmDesc gg = q8(T, 2 * F, H, qrow, ex + Q_N2, wgu.q, wgu.e, gu, 2 * F, EPI_SWIGLU_FWD);
         gg.C2 = act;  // s = silu(g) u
         gg.ldc2 = F;
         gg.half_n = F;
-        ZB_TRY(gemm_fp8(gg, s));
-        ZB_TRY(quantize_e4m3(act, T, F, F, qrow, F, u8(st.slot_tensor(mb, l, L_ST)), T, ex + Q_S, part, s));
+        gg.amax = part;
+        int n_parts = 0;
+        ZB_TRY(gemm_fp8(gg, s, &n_parts, (int)st.lay.amax_cap));
+        ZB_TRY(quantize_from(st, act, T, F, qrow, u8(st.slot_tensor(mb, l, L_ST)), ex + Q_S, part, n_parts, s));
         GemmDesc gd = q8(T, H, F, qrow, ex + Q_S, wd.q, wd.e, out, H, EPI_RESID);
         gd.R = h1;
         gd.ldr = H;
@@ -190,24 +207,31 @@ int32_t run_backward_input_fp8(zb_stage& st, int mb, const void* dy, void* dx, h
         int32_t* ex = i32(st.slot_tensor(mb, l, L_QEXP));
         bf16_t* dest = (l == 0) ? bf(dx) : pingpong[l & 1];
 
-        ZB_TRY(quantize_e4m3(dout, T, H, H, qrow, H, u8(st.slot_tensor(mb, l, L_DOUTT)), T, ex + Q_DOUT, part, s));
+        // the incoming gradient gets a pass for its maximum; the other
+        // quantized tensors come with the partial maxima their producer left
+        // (below the last layer, dout is the previous layer's norm backward)
+        if (l == d.n_layers - 1)
+            ZB_TRY(quantize_e4m3(dout, T, H, H, qrow, H, u8(st.slot_tensor(mb, l, L_DOUTT)), T, ex + Q_DOUT, part, s));
+        else
+            ZB_TRY(quantize_from(st, dout, T, H, qrow, u8(st.slot_tensor(mb, l, L_DOUTT)), ex + Q_DOUT, part, T, s));
         // ds = dout . Wd  (Wd^T codes [F][H]), SwiGLU backward into [dg | du]
         GemmDesc gd = q8(T, F, H, qrow, ex + Q_DOUT, wd.qt, wd.e, dgu, 2 * F, EPI_SWIGLU_BWD);
         gd.R = gu;
         gd.ldr = 2 * F;
         gd.half_n = F;
-        ZB_TRY(gemm_fp8(gd, s));
-        ZB_TRY(quantize_e4m3(dgu, T, 2 * F, 2 * F, qrow, 2 * F, u8(st.slot_tensor(mb, l, L_DGUT)), T, ex + Q_DGU, part,
-                             s));
+        gd.amax = part;
+        int n_parts = 0;
+        ZB_TRY(gemm_fp8(gd, s, &n_parts, (int)st.lay.amax_cap));
+        ZB_TRY(quantize_from(st, dgu, T, 2 * F, qrow, u8(st.slot_tensor(mb, l, L_DGUT)), ex + Q_DGU, part, n_parts, s));
         ZB_TRY(gemm_fp8(q8(T, H, 2 * F, qrow, ex + Q_DGU, wgu.qt, wgu.e, dn2, H), s));
-        ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, dout, dh1, T, H, s));
-        ZB_TRY(quantize_e4m3(dh1, T, H, H, qrow, H, u8(st.slot_tensor(mb, l, L_DH1T)), T, ex + Q_DH1, part, s));
+        ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, dout, dh1, T, H, s, nullptr, part));
+        ZB_TRY(quantize_from(st, dh1, T, H, qrow, u8(st.slot_tensor(mb, l, L_DH1T)), ex + Q_DH1, part, T, s));
         ZB_TRY(gemm_fp8(q8(T, D.QD, H, qrow, ex + Q_DH1, wo.qt, wo.e, da, D.QD), s));
         ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, ascratch, T, d.n_heads, d.n_kv_heads, s));
         ZB_TRY(quantize_e4m3(dqkv, T, D.QKV, D.QKV, qrow, D.QKV, u8(st.slot_tensor(mb, l, L_DQKVT)), T, ex + Q_DQKV,
                              part, s));
         ZB_TRY(gemm_fp8(q8(T, H, D.QKV, qrow, ex + Q_DQKV, wqkv.qt, wqkv.e, dn1, H), s));
-        ZB_TRY(rmsnorm_bwd(xl, r1, cbf(w[4]), dn1, dh1, dest, T, H, s));
+        ZB_TRY(rmsnorm_bwd(xl, r1, cbf(w[4]), dn1, dh1, dest, T, H, s, nullptr, l > 0 ? part : nullptr));
         dout = dest;
     }
     return ZB_OK;

@@ -154,11 +154,15 @@ void Layout::build(const zb_stage_desc& d) {
     w8_e.clear();
     if (d.kind == ZB_LLAMA && d.dtype == ZB_FP8) {
         const size_t QD = (size_t)d.n_heads * d.head_dim, QKV = QD + 2 * (size_t)d.n_kv_heads * d.head_dim;
+        // partial maxima: the amax pass's, T of an RMSNorm, or 4 per workgroup
+        // of a SwiGLU product (at most ceil(T/128) x ceil(F/128) half-height
+        // tiles), then the reduced value
+        amax_cap = std::max({(size_t)AMAX_PARTS, T, ((T + 127) / 128) * ((F + 127) / 128) * 4});
         // F: one bf16 activation (n1, n2 or s), its row-major codes, amax partials
         f_act = 0;
         f_q = align_up(T * std::max(H, F) * 2);
         f_part = f_q + align_up(T * std::max({H, QD, F}));
-        scratch_f = f_part + align_up(AMAX_PARTS * 4);
+        scratch_f = f_part + align_up((amax_cap + 1) * 4);
         // B: after the bf16 stage's scratch, dg|du, dh1, dq|dk|dv, two
         // ping-pong output gradients, row-major codes, amax partials
         b_dgu = scratch_b;
@@ -168,7 +172,7 @@ void Layout::build(const zb_stage_desc& d) {
         b_dout[1] = b_dout[0] + align_up(T * H * 2);
         b_q = b_dout[1] + align_up(T * H * 2);
         b_part = b_q + align_up(T * std::max({2 * F, QKV, H}));
-        scratch_b = b_part + align_up(AMAX_PARTS * 4);
+        scratch_b = b_part + align_up((amax_cap + 1) * 4);
         // E4M3 copies [out][in] and [in][out] of every linear weight, one exponent each
         const int nw = 6 * d.n_layers;
         w8_q.assign(nw, 0);

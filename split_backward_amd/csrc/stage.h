@@ -37,6 +37,10 @@ struct Layout {
     size_t scratch_f = 0, w8_bytes = 0;
     size_t f_act = 0, f_q = 0, f_part = 0;                                  // F scratch
     size_t b_dgu = 0, b_dh1 = 0, b_dqkv = 0, b_dout[2] = {0, 0}, b_q = 0, b_part = 0;  // B scratch
+    // floats of partial maxima at f_part and b_part (the amax pass's, one per
+    // row of an RMSNorm, or one per wave of a SwiGLU GEMM launch), followed
+    // by the one float they reduce to
+    size_t amax_cap = 0;
     std::vector<size_t> w8_q, w8_qt, w8_e;                                  // per weight index (0 if none)
     // bf16 Llama stages: transposed copies [in][out] of the linear weights,
     // which the B pass reads so that its products have both operands

@@ -180,6 +180,15 @@ def test_fp8_stage_products_from_its_own_codes():
                                                zb.L_DH1T, zb.L_DQKVT)}
             e_of = dict(zip((zb.L_N1T, zb.L_AT, zb.L_N2T, zb.L_ST, zb.L_DOUTT, zb.L_DGUT, zb.L_DH1T, zb.L_DQKVT),
                             ex.tolist()))
+            # Each exponent is the smallest with max|x| <= 448 * 2^e, so
+            # max|x| 2^-e lies in (224, 448] and the largest code, its E4M3
+            # rounding, in [224, 448]: an exponent one too large leaves it at
+            # most 224, one too small saturates.  This holds whichever kernel
+            # found the maximum (a pass over the tensor, or the partial
+            # maxima its producer left).
+            for k, c in codes.items():
+                top = float(np.max(np.abs(o8.e4m3_decode(c))))
+                assert 224.0 <= top <= 448.0, (j, l, k, e_of[k], top)
             prod = lambda k, wi, tr=False: o8.product_nt(codes[k], e_of[k], W[wi][0].T if tr else W[wi][0], W[wi][1])
             w0 = 6 * l
             x = to_f64(T_(zb.L_X))
