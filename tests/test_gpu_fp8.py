@@ -326,6 +326,13 @@ def test_fp8_benchmark_configuration_sampled():
             T_ = lambda which: st.stash(j, l, which)
             ex = T_(zb.L_QEXP).cpu().numpy().ravel().tolist()
             e_n1, e_a, e_n2, e_s, e_dout, e_dgu, e_dh1, e_dqkv = ex
+            # every exponent the smallest that fits (largest code in [224, 448],
+            # as in the small-stage test), over each whole tensor; E4M3
+            # magnitudes order as their 7-bit codes (0x7f is NaN)
+            for k in (zb.L_N1T, zb.L_AT, zb.L_N2T, zb.L_ST, zb.L_DOUTT, zb.L_DGUT, zb.L_DH1T, zb.L_DQKVT):
+                top_code = int((T_(k) & 0x7F).max().item())
+                top = float(o8.e4m3_decode(np.array([top_code], dtype=np.uint8))[0])
+                assert 224.0 <= top <= 448.0, (j, l, k, top_code)
             w = 6 * l
             out = ys[j] if l == L - 1 else st.stash(j, l + 1, zb.L_X)
             check("qkv", T_(zb.L_QKV), T_(zb.L_N1T), e_n1, W8[w][0], W8[w][2])
