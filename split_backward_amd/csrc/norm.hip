@@ -199,19 +199,29 @@ __global__ __launch_bounds__(256) void dgamma_partial_kernel(const bf16_t* __res
     }
 }
 
-// dgamma += sum of the chunk partials, chunks in ascending order; four
-// independent partial sums per column keep the loads in flight.
+// dgamma += sum of the chunk partials.  A workgroup owns 64 columns; its four
+// waves each sum a quarter of the chunks (in ascending order, four
+// independent partial sums per column to keep loads in flight) and the
+// quarters are added in order: a fixed order, so deterministic, with four
+// times the loads in flight of one wave per column.
 __global__ __launch_bounds__(256) void dgamma_reduce_kernel(const float* __restrict__ part, float* __restrict__ dgamma,
                                                             int nchunks, int H) {
-    const int col = blockIdx.x * 256 + threadIdx.x;
-    if (col >= H) return;
+    __shared__ float red[4][64];
+    const int lc = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int col = blockIdx.x * 64 + lc;
+    const int per = (nchunks + 3) / 4;
+    const int c1 = min(nchunks, (q + 1) * per);
     float s[4] = {0.f, 0.f, 0.f, 0.f};
-    int c = 0;
-    for (; c + 4 <= nchunks; c += 4)
+    if (col < H) {
+        int c = q * per;
+        for (; c + 4 <= c1; c += 4)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s[k] += part[(int64_t)(c + k) * H + col];
-    for (; c < nchunks; ++c) s[0] += part[(int64_t)c * H + col];
-    dgamma[col] += (s[0] + s[1]) + (s[2] + s[3]);
+            for (int k = 0; k < 4; ++k) s[k] += part[(int64_t)(c + k) * H + col];
+        for (; c < c1; ++c) s[0] += part[(int64_t)c * H + col];
+    }
+    red[q][lc] = (s[0] + s[1]) + (s[2] + s[3]);
+    __syncthreads();
+    if (q == 0 && col < H) dgamma[col] += ((red[0][lc] + red[1][lc]) + red[2][lc]) + red[3][lc];
 }
 
 __global__ void fill_f32_kernel(float* p, size_t n, float v) {
@@ -377,7 +387,7 @@ int32_t rmsnorm_dgamma(const bf16_t* x, const float* r, const bf16_t* dn, float*
     const int nch = (T + DG_ROWS - 1) / DG_ROWS;
     hipLaunchKernelGGL(dgamma_partial_kernel, dim3((H + 511) / 512, nch), dim3(256), 0, s, x, r, dn, scratch, T, H);
     ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3((H + 255) / 256), dim3(256), 0, s, scratch, dgamma, nch, H);
+    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3((H + 63) / 64), dim3(256), 0, s, scratch, dgamma, nch, H);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
 }
