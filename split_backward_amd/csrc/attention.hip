@@ -241,15 +241,31 @@ __device__ __forceinline__ int xcd_item(int b, int n) {
     return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// Largest bf16 magnitude among the four values of two packed words (sign
+// bits cleared: magnitudes order as their bit patterns).  TRACK kernels (the
+// fp8 stage) fold it over every value they store and leave one maximum per
+// wave, from which the next product's quantization takes its exponent.
+__device__ __forceinline__ uint32_t mag_max(uint32_t m, const u32x2& v) {
+    const uint32_t a = v[0] & 0x7fff7fffu, b = v[1] & 0x7fff7fffu;
+    m = max(m, max(a & 0xffffu, a >> 16));
+    return max(m, max(b & 0xffffu, b >> 16));
+}
+// Wave maximum of m, written by lane 0 to *out as the bf16 value (a float).
+__device__ __forceinline__ void wave_mag_out(uint32_t m, float* out) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    if ((threadIdx.x & 63) == 0) *out = __uint_as_float(m << 16);
+}
+
 // ======================================================== forward ========
 constexpr int FQ = 128, FKV = 64, FTHR = 256;
 constexpr int KV_TILE = FKV * D * 2;  // 16 KB
 
 // One query block qb (32 NW queries, a wave's 32 each) of head h.
-template <int NW>
+template <int NW, bool TRACK = false>
 __device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_TILE], const bf16_t* __restrict__ qkv,
                                                bf16_t* __restrict__ o, float* __restrict__ lse, int T, int nq,
-                                               int nkv) {
+                                               int nkv, uint32_t& mx) {
     constexpr int QB = 32 * NW;  // queries per block
     const int ld = (nq + 2 * nkv) * D;
     const int grp = h / (nq / nkv);
@@ -383,6 +399,7 @@ __device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_
             v[0] = uint32_t(f2bf(oacc[db][rg * 4] * inv)) | (uint32_t(f2bf(oacc[db][rg * 4 + 1] * inv)) << 16);
             v[1] = uint32_t(f2bf(oacc[db][rg * 4 + 2] * inv)) | (uint32_t(f2bf(oacc[db][rg * 4 + 3] * inv)) << 16);
             *reinterpret_cast<u32x2*>(o + (int64_t)q * (nq * D) + h * D + d) = v;
+            if constexpr (TRACK) mx = mag_max(mx, v);
         }
     if (g == 0) lse[(int64_t)h * T + q] = m + log2f(l);
 }
@@ -394,19 +411,21 @@ __device__ __forceinline__ void attn_fwd_block(int qb, int h, char (*sm)[2 * KV_
 // of 256 queries per CU, whose eight waves share each K/V tile (half the
 // DMA per query of two 128-query workgroups); NW = 4 for token counts that
 // are not a multiple of 256.
-template <int NW>
+template <int NW, bool TRACK = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                                    bf16_t* __restrict__ o, float* __restrict__ lse,
-                                                                   int T, int nq, int nkv) {
+                                                                   int T, int nq, int nkv, float* __restrict__ amax) {
     __shared__ __attribute__((aligned(1024))) char sm[2][2 * KV_TILE];  // [stage][K | V]
     const int nb = T / (32 * NW), npair = (nb + 1) / 2;
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int h = item / npair, x = item % npair;
     const int a = nb - 1 - x, b = x;
+    uint32_t mx = 0;
     for (int pass = 0; pass < (b < a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();  // every wave is done with the stages
-        attn_fwd_block<NW>(pass ? b : a, h, sm, qkv, o, lse, T, nq, nkv);
+        attn_fwd_block<NW, TRACK>(pass ? b : a, h, sm, qkv, o, lse, T, nq, nkv, mx);
     }
+    if constexpr (TRACK) wave_mag_out(mx, amax + blockIdx.x * NW + (threadIdx.x >> 6));
 }
 
 // =================================================== delta kernel ========
@@ -472,9 +491,10 @@ struct DqSmem {
     char k[DQ_K_STAGES][KV_TILE];
     char s[DQ_S_STAGES][DS_STAGE];
 };
+template <bool TRACK = false>
 __device__ __forceinline__ void attn_dq_block(int qb, int h, DqSmem& sm, const bf16_t* __restrict__ qkv,
                                               const bf16_t* __restrict__ dst, bf16_t* __restrict__ dqkv, int T, int nq,
-                                              int nkv) {
+                                              int nkv, uint32_t& mx) {
     const int ld = (nq + 2 * nkv) * D;
     const int grp = h / (nq / nkv);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -562,22 +582,27 @@ __device__ __forceinline__ void attn_dq_block(int qb, int h, DqSmem& sm, const b
             v[0] = uint32_t(f2bf(dacc[db][rg * 4] * scale)) | (uint32_t(f2bf(dacc[db][rg * 4 + 1] * scale)) << 16);
             v[1] = uint32_t(f2bf(dacc[db][rg * 4 + 2] * scale)) | (uint32_t(f2bf(dacc[db][rg * 4 + 3] * scale)) << 16);
             *reinterpret_cast<u32x2*>(dqkv + (int64_t)q * ld + h * D + d) = v;
+            if constexpr (TRACK) mx = mag_max(mx, v);
         }
 }
 
 // Paired query blocks as in the forward kernel; 1-D grid, items head-major.
+template <bool TRACK = false>
 __global__ __launch_bounds__(FTHR, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
                                                           const bf16_t* __restrict__ dst,
-                                                          bf16_t* __restrict__ dqkv, int T, int nq, int nkv) {
+                                                          bf16_t* __restrict__ dqkv, int T, int nq, int nkv,
+                                                          float* __restrict__ amax) {
     __shared__ __attribute__((aligned(1024))) DqSmem sm;
     const int nb = T / FQ, npair = (nb + 1) / 2;
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int h = item / npair, x = item % npair;
     const int a = nb - 1 - x, b = x;
+    uint32_t mx = 0;
     for (int pass = 0; pass < (b < a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();
-        attn_dq_block(pass ? b : a, h, sm, qkv, dst, dqkv, T, nq, nkv);
+        attn_dq_block<TRACK>(pass ? b : a, h, sm, qkv, dst, dqkv, T, nq, nkv, mx);
     }
+    if constexpr (TRACK) wave_mag_out(mx, amax + blockIdx.x * (FTHR / 64) + (threadIdx.x >> 6));
 }
 
 // ===================================================== dk / dv kernel ====
@@ -596,13 +621,13 @@ constexpr int BQB = 32;
 constexpr int Q_TILE = BQB * D * 2;  // 8 KB
 constexpr int KV_STAGES = 2;
 
-template <int NW>
+template <int NW, bool TRACK = false>
 __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], char* svt, float (*sl)[2][BQB],
                                                const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dout,
                                                const float* __restrict__ lse, const float* __restrict__ delta,
                                                bf16_t* __restrict__ dqkv, float* __restrict__ part,
                                                bf16_t* __restrict__ dst, int T, int nq, int nkv, int grp, int zi,
-                                               int nz) {
+                                               int nz, uint32_t& mx) {
     const int ld = (nq + 2 * nkv) * D;
     const int ldo = nq * D;
     // The group's query heads split over nz workgroups (head subset zi);
@@ -818,19 +843,22 @@ __device__ __forceinline__ void attn_dkv_block(int kb, char (*sm)[2 * Q_TILE], c
             vv[1] = uint32_t(f2bf(dv[db][rg * 4 + 2])) | (uint32_t(f2bf(dv[db][rg * 4 + 3])) << 16);
             *reinterpret_cast<u32x2*>(dqkv + (int64_t)key * ld + nq * D + grp * D + d) = vk;
             *reinterpret_cast<u32x2*>(dqkv + (int64_t)key * ld + (nq + nkv) * D + grp * D + d) = vv;
+            if constexpr (TRACK) mx = mag_max(mag_max(mx, vk), vv);
         }
 }
 
 // Key block kb sweeps the query blocks at or after it: pairs kb with its
 // mirror so every workgroup does the same work.
-template <int NW>
+// TRACK (with part null): the waves' maxima of the dK, dV they store go to
+// amax[NW * workgroup + wave].
+template <int NW, bool TRACK = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
                                                                    const bf16_t* __restrict__ dout,
                                                                    const float* __restrict__ lse,
                                                                    const float* __restrict__ delta,
                                                                    bf16_t* __restrict__ dqkv, float* __restrict__ part,
                                                                    bf16_t* __restrict__ dst, int T, int nq, int nkv,
-                                                                   int nz) {
+                                                                   int nz, float* __restrict__ amax) {
     __shared__ __attribute__((aligned(1024))) char sm[KV_STAGES][2 * Q_TILE];  // [stage][Q | dO]
     __shared__ __attribute__((aligned(1024))) char svt[32 * NW * D * 2];       // V rows of the block
     __shared__ float sl[KV_STAGES][2][BQB];                                     // [stage][lse | delta]
@@ -839,18 +867,45 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_dkv_kernel(const bf16_t*
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int x = item % npair, zi = (item / npair) % nz, grp = item / (npair * nz);
     const int a = x, b = nb - 1 - x;  // a: the longer sweep
+    uint32_t mx = 0;
     for (int pass = 0; pass < (b > a ? 2 : 1); ++pass) {
         if (pass) wg_barrier();
-        attn_dkv_block<NW>(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, part, dst, T, nq, nkv, grp, zi, nz);
+        attn_dkv_block<NW, TRACK>(pass ? b : a, sm, svt, sl, qkv, dout, lse, delta, dqkv, part, dst, T, nq, nkv, grp,
+                                  zi, nz, mx);
     }
+    if constexpr (TRACK) wave_mag_out(mx, amax + blockIdx.x * NW + (threadIdx.x >> 6));
 }
 
 // dK = scale * sum_z part[z][.][.][0], dV = sum_z part[z][.][.][1], summed in
 // subset order (deterministic); one thread per 4 consecutive elements.
+// TRACK: the waves' maxima of what they store go to amax[4 * workgroup + wave].
+template <bool TRACK = false>
 __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(const float* __restrict__ part, bf16_t* __restrict__ dqkv,
-                                                              int T, int nq, int nkv, int nsplit) {
+                                                              int T, int nq, int nkv, int nsplit,
+                                                              float* __restrict__ amax) {
     const int64_t per = (int64_t)T * nkv * 2 * D;  // floats per subset
     const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (TRACK) {
+        // every lane reaches the wave's maximum: lanes past the end add zero
+        uint32_t mx = 0;
+        if (i4 < per) {
+            floatx4 acc = *reinterpret_cast<const floatx4*>(part + i4);
+            for (int z = 1; z < nsplit; ++z) acc += *reinterpret_cast<const floatx4*>(part + z * per + i4);
+            const int d = (int)(i4 % D);
+            const int which = (int)((i4 / D) % 2);
+            const int grp = (int)((i4 / (2 * D)) % nkv);
+            const int key = (int)(i4 / (2 * D * nkv));
+            const float sc = which == 0 ? 1.f / sqrtf((float)D) : 1.f;
+            u32x2 v;
+            v[0] = uint32_t(f2bf(acc[0] * sc)) | (uint32_t(f2bf(acc[1] * sc)) << 16);
+            v[1] = uint32_t(f2bf(acc[2] * sc)) | (uint32_t(f2bf(acc[3] * sc)) << 16);
+            const int ld = (nq + 2 * nkv) * D;
+            *reinterpret_cast<u32x2*>(dqkv + (int64_t)key * ld + (nq + which * nkv + grp) * D + d) = v;
+            mx = mag_max(mx, v);
+        }
+        wave_mag_out(mx, amax + blockIdx.x * 4 + (threadIdx.x >> 6));
+        return;
+    }
     if (i4 >= per) return;
     floatx4 acc = *reinterpret_cast<const floatx4*>(part + i4);
     for (int z = 1; z < nsplit; ++z) acc += *reinterpret_cast<const floatx4*>(part + z * per + i4);
@@ -888,13 +943,40 @@ size_t ds_bytes(int T, int nq) { return ((size_t)nq * T * T * 2 + 255) / 256 * 2
 
 }  // namespace
 
-int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s) {
+// Grids of the launches below (workgroups), shared with the partial-maxima counts.
+namespace {
+int fwd_grid(int T, int nq) { return T % 256 == 0 ? (T / 256 + 1) / 2 * nq : (T / 128 + 1) / 2 * nq; }
+int dkv_grid(int T, int nkv, int z) { return dkv_waves(T) == 8 ? (T / 256 + 1) / 2 * nkv * z : (T / 128 + 1) / 2 * nkv * z; }
+int64_t reduce_grid(int T, int nkv) { return ((int64_t)T * nkv * 2 * D / 4 + 255) / 256; }
+int dq_grid(int T, int nq) { return (T / FQ + 1) / 2 * nq; }
+int fwd_parts(int T, int nq) { return fwd_grid(T, nq) * (T % 256 == 0 ? 8 : 4); }
+int64_t bwd_parts(int T, int nq, int nkv) {
+    const int z = dkv_split(T, nq, nkv);
+    return (z > 1 ? reduce_grid(T, nkv) * 4 : (int64_t)dkv_grid(T, nkv, z) * dkv_waves(T)) + dq_grid(T, nq) * (FTHR / 64);
+}
+}  // namespace
+
+int64_t attn_amax_parts(int T, int nq, int nkv) {
+    if (!shapes_ok(T, nq, nkv)) return 0;
+    return std::max<int64_t>(fwd_parts(T, nq), bwd_parts(T, nq, nkv));
+}
+
+int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s, float* amax,
+                 int* amax_n) {
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
-    if (T % 256 == 0)
-        hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3((T / 256 + 1) / 2 * nq), dim3(512), 0, s, qkv, o, lse, T, nq, nkv);
-    else
-        hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3((T / 128 + 1) / 2 * nq), dim3(256), 0, s, qkv, o, lse, T, nq, nkv);
+    const dim3 grid(fwd_grid(T, nq));
+    if (amax) {
+        if (T % 256 == 0)
+            hipLaunchKernelGGL((attn_fwd_kernel<8, true>), grid, dim3(512), 0, s, qkv, o, lse, T, nq, nkv, amax);
+        else
+            hipLaunchKernelGGL((attn_fwd_kernel<4, true>), grid, dim3(256), 0, s, qkv, o, lse, T, nq, nkv, amax);
+    } else if (T % 256 == 0) {
+        hipLaunchKernelGGL(attn_fwd_kernel<8>, grid, dim3(512), 0, s, qkv, o, lse, T, nq, nkv, nullptr);
+    } else {
+        hipLaunchKernelGGL(attn_fwd_kernel<4>, grid, dim3(256), 0, s, qkv, o, lse, T, nq, nkv, nullptr);
+    }
     ZB_HIP(hipGetLastError());
+    if (amax_n) *amax_n = amax ? fwd_parts(T, nq) : 0;
     return ZB_OK;
 }
 
@@ -905,7 +987,7 @@ size_t attn_bwd_scratch_bytes(int T, int nq, int nkv) {
 }
 
 int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout, bf16_t* dqkv, float* delta,
-                 void* scratch, int T, int nq, int nkv, hipStream_t s) {
+                 void* scratch, int T, int nq, int nkv, hipStream_t s, float* amax, int* amax_n) {
     if (!shapes_ok(T, nq, nkv)) return fail(ZB_EINVAL, "attention: tokens must be a multiple of 128");
     if (scratch == nullptr) return fail(ZB_EINVAL, "attention: missing backward scratch");
     bf16_t* dst = static_cast<bf16_t*>(scratch);
@@ -915,23 +997,47 @@ int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf1
     const int64_t pairs = (int64_t)T * nq;
     hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, s, o, dout, delta, T, nq);
     ZB_HIP(hipGetLastError());
-    // dK, dV (or their per-subset partials) and dS^T
-    if (dkv_waves(T) == 8)
-        hipLaunchKernelGGL(attn_dkv_kernel<8>, dim3((T / 256 + 1) / 2 * nkv * z), dim3(512), 0, s, qkv, dout, lse,
-                           delta, dqkv, part, dst, T, nq, nkv, z);
-    else
-        hipLaunchKernelGGL(attn_dkv_kernel<4>, dim3((T / 128 + 1) / 2 * nkv * z), dim3(256), 0, s, qkv, dout, lse,
-                           delta, dqkv, part, dst, T, nq, nkv, z);
+    // dK, dV (or their per-subset partials) and dS^T; with amax, the kernel
+    // that stores dK, dV (this one, or the reduction) leaves its maxima first,
+    // the dq kernel's follow
+    const bool track_dkv = amax && z == 1;
+    const dim3 g_dkv(dkv_grid(T, nkv, z));
+    if (dkv_waves(T) == 8) {
+        if (track_dkv)
+            hipLaunchKernelGGL((attn_dkv_kernel<8, true>), g_dkv, dim3(512), 0, s, qkv, dout, lse, delta, dqkv, part,
+                               dst, T, nq, nkv, z, amax);
+        else
+            hipLaunchKernelGGL(attn_dkv_kernel<8>, g_dkv, dim3(512), 0, s, qkv, dout, lse, delta, dqkv, part, dst, T,
+                               nq, nkv, z, nullptr);
+    } else {
+        if (track_dkv)
+            hipLaunchKernelGGL((attn_dkv_kernel<4, true>), g_dkv, dim3(256), 0, s, qkv, dout, lse, delta, dqkv, part,
+                               dst, T, nq, nkv, z, amax);
+        else
+            hipLaunchKernelGGL(attn_dkv_kernel<4>, g_dkv, dim3(256), 0, s, qkv, dout, lse, delta, dqkv, part, dst, T,
+                               nq, nkv, z, nullptr);
+    }
     ZB_HIP(hipGetLastError());
+    int64_t n_parts = track_dkv ? (int64_t)dkv_grid(T, nkv, z) * dkv_waves(T) : 0;
     if (z > 1) {
-        const int64_t n4 = (int64_t)T * nkv * 2 * D / 4;
-        hipLaunchKernelGGL(attn_dkv_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, part, dqkv, T,
-                           nq, nkv, z);
+        const dim3 g_red((unsigned)reduce_grid(T, nkv));
+        if (amax) {
+            hipLaunchKernelGGL((attn_dkv_reduce_kernel<true>), g_red, dim3(256), 0, s, part, dqkv, T, nq, nkv, z, amax);
+            n_parts = reduce_grid(T, nkv) * 4;
+        } else {
+            hipLaunchKernelGGL(attn_dkv_reduce_kernel<false>, g_red, dim3(256), 0, s, part, dqkv, T, nq, nkv, z,
+                               nullptr);
+        }
         ZB_HIP(hipGetLastError());
     }
     // dQ = dS K from the scratch
-    hipLaunchKernelGGL(attn_dq_kernel, dim3((T / FQ + 1) / 2 * nq), dim3(FTHR), 0, s, qkv, dst, dqkv, T, nq, nkv);
+    const dim3 g_dq(dq_grid(T, nq));
+    if (amax)
+        hipLaunchKernelGGL((attn_dq_kernel<true>), g_dq, dim3(FTHR), 0, s, qkv, dst, dqkv, T, nq, nkv, amax + n_parts);
+    else
+        hipLaunchKernelGGL(attn_dq_kernel<false>, g_dq, dim3(FTHR), 0, s, qkv, dst, dqkv, T, nq, nkv, nullptr);
     ZB_HIP(hipGetLastError());
+    if (amax_n) *amax_n = amax ? (int)(n_parts + (int64_t)dq_grid(T, nq) * (FTHR / 64)) : 0;
     return ZB_OK;
 }
 

@@ -172,14 +172,21 @@ size_t rmsnorm_dgamma_scratch_floats(int T, int H);
 // -------------------------------------------------------------- attention --
 // Causal GQA attention, head_dim 128.  q/k/v are column blocks of the packed
 // qkv [T, (nq + 2 nkv) * 128] buffer; o [T, nq*128]; lse f32 [nq, T].
-int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s);
+// With `amax` set, every wave that stores o also leaves the largest magnitude
+// it stored (a bf16 value widened to f32) in amax[0 .. *amax_n); the count is
+// at most attn_amax_parts(T, nq, nkv).
+int32_t attn_fwd(const bf16_t* qkv, bf16_t* o, float* lse, int T, int nq, int nkv, hipStream_t s,
+                 float* amax = nullptr, int* amax_n = nullptr);
+int64_t attn_amax_parts(int T, int nq, int nkv);
 // dqkv [T, (nq + 2 nkv)*128]; delta scratch f32 [nq, T]; scratch: device
 // memory of attn_bwd_scratch_bytes(T, nq, nkv) bytes (dS^T in bf16
 // [nq][T][T], then fp32 partial dK, dV when the query heads of a KV head are
 // split over workgroups).
 size_t attn_bwd_scratch_bytes(int T, int nq, int nkv);
+// `amax`, `amax_n`: as for attn_fwd, over every element of dqkv.
 int32_t attn_bwd(const bf16_t* qkv, const bf16_t* o, const float* lse, const bf16_t* dout,
-                 bf16_t* dqkv, float* delta, void* scratch, int T, int nq, int nkv, hipStream_t s);
+                 bf16_t* dqkv, float* delta, void* scratch, int T, int nq, int nkv, hipStream_t s,
+                 float* amax = nullptr, int* amax_n = nullptr);
 
 // ---------------------------------------------------------------- debug ---
 // Ring-slot tags (debug.hip): tags[slot] = 4 * mb + phase (1 F, 2 B, 3 W

@@ -15,9 +15,10 @@
 //   product).  The same tensor, the same exponent, the same codes.
 // * Its maximum comes from the kernel that wrote it where that kernel can
 //   give it cheaply: the RMSNorm kernels (forward and backward) leave one
-//   per row, the SwiGLU GEMM epilogues one per wave, and a one-workgroup
-//   kernel reduces them.  The attention outputs (a, dq|dk|dv) and the
-//   stage's incoming gradient take a pass over the tensor instead.
+//   per row, the SwiGLU GEMM epilogues and the attention kernels one per
+//   storing wave, and a one-workgroup kernel reduces them.  Only the
+//   stage's incoming gradient, written outside the stage, takes a pass over
+//   the tensor instead.
 // * Weights are quantized once per iteration (first F after creation or an
 //   optimizer step) into [out][in] codes (F's B operand, K = in) and
 //   [in][out] codes (B's B operand, K = out).
@@ -124,6 +125,17 @@ static int32_t quantize_from(zb_stage& st, const bf16_t* x, int rows, int cols, 
     return quantize_e4m3_from_partials(x, rows, cols, cols, q, cols, qt, rows, e, part, n, part + st.lay.amax_cap, s);
 }
 
+// The attention forward with its output's partial maxima, after checking
+// that they fit.
+static int32_t attn_fwd_tracked(zb_stage& st, const bf16_t* qkv, bf16_t* a, float* lse, float* part, int* n,
+                                hipStream_t s) {
+    const zb_stage_desc& d = st.desc;
+    const int T = dims_of(d).T;
+    if (attn_amax_parts(T, d.n_heads, d.n_kv_heads) > (int64_t)st.lay.amax_cap)
+        return fail(ZB_EINVAL, "fp8 stage: more partial maxima than the scratch holds");
+    return attn_fwd(qkv, a, lse, T, d.n_heads, d.n_kv_heads, s, part, n);
+}
+
 int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_t s) {
     const zb_stage_desc& d = st.desc;
     const Dims D = dims_of(d);
@@ -152,8 +164,9 @@ int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_
         else ZB_TRY(rmsnorm_fwd(xl, cbf(w[4]), act, r1, T, H, d.rms_eps, s, nullptr, part));
         ZB_TRY(quantize_from(st, act, T, H, qrow, u8(st.slot_tensor(mb, l, L_N1T)), ex + Q_N1, part, T, s));
         ZB_TRY(gemm_fp8(q8(T, D.QKV, H, qrow, ex + Q_N1, wqkv.q, wqkv.e, qkv, D.QKV), s));
-        ZB_TRY(attn_fwd(qkv, a, lse, T, d.n_heads, d.n_kv_heads, s));
-        ZB_TRY(quantize_e4m3(a, T, D.QD, D.QD, qrow, D.QD, u8(st.slot_tensor(mb, l, L_AT)), T, ex + Q_A, part, s));
+        int n_parts = 0;
+        ZB_TRY(attn_fwd_tracked(st, qkv, a, lse, part, &n_parts, s));
+        ZB_TRY(quantize_from(st, a, T, D.QD, qrow, u8(st.slot_tensor(mb, l, L_AT)), ex + Q_A, part, n_parts, s));
         GemmDesc go = q8(T, H, D.QD, qrow, ex + Q_A, wo.q, wo.e, h1, H, EPI_RESID);
         go.R = xl;
         go.ldr = H;
@@ -165,7 +178,6 @@ int32_t run_forward_fp8(zb_stage& st, int mb, const void* x, void* y, hipStream_
         gg.ldc2 = F;
         gg.half_n = F;
         gg.amax = part;
-        int n_parts = 0;
         ZB_TRY(gemm_fp8(gg, s, &n_parts, (int)st.lay.amax_cap));
         ZB_TRY(quantize_from(st, act, T, F, qrow, u8(st.slot_tensor(mb, l, L_ST)), ex + Q_S, part, n_parts, s));
         GemmDesc gd = q8(T, H, F, qrow, ex + Q_S, wd.q, wd.e, out, H, EPI_RESID);
@@ -227,9 +239,11 @@ int32_t run_backward_input_fp8(zb_stage& st, int mb, const void* dy, void* dx, h
         ZB_TRY(rmsnorm_bwd(h1, r2, cbf(w[5]), dn2, dout, dh1, T, H, s, nullptr, part));
         ZB_TRY(quantize_from(st, dh1, T, H, qrow, u8(st.slot_tensor(mb, l, L_DH1T)), ex + Q_DH1, part, T, s));
         ZB_TRY(gemm_fp8(q8(T, D.QD, H, qrow, ex + Q_DH1, wo.qt, wo.e, da, D.QD), s));
-        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, ascratch, T, d.n_heads, d.n_kv_heads, s));
-        ZB_TRY(quantize_e4m3(dqkv, T, D.QKV, D.QKV, qrow, D.QKV, u8(st.slot_tensor(mb, l, L_DQKVT)), T, ex + Q_DQKV,
-                             part, s));
+        if (attn_amax_parts(T, d.n_heads, d.n_kv_heads) > (int64_t)st.lay.amax_cap)
+            return fail(ZB_EINVAL, "fp8 stage: more partial maxima than the scratch holds");
+        ZB_TRY(attn_bwd(qkv, a, lse, da, dqkv, delta, ascratch, T, d.n_heads, d.n_kv_heads, s, part, &n_parts));
+        ZB_TRY(quantize_from(st, dqkv, T, D.QKV, qrow, u8(st.slot_tensor(mb, l, L_DQKVT)), ex + Q_DQKV, part, n_parts,
+                             s));
         ZB_TRY(gemm_fp8(q8(T, H, D.QKV, qrow, ex + Q_DQKV, wqkv.qt, wqkv.e, dn1, H), s));
         ZB_TRY(rmsnorm_bwd(xl, r1, cbf(w[4]), dn1, dh1, dest, T, H, s, nullptr, l > 0 ? part : nullptr));
         dout = dest;

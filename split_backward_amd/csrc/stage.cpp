@@ -154,10 +154,12 @@ void Layout::build(const zb_stage_desc& d) {
     w8_e.clear();
     if (d.kind == ZB_LLAMA && d.dtype == ZB_FP8) {
         const size_t QD = (size_t)d.n_heads * d.head_dim, QKV = QD + 2 * (size_t)d.n_kv_heads * d.head_dim;
-        // partial maxima: the amax pass's, T of an RMSNorm, or 4 per workgroup
+        // partial maxima: the amax pass's, T of an RMSNorm, 4 per workgroup
         // of a SwiGLU product (at most ceil(T/128) x ceil(F/128) half-height
-        // tiles), then the reduced value
-        amax_cap = std::max({(size_t)AMAX_PARTS, T, ((T + 127) / 128) * ((F + 127) / 128) * 4});
+        // tiles) or one per storing wave of the attention kernels, then the
+        // reduced value
+        amax_cap = std::max({(size_t)AMAX_PARTS, T, ((T + 127) / 128) * ((F + 127) / 128) * 4,
+                             (size_t)attn_amax_parts((int)T, d.n_heads, d.n_kv_heads)});
         // F: one bf16 activation (n1, n2 or s), its row-major codes, amax partials
         f_act = 0;
         f_q = align_up(T * std::max(H, F) * 2);
