@@ -98,17 +98,38 @@ __device__ __forceinline__ int scale_exponent(float amax) {
     return f <= 0.875f ? x - 9 : x - 8;
 }
 
-// One 64 x 64 tile per block (blockIdx.x: column tile, blockIdx.y: row
-// tile); thread t converts 16 consecutive columns of row t / 4.  rows and
-// cols are multiples of 16.  Codes of four values go into one dword with two
-// packed conversions.
+// One QR x 64 tile per block (QR = 64 RG; blockIdx.x: column tile,
+// blockIdx.y: row tile); thread t converts 16 consecutive columns of rows
+// t / 4 + 64 g, g < RG.  rows and cols are multiples of 16.  Codes of four
+// values go into one dword with two packed conversions.
+template <int RG>
 __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict__ x, int rows, int cols, int64_t ld,
                                                        const float* __restrict__ part, int nparts,
                                                        int32_t* __restrict__ e_out, uint8_t* __restrict__ q,
                                                        int64_t ldq, uint8_t* __restrict__ qt, int64_t ldqt) {
-    __shared__ uint32_t tile[QT][QT / 4 + 1];  // codes, 4 per word, padded row
+    constexpr int QR = 64 * RG;
+    __shared__ uint32_t tile[QR][QT / 4 + 1];  // codes, 4 per word, padded row
     __shared__ float red[4];
     const int tid = threadIdx.x;
+    const int r0 = blockIdx.y * QR, c0 = blockIdx.x * QT;
+    const int rr = tid >> 2, cc = (tid & 3) * 16;
+    const int c = c0 + cc;
+    // the tile's values are requested before the partial maxima, so that a
+    // block waits for one memory round trip, not two in a row
+    u32x4 a[RG], b[RG];
+    bool in[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int r = r0 + rr + 64 * g;
+        in[g] = r < rows && c < cols;
+        a[g] = u32x4{0u, 0u, 0u, 0u};
+        b[g] = u32x4{0u, 0u, 0u, 0u};
+        if (in[g]) {
+            const bf16_t* src = x + (int64_t)r * ld + c;
+            a[g] = *reinterpret_cast<const u32x4*>(src);
+            b[g] = *reinterpret_cast<const u32x4*>(src + 8);
+        }
+    }
     // every block reduces the partial maxima itself (the same values in the
     // same order, so the same exponent); block (0, 0) publishes it
     float am = 0.f;
@@ -119,50 +140,55 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
     const int e = scale_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
     if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) *e_out = e;
     const int ne = -e;  // x * 2^-e with v_ldexp_f32: exact, whatever the range of 2^-e
-    const int r0 = blockIdx.y * QT, c0 = blockIdx.x * QT;
-    const int rr = tid >> 2, cc = (tid & 3) * 16;
-    const int r = r0 + rr, c = c0 + cc;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (r < rows && c < cols) {
-        const bf16_t* src = x + (int64_t)r * ld + c;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(src);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(src + 8);
-        const uint32_t v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float f0 = __builtin_ldexpf(__uint_as_float(v[2 * k] << 16), ne);
-            const float f1 = __builtin_ldexpf(__uint_as_float(v[2 * k] & 0xffff0000u), ne);
-            const float f2 = __builtin_ldexpf(__uint_as_float(v[2 * k + 1] << 16), ne);
-            const float f3 = __builtin_ldexpf(__uint_as_float(v[2 * k + 1] & 0xffff0000u), ne);
-            int p = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, p, true);
-            w[k] = (uint32_t)p;
+    for (int g = 0; g < RG; ++g) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (in[g]) {
+            const uint32_t v[8] = {a[g][0], a[g][1], a[g][2], a[g][3], b[g][0], b[g][1], b[g][2], b[g][3]};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float f0 = __builtin_ldexpf(__uint_as_float(v[2 * k] << 16), ne);
+                const float f1 = __builtin_ldexpf(__uint_as_float(v[2 * k] & 0xffff0000u), ne);
+                const float f2 = __builtin_ldexpf(__uint_as_float(v[2 * k + 1] << 16), ne);
+                const float f3 = __builtin_ldexpf(__uint_as_float(v[2 * k + 1] & 0xffff0000u), ne);
+                int p = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+                p = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, p, true);
+                w[k] = (uint32_t)p;
+            }
+            if (q) *reinterpret_cast<u32x4*>(q + (int64_t)(r0 + rr + 64 * g) * ldq + c) = u32x4{w[0], w[1], w[2], w[3]};
         }
-        if (q) *reinterpret_cast<u32x4*>(q + (int64_t)r * ldq + c) = u32x4{w[0], w[1], w[2], w[3]};
+        if (qt) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tile[rr + 64 * g][cc / 4 + k] = w[k];
+        }
     }
     if (!qt) return;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) tile[rr][cc / 4 + k] = w[k];
     __syncthreads();
     // transposed: thread t writes 16 codes of output row c0 + t / 4 (input
-    // column), input rows r0 + (t % 4) * 16 .. + 15
-    const int oc = tid >> 2, orow = (tid & 3) * 16;
-    const int gc = c0 + oc, gr = r0 + orow;
-    if (gc < cols && gr < rows) {
-        uint32_t o[4];
+    // column) for each g: input rows r0 + (t % 4) * 16 + 64 g .. + 15
+    const int oc = tid >> 2, gc = c0 + oc;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t acc = 0u;
+    for (int g = 0; g < RG; ++g) {
+        const int orow = (tid & 3) * 16 + 64 * g, gr = r0 + orow;
+        if (gc < cols && gr < rows) {
+            uint32_t o[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t word = tile[orow + 4 * k + j][oc >> 2];
-                acc |= ((word >> (8 * (oc & 3))) & 0xffu) << (8 * j);
+            for (int k = 0; k < 4; ++k) {
+                uint32_t acc = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t word = tile[orow + 4 * k + j][oc >> 2];
+                    acc |= ((word >> (8 * (oc & 3))) & 0xffu) << (8 * j);
+                }
+                o[k] = acc;
             }
-            o[k] = acc;
+            *reinterpret_cast<u32x4*>(qt + (int64_t)gc * ldqt + gr) = u32x4{o[0], o[1], o[2], o[3]};
         }
-        *reinterpret_cast<u32x4*>(qt + (int64_t)gc * ldqt + gr) = u32x4{o[0], o[1], o[2], o[3]};
     }
 }
+
+// Rows per quantize tile: 64 QRG.
+constexpr int QRG = 2;
 
 }  // namespace
 
@@ -180,7 +206,7 @@ int32_t quantize_e4m3(const bf16_t* x, int rows, int cols, int64_t ld, uint8_t* 
     const int nparts = (int)std::min<int64_t>(AMAX_PARTS, (chunks + 1023) / 1024);
     hipLaunchKernelGGL(amax_partial_kernel, dim3(nparts), dim3(256), 0, s, x, rows, cols, ld, part);
     ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(quantize_kernel, dim3((cols + QT - 1) / QT, (rows + QT - 1) / QT), dim3(256), 0, s, x, rows,
+    hipLaunchKernelGGL(quantize_kernel<QRG>, dim3((cols + QT - 1) / QT, (rows + 64 * QRG - 1) / (64 * QRG)), dim3(256), 0, s, x, rows,
                        cols, ld, part, nparts, e_out, q, ldq, qt, ldqt);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
@@ -198,7 +224,7 @@ int32_t quantize_e4m3_from_partials(const bf16_t* x, int rows, int cols, int64_t
         return fail(ZB_EINVAL, "quantize_e4m3: pointers must be 16-byte aligned");
     hipLaunchKernelGGL(amax_reduce_kernel, dim3(1), dim3(1024), 0, s, part, nparts, amax);
     ZB_HIP(hipGetLastError());
-    hipLaunchKernelGGL(quantize_kernel, dim3((cols + QT - 1) / QT, (rows + QT - 1) / QT), dim3(256), 0, s, x, rows,
+    hipLaunchKernelGGL(quantize_kernel<QRG>, dim3((cols + QT - 1) / QT, (rows + 64 * QRG - 1) / (64 * QRG)), dim3(256), 0, s, x, rows,
                        cols, ld, amax, 1, e_out, q, ldq, qt, ldqt);
     ZB_HIP(hipGetLastError());
     return ZB_OK;
