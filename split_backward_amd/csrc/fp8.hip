@@ -14,12 +14,13 @@
 //   amax_partial_kernel   max|x| of grid-strided 16-byte chunks -> up to
 //                         AMAX_PARTS partial maxima
 //   quantize_kernel       the exponent from the partials (every block), then
-//                         64 x 64 tiles: codes row-major [rows][cols] and/or
+//                         128 x 64 tiles: codes row-major [rows][cols] and/or
 //                         transposed [cols][rows] (through LDS), so that a
 //                         product's K index is contiguous whichever operand
 //                         the tensor becomes.
 // Where the kernel that wrote x already produced partial maxima (the RMSNorm
-// kernels per row, the SwiGLU GEMM epilogues per wave), amax_reduce_kernel
+// kernels per row, the SwiGLU GEMM epilogues and the attention kernels per
+// storing wave), amax_reduce_kernel
 // folds them into one value instead of the pass over x.
 #include <algorithm>
 #include <cmath>
