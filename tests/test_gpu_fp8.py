@@ -215,6 +215,26 @@ def test_fp8_stage_products_from_its_own_codes(shape):
             S.record("dgu codes", o8.dequantize(codes[zb.L_DGUT], e_of[zb.L_DGUT]), np.concatenate([dg, du], 1),
                      2.0 ** -4 + 5e-3)
             S.record("gate/up bwd", to_f64(T_(zb.L_DN2)), prod(zb.L_DGUT, w0 + 2, tr=True), 5e-3)
+            # the attention outputs' codes against what they encode (their
+            # exponents come from the attention kernels' partial maxima: one
+            # that missed the wave holding the maximum would leave the
+            # exponent too small, and the largest values saturated): a against
+            # the stashed bf16 a, dq|dk|dv against the oracle's attention
+            # backward of the stashed q, k, v with da = q(dh1) q(Wo)
+            S.record("a codes", o8.dequantize(codes[zb.L_AT], e_of[zb.L_AT]), to_f64(T_(zb.L_A)), 2.0 ** -4)
+            nq, nkv, hd = shape.n_heads, shape.n_kv_heads, shape.head_dim
+            qkv = to_f64(T_(zb.L_QKV))
+            QD, KVD = nq * hd, nkv * hd
+            q_, k_, v_ = qkv[:, :QD], qkv[:, QD:QD + KVD], qkv[:, QD + KVD:]
+            da = prod(zb.L_DH1T, w0 + 1, tr=True)
+            dqkv = np.zeros_like(qkv)
+            for h in range(nq):
+                g = h // (nq // nkv)
+                dqh, dkp, dvp = od.attn_head_bwd(q_, k_, v_, da, h, nq, nkv, hd)
+                dqkv[:, h * hd:(h + 1) * hd] = dqh
+                dqkv[:, QD + g * hd:QD + (g + 1) * hd] += dkp
+                dqkv[:, QD + KVD + g * hd:QD + KVD + (g + 1) * hd] += dvp
+            S.record("dqkv codes", o8.dequantize(codes[zb.L_DQKVT], e_of[zb.L_DQKVT]), dqkv, 2.0 ** -4 + 2e-2)
             S.record("qkv bwd", to_f64(T_(zb.L_DN1)), prod(zb.L_DQKVT, w0, tr=True), 5e-3)
             if l == L - 1:
                 S.record("dout codes", o8.dequantize(codes[zb.L_DOUTT], e_of[zb.L_DOUTT]), to_f64(dyd[j]), 2.0 ** -4)
